@@ -1,0 +1,262 @@
+"""Pins of the oracle's FP8 decode and scale-then-cast (CPU only).
+
+Cast definition: "Training and inference of large language models using 8-bit
+floating point", review page, "Proposed method", bullets 3-4 (scale the input
+before the FP8 cast; E4 for weights/activations, E5 for gradients).  Rounding
+to nearest with ties to the even code, saturation, kept subnormals, signed
+zero and NaN -> 0x7F|sign are the readings this library takes.
+
+Independent references used here, none of which shares code with the oracle:
+  * torch's float8_e4m3fn / float8_e5m2 decode of all 256 codes;
+  * torch's float32 -> float8 conversion (round-to-nearest-even, no saturation)
+    after clamping to +-fmt_max, on values that are exact in float32;
+  * a brute-force nearest-code search over the sorted non-negative finite code
+    values, in exact float64 arithmetic;
+  * hand-derived codes in tests/golden/cast_closed_form.txt.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+E4M3, E5M2 = 0, 1
+TORCH_FMT = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
+FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
+MAXCODE = {E4M3: 0x7E, E5M2: 0x7B}
+QUANTUM = {E4M3: 2.0 ** -9, E5M2: 2.0 ** -16}   # smallest subnormal
+FMT_NAME = {"E4M3": E4M3, "E5M2": E5M2}
+
+
+def torch_code_values(fmt):
+    """float64 value of each of the 256 codes, decoded by torch."""
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(TORCH_FMT[fmt]).to(torch.float64).numpy()
+
+
+def bf16_values(words):
+    """Exact float64 value of bf16 words (via torch's bf16 -> float64)."""
+    return torch.from_numpy(words.astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def nearest_code_bruteforce(v, fmt):
+    """Code nearest to each float64 v (exact), ties to the even code,
+    saturating at fmt_max, NaN -> 0x7F|sign.  Independent of the oracle's
+    shift-and-round: it searches the sorted table of code values."""
+    table = torch_code_values(fmt)
+    mags = table[: MAXCODE[fmt] + 1]            # codes 0..maxcode, increasing values
+    assert np.all(np.diff(mags) > 0)
+    sign = np.signbit(v)
+    a = np.abs(v)
+    nan = np.isnan(a)
+    a = np.where(nan, 0.0, np.minimum(a, FMT_MAX[fmt]))
+    hi = np.searchsorted(mags, a, side="left")  # first code with value >= a
+    hi = np.minimum(hi, len(mags) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - mags[lo]
+    dhi = mags[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == mags[hi], hi, code)
+    code = np.where(nan, 0x7F, code).astype(np.uint8)
+    return (code | (sign.astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def torch_cast(v, fmt):
+    """torch's RNE conversion of clamp(v, +-max); v must be exact in float32
+    or tiny (|v| < 2^-126, which every format rounds to a signed zero)."""
+    v = np.asarray(v, dtype=np.float64)
+    tiny = (np.abs(v) < 2.0 ** -126) & ~np.isnan(v)
+    c = np.clip(v, -FMT_MAX[fmt], FMT_MAX[fmt])
+    c32 = c.astype(np.float32)
+    ok = tiny | np.isnan(v) | (c32.astype(np.float64) == c)
+    assert np.all(ok), "torch reference needs float32-exact inputs"
+    out = torch.from_numpy(c32).to(TORCH_FMT[fmt]).view(torch.uint8).numpy().copy()
+    out[tiny] = np.where(np.signbit(v[tiny]), 0x80, 0x00)
+    return out
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_decode_all_codes_matches_torch(orc, fmt):
+    ours = orc.decode_fp8(np.arange(256), fmt)
+    ref = torch_code_values(fmt)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(ours[m], ref[m])
+    assert np.array_equal(np.signbit(ours[m]), np.signbit(ref[m]))
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_decode_then_encode_is_identity(orc, fmt):
+    vals = torch_code_values(fmt)
+    finite = np.where(np.isfinite(vals))[0]
+    f32 = vals[finite].astype(np.float32)
+    assert np.array_equal(f32.astype(np.float64), vals[finite])
+    # fp32 words
+    assert np.array_equal(orc.scale_cast(f32, 0, fmt), finite.astype(np.uint8))
+    # bf16 words (every FP8 value is exact in bf16)
+    bf = torch.from_numpy(f32).to(torch.bfloat16)
+    assert np.array_equal(bf.to(torch.float64).numpy(), vals[finite])
+    words = bf.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.scale_cast(words, 0, fmt), finite.astype(np.uint8))
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_nan_and_infinite_codes(orc, fmt):
+    vals = torch_code_values(fmt)
+    # every NaN code decodes to NaN and re-encodes to 0x7F|sign
+    nan_codes = np.where(np.isnan(vals))[0]
+    words = vals[nan_codes].astype(np.float32)
+    words = words.view(np.uint32) | np.where(nan_codes >= 128, 0x80000000, 0).astype(np.uint32)
+    out = orc.scale_cast(words, 0, fmt)
+    assert np.array_equal(out, np.where(nan_codes >= 128, 0xFF, 0x7F).astype(np.uint8))
+    # infinities (the E5M2 inf codes included) saturate to +-max
+    inf = np.array([np.inf, -np.inf], dtype=np.float32)
+    assert list(orc.scale_cast(inf, 0, fmt)) == [MAXCODE[fmt], MAXCODE[fmt] | 0x80]
+    assert list(orc.scale_cast(inf, -50, fmt)) == [MAXCODE[fmt], MAXCODE[fmt] | 0x80]
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_midpoints_go_to_even_code_and_neighbours_to_nearer(orc, fmt):
+    vals = torch_code_values(fmt)[: MAXCODE[fmt] + 1]
+    mids = (vals[:-1] + vals[1:]) / 2                  # exact in fp32 (<= 5 significant bits)
+    m32 = mids.astype(np.float32)
+    assert np.array_equal(m32.astype(np.float64), mids)
+    lo = np.arange(len(mids))
+    even = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8)
+    assert np.array_equal(orc.scale_cast(m32, 0, fmt), even)
+    assert np.array_equal(orc.scale_cast(-m32, 0, fmt), even | 0x80)
+    up = np.nextafter(m32, np.float32(np.inf))
+    dn = np.nextafter(m32, np.float32(0))
+    assert np.array_equal(orc.scale_cast(up, 0, fmt), (lo + 1).astype(np.uint8))
+    assert np.array_equal(orc.scale_cast(dn, 0, fmt), lo.astype(np.uint8))
+    # the midpoint above fmt_max and beyond saturates
+    top = np.float32(vals[-1] * (1 + 2.0 ** -(4 if fmt == E4M3 else 3)))
+    big = np.array([top, np.nextafter(top, np.float32(np.inf)), 3.0e38], dtype=np.float32)
+    assert list(orc.scale_cast(big, 0, fmt)) == [MAXCODE[fmt]] * 3
+
+
+def _bias_sweep():
+    return list(range(-140, 161))
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_every_bf16_times_bias_sweep_matches_torch(orc, fmt):
+    words = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = bf16_values(words)
+    for b in _bias_sweep():
+        v = x * 2.0 ** b                 # exact in float64
+        ours = orc.scale_cast(words, b, fmt)
+        ref = torch_cast(v, fmt)
+        if not np.array_equal(ours, ref):
+            bad = np.where(ours != ref)[0][:5]
+            raise AssertionError(f"bias {b}: words {words[bad]} ours {ours[bad]} torch {ref[bad]}")
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_every_bf16_matches_bruteforce_nearest(orc, fmt):
+    words = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = bf16_values(words)
+    for b in [-140, -126, -60, -20, -9, -1, 0, 1, 5, 9, 17, 33, 60, 126, 133, 140, 149, 160]:
+        v = x * 2.0 ** b
+        ours = orc.scale_cast(words, b, fmt)
+        ref = nearest_code_bruteforce(v, fmt)
+        if not np.array_equal(ours, ref):
+            bad = np.where(ours != ref)[0][:5]
+            raise AssertionError(f"bias {b}: words {words[bad]} ours {ours[bad]} brute {ref[bad]}")
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_random_fp32_words_match_bruteforce(orc, fmt):
+    rng = np.random.default_rng(7)
+    words = rng.integers(0, 2 ** 32, 400_000, dtype=np.uint64).astype(np.uint32)
+    # concentrate half of them near the FP8 range
+    e = rng.integers(100, 150, 200_000).astype(np.uint32)
+    words[:200_000] = (words[:200_000] & 0x807FFFFF) | (e << 23)
+    with np.errstate(invalid="ignore"):
+        x = words.view(np.float32).astype(np.float64)
+    for b in [-30, -3, 0, 2, 11, 40, 130]:
+        ours = orc.scale_cast(words, b, fmt)
+        ref = nearest_code_bruteforce(x * 2.0 ** b, fmt)
+        assert np.array_equal(ours, ref), f"bias {b}"
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(HERE, "golden", name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].split()
+            if line:
+                rows.append(line)
+    return rows
+
+
+def test_golden_closed_form_codes(orc):
+    rows = _golden("cast_closed_form.txt")
+    assert len(rows) >= 30
+    for fmt_s, bits, bias, expected in rows:
+        w = np.array([int(bits, 16)], dtype=np.uint32)
+        got = int(orc.scale_cast(w, int(bias), FMT_NAME[fmt_s])[0])
+        assert got == int(expected, 16), (fmt_s, bits, bias, hex(got), expected)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_underflow_invariant(orc, fmt):
+    q = QUANTUM[fmt]
+    rng = np.random.default_rng(11)
+    # magnitudes in (0, q/2] -> signed zero; (q/2, q] -> +-q
+    a = rng.uniform(0, 1, 100_000) * q / 2
+    a = np.concatenate([a, [q / 2]]).astype(np.float32)
+    a = a[a > 0]
+    assert np.all(a.astype(np.float64) <= q / 2)
+    assert np.all(orc.scale_cast(a, 0, fmt) == 0x00)
+    assert np.all(orc.scale_cast(-a, 0, fmt) == 0x80)
+    b = (q / 2 + rng.uniform(0, 1, 100_000) * q / 2).astype(np.float32)
+    b = b[(b.astype(np.float64) > q / 2) & (b.astype(np.float64) <= q)]
+    assert np.all(orc.scale_cast(b, 0, fmt) == 0x01)
+    assert np.all(orc.scale_cast(-b, 0, fmt) == 0x81)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_power_of_two_identity(orc, fmt):
+    """cast(x, b) == cast(x * 2^k, b - k) whenever x * 2^k is exact; and
+    deq(cast(x, b)) * 2^-b == x when x * 2^b lies on the FP8 grid."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal(50_000).astype(np.float32)
+    for k in (-20, -3, 1, 7, 30):
+        xk = (x.astype(np.float64) * 2.0 ** k).astype(np.float32)
+        assert np.array_equal(xk.astype(np.float64), x.astype(np.float64) * 2.0 ** k)
+        for b in (0, 4, 9):
+            assert np.array_equal(orc.scale_cast(x, b, fmt), orc.scale_cast(xk, b - k, fmt))
+    vals = torch_code_values(fmt)
+    grid = vals[np.isfinite(vals)]
+    for b in (-12, 0, 5, 40):
+        xg = (grid * 2.0 ** -b).astype(np.float32)
+        assert np.array_equal(xg.astype(np.float64), grid * 2.0 ** -b)
+        back = orc.decode_fp8(orc.scale_cast(xg, b, fmt), fmt) * 2.0 ** -b
+        assert np.array_equal(back, grid * 2.0 ** -b)
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_saturation_invariant_with_amax_bias(orc, fmt):
+    """With margin >= 0 nothing needs clamping: the largest element's code
+    sits in the top two binades and no code is the saturated one unless the
+    value itself rounds there."""
+    rng = np.random.default_rng(3)
+    for trial in range(20):
+        sigma = 10.0 ** rng.uniform(-7, 4)
+        x = (rng.standard_normal(4096) * sigma).astype(np.float32)
+        a_bits = orc.amax_bits(x)
+        for margin in (0, 1, 3):
+            b = orc.compute_bias(a_bits, fmt, margin)
+            v = np.abs(x.astype(np.float64)) * 2.0 ** b
+            assert v.max() <= FMT_MAX[fmt] / 2 ** margin
+            codes = orc.scale_cast(x, b, fmt) & 0x7F
+            top = int(codes.max())
+            # amax * 2^b lies in (fmt_max / 2^(margin+1), fmt_max / 2^margin], so
+            # the largest code's exponent field is one of the top two (shifted
+            # down by the margin); rounding up cannot leave that pair
+            mb = 3 if fmt == E4M3 else 2
+            top_binade = (MAXCODE[fmt] >> mb)
+            assert (top >> mb) in (top_binade - margin, top_binade - margin - 1)
+            assert np.all(codes <= MAXCODE[fmt])
