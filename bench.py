@@ -1,0 +1,325 @@
+"""Benchmark of the FP8-AMAX scaled linear layer on one MI355X.
+
+One step = the whole hot path over one batch of the workload: for every
+activation (and gradient) quantised inside the step, amax -> compute_bias ->
+scale-and-cast, then every FP8 product of the workload.  Weights that the
+workload treats as static are quantised once before timing.  The default
+workload is the Llama-2-70B-shaped single-layer inference (8192 tokens,
+hidden 8192, QKV 8192->10240, O 8192->8192, gate/up 8192->28672, down
+28672->8192).
+
+Prints one JSON line: whole-step TFLOP/s (amax + bias + cast included), the
+roofline of the dominant kernel (the FP8 GEMM) measured with HIP events on the
+launch stream, the cast's HBM throughput, and the CPU oracle timed on a
+bounded sample of the same step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5, help="1..5 (see synth.WORKLOADS)")
+    ap.add_argument("--cpu-rows", type=int, default=64, help="rows of each product in the CPU sample")
+    ap.add_argument("--cpu-cols", type=int, default=2048, help="columns of each product in the CPU sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def plan_of(w):
+    """Launch order of one step: ('quant', tensor) before first use, then ('gemm', linear, pass)."""
+    plan, done = [], set()
+    for l in w.linears:
+        for which in l.passes:
+            need = {"fwd": (l.x, l.w), "dgrad": (l.dy, l.w), "wgrad": (l.dy, l.x)}[which]
+            for n in need:
+                if w.tensor(n).timed and n not in done:
+                    plan.append(("quant", n))
+                    done.add(n)
+            plan.append(("gemm", l, which))
+    return plan
+
+
+def gemm_operands(l, which):
+    """(a tensor, b tensor, output shape) of one product."""
+    if which == "fwd":
+        return l.x, l.w, (l.M, l.N)
+    if which == "dgrad":
+        return l.dy, l.w, (l.M, l.K)
+    return l.dy, l.x, (l.N, l.K)
+
+
+def file_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_record(kernel_source):
+    """HBM bytes per launch from committed PMC counters, valid only while the
+    kernel source they were taken on is unchanged."""
+    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != file_sha(kernel_source):
+        return None
+    return rec
+
+
+def cpu_baseline(w, host, rows, cols):
+    """The oracle, as it stands, on a bounded sample of the step: amax + cast of
+    the first `rows` rows of every quantised-in-step tensor, and a rows x cols
+    block of every product; scaled to the step by the sampled fraction."""
+    import numpy as np
+    import oracle
+    import synth
+
+    plan = plan_of(w)
+    codes, biases = {}, {}
+    # static operands: quantised offline (untimed), like the GPU leg; only the
+    # sampled rows are cast, with the bias of the whole tensor
+    t_quant = t_gemm = 0.0
+    step_quant_elems = 0
+    sampled_quant_elems = 0
+    for t in w.tensors:
+        words = synth.bf16_words(host[t.name])
+        if t.timed:
+            step_quant_elems += words.size
+            r = min(rows, t.shape[0])
+            sl = words[:r]
+            sampled_quant_elems += sl.size
+            t0 = time.perf_counter()
+            a = oracle.amax_bits(sl)
+            b = oracle.compute_bias(a, t.fmt, t.margin)
+            c = oracle.scale_cast(sl, b, t.fmt)
+            t_quant += time.perf_counter() - t0
+            # the products below need every row their sample touches
+            codes[t.name] = c
+            biases[t.name] = b
+        else:
+            b = oracle.compute_bias(oracle.amax_bits(words), t.fmt, t.margin)
+            biases[t.name] = b
+            codes[t.name] = None  # cast on demand below (untimed)
+    flops_sample = 0
+    for item in plan:
+        if item[0] != "gemm":
+            continue
+        _, l, which = item
+        an, bn, (R, C) = gemm_operands(l, which)
+        r, c = min(rows, R), min(cols, C)
+        ta, tb = w.tensor(an), w.tensor(bn)
+        wa, wb = synth.bf16_words(host[an]), synth.bf16_words(host[bn])
+        # operands restricted to what the r x c block reads (untimed preparation)
+        if which == "fwd":       # X[r, K], W[c, K]
+            a8 = oracle.scale_cast(wa[:r], biases[an], ta.fmt)
+            b8 = oracle.scale_cast(wb[:c], biases[bn], tb.fmt)
+            fn = oracle.gemm_fwd
+        elif which == "dgrad":   # dY[r, N], W[N, c]
+            a8 = oracle.scale_cast(wa[:r], biases[an], ta.fmt)
+            b8 = oracle.scale_cast(np.ascontiguousarray(wb[:, :c]), biases[bn], tb.fmt)
+            fn = oracle.gemm_dgrad
+        else:                    # dY[M, r], X[M, c]
+            a8 = oracle.scale_cast(np.ascontiguousarray(wa[:, :r]), biases[an], ta.fmt)
+            b8 = oracle.scale_cast(np.ascontiguousarray(wb[:, :c]), biases[bn], tb.fmt)
+            fn = oracle.gemm_wgrad
+        t0 = time.perf_counter()
+        fn(a8, ta.fmt, biases[an], b8, tb.fmt, biases[bn])
+        t_gemm += time.perf_counter() - t0
+        contraction = {"fwd": l.K, "dgrad": l.N, "wgrad": l.M}[which]
+        flops_sample += 2 * r * c * contraction
+    step_flops = w.flops()
+    # extrapolate each part by its own sampled fraction
+    t_step = t_quant * (step_quant_elems / max(sampled_quant_elems, 1)) + t_gemm * (step_flops / flops_sample)
+    return {
+        "value": step_flops / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": (f"first {rows} rows of each in-step quantisation (amax+bias+cast, 1 thread) and a "
+                   f"{rows}x{cols} output block of every product (OpenMP over rows); each part scaled "
+                   f"to the full step by its sampled fraction; sampled time {t_quant + t_gemm:.1f} s"),
+        "seconds_sampled": round(t_quant + t_gemm, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import fp8_precision_linear_amd as fl
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[args.workload]
+    plan = plan_of(w)
+
+    host = {t.name: synth.workload_tensor(w, t.name) for t in w.tensors}
+    x = {n: v.to(dev) for n, v in host.items()}
+    q = {}   # name -> (codes, bias, amax, fmt)
+    for t in w.tensors:
+        codes = torch.empty(t.shape, dtype=torch.uint8, device=dev)
+        bias = torch.empty(1, dtype=torch.int32, device=dev)
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+        q[t.name] = (codes, bias, amax, t.fmt)
+        if not t.timed:   # static weights: quantised once, outside the timed step
+            fl.amax(x[t.name], out=amax)
+            fl.compute_bias(amax, t.fmt, t.margin, out=bias)
+            fl.scale_cast(x[t.name], bias, t.fmt, out=codes)
+    outs = {}
+    for item in plan:
+        if item[0] == "gemm":
+            _, l, which = item
+            outs[(l.name, which)] = torch.empty(gemm_operands(l, which)[2], dtype=torch.float32, device=dev)
+    gemm_fn = {"fwd": fl.scaled_gemm_fwd, "dgrad": fl.scaled_gemm_dgrad, "wgrad": fl.scaled_gemm_wgrad}
+
+    def step(ev=None):
+        for item in plan:
+            if item[0] == "quant":
+                n = item[1]
+                codes, bias, amax, fmt = q[n]
+                t = w.tensor(n)
+                if ev is not None:
+                    ev.append(("quant_start", n, torch.cuda.Event(enable_timing=True)))
+                    ev[-1][2].record()
+                fl.amax(x[n], out=amax)
+                if ev is not None:
+                    ev.append(("amax_end", n, torch.cuda.Event(enable_timing=True)))
+                    ev[-1][2].record()
+                fl.compute_bias(amax, fmt, t.margin, out=bias)
+                if ev is not None:
+                    ev.append(("bias_end", n, torch.cuda.Event(enable_timing=True)))
+                    ev[-1][2].record()
+                fl.scale_cast(x[n], bias, fmt, out=codes)
+                if ev is not None:
+                    ev.append(("cast_end", n, torch.cuda.Event(enable_timing=True)))
+                    ev[-1][2].record()
+            else:
+                _, l, which = item
+                an, bn, _ = gemm_operands(l, which)
+                a8, ba, _, fa = q[an]
+                b8, bb, _, fb = q[bn]
+                if ev is not None:
+                    ev.append(("gemm_start", (l.name, which), torch.cuda.Event(enable_timing=True)))
+                    ev[-1][2].record()
+                gemm_fn[which](a8, fa, ba, b8, fb, bb, out=outs[(l.name, which)])
+                if ev is not None:
+                    ev.append(("gemm_end", (l.name, which), torch.cuda.Event(enable_timing=True)))
+                    ev[-1][2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, wall clock, synchronised on both sides
+    ev = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(ev)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-kernel durations from the events (same stream as the launches)
+    gemm_ms = amax_ms = bias_ms = cast_ms = 0.0
+    last = {}
+    for kind, key, e in ev:
+        if kind == "quant_start":
+            last["q"] = e
+        elif kind == "amax_end":
+            amax_ms += last["q"].elapsed_time(e)
+            last["a"] = e
+        elif kind == "bias_end":
+            bias_ms += last["a"].elapsed_time(e)
+            last["b"] = e
+        elif kind == "cast_end":
+            cast_ms += last["b"].elapsed_time(e)
+        elif kind == "gemm_start":
+            last["g"] = e
+        elif kind == "gemm_end":
+            gemm_ms += last["g"].elapsed_time(e)
+    K = args.steps
+    step_flops = w.flops()
+    gemm_launches = sum(1 for i in plan if i[0] == "gemm")
+    quant_elems = sum(int(torch.tensor(w.tensor(i[1]).shape).prod()) for i in plan if i[0] == "quant")
+    gemm_tflops = step_flops * K / (gemm_ms * 1e-3) / 1e12
+    cast_gbs = 3.0 * quant_elems * K / (cast_ms * 1e-3) / 1e9 if cast_ms > 0 else None
+    amax_gbs = 2.0 * quant_elems * K / (amax_ms * 1e-3) / 1e9 if amax_ms > 0 else None
+
+    rec = traffic_record(os.path.join(ROOT, "fp8_precision_linear_amd", "csrc", "gemm.hip"))
+    traffic = rec["bytes_per_launch"] if rec else None
+
+    line = {
+        "metric": "FP8-AMAX scaled GEMM TFLOP/s incl. amax+cast; cast GB/s vs HBM peak",
+        "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "tokens": w.linears[0].M,
+            "products": [f"{l.name}:{p}:{l.M}x{l.N}x{l.K}" for l in w.linears for p in l.passes],
+            "in_step_quantised": [i[1] for i in plan if i[0] == "quant"],
+            "accumulate": "f32",
+            "parallelism": "single-gpu",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_kernel (FP8 MFMA 32x32x64)",
+            "achieved": round(gemm_tflops, 2),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(gemm_ms * 1e3 / (K * gemm_launches), 2),
+            "flops_per_launch_avg": step_flops / gemm_launches,
+        },
+        "cast": {
+            "bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
+            "achieved": round(cast_gbs, 1) if cast_gbs else None,
+            "frac": round(cast_gbs / PEAK_HBM_GBS, 4) if cast_gbs else None,
+            "bytes_per_element": 3,
+            "avg_launch_us": round(cast_ms * 1e3 / max(K * len([i for i in plan if i[0] == 'quant']), 1), 2),
+        },
+        "amax": {
+            "bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
+            "achieved": round(amax_gbs, 1) if amax_gbs else None,
+            "frac": round(amax_gbs / PEAK_HBM_GBS, 4) if amax_gbs else None,
+            "bytes_per_element": 2,
+        },
+        "step_breakdown_ms": {"gemm": round(gemm_ms / K, 4), "amax": round(amax_ms / K, 4),
+                              "bias": round(bias_ms / K, 4), "cast": round(cast_ms / K, 4)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, host, args.cpu_rows, args.cpu_cols)
+        line["cpu_baseline"]["vs_gpu"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+"""Python binding of libfp8lin, the FP8-AMAX scaled linear layer for MI355X.
+
+Argument marshalling only: every step runs in the library's HIP kernels
+(declared in include/fp8lin.h).  PyTorch provides device memory and the
+current stream; results stay on the device.
+
+The method: "Training and inference of large language models using 8-bit
+floating point" (Perez, Zhang et al., 2023), review page, "Proposed method":
+per-tensor amax -> compute_bias -> scale and cast to E4M3 (weights,
+activations) or E5M2 (gradients) -> FP8 matmul, unscaled afterwards.
+
+Importing this module loads the library and raises ImportError if it is not
+built; build it with ``python fp8_precision_linear_amd/build.py``.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
+
+E4M3, E5M2 = 0, 1
+BF16, FP32 = 0, 1
+FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
+MAX_MARGIN = 64
+
+STATUS = {0: "FP8_OK", -1: "FP8_ERR_NULL", -2: "FP8_ERR_SIZE", -3: "FP8_ERR_FORMAT",
+          -4: "FP8_ERR_DTYPE", -5: "FP8_ERR_ALIGN", -6: "FP8_ERR_MARGIN",
+          -7: "FP8_ERR_DEVICE", -8: "FP8_ERR_HIP"}
+
+# Exported symbols and their C signatures (include/fp8lin.h).
+_vp, _i64, _i32, _ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+SIGNATURES = {
+    "fp8_status_string": (ctypes.c_char_p, [_ci]),
+    "fp8_amax": (_ci, [_vp, _ci, _i64, _vp, _vp]),
+    "fp8_compute_bias": (_ci, [_vp, _ci, _i32, _vp, _vp]),
+    "fp8_scale_cast": (_ci, [_vp, _ci, _i64, _vp, _ci, _vp, _vp]),
+    "fp8_scaled_gemm_fwd": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "fp8_scaled_gemm_dgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "fp8_scaled_gemm_wgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run python fp8_precision_linear_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class Fp8Error(RuntimeError):
+    def __init__(self, fn, status):
+        msg = lib.fp8_status_string(status).decode()
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Fp8Error(fn, status)
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"inputs are bfloat16 or float32 tensors, got {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous CUDA (HIP) tensors")
+
+
+def amax(x, out=None, stream=None):
+    """float32[1] device tensor holding max|x| (fp8_amax)."""
+    _need_cuda(x)
+    out = torch.empty(1, dtype=torch.float32, device=x.device) if out is None else out
+    _check("fp8_amax", lib.fp8_amax(_ptr(x), _dtype_code(x), x.numel(), _ptr(out), _stream(stream)))
+    return out
+
+
+def compute_bias(amax_t, fmt, margin=0, out=None, stream=None):
+    """int32[1] device tensor: floor(log2(fmt_max / amax)) - margin (fp8_compute_bias)."""
+    _need_cuda(amax_t)
+    out = torch.empty(1, dtype=torch.int32, device=amax_t.device) if out is None else out
+    _check("fp8_compute_bias",
+           lib.fp8_compute_bias(_ptr(amax_t), int(fmt), int(margin), _ptr(out), _stream(stream)))
+    return out
+
+
+def scale_cast(x, bias, fmt, out=None, stream=None):
+    """uint8 device tensor of FP8 codes of x * 2^bias, same shape as x (fp8_scale_cast)."""
+    _need_cuda(x, bias)
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    _check("fp8_scale_cast", lib.fp8_scale_cast(_ptr(x), _dtype_code(x), x.numel(), _ptr(bias),
+                                                int(fmt), _ptr(out), _stream(stream)))
+    return out
+
+
+def quantize(x, fmt, margin=0, stream=None):
+    """(codes, bias, amax) of a tensor: the three quantisation calls in order."""
+    a = amax(x, stream=stream)
+    b = compute_bias(a, fmt, margin, stream=stream)
+    return scale_cast(x, b, fmt, stream=stream), b, a
+
+
+def scaled_gemm_fwd(x8, fx, bx, w8, fw, bw, out=None, stream=None):
+    """Y[M, N] = 2^-(bx+bw) * X8[M, K] @ W8[N, K]^T in float32 (fp8_scaled_gemm_fwd)."""
+    _need_cuda(x8, w8, bx, bw)
+    M, K = x8.shape
+    N, K2 = w8.shape
+    if K != K2:
+        raise ValueError("contraction sizes differ")
+    out = torch.empty((M, N), dtype=torch.float32, device=x8.device) if out is None else out
+    _check("fp8_scaled_gemm_fwd",
+           lib.fp8_scaled_gemm_fwd(_ptr(x8), int(fx), _ptr(bx), _ptr(w8), int(fw), _ptr(bw),
+                                   M, N, K, _ptr(out), _stream(stream)))
+    return out
+
+
+def scaled_gemm_dgrad(dy8, fdy, bdy, w8, fw, bw, out=None, stream=None):
+    """dX[M, K] = 2^-(bdy+bw) * dY8[M, N] @ W8[N, K] in float32 (fp8_scaled_gemm_dgrad)."""
+    _need_cuda(dy8, w8, bdy, bw)
+    M, N = dy8.shape
+    N2, K = w8.shape
+    if N != N2:
+        raise ValueError("contraction sizes differ")
+    out = torch.empty((M, K), dtype=torch.float32, device=dy8.device) if out is None else out
+    _check("fp8_scaled_gemm_dgrad",
+           lib.fp8_scaled_gemm_dgrad(_ptr(dy8), int(fdy), _ptr(bdy), _ptr(w8), int(fw), _ptr(bw),
+                                     M, N, K, _ptr(out), _stream(stream)))
+    return out
+
+
+def scaled_gemm_wgrad(dy8, fdy, bdy, x8, fx, bx, out=None, stream=None):
+    """dW[N, K] = 2^-(bdy+bx) * dY8[M, N]^T @ X8[M, K] in float32 (fp8_scaled_gemm_wgrad)."""
+    _need_cuda(dy8, x8, bdy, bx)
+    M, N = dy8.shape
+    M2, K = x8.shape
+    if M != M2:
+        raise ValueError("contraction sizes differ")
+    out = torch.empty((N, K), dtype=torch.float32, device=dy8.device) if out is None else out
+    _check("fp8_scaled_gemm_wgrad",
+           lib.fp8_scaled_gemm_wgrad(_ptr(dy8), int(fdy), _ptr(bdy), _ptr(x8), int(fx), _ptr(bx),
+                                     M, N, K, _ptr(out), _stream(stream)))
+    return out

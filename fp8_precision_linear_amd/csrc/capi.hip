@@ -1,0 +1,133 @@
+// C ABI of libfp8lin: argument checks on the host, then kernel launches on the
+// caller's stream.  No allocation, no host synchronisation, no state beyond a
+// per-device "is this gfx950" flag.
+#include <atomic>
+#include <cstring>
+
+#include "internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950, 2 = something else.
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+bool bad_format(int f) { return f != FP8_E4M3 && f != FP8_E5M2; }
+bool bad_dtype(int d) { return d != FP8_IN_BF16 && d != FP8_IN_FP32; }
+bool bad_dim(int64_t v) { return v < 0 || v > (int64_t)0x7FFFFFFF; }
+
+// The current device must be a gfx950.  Checked once per device.
+int device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8_ERR_DEVICE;
+  if (dev >= kMaxDevices) return FP8_ERR_DEVICE;
+  int state = g_arch_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FP8_ERR_DEVICE;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? FP8_OK : FP8_ERR_DEVICE;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
+
+int gemm_checks(const uint8_t* a, int fa, const int32_t* ba, const uint8_t* b, int fb,
+                const int32_t* bb, int64_t M, int64_t N, int64_t K, const float* out,
+                int64_t a_elems, int64_t b_elems) {
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8_ERR_SIZE;
+  if (bad_format(fa) || bad_format(fb)) return FP8_ERR_FORMAT;
+  if (M == 0 || N == 0) return FP8_OK;
+  if (!out || !ba || !bb) return FP8_ERR_NULL;
+  if ((a_elems > 0 && !a) || (b_elems > 0 && !b)) return FP8_ERR_NULL;
+  if (misaligned(out) || (a && misaligned(a)) || (b && misaligned(b))) return FP8_ERR_ALIGN;
+  return FP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_string(int status) {
+  switch (status) {
+    case FP8_OK: return "ok";
+    case FP8_ERR_NULL: return "a required pointer is NULL";
+    case FP8_ERR_SIZE: return "a size is negative or too large";
+    case FP8_ERR_FORMAT: return "unknown FP8 format";
+    case FP8_ERR_DTYPE: return "unknown input dtype";
+    case FP8_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FP8_ERR_MARGIN: return "margin out of range";
+    case FP8_ERR_DEVICE: return "no gfx950 HIP device is current";
+    case FP8_ERR_HIP: return "a HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fp8_amax(const void* x, fp8_dtype_t dtype, int64_t n, float* amax, void* stream) {
+  if (n < 0) return FP8_ERR_SIZE;
+  if (bad_dtype(dtype)) return FP8_ERR_DTYPE;
+  if (!amax || (n > 0 && !x)) return FP8_ERR_NULL;
+  if (n > 0 && misaligned(x)) return FP8_ERR_ALIGN;
+  if (int s = device_ok()) return s;
+  return hip_status(fp8lin::launch_amax(x, dtype, n, amax, (hipStream_t)stream));
+}
+
+int fp8_compute_bias(const float* amax, fp8_format_t fmt, int32_t margin, int32_t* bias,
+                     void* stream) {
+  if (bad_format(fmt)) return FP8_ERR_FORMAT;
+  if (margin > FP8_MAX_MARGIN || margin < -FP8_MAX_MARGIN) return FP8_ERR_MARGIN;
+  if (!amax || !bias) return FP8_ERR_NULL;
+  if (int s = device_ok()) return s;
+  return hip_status(fp8lin::launch_bias(amax, fmt, margin, bias, (hipStream_t)stream));
+}
+
+int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* bias,
+                   fp8_format_t fmt, uint8_t* y, void* stream) {
+  if (n < 0) return FP8_ERR_SIZE;
+  if (bad_dtype(dtype)) return FP8_ERR_DTYPE;
+  if (bad_format(fmt)) return FP8_ERR_FORMAT;
+  if (n == 0) return FP8_OK;
+  if (!x || !y || !bias) return FP8_ERR_NULL;
+  if (misaligned(x) || misaligned(y)) return FP8_ERR_ALIGN;
+  if (int s = device_ok()) return s;
+  return hip_status(fp8lin::launch_cast(x, dtype, n, bias, fmt, y, (hipStream_t)stream));
+}
+
+int fp8_scaled_gemm_fwd(const uint8_t* x8, fp8_format_t fx, const int32_t* bx,
+                        const uint8_t* w8, fp8_format_t fw, const int32_t* bw, int64_t M,
+                        int64_t N, int64_t K, float* y, void* stream) {
+  if (int s = gemm_checks(x8, fx, bx, w8, fw, bw, M, N, K, y, M * K, N * K)) return s;
+  if (M == 0 || N == 0) return FP8_OK;
+  if (int s = device_ok()) return s;
+  fp8lin::GemmProblem p{x8, K, true, fx, bx, w8, K, true, fw, bw, y, N, (int)M, (int)N, (int)K};
+  return hip_status(fp8lin::launch_gemm(p, (hipStream_t)stream));
+}
+
+int fp8_scaled_gemm_dgrad(const uint8_t* dy8, fp8_format_t fdy, const int32_t* bdy,
+                          const uint8_t* w8, fp8_format_t fw, const int32_t* bw, int64_t M,
+                          int64_t N, int64_t K, float* dx, void* stream) {
+  // dX[M x K]: rows m of dY8 (contraction N contiguous) times W8 read as
+  // [contraction N][K] (contraction is the slow index).
+  if (int s = gemm_checks(dy8, fdy, bdy, w8, fw, bw, M, K, N, dx, M * N, N * K)) return s;
+  if (M == 0 || K == 0) return FP8_OK;
+  if (int s = device_ok()) return s;
+  fp8lin::GemmProblem p{dy8, N, true, fdy, bdy, w8, K, false, fw, bw, dx, K,
+                        (int)M, (int)K, (int)N};
+  return hip_status(fp8lin::launch_gemm(p, (hipStream_t)stream));
+}
+
+int fp8_scaled_gemm_wgrad(const uint8_t* dy8, fp8_format_t fdy, const int32_t* bdy,
+                          const uint8_t* x8, fp8_format_t fx, const int32_t* bx, int64_t M,
+                          int64_t N, int64_t K, float* dw, void* stream) {
+  // dW[N x K]: dY8 read as [contraction M][N] times X8 read as [contraction M][K].
+  if (int s = gemm_checks(dy8, fdy, bdy, x8, fx, bx, N, K, M, dw, M * N, M * K)) return s;
+  if (N == 0 || K == 0) return FP8_OK;
+  if (int s = device_ok()) return s;
+  fp8lin::GemmProblem p{dy8, N, false, fdy, bdy, x8, K, false, fx, bx, dw, K,
+                        (int)N, (int)K, (int)M};
+  return hip_status(fp8lin::launch_gemm(p, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,320 @@
+// FP8 x FP8 products with fp32 accumulation for gfx950, unscaled after the
+// matmul by 2^-(bias_a + bias_b).
+//
+// "Training and inference of large language models using 8-bit floating
+// point", review page, "Proposed method", bullet 3 (scale before the cast,
+// unscale after the matrix multiplication) and bullet 5 (training: forward,
+// data-gradient and weight-gradient products; inference).
+//
+// Design (MI355X / CDNA4):
+//  * v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales (E8M0 127 = 2^0):
+//    the operand formats (E4M3 or E5M2) are per-instruction fields, so every
+//    format pairing runs at the same dense FP8 rate.
+//  * A workgroup of 4 wave64s computes a BM x BN tile (2 x 2 waves, each a
+//    BM/2 x BN/2 block of 32x32 MFMA tiles).  The contraction advances 128
+//    bytes per stage through a double-buffered LDS tile pair; global loads of
+//    the next stage are in flight while the MFMAs consume the current one.
+//  * LDS keeps every operand tile contraction-contiguous ([row][128 bytes]),
+//    16-byte chunks XOR-swizzled by (row ^ row >> 4) & 7, so a lane reads its
+//    32-byte MFMA fragment with two conflict-free ds_read_b128.  An operand
+//    whose contraction index is the slow one in memory (the weight in the
+//    data gradient, both operands in the weight gradient) is loaded as
+//    16-byte rows and byte-transposed in registers on its way into LDS.
+//  * Tiles are numbered so that the workgroups the dispatcher sends to one XCD
+//    (blockIdx % 8) take a contiguous run of tiles, grouped 8 tile-rows at a
+//    time, so neighbouring tiles share operand panels in that XCD's L2.
+//  * The unscale is one v_ldexp_f32 per output in the epilogue (exact unless
+//    the result is an fp32 subnormal).
+#include <cstdlib>
+#include <type_traits>
+
+#include "internal.h"
+
+namespace fp8lin {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kBK = 128;  // contraction bytes per LDS stage
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 4)) & 7; }
+
+// Byte offset of logical 16-byte chunk c (0..7) of tile row r.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * kBK + ((c ^ swz(r)) << 4); }
+
+// Bytes [i, i+16) of a row, zero where i + j >= limit.
+__device__ __forceinline__ uint4 load16_partial(const uint8_t* row, int i, int limit) {
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (i + j < limit) w[j >> 2] |= (uint32_t)row[i + j] << (8 * (j & 3));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int w) {
+  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ uint32_t byte_of(const uint4& v, int j) {
+  return (word_of(v, j >> 2) >> (8 * (j & 3))) & 0xFFu;
+}
+
+// Operand tile whose contraction index is contiguous in memory:
+// rows [row0, row0 + R) x bytes [k0, k0 + 128).
+template <int R>
+struct KMajorLoader {
+  static constexpr int kChunks = R * (kBK / 16) / kThreads;  // 16-byte chunks per lane
+  uint4 v[kChunks];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t ld, int row0,
+                                       int rows, int k0, int K, bool vec) {
+#pragma unroll
+    for (int p = 0; p < kChunks; ++p) {
+      const int q = (int)threadIdx.x + kThreads * p, r = q >> 3, c = q & 7;
+      const int gr = row0 + r, gk = k0 + c * 16;
+      if (gr < rows && gk < K) {
+        const uint8_t* src = base + (int64_t)gr * ld;
+        if (vec && gk + 16 <= K)
+          v[p] = *reinterpret_cast<const uint4*>(src + gk);
+        else
+          v[p] = load16_partial(src, gk, K);
+      } else {
+        v[p] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* lds) const {
+#pragma unroll
+    for (int p = 0; p < kChunks; ++p) {
+      const int q = (int)threadIdx.x + kThreads * p, r = q >> 3, c = q & 7;
+      *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = v[p];
+    }
+  }
+};
+
+// Operand tile whose contraction index is the slow one in memory: memory rows
+// [k0, k0 + 128) x bytes [mn0, mn0 + R).  Each lane loads KU memory rows of 16
+// bytes and writes 16 tile rows of KU contraction bytes.
+template <int R>
+struct MNMajorLoader {
+  static constexpr int KU = R / 32;  // contraction rows per lane (8 or 4)
+  static constexpr int NU = R / 16;  // 16-byte column groups across the tile
+  static_assert(KU == 8 || KU == 4, "tile size");
+  uint4 v[KU];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t ld, int mn0,
+                                       int mns, int k0, int K, bool vec) {
+    const int mu = (int)threadIdx.x % NU, kb = (int)threadIdx.x / NU;
+    const int gmn = mn0 + mu * 16;
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int gk = k0 + kb * KU + i;
+      if (gk < K && gmn < mns) {
+        const uint8_t* src = base + (int64_t)gk * ld;
+        if (vec && gmn + 16 <= mns)
+          v[i] = *reinterpret_cast<const uint4*>(src + gmn);
+        else
+          v[i] = load16_partial(src, gmn, mns);
+      } else {
+        v[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint8_t* lds) const {
+    const int mu = (int)threadIdx.x % NU, kb = (int)threadIdx.x / NU;
+    const int kbyte = kb * KU;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = mu * 16 + j;
+      uint8_t* dst = lds + r * kBK + (((kbyte >> 4) ^ swz(r)) << 4) + (kbyte & 15);
+      const uint32_t lo = byte_of(v[0], j) | (byte_of(v[1], j) << 8) | (byte_of(v[2], j) << 16) |
+                          (byte_of(v[3], j) << 24);
+      if constexpr (KU == 8) {
+        const uint32_t hi = byte_of(v[4], j) | (byte_of(v[5], j) << 8) |
+                            (byte_of(v[6], j) << 16) | (byte_of(v[7], j) << 24);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = lo;
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  int t = bid;
+  if ((total & 7) == 0) t = (bid & 7) * (total >> 3) + (bid >> 3);
+  constexpr int G = 8;
+  const int width = G * tiles_n;
+  const int first_m = (t / width) * G;
+  const int gsize = min(tiles_m - first_m, G);
+  tm = first_m + (t % width) % gsize;
+  tn = (t % width) / gsize;
+}
+
+template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int FA, int FB>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n,
+                                                        bool vec_a, bool vec_b) {
+  constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 MFMA tiles per wave
+  constexpr int kStage = (BM + BN) * kBK;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+
+  using LoaderA = typename std::conditional<A_KMAJOR, KMajorLoader<BM>, MNMajorLoader<BM>>::type;
+  using LoaderB = typename std::conditional<B_KMAJOR, KMajorLoader<BN>, MNMajorLoader<BN>>::type;
+
+  int tm, tn;
+  tile_coords((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  LoaderA la;
+  LoaderB lb;
+  v16f acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nk = (p.k + kBK - 1) / kBK;
+  if (nk > 0) {
+    la.load(p.a, p.lda, m0, p.m, 0, p.k, vec_a);
+    lb.load(p.b, p.ldb, n0, p.n, 0, p.k, vec_b);
+    la.store(smem);
+    lb.store(smem + BM * kBK);
+    __syncthreads();
+  }
+
+  const int h = lane >> 5, rl = lane & 31;
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t* cur = smem + (kt & 1) * kStage;
+    uint8_t* nxt = smem + ((kt + 1) & 1) * kStage;
+    const bool more = kt + 1 < nk;
+    if (more) {
+      la.load(p.a, p.lda, m0, p.m, (kt + 1) * kBK, p.k, vec_a);
+      lb.load(p.b, p.ldb, n0, p.n, (kt + 1) * kBK, p.k, vec_b);
+    }
+    const uint8_t* As = cur;
+    const uint8_t* Bs = cur + BM * kBK;
+#pragma unroll
+    for (int s = 0; s < kBK / 64; ++s) {
+      const int c0 = s * 4 + h * 2;  // this lane's 32 contraction bytes: chunks c0, c0 + 1
+      v8i af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wm * (BM / 2) + i * 32 + rl;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(As + lds_off(r, c0));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(As + lds_off(r, c0 + 1));
+        af[i] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                    (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wn * (BN / 2) + j * 32 + rl;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(Bs + lds_off(r, c0));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(Bs + lds_off(r, c0 + 1));
+        bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
+                    (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af[i], bf[j], acc[i][j], FA, FB, 0, 127, 0, 127);
+    }
+    if (more) {
+      la.store(nxt);
+      lb.store(nxt + BM * kBK);
+    }
+    __syncthreads();
+  }
+
+  // 32x32 accumulator layout: register r of lane l holds row
+  // 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32 of the MFMA tile.
+  const int unscale = -(*p.bias_a + *p.bias_b);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * (BN / 2) + j * 32 + rl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < p.m && col < p.n)
+          p.c[(int64_t)row * p.ldc + col] = __builtin_ldexpf(acc[i][j][r], unscale);
+      }
+    }
+}
+
+template <int BM, int BN, bool AK, bool BK>
+hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
+  const int tiles_m = (p.m + BM - 1) / BM, tiles_n = (p.n + BN - 1) / BN;
+  const bool vec_a = ((uintptr_t)p.a % 16 == 0) && (p.lda % 16 == 0);
+  const bool vec_b = ((uintptr_t)p.b % 16 == 0) && (p.ldb % 16 == 0);
+  const dim3 grid(tiles_m * tiles_n), block(kThreads);
+#define FP8LIN_GEMM_CASE(FA, FB)                                                              \
+  if (p.fmt_a == FA && p.fmt_b == FB) {                                                       \
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, FA, FB>), grid, block, 0, stream, p,      \
+                       tiles_m, tiles_n, vec_a, vec_b);                                       \
+    return hipGetLastError();                                                                 \
+  }
+  FP8LIN_GEMM_CASE(FP8_E4M3, FP8_E4M3)
+  FP8LIN_GEMM_CASE(FP8_E5M2, FP8_E4M3)
+  FP8LIN_GEMM_CASE(FP8_E4M3, FP8_E5M2)
+  FP8LIN_GEMM_CASE(FP8_E5M2, FP8_E5M2)
+#undef FP8LIN_GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
+// Fraction of the chip's workgroup slots doing useful work over all waves of
+// tiles, weighted by how much of each tile is inside the matrix.
+double tile_efficiency(int m, int n, int bm, int bn) {
+  const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn, tiles = tm * tn;
+  const int64_t slots = 256;
+  const int64_t waves = (tiles + slots - 1) / slots;
+  const double fill = (double)tiles / (double)(waves * slots);
+  const double inside = ((double)m * n) / ((double)tm * bm * tn * bn);
+  return fill * inside;
+}
+
+// FP8LIN_GEMM_TILE=128 or 256 pins the tile size (tuning and tests);
+// otherwise it is chosen from the shape.
+int forced_tile() {
+  const char* s = std::getenv("FP8LIN_GEMM_TILE");
+  if (!s) return 0;
+  const int v = std::atoi(s);
+  return (v == 128 || v == 256) ? v : 0;
+}
+
+template <bool AK, bool BK>
+hipError_t launch_layout(const GemmProblem& p, hipStream_t stream) {
+  // The 256x256 tile does twice the MFMA work per byte of LDS and global
+  // traffic of the 128x128 one; prefer it unless it leaves most CUs idle.
+  int tile = forced_tile();
+  if (tile == 0) {
+    const double e256 = tile_efficiency(p.m, p.n, 256, 256);
+    const double e128 = tile_efficiency(p.m, p.n, 128, 128) * 0.75;
+    tile = e256 >= e128 ? 256 : 128;
+  }
+  if (tile == 256) return launch_tiles<256, 256, AK, BK>(p, stream);
+  return launch_tiles<128, 128, AK, BK>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
+  if (p.m <= 0 || p.n <= 0) return hipSuccess;
+  if (p.a_kmajor && p.b_kmajor) return launch_layout<true, true>(p, stream);
+  if (p.a_kmajor && !p.b_kmajor) return launch_layout<true, false>(p, stream);
+  if (!p.a_kmajor && !p.b_kmajor) return launch_layout<false, false>(p, stream);
+  return launch_layout<false, true>(p, stream);
+}
+
+}  // namespace fp8lin

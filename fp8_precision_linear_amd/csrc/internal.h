@@ -1,0 +1,39 @@
+// Internal declarations shared by the HIP translation units of libfp8lin.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8lin.h"
+
+namespace fp8lin {
+
+// Quantisation kernels (quant.hip).
+hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t stream);
+hipError_t launch_bias(const float* amax, int fmt, int32_t margin, int32_t* bias,
+                       hipStream_t stream);
+hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias, int fmt,
+                       uint8_t* y, hipStream_t stream);
+
+// One FP8 product C[m][n] = 2^-(*bias_a + *bias_b) * sum_k A(m, k) * B(k, n).
+// A(m, k) lives at a[m * lda + k] when a_kmajor, else at a[k * lda + m];
+// B(k, n) lives at b[n * ldb + k] when b_kmajor, else at b[k * ldb + n].
+struct GemmProblem {
+  const uint8_t* a;
+  int64_t lda;
+  bool a_kmajor;
+  int fmt_a;
+  const int32_t* bias_a;
+  const uint8_t* b;
+  int64_t ldb;
+  bool b_kmajor;
+  int fmt_b;
+  const int32_t* bias_b;
+  float* c;
+  int64_t ldc;
+  int m, n, k;
+};
+
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+
+}  // namespace fp8lin

@@ -1,0 +1,319 @@
+// Per-tensor amax, compute_bias and scale-then-cast for gfx950.
+//
+// "Training and inference of large language models using 8-bit floating
+// point", review page, "Proposed method", bullets 1-4: a per-tensor maximum
+// absolute value, a power-of-two bias from log2(format max / amax) with a
+// margin, and a cast of the scaled tensor to E4M3 (weights, activations) or
+// E5M2 (gradients).
+//
+// All three are HBM-streaming kernels: 16-byte loads and stores per lane,
+// grid-stride loops, several loads in flight per lane.  amax reduces on the
+// integer magnitude bits (for non-negative IEEE values integer order is value
+// order, with NaN above inf), so the result is exact and independent of the
+// reduction order: wave shuffle, then LDS across the block's waves, then one
+// atomicMax per block.
+#include "internal.h"
+
+namespace fp8lin {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
+  return v;
+}
+
+// Block-wide max of v, folded into *out with one atomic per block.
+__device__ __forceinline__ void block_max_to(uint32_t v, uint32_t* out) {
+  __shared__ uint32_t part[kWaves];
+  v = wave_max_u32(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = part[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = max(m, part[w]);
+    atomicMax(out, m);
+  }
+}
+
+__global__ void amax_clear_kernel(uint32_t* out) { *out = 0u; }
+
+// bf16: each 16-byte vector holds 8 values; the running max is kept as two
+// packed 16-bit magnitudes (sign bits masked off).
+__device__ __forceinline__ u16x2 bf16_mag2(uint32_t w) {
+  uint32_t m = w & 0x7FFF7FFFu;
+  return *reinterpret_cast<u16x2*>(&m);
+}
+
+__device__ __forceinline__ u16x2 vmax_bf16(u16x2 acc, uint4 v) {
+  acc = __builtin_elementwise_max(acc, bf16_mag2(v.x));
+  acc = __builtin_elementwise_max(acc, bf16_mag2(v.y));
+  acc = __builtin_elementwise_max(acc, bf16_mag2(v.z));
+  acc = __builtin_elementwise_max(acc, bf16_mag2(v.w));
+  return acc;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __restrict__ x,
+                                                             int64_t nvec,
+                                                             const uint16_t* __restrict__ tail,
+                                                             int ntail, uint32_t* out) {
+  u16x2 acc = {0, 0};
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    uint4 v0 = x[i], v1 = x[i + stride], v2 = x[i + 2 * stride], v3 = x[i + 3 * stride];
+    acc = vmax_bf16(acc, v0);
+    acc = vmax_bf16(acc, v1);
+    acc = vmax_bf16(acc, v2);
+    acc = vmax_bf16(acc, v3);
+  }
+  for (; i < nvec; i += stride) acc = vmax_bf16(acc, x[i]);
+  uint32_t m = max((uint32_t)acc.x, (uint32_t)acc.y);
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7FFFu));
+  block_max_to(m << 16, out);  // bf16 magnitude widened to fp32 bits
+}
+
+__device__ __forceinline__ uint32_t vmax_f32(uint32_t acc, uint4 v) {
+  acc = max(acc, max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu));
+  acc = max(acc, max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
+  return acc;
+}
+
+__global__ __launch_bounds__(kThreads) void amax_f32_kernel(const uint4* __restrict__ x,
+                                                            int64_t nvec,
+                                                            const uint32_t* __restrict__ tail,
+                                                            int ntail, uint32_t* out) {
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    uint4 v0 = x[i], v1 = x[i + stride], v2 = x[i + 2 * stride], v3 = x[i + 3 * stride];
+    m = vmax_f32(m, v0);
+    m = vmax_f32(m, v1);
+    m = vmax_f32(m, v2);
+    m = vmax_f32(m, v3);
+  }
+  for (; i < nvec; i += stride) m = vmax_f32(m, x[i]);
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max(m, tail[threadIdx.x] & 0x7FFFFFFFu);
+  block_max_to(m, out);
+}
+
+// ---------------------------------------------------------------- bias
+// floor(log2(fmt_max / A)) - margin with fmt_max = 1.75 * 2^emax.  Writing
+// A = (1 + f) * 2^e with f in [0, 1): fmt_max / A = 1.75 / (1 + f) * 2^(emax - e)
+// and 1.75 / (1 + f) lies in (0.875, 1.75], so its floor(log2) is 0 when
+// 1 + f <= 1.75 (fraction field <= 0x600000) and -1 otherwise.
+__device__ __forceinline__ int32_t bias_from_amax_bits(uint32_t a, int fmt, int32_t margin) {
+  if (a == 0u || a >= 0x7F800000u) return 0;  // zero, inf, NaN (or a negative input)
+  int e;
+  uint32_t frac;
+  if ((a >> 23) == 0u) {  // subnormal: normalise on the leading one
+    const int p = 31 - __clz(a);
+    e = p - 149;
+    frac = (a << (23 - p)) & 0x7FFFFFu;
+  } else {
+    e = (int)(a >> 23) - 127;
+    frac = a & 0x7FFFFFu;
+  }
+  const int emax = fmt == FP8_E4M3 ? 8 : 15;
+  return emax - e - (frac > 0x600000u ? 1 : 0) - margin;
+}
+
+__global__ void bias_kernel(const uint32_t* __restrict__ amax, int fmt, int32_t margin,
+                            int32_t* __restrict__ bias) {
+  *bias = bias_from_amax_bits(*amax, fmt, margin);
+}
+
+// ---------------------------------------------------------------- cast
+// x * 2^b is formed exactly with ldexp: fp32 denormals are kept (the kernels
+// run with denormal mode "preserve"), results at or above 2^-126 are exact,
+// smaller ones cast to a signed zero in both formats anyway, and results past
+// the fp32 range become inf, which saturates like any value above fmt_max.
+// The magnitude bits a of the scaled value are then rounded to the format:
+//   normal range    round-to-nearest-even on the dropped fraction bits, the
+//                   exponent re-biased by one constant (a carry moves into the
+//                   next binade on its own);
+//   subnormal range adding 2^(23 + emin - mbits) -- the power of two whose
+//                   fp32 ulp is the format's smallest subnormal -- lets the
+//                   fp32 adder round to that quantum; the integer difference
+//                   of the bit patterns is the code;
+// then saturation at the largest finite code and NaN -> 0x7F, sign copied.
+template <int FMT>
+__device__ __forceinline__ uint32_t fp8_code(uint32_t xbits, int32_t b) {
+  const uint32_t vb = __float_as_uint(__builtin_ldexpf(__uint_as_float(xbits), b));
+  const uint32_t a = vb & 0x7FFFFFFFu;
+  uint32_t code;
+  if constexpr (FMT == FP8_E4M3) {
+    // normal: code = (fp32 exponent - 120) * 8 + top 3 fraction bits, rounded
+    const uint32_t nrm = (a + (0x7FFFFu - 0x3C000000u) + ((a >> 20) & 1u)) >> 20;
+    // subnormal (|v| < 2^-6): the ulp of 2^14 in fp32 is 2^-9
+    const uint32_t sub = __float_as_uint(__uint_as_float(a) + 16384.0f) - 0x46800000u;
+    code = a < 0x3C800000u ? sub : nrm;
+    code = min(code, 0x7Eu);
+  } else {
+    // normal: code = (fp32 exponent - 112) * 4 + top 2 fraction bits, rounded
+    const uint32_t nrm = (a + (0xFFFFFu - 0x38000000u) + ((a >> 21) & 1u)) >> 21;
+    // subnormal (|v| < 2^-14): the ulp of 2^7 in fp32 is 2^-16
+    const uint32_t sub = __float_as_uint(__uint_as_float(a) + 128.0f) - 0x43000000u;
+    code = a < 0x38800000u ? sub : nrm;
+    code = min(code, 0x7Bu);
+  }
+  code = a > 0x7F800000u ? 0x7Fu : code;
+  return code | ((vb >> 24) & 0x80u);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t pack4_bf16(uint32_t w0, uint32_t w1, int32_t b) {
+  const uint32_t c0 = fp8_code<FMT>(w0 << 16, b);
+  const uint32_t c1 = fp8_code<FMT>(w0 & 0xFFFF0000u, b);
+  const uint32_t c2 = fp8_code<FMT>(w1 << 16, b);
+  const uint32_t c3 = fp8_code<FMT>(w1 & 0xFFFF0000u, b);
+  return c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t pack4_f32(uint4 v, int32_t b) {
+  return fp8_code<FMT>(v.x, b) | (fp8_code<FMT>(v.y, b) << 8) | (fp8_code<FMT>(v.z, b) << 16) |
+         (fp8_code<FMT>(v.w, b) << 24);
+}
+
+// One unit = 16 elements -> one 16-byte store.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const uint4* __restrict__ x,
+                                                             int64_t nunit,
+                                                             const int32_t* __restrict__ bias,
+                                                             uint4* __restrict__ y,
+                                                             const uint16_t* __restrict__ tail_x,
+                                                             uint8_t* __restrict__ tail_y,
+                                                             int ntail) {
+  const int32_t b = *bias;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + stride < nunit; i += 2 * stride) {
+    const uint4 a0 = x[2 * i], a1 = x[2 * i + 1];
+    const uint4 d0 = x[2 * (i + stride)], d1 = x[2 * (i + stride) + 1];
+    uint4 o, p;
+    o.x = pack4_bf16<FMT>(a0.x, a0.y, b);
+    o.y = pack4_bf16<FMT>(a0.z, a0.w, b);
+    o.z = pack4_bf16<FMT>(a1.x, a1.y, b);
+    o.w = pack4_bf16<FMT>(a1.z, a1.w, b);
+    p.x = pack4_bf16<FMT>(d0.x, d0.y, b);
+    p.y = pack4_bf16<FMT>(d0.z, d0.w, b);
+    p.z = pack4_bf16<FMT>(d1.x, d1.y, b);
+    p.w = pack4_bf16<FMT>(d1.z, d1.w, b);
+    y[i] = o;
+    y[i + stride] = p;
+  }
+  for (; i < nunit; i += stride) {
+    const uint4 a0 = x[2 * i], a1 = x[2 * i + 1];
+    uint4 o;
+    o.x = pack4_bf16<FMT>(a0.x, a0.y, b);
+    o.y = pack4_bf16<FMT>(a0.z, a0.w, b);
+    o.z = pack4_bf16<FMT>(a1.x, a1.y, b);
+    o.w = pack4_bf16<FMT>(a1.z, a1.w, b);
+    y[i] = o;
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail)
+    tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>((uint32_t)tail_x[threadIdx.x] << 16, b);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restrict__ x,
+                                                            int64_t nunit,
+                                                            const int32_t* __restrict__ bias,
+                                                            uint4* __restrict__ y,
+                                                            const uint32_t* __restrict__ tail_x,
+                                                            uint8_t* __restrict__ tail_y,
+                                                            int ntail) {
+  const int32_t b = *bias;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nunit; i += stride) {
+    const uint4 a0 = x[4 * i], a1 = x[4 * i + 1], a2 = x[4 * i + 2], a3 = x[4 * i + 3];
+    uint4 o;
+    o.x = pack4_f32<FMT>(a0, b);
+    o.y = pack4_f32<FMT>(a1, b);
+    o.z = pack4_f32<FMT>(a2, b);
+    o.w = pack4_f32<FMT>(a3, b);
+    y[i] = o;
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail)
+    tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>(tail_x[threadIdx.x], b);
+}
+
+// Enough blocks to cover every CU several times over, capped so each lane
+// keeps a few loads in flight through the grid-stride loop.
+int stream_blocks(int64_t units_per_thread_work) {
+  const int64_t want = (units_per_thread_work + kThreads - 1) / kThreads;
+  const int64_t cap = 256 * 8;
+  return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+}  // namespace
+
+hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t stream) {
+  uint32_t* out = reinterpret_cast<uint32_t*>(amax);
+  hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, out);
+  if (n > 0) {
+    if (dtype == FP8_IN_BF16) {
+      const int64_t nvec = n / 8;
+      const int ntail = (int)(n - nvec * 8);
+      const uint16_t* tail = static_cast<const uint16_t*>(x) + nvec * 8;
+      hipLaunchKernelGGL(amax_bf16_kernel, dim3(stream_blocks(nvec / 4)), dim3(kThreads), 0,
+                         stream, static_cast<const uint4*>(x), nvec, tail, ntail, out);
+    } else {
+      const int64_t nvec = n / 4;
+      const int ntail = (int)(n - nvec * 4);
+      const uint32_t* tail = static_cast<const uint32_t*>(x) + nvec * 4;
+      hipLaunchKernelGGL(amax_f32_kernel, dim3(stream_blocks(nvec / 4)), dim3(kThreads), 0,
+                         stream, static_cast<const uint4*>(x), nvec, tail, ntail, out);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bias(const float* amax, int fmt, int32_t margin, int32_t* bias,
+                       hipStream_t stream) {
+  hipLaunchKernelGGL(bias_kernel, dim3(1), dim3(1), 0, stream,
+                     reinterpret_cast<const uint32_t*>(amax), fmt, margin, bias);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias, int fmt,
+                       uint8_t* y, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t nunit = n / 16;
+  const int ntail = (int)(n - nunit * 16);
+  uint8_t* tail_y = y + nunit * 16;
+  uint4* yv = reinterpret_cast<uint4*>(y);
+  if (dtype == FP8_IN_BF16) {
+    const uint16_t* tail_x = static_cast<const uint16_t*>(x) + nunit * 16;
+    const uint4* xv = static_cast<const uint4*>(x);
+    const dim3 grid(stream_blocks(nunit / 2));
+    if (fmt == FP8_E4M3)
+      hipLaunchKernelGGL(cast_bf16_kernel<FP8_E4M3>, grid, dim3(kThreads), 0, stream, xv, nunit,
+                         bias, yv, tail_x, tail_y, ntail);
+    else
+      hipLaunchKernelGGL(cast_bf16_kernel<FP8_E5M2>, grid, dim3(kThreads), 0, stream, xv, nunit,
+                         bias, yv, tail_x, tail_y, ntail);
+  } else {
+    const uint32_t* tail_x = static_cast<const uint32_t*>(x) + nunit * 16;
+    const uint4* xv = static_cast<const uint4*>(x);
+    const dim3 grid(stream_blocks(nunit));
+    if (fmt == FP8_E4M3)
+      hipLaunchKernelGGL(cast_f32_kernel<FP8_E4M3>, grid, dim3(kThreads), 0, stream, xv, nunit,
+                         bias, yv, tail_x, tail_y, ntail);
+    else
+      hipLaunchKernelGGL(cast_f32_kernel<FP8_E5M2>, grid, dim3(kThreads), 0, stream, xv, nunit,
+                         bias, yv, tail_x, tail_y, ntail);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp8lin

@@ -1,0 +1,133 @@
+/*
+ * fp8lin -- FP8-AMAX scaled linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the native library (libfp8lin.so).  Plain pointers and sizes only.
+ *
+ * The method: "Training and inference of large language models using 8-bit
+ * floating point" (Perez, Zhang et al., 2023), review page, section "Proposed
+ * method".  Each weight, activation and gradient tensor gets a per-tensor scale
+ * from its maximum absolute value (bullet 1); compute_bias turns that value
+ * into a power-of-two exponent from log2(format max / amplitude) with a
+ * configurable margin (bullet 2); the tensor is scaled before the FP8 cast and
+ * the matmul result is unscaled afterwards (bullet 3); weights and activations
+ * use E4 (E4M3), gradients E5 (E5M2) (bullet 4); the same products serve
+ * training (forward, data gradient, weight gradient) and post-training
+ * quantised inference (bullet 5).
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are device memory of the current HIP device (for example
+ *    torch.empty(..., device="cuda").data_ptr()).  The caller allocates every
+ *    buffer; the library never allocates, frees or keeps a pointer.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    on it and the call returns without waiting; nothing is copied to the host.
+ *  - Matrices are row-major and dense (leading dimension = column count).
+ *  - Arguments are checked on the host before any HIP call; on error the call
+ *    returns a negative status synchronously and leaves every output untouched.
+ *    A launch failure returns FP8_ERR_HIP; a fault during execution surfaces at
+ *    the caller's next synchronisation.
+ *  - Calls are thread-safe.  Calls that write the same output must not overlap.
+ */
+#ifndef FP8LIN_H
+#define FP8LIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* FP8 encodings (OCP 8-bit floating point): the page's FP8_E4 and FP8_E5. */
+typedef enum {
+  FP8_E4M3 = 0, /* 1-4-3, exponent bias 7, max 448, no infinity, NaN = S.1111.111 */
+  FP8_E5M2 = 1  /* 1-5-2, exponent bias 15, max 57344, inf = S.11111.00 (never produced) */
+} fp8_format_t;
+
+/* Element type of a high-precision input tensor. */
+typedef enum {
+  FP8_IN_BF16 = 0, /* 2-byte bfloat16 */
+  FP8_IN_FP32 = 1  /* 4-byte IEEE binary32 */
+} fp8_dtype_t;
+
+/* Status codes. */
+#define FP8_OK 0
+#define FP8_ERR_NULL (-1)   /* a required pointer is NULL */
+#define FP8_ERR_SIZE (-2)   /* a size is negative or too large */
+#define FP8_ERR_FORMAT (-3) /* format is not an fp8_format_t */
+#define FP8_ERR_DTYPE (-4)  /* dtype is not an fp8_dtype_t */
+#define FP8_ERR_ALIGN (-5)  /* a pointer that must be 16-byte aligned is not */
+#define FP8_ERR_MARGIN (-6) /* |margin| > FP8_MAX_MARGIN */
+#define FP8_ERR_DEVICE (-7) /* no HIP device, or the current device is not gfx950 */
+#define FP8_ERR_HIP (-8)    /* a HIP launch failed */
+
+#define FP8_MAX_MARGIN 64
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fp8_status_string(int status);
+
+/*
+ * Per-tensor maximum absolute value ("Proposed method", bullet 1).
+ *   x     device, n elements of `dtype`, 16-byte aligned.
+ *   amax  device, one float: written with max_i |x_i|.  The result is exact
+ *         (a bf16 value widens to float without rounding).  Any NaN element
+ *         makes it the NaN with the largest magnitude bits; otherwise any
+ *         infinity makes it +inf; n == 0 gives +0.
+ * Two launches on `stream`: one clearing *amax, one reduction.
+ */
+int fp8_amax(const void* x, fp8_dtype_t dtype, int64_t n, float* amax, void* stream);
+
+/*
+ * Scaling bias ("Proposed method", bullet 2): the largest integer b with
+ * amax * 2^b <= fmt_max, minus `margin`, i.e. floor(log2(fmt_max/amax)) - margin,
+ * evaluated exactly from the exponent and mantissa fields.  fmt_max is 448
+ * (E4M3) or 57344 (E5M2).  An amax of 0, inf or NaN gives b = 0 and the margin
+ * is not applied.
+ *   amax  device, one float (normally the output of fp8_amax).
+ *   bias  device, one int32, written.
+ *   |margin| <= FP8_MAX_MARGIN; a positive margin leaves headroom below
+ *   fmt_max, a negative one makes the largest values saturate.
+ */
+int fp8_compute_bias(const float* amax, fp8_format_t fmt, int32_t margin, int32_t* bias,
+                     void* stream);
+
+/*
+ * Scale then cast ("Proposed method", bullets 3-4): y[i] = FP8 code nearest to
+ * x[i] * 2^bias.  The product is exact; rounding is to nearest with ties to the
+ * even code; magnitudes beyond fmt_max and infinities saturate to the largest
+ * finite code; FP8 subnormals are produced; zero and underflow keep the sign
+ * (-0 is 0x80); NaN becomes 0x7F | sign.
+ *   x     device, n elements of `dtype`, 16-byte aligned.
+ *   bias  device, one int32 (normally the output of fp8_compute_bias).
+ *   y     device, n bytes, 16-byte aligned, written.
+ */
+int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* bias,
+                   fp8_format_t fmt, uint8_t* y, void* stream);
+
+/*
+ * The three FP8 x FP8 products with fp32 accumulation, unscaled after the
+ * matmul ("Proposed method", bullets 3 and 5).  Each output is overwritten
+ * (no accumulation into it).  Operands may use either format in any pairing.
+ * All pointers are device memory; byte operands and outputs must be 16-byte
+ * aligned.  M, N, K >= 0 (K == 0 writes zeros; M == 0 or N == 0 is a no-op).
+ * bx, bw, bdy: device, one int32 each -- the operands' scaling biases.
+ */
+
+/* Forward: Y[M x N] = 2^-(bx+bw) * X8[M x K] . W8[N x K]^T */
+int fp8_scaled_gemm_fwd(const uint8_t* x8, fp8_format_t fx, const int32_t* bx,
+                        const uint8_t* w8, fp8_format_t fw, const int32_t* bw,
+                        int64_t M, int64_t N, int64_t K, float* y, void* stream);
+
+/* Data gradient: dX[M x K] = 2^-(bdy+bw) * dY8[M x N] . W8[N x K] */
+int fp8_scaled_gemm_dgrad(const uint8_t* dy8, fp8_format_t fdy, const int32_t* bdy,
+                          const uint8_t* w8, fp8_format_t fw, const int32_t* bw,
+                          int64_t M, int64_t N, int64_t K, float* dx, void* stream);
+
+/* Weight gradient: dW[N x K] = 2^-(bdy+bx) * dY8[M x N]^T . X8[M x K] */
+int fp8_scaled_gemm_wgrad(const uint8_t* dy8, fp8_format_t fdy, const int32_t* bdy,
+                          const uint8_t* x8, fp8_format_t fx, const int32_t* bx,
+                          int64_t M, int64_t N, int64_t K, float* dw, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8LIN_H */

@@ -51,6 +51,8 @@ def lib():
             build()
         L = ctypes.CDLL(_LIB)
         vp, i64, i32, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+        L.oracle_threads.restype = ci
+        L.oracle_threads.argtypes = []
         L.oracle_amax.restype = ctypes.c_uint32
         L.oracle_amax.argtypes = [vp, ci, i64]
         L.oracle_compute_bias.restype = i32
@@ -69,6 +71,11 @@ def lib():
             f.argtypes = [vp, ci, i32, vp, ci, i32, i64, i64, i64, vp, vp, i64, vp, vp]
         _lib = L
     return _lib
+
+
+def threads():
+    """Threads the oracle's OpenMP loops use."""
+    return int(lib().oracle_threads())
 
 
 def _words(x):

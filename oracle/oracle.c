@@ -41,11 +41,23 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_BF16 0
 #define ORACLE_F32 1
 #define ORACLE_E4M3 0
 #define ORACLE_E5M2 1
+
+/* Threads the OpenMP loops below may use (1 without OpenMP). */
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 enum { CLS_ZERO = 0, CLS_FINITE = 1, CLS_INF = 2, CLS_NAN = 3 };
 

@@ -1,0 +1,115 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/fp8lin.h declares, and rejects bad arguments on the host before any
+HIP call, with the documented status codes."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8lin.h")
+
+import fp8_precision_linear_amd as fl  # noqa: E402
+
+L = fl.lib
+P = ctypes.c_void_p
+A16, A32, A48 = P(16), P(32), P(48)   # aligned fake addresses: never dereferenced here
+MIS = P(17)                           # misaligned fake address
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_[a-z0-9_]+)\s*\(", text)))
+
+
+def status(code):
+    return {v: k for k, v in fl.STATUS.items()}[code]
+
+
+def test_every_declared_function_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in fl.SIGNATURES, n
+
+
+def test_status_strings():
+    for code in list(fl.STATUS) + [-99]:
+        s = L.fp8_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def test_amax_argument_checks():
+    assert L.fp8_amax(A16, 0, -1, A32, None) == status("FP8_ERR_SIZE")
+    assert L.fp8_amax(A16, 7, 10, A32, None) == status("FP8_ERR_DTYPE")
+    assert L.fp8_amax(None, 0, 10, A32, None) == status("FP8_ERR_NULL")
+    assert L.fp8_amax(A16, 0, 10, None, None) == status("FP8_ERR_NULL")
+    assert L.fp8_amax(MIS, 1, 10, A32, None) == status("FP8_ERR_ALIGN")
+
+
+def test_bias_argument_checks():
+    assert L.fp8_compute_bias(A16, 2, 0, A32, None) == status("FP8_ERR_FORMAT")
+    assert L.fp8_compute_bias(A16, 0, 65, A32, None) == status("FP8_ERR_MARGIN")
+    assert L.fp8_compute_bias(A16, 1, -65, A32, None) == status("FP8_ERR_MARGIN")
+    assert L.fp8_compute_bias(None, 0, 0, A32, None) == status("FP8_ERR_NULL")
+    assert L.fp8_compute_bias(A16, 0, 0, None, None) == status("FP8_ERR_NULL")
+
+
+def test_cast_argument_checks():
+    assert L.fp8_scale_cast(A16, 0, -5, A32, 0, A48, None) == status("FP8_ERR_SIZE")
+    assert L.fp8_scale_cast(A16, 3, 5, A32, 0, A48, None) == status("FP8_ERR_DTYPE")
+    assert L.fp8_scale_cast(A16, 0, 5, A32, -1, A48, None) == status("FP8_ERR_FORMAT")
+    assert L.fp8_scale_cast(A16, 0, 5, None, 0, A48, None) == status("FP8_ERR_NULL")
+    assert L.fp8_scale_cast(A16, 0, 5, A32, 0, None, None) == status("FP8_ERR_NULL")
+    assert L.fp8_scale_cast(MIS, 0, 5, A32, 0, A48, None) == status("FP8_ERR_ALIGN")
+    assert L.fp8_scale_cast(A16, 0, 5, A32, 0, MIS, None) == status("FP8_ERR_ALIGN")
+    # n == 0 is a no-op: nothing is checked further and nothing is launched
+    assert L.fp8_scale_cast(None, 0, 0, None, 0, None, None) == 0
+
+
+@pytest.mark.parametrize("fn", ["fp8_scaled_gemm_fwd", "fp8_scaled_gemm_dgrad", "fp8_scaled_gemm_wgrad"])
+def test_gemm_argument_checks(fn):
+    f = getattr(L, fn)
+    ok = (A16, 0, A32, A48, 0, A32, 64, 64, 64, A16, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["a", "fa", "ba", "b", "fb", "bb", "M", "N", "K", "out", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    assert call(M=-1) == status("FP8_ERR_SIZE")
+    assert call(K=1 << 31) == status("FP8_ERR_SIZE")
+    assert call(fa=2) == status("FP8_ERR_FORMAT")
+    assert call(fb=-1) == status("FP8_ERR_FORMAT")
+    assert call(out=None) == status("FP8_ERR_NULL")
+    assert call(ba=None) == status("FP8_ERR_NULL")
+    assert call(a=None) == status("FP8_ERR_NULL")
+    assert call(b=None) == status("FP8_ERR_NULL")
+    assert call(a=MIS) == status("FP8_ERR_ALIGN")
+    assert call(out=MIS) == status("FP8_ERR_ALIGN")
+    # an empty output is a no-op whatever the pointers are; an empty
+    # contraction still writes the (zero) output, so it needs the pointers
+    out_dim, contraction = {"fp8_scaled_gemm_fwd": ("M", "K"), "fp8_scaled_gemm_dgrad": ("M", "N"),
+                            "fp8_scaled_gemm_wgrad": ("N", "M")}[fn]
+    assert call(**{out_dim: 0}, a=None, b=None, out=None, ba=None) == 0
+    assert call(**{contraction: 0}, out=None) == status("FP8_ERR_NULL")
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
+def test_valid_calls_without_a_device_report_no_device():
+    assert L.fp8_amax(A16, 0, 10, A32, None) == status("FP8_ERR_DEVICE")
+    assert L.fp8_compute_bias(A16, 0, 0, A32, None) == status("FP8_ERR_DEVICE")
+    assert L.fp8_scale_cast(A16, 0, 5, A32, 0, A48, None) == status("FP8_ERR_DEVICE")
+    assert L.fp8_scaled_gemm_fwd(A16, 0, A32, A48, 0, A32, 64, 64, 64, A16, None) == status("FP8_ERR_DEVICE")
+
+
+def test_python_wrappers_reject_cpu_tensors():
+    x = torch.zeros(16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fl.amax(x)

@@ -1,0 +1,183 @@
+"""GPU parity of the three FP8 products against the CPU oracle.
+
+Forward Y = X8 W8^T, data gradient dX = dY8 W8, weight gradient dW = dY8^T X8,
+each unscaled by 2^-(bias_a + bias_b) ("Training and inference of large
+language models using 8-bit floating point", review page, "Proposed method",
+bullets 3 and 5).  The bar, elementwise:
+    |gpu - oracle| <= 1e-5 * 2^-(ba+bb) * sum_k |a_k| |b_k|
+so an all-zero row or column must be exactly 0.  The FP8 operands are made by
+the oracle (or drawn as codes) and uploaded: nothing the GPU computed feeds
+an expected value.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import check_gemm, i32_dev, need_gpu, say, u8_dev
+
+pytestmark = pytest.mark.gpu
+E4M3, E5M2 = 0, 1
+PAIRS = [(E4M3, E4M3), (E5M2, E4M3), (E4M3, E5M2), (E5M2, E5M2)]
+
+
+@pytest.fixture(scope="module")
+def fl():
+    return need_gpu()
+
+
+@pytest.fixture(params=["auto", "128", "256"])
+def tile(request, monkeypatch):
+    if request.param != "auto":
+        monkeypatch.setenv("FP8LIN_GEMM_TILE", request.param)
+    else:
+        monkeypatch.delenv("FP8LIN_GEMM_TILE", raising=False)
+    return request.param
+
+
+def finite_codes(rng, shape, fmt):
+    c = rng.integers(0, 256, shape, dtype=np.uint8)
+    bad = (c & 0x7F) == 0x7F if fmt == E4M3 else (c & 0x7F) >= 0x7C
+    c[bad] &= 0xF0
+    return c
+
+
+def run(fl, which, a8, fa, ba, b8, fb, bb):
+    """GPU product through the C ABI; returns a float32 numpy array."""
+    A, B = u8_dev(a8), u8_dev(b8)
+    BA, BB = i32_dev(ba), i32_dev(bb)
+    fn = {"fwd": fl.scaled_gemm_fwd, "dgrad": fl.scaled_gemm_dgrad, "wgrad": fl.scaled_gemm_wgrad}[which]
+    return fn(A, fa, BA, B, fb, BB).cpu().numpy()
+
+
+def reference(which, a8, fa, ba, b8, fb, bb):
+    fn = {"fwd": oracle.gemm_fwd, "dgrad": oracle.gemm_dgrad, "wgrad": oracle.gemm_wgrad}[which]
+    return fn(a8, fa, ba, b8, fb, bb)
+
+
+def operands(rng, which, M, N, K, fa, fb):
+    """(a8, b8) in the layouts of the product: fwd X8[MxK], W8[NxK];
+    dgrad dY8[MxN], W8[NxK]; wgrad dY8[MxN], X8[MxK]."""
+    if which == "fwd":
+        return finite_codes(rng, (M, K), fa), finite_codes(rng, (N, K), fb)
+    if which == "dgrad":
+        return finite_codes(rng, (M, N), fa), finite_codes(rng, (N, K), fb)
+    return finite_codes(rng, (M, N), fa), finite_codes(rng, (M, K), fb)
+
+
+SHAPES = [(300, 520, 392), (1, 17, 1), (64, 64, 0), (257, 129, 1000), (128, 256, 256),
+          (33, 700, 130), (512, 512, 128), (260, 300, 17)]
+
+
+@pytest.mark.parametrize("which", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("fa,fb", PAIRS)
+def test_small_and_ragged_shapes(fl, tile, which, fa, fb):
+    rng = np.random.default_rng(hash((which, fa, fb)) & 0xFFFF)
+    for (M, N, K) in SHAPES:
+        a8, b8 = operands(rng, which, M, N, K, fa, fb)
+        ba, bb = (int(v) for v in rng.integers(-12, 20, 2))
+        say("gemm", which, "tile", tile, "fmts", fa, fb, "MNK", M, N, K)
+        got = run(fl, which, a8, fa, ba, b8, fb, bb)
+        ref, bound = reference(which, a8, fa, ba, b8, fb, bb)
+        assert got.shape == ref.shape
+        check_gemm(got, ref, bound, f"{which} {M}x{N}x{K} fmts {fa},{fb} tile {tile}")
+
+
+@pytest.mark.parametrize("which", ["fwd", "dgrad", "wgrad"])
+def test_identity_operand_is_exact_including_subnormals(fl, tile, which):
+    """With the other operand the identity (code 0x38 = 1.0), every output is a
+    single product: exact, so FP8 subnormal inputs must not be flushed."""
+    rng = np.random.default_rng(17)
+    n = 160
+    eye = np.where(np.eye(n, dtype=bool), 0x38, 0x00).astype(np.uint8)
+    codes = finite_codes(rng, (n, n), E5M2)
+    codes[:, :40] = rng.integers(0, 4, (n, 40)).astype(np.uint8) | (rng.integers(0, 2, (n, 40)).astype(np.uint8) << 7)
+    vals = oracle.decode_fp8(codes, E5M2)
+    say("identity", which, "tile", tile)
+    if which == "fwd":
+        got = run(fl, which, codes, E5M2, 3, eye, E4M3, 0)
+        want = vals * 2.0 ** -3
+    elif which == "dgrad":
+        got = run(fl, which, codes, E5M2, 3, eye, E4M3, 0)
+        want = vals * 2.0 ** -3
+    else:
+        got = run(fl, which, codes, E5M2, 3, eye, E4M3, 0)
+        want = vals.T * 2.0 ** -3
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_all_positive_long_contraction_stays_within_bound(fl):
+    """Accumulation stress: same-sign products over K = 28672 (the longest
+    contraction in the workloads), where fp32 rounding adds up fastest."""
+    rng = np.random.default_rng(99)
+    M, N, K = 96, 80, 28672
+    x8 = rng.integers(0x30, 0x60, (M, K), dtype=np.uint8)   # positive E4M3 codes
+    w8 = rng.integers(0x30, 0x60, (N, K), dtype=np.uint8)
+    say("positive long K", M, N, K)
+    got = run(fl, "fwd", x8, E4M3, 0, w8, E4M3, 0)
+    ref, bound = oracle.gemm_fwd(x8, E4M3, 0, w8, E4M3, 0)
+    worst = check_gemm(got, ref, bound, "all-positive fwd K=28672")
+    print("worst err/bound", worst)
+
+
+def _sample_positions(rng, rows, cols, count=65536):
+    r = rng.integers(0, rows, count)
+    c = rng.integers(0, cols, count)
+    # plus the first and the last 256 x 256 output tiles
+    t = np.arange(256)
+    fr, fc = np.meshgrid(t[t < rows], t[t < cols], indexing="ij")
+    lr, lc = np.meshgrid(np.arange(max(rows - 256, 0), rows), np.arange(max(cols - 256, 0), cols), indexing="ij")
+    return (np.concatenate([r, fr.ravel(), lr.ravel()]).astype(np.int64),
+            np.concatenate([c, fc.ravel(), lc.ravel()]).astype(np.int64))
+
+
+def _quantized(w, name, cache):
+    if name not in cache:
+        t = w.tensor(name)
+        words = synth.bf16_words(synth.workload_tensor(w, name))
+        a, b, codes = oracle.quantize(words, t.fmt, t.margin)
+        cache[name] = (codes, b, t.fmt)
+    return cache[name]
+
+
+@pytest.mark.parametrize("wl", [1, 2, 3, 4, 5])
+def test_workload_products(fl, wl):
+    """Every product of a workload at its full size, in the launch configuration
+    the benchmark uses; the oracle checks every output for the two small
+    workloads and 65536 random outputs plus the first and last 256x256 tiles
+    of each product for the others."""
+    w = synth.WORKLOADS[wl]
+    rng = np.random.default_rng(wl)
+    cache = {}
+    full = wl <= 2
+    for l in w.linears:
+        x8, bx, fx = _quantized(w, l.x, cache)
+        wt8, bw, fw = _quantized(w, l.w, cache)
+        if l.dy:
+            dy8, bdy, fdy = _quantized(w, l.dy, cache)
+        for which in l.passes:
+            if which == "fwd":
+                a8, fa, ba, b8, fb, bb = x8, fx, bx, wt8, fw, bw
+                shape = (l.M, l.N)
+            elif which == "dgrad":
+                a8, fa, ba, b8, fb, bb = dy8, fdy, bdy, wt8, fw, bw
+                shape = (l.M, l.K)
+            else:
+                a8, fa, ba, b8, fb, bb = dy8, fdy, bdy, x8, fx, bx
+                shape = (l.N, l.K)
+            say("workload", wl, l.name, which, "out", shape)
+            got = run(fl, which, a8, fa, ba, b8, fb, bb)
+            assert got.shape == shape
+            if full:
+                ref, bound = reference(which, a8, fa, ba, b8, fb, bb)
+                check_gemm(got, ref, bound, f"wl{wl} {l.name} {which}")
+            else:
+                rows, cols = _sample_positions(rng, *shape)
+                at = {"fwd": oracle.gemm_fwd_at, "dgrad": oracle.gemm_dgrad_at,
+                      "wgrad": oracle.gemm_wgrad_at}[which]
+                ref, bound = at(a8, fa, ba, b8, fb, bb, rows, cols)
+                check_gemm(got[rows, cols], ref, bound, f"wl{wl} {l.name} {which}")
+            del got

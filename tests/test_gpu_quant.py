@@ -1,0 +1,136 @@
+"""GPU parity of amax, compute_bias and scale-then-cast against the CPU oracle.
+
+All three must match bit for bit ("Training and inference of large language
+models using 8-bit floating point", review page, "Proposed method", bullets
+1-4).  Every call goes through the C ABI (the ctypes binding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import bf16_dev, f32_dev, i32_dev, need_gpu, say, words_of
+
+pytestmark = pytest.mark.gpu
+E4M3, E5M2 = 0, 1
+
+
+@pytest.fixture(scope="module")
+def fl():
+    return need_gpu()
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_cast_every_bf16_word_for_every_bias(fl, fmt):
+    words = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = bf16_dev(words)
+    biases = list(range(-140, 161)) + [-200, 221]
+    out = torch.empty((len(biases), 65536), dtype=torch.uint8, device="cuda")
+    say("cast all bf16 words", "fmt", fmt, "biases", biases[0], "..", biases[-1])
+    for r, b in enumerate(biases):
+        fl.scale_cast(x, i32_dev(b), fmt, out=out[r])
+    got = out.cpu().numpy()
+    for r, b in enumerate(biases):
+        ref = oracle.scale_cast(words, b, fmt)
+        if not np.array_equal(got[r], ref):
+            bad = np.where(got[r] != ref)[0][:8]
+            raise AssertionError(f"fmt {fmt} bias {b}: words {words[bad]} gpu {got[r][bad]} oracle {ref[bad]}")
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_cast_fp32_words(fl, fmt):
+    rng = np.random.default_rng(21)
+    words = rng.integers(0, 2 ** 32, 2_000_003, dtype=np.uint64).astype(np.uint32)
+    e = rng.integers(95, 150, 1_000_000).astype(np.uint32)
+    words[:1_000_000] = (words[:1_000_000] & 0x807FFFFF) | (e << 23)
+    words[1_000_000:1_000_100] = np.arange(100, dtype=np.uint32)       # fp32 subnormals
+    x = f32_dev(words)
+    for b in (-150, -40, -6, 0, 1, 9, 17, 64, 140, 220):
+        say("cast fp32 words", "fmt", fmt, "bias", b, "n", words.size)
+        got = fl.scale_cast(x, i32_dev(b), fmt).cpu().numpy()
+        ref = oracle.scale_cast(words, b, fmt)
+        assert np.array_equal(got, ref), f"bias {b}: {np.count_nonzero(got != ref)} codes differ"
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 15, 16, 17, 31, 33, 255, 4097, 1_000_003])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_amax_and_cast_ragged_sizes(fl, n, dtype):
+    rng = np.random.default_rng(n)
+    v = (rng.standard_normal(n) * 3).astype(np.float32)
+    if dtype == "bf16":
+        words = synth.bf16_words(torch.from_numpy(v).to(torch.bfloat16))
+        x = bf16_dev(words)
+    else:
+        words = v.view(np.uint32)
+        x = f32_dev(words)
+    say("ragged", dtype, "n", n)
+    a = fl.amax(x)
+    assert int(words_of(a)[0]) == oracle.amax_bits(words)
+    for fmt, margin in ((E4M3, 0), (E5M2, 2), (E4M3, -1)):
+        b = fl.compute_bias(a, fmt, margin)
+        assert int(b.item()) == oracle.compute_bias(oracle.amax_bits(words), fmt, margin)
+        y = fl.scale_cast(x, b, fmt).cpu().numpy()
+        assert np.array_equal(y, oracle.scale_cast(words, int(b.item()), fmt))
+
+
+def test_amax_special_values_anywhere(fl):
+    rng = np.random.default_rng(3)
+    n = 100_003
+    base = synth.bf16_words(torch.from_numpy(rng.standard_normal(n).astype(np.float32)).to(torch.bfloat16))
+    cases = {"+inf": 0x7F80, "-inf": 0xFF80, "nan": 0x7FC0, "-nan big": 0xFFFF, "huge": 0x7F7F,
+             "-huge": 0xFF7F, "subnormal only": None}
+    for name, w in cases.items():
+        for pos in (0, 5, n // 2, n - 9, n - 1):     # head, inside a vector, middle, tail
+            words = base.copy()
+            if w is None:
+                words = (np.arange(n) % 0x7F + 1).astype(np.uint16)     # all bf16 subnormals
+            else:
+                words[pos] = w
+            say("amax special", name, "pos", pos)
+            got = int(words_of(fl.amax(bf16_dev(words)))[0])
+            assert got == oracle.amax_bits(words), (name, pos, hex(got))
+    # empty tensor -> +0 (the clear still runs)
+    a = torch.full((1,), 7.0, device="cuda")
+    fl.lib.fp8_amax(None, 0, 0, a.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert a.item() == 0.0
+
+
+@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+def test_bias_every_positive_bf16_amax(fl, fmt):
+    words = np.arange(1, 0x7F80, dtype=np.uint32)
+    step = 1 if fmt == E4M3 else 5
+    bits = (words[::step] << 16).astype(np.uint32)
+    amax = f32_dev(bits)
+    out = torch.empty(bits.size, dtype=torch.int32, device="cuda")
+    say("bias sweep", fmt, bits.size)
+    for i in range(bits.size):
+        fl.compute_bias(amax[i:i + 1], fmt, 0, out=out[i:i + 1])
+    got = out.cpu().numpy()
+    ref = np.array([oracle.compute_bias(int(b), fmt, 0) for b in bits])
+    assert np.array_equal(got, ref)
+    # margins and special amax values
+    specials = [0, 0x80000000, 0x7F800000, 0x7FC00000, 1, 0x7F7FFFFF, 0x43E00000, 0x43E00001]
+    for s in specials:
+        for m in (-64, -3, 0, 1, 64):
+            b = fl.compute_bias(f32_dev(np.array([s], np.uint32)), fmt, m)
+            assert int(b.item()) == oracle.compute_bias(s, fmt, m), (hex(s), m)
+
+
+@pytest.mark.parametrize("wl", [1, 2, 3, 4, 5])
+def test_workload_tensors_bit_exact(fl, wl):
+    w = synth.WORKLOADS[wl]
+    for t in w.tensors:
+        x = synth.workload_tensor(w, t.name)
+        words = synth.bf16_words(x)
+        say("workload", wl, t.name, tuple(t.shape), "fmt", t.fmt, "margin", t.margin)
+        codes, bias, amax = fl.quantize(x.cuda(), t.fmt, t.margin)
+        a_ref = oracle.amax_bits(words)
+        b_ref = oracle.compute_bias(a_ref, t.fmt, t.margin)
+        assert int(words_of(amax)[0]) == a_ref, t.name
+        assert int(bias.item()) == b_ref, t.name
+        got = codes.cpu().numpy().reshape(-1)
+        ref = oracle.scale_cast(words.reshape(-1), b_ref, t.fmt)
+        assert np.array_equal(got, ref), f"{t.name}: {np.count_nonzero(got != ref)} codes differ"
+        del codes, x
