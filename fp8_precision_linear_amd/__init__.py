@@ -27,7 +27,11 @@ MAX_MARGIN = 64
 
 STATUS = {0: "FP8_OK", -1: "FP8_ERR_NULL", -2: "FP8_ERR_SIZE", -3: "FP8_ERR_FORMAT",
           -4: "FP8_ERR_DTYPE", -5: "FP8_ERR_ALIGN", -6: "FP8_ERR_MARGIN",
-          -7: "FP8_ERR_DEVICE", -8: "FP8_ERR_HIP"}
+          -7: "FP8_ERR_DEVICE", -8: "FP8_ERR_HIP", -9: "FP8_ERR_OP"}
+
+# Product arithmetic (fp8_scaled_gemm's `math`) and products (its `op`).
+MATH_EXACT, MATH_NATIVE_FP8 = 0, 1
+OP_FWD, OP_DGRAD, OP_WGRAD = 0, 1, 2
 
 # Exported symbols and their C signatures (include/fp8lin.h).
 _vp, _i64, _i32, _ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
@@ -36,6 +40,7 @@ SIGNATURES = {
     "fp8_amax": (_ci, [_vp, _ci, _i64, _vp, _vp]),
     "fp8_compute_bias": (_ci, [_vp, _ci, _i32, _vp, _vp]),
     "fp8_scale_cast": (_ci, [_vp, _ci, _i64, _vp, _ci, _vp, _vp]),
+    "fp8_scaled_gemm": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_fwd": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_dgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_wgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
@@ -163,4 +168,29 @@ def scaled_gemm_wgrad(dy8, fdy, bdy, x8, fx, bx, out=None, stream=None):
     _check("fp8_scaled_gemm_wgrad",
            lib.fp8_scaled_gemm_wgrad(_ptr(dy8), int(fdy), _ptr(bdy), _ptr(x8), int(fx), _ptr(bx),
                                      M, N, K, _ptr(out), _stream(stream)))
+    return out
+
+
+def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=None):
+    """Any of the three products with a chosen arithmetic (fp8_scaled_gemm).
+    op: OP_FWD (a = X8[M, K], b = W8[N, K]), OP_DGRAD (a = dY8[M, N], b = W8[N, K])
+    or OP_WGRAD (a = dY8[M, N], b = X8[M, K]); math: MATH_EXACT or MATH_NATIVE_FP8."""
+    _need_cuda(a8, b8, ba, bb)
+    if op == OP_FWD:
+        (M, K), (N, K2) = a8.shape, b8.shape
+        shape, ok = (M, N), K == K2
+    elif op == OP_DGRAD:
+        (M, N), (N2, K) = a8.shape, b8.shape
+        shape, ok = (M, K), N == N2
+    elif op == OP_WGRAD:
+        (M, N), (M2, K) = a8.shape, b8.shape
+        shape, ok = (N, K), M == M2
+    else:
+        raise ValueError(f"unknown op {op}")
+    if not ok:
+        raise ValueError("contraction sizes differ")
+    out = torch.empty(shape, dtype=torch.float32, device=a8.device) if out is None else out
+    _check("fp8_scaled_gemm",
+           lib.fp8_scaled_gemm(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8), int(fb),
+                               _ptr(bb), M, N, K, _ptr(out), _stream(stream)))
     return out

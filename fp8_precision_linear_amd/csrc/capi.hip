@@ -61,6 +61,7 @@ const char* fp8_status_string(int status) {
     case FP8_ERR_MARGIN: return "margin out of range";
     case FP8_ERR_DEVICE: return "no gfx950 HIP device is current";
     case FP8_ERR_HIP: return "a HIP launch failed";
+    case FP8_ERR_OP: return "unknown product or math selector";
     default: return "unknown status";
   }
 }
@@ -95,39 +96,63 @@ int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* b
   return hip_status(fp8lin::launch_cast(x, dtype, n, bias, fmt, y, (hipStream_t)stream));
 }
 
+int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
+                    const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
+                    int64_t M, int64_t N, int64_t K, float* out, void* stream) {
+  if (math != FP8_GEMM_EXACT && math != FP8_GEMM_NATIVE_FP8) return FP8_ERR_OP;
+  hipStream_t st = (hipStream_t)stream;
+  switch (op) {
+    case FP8_GEMM_FWD: {
+      // Y[M x N]: X8 and W8 both contraction (K) contiguous.
+      if (int s = gemm_checks(a, fa, ba, b, fb, bb, M, N, K, out, M * K, N * K)) return s;
+      if (M == 0 || N == 0) return FP8_OK;
+      if (int s = device_ok()) return s;
+      fp8lin::GemmProblem p{a, K, true, fa, ba, b, K, true, fb, bb, out, N,
+                            (int)M, (int)N, (int)K, math};
+      return hip_status(fp8lin::launch_gemm_fwd(p, st));
+    }
+    case FP8_GEMM_DGRAD: {
+      // dX[M x K]: rows of dY8 (contraction N contiguous) times W8 read as
+      // [contraction N][K] (the contraction is its slow index).
+      if (int s = gemm_checks(a, fa, ba, b, fb, bb, M, K, N, out, M * N, N * K)) return s;
+      if (M == 0 || K == 0) return FP8_OK;
+      if (int s = device_ok()) return s;
+      fp8lin::GemmProblem p{a, N, true, fa, ba, b, K, false, fb, bb, out, K,
+                            (int)M, (int)K, (int)N, math};
+      return hip_status(fp8lin::launch_gemm_dgrad(p, st));
+    }
+    case FP8_GEMM_WGRAD: {
+      // dW[N x K]: dY8 read as [contraction M][N] times X8 read as [contraction M][K].
+      if (int s = gemm_checks(a, fa, ba, b, fb, bb, N, K, M, out, M * N, M * K)) return s;
+      if (N == 0 || K == 0) return FP8_OK;
+      if (int s = device_ok()) return s;
+      fp8lin::GemmProblem p{a, N, false, fa, ba, b, K, false, fb, bb, out, K,
+                            (int)N, (int)K, (int)M, math};
+      return hip_status(fp8lin::launch_gemm_wgrad(p, st));
+    }
+    default:
+      return FP8_ERR_OP;
+  }
+}
+
 int fp8_scaled_gemm_fwd(const uint8_t* x8, fp8_format_t fx, const int32_t* bx,
                         const uint8_t* w8, fp8_format_t fw, const int32_t* bw, int64_t M,
                         int64_t N, int64_t K, float* y, void* stream) {
-  if (int s = gemm_checks(x8, fx, bx, w8, fw, bw, M, N, K, y, M * K, N * K)) return s;
-  if (M == 0 || N == 0) return FP8_OK;
-  if (int s = device_ok()) return s;
-  fp8lin::GemmProblem p{x8, K, true, fx, bx, w8, K, true, fw, bw, y, N, (int)M, (int)N, (int)K};
-  return hip_status(fp8lin::launch_gemm(p, (hipStream_t)stream));
+  return fp8_scaled_gemm(FP8_GEMM_FWD, FP8_GEMM_EXACT, x8, fx, bx, w8, fw, bw, M, N, K, y, stream);
 }
 
 int fp8_scaled_gemm_dgrad(const uint8_t* dy8, fp8_format_t fdy, const int32_t* bdy,
                           const uint8_t* w8, fp8_format_t fw, const int32_t* bw, int64_t M,
                           int64_t N, int64_t K, float* dx, void* stream) {
-  // dX[M x K]: rows m of dY8 (contraction N contiguous) times W8 read as
-  // [contraction N][K] (contraction is the slow index).
-  if (int s = gemm_checks(dy8, fdy, bdy, w8, fw, bw, M, K, N, dx, M * N, N * K)) return s;
-  if (M == 0 || K == 0) return FP8_OK;
-  if (int s = device_ok()) return s;
-  fp8lin::GemmProblem p{dy8, N, true, fdy, bdy, w8, K, false, fw, bw, dx, K,
-                        (int)M, (int)K, (int)N};
-  return hip_status(fp8lin::launch_gemm(p, (hipStream_t)stream));
+  return fp8_scaled_gemm(FP8_GEMM_DGRAD, FP8_GEMM_EXACT, dy8, fdy, bdy, w8, fw, bw, M, N, K, dx,
+                         stream);
 }
 
 int fp8_scaled_gemm_wgrad(const uint8_t* dy8, fp8_format_t fdy, const int32_t* bdy,
                           const uint8_t* x8, fp8_format_t fx, const int32_t* bx, int64_t M,
                           int64_t N, int64_t K, float* dw, void* stream) {
-  // dW[N x K]: dY8 read as [contraction M][N] times X8 read as [contraction M][K].
-  if (int s = gemm_checks(dy8, fdy, bdy, x8, fx, bx, N, K, M, dw, M * N, M * K)) return s;
-  if (N == 0 || K == 0) return FP8_OK;
-  if (int s = device_ok()) return s;
-  fp8lin::GemmProblem p{dy8, N, false, fdy, bdy, x8, K, false, fx, bx, dw, K,
-                        (int)N, (int)K, (int)M};
-  return hip_status(fp8lin::launch_gemm(p, (hipStream_t)stream));
+  return fp8_scaled_gemm(FP8_GEMM_WGRAD, FP8_GEMM_EXACT, dy8, fdy, bdy, x8, fx, bx, M, N, K, dw,
+                         stream);
 }
 
 }  // extern "C"

@@ -25,16 +25,27 @@
 //    time, so neighbouring tiles share operand panels in that XCD's L2.
 //  * The unscale is one v_ldexp_f32 per output in the epilogue (exact unless
 //    the result is an fp32 subnormal).
+#pragma once
+
 #include <cstdlib>
 #include <type_traits>
 
 #include "internal.h"
 
 namespace fp8lin {
-namespace {
+namespace gemm_detail {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// Product arithmetic.  kMathExact sums products with fp32 accuracy (fp16
+// MFMAs on the exactly widened operands); kMathNativeFp8 feeds the FP8 codes
+// to the FP8 MFMA, which is twice as fast but sums the 64 products of each
+// instruction with only ~13 bits kept below the largest one.
+constexpr int kMathExact = FP8LIN_MATH_EXACT;
+constexpr int kMathNativeFp8 = FP8LIN_MATH_NATIVE_FP8;
 
 constexpr int kThreads = 256;
 constexpr int kBK = 128;  // contraction bytes per LDS stage
@@ -156,7 +167,31 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
   tn = (t % width) / gsize;
 }
 
-template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int FA, int FB>
+// Four FP8 codes (one dword) as four fp16 values (two dwords), exactly.
+// E5M2 shares fp16's sign, exponent width and bias: its code is the high byte
+// of the fp16 with the same value (subnormals, inf and NaN included).  Every
+// E4M3 value is a normal fp16; it goes through v_cvt_pk_f32_fp8 (exact) and a
+// pack to fp16 that cannot round.
+template <int FMT>
+__device__ __forceinline__ uint2 fp8x4_to_f16(uint32_t w) {
+  if constexpr (FMT == FP8_E5M2) {
+    return make_uint2(((w & 0xFFu) << 8) | ((w & 0xFF00u) << 16),
+                      ((w >> 8) & 0xFF00u) | (w & 0xFF000000u));
+  } else {
+    const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo[0], lo[1])),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi[0], hi[1])));
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
+  const uint2 a = fp8x4_to_f16<FMT>((uint32_t)w0), b = fp8x4_to_f16<FMT>((uint32_t)w1);
+  return __builtin_bit_cast(v8h, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int FA, int FB, int MATH>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                         bool vec_a, bool vec_b) {
   constexpr int TM = BM / 64, TN = BN / 64;  // 32x32 MFMA tiles per wave
@@ -222,12 +257,32 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles
         bf[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                     (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
       }
+      if constexpr (MATH == kMathNativeFp8) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              af[i], bf[j], acc[i][j], FA, FB, 0, 127, 0, 127);
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[i], bf[j], acc[i][j], FA, FB, 0, 127, 0, 127);
+      } else {
+        // Exact math: the lane's 32 codes become 32 fp16 values (no rounding:
+        // every E4M3 and E5M2 value is an fp16 value) fed to four 32x32x16
+        // fp16 MFMAs; step q takes the lane's bytes [8q, 8q + 8), the same
+        // contraction indices in A and B.
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v8h ah[TM], bh[TN];
+#pragma unroll
+          for (int i = 0; i < TM; ++i) ah[i] = fp8x8_to_f16<FA>(af[i][2 * q], af[i][2 * q + 1]);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) bh[j] = fp8x8_to_f16<FB>(bf[j][2 * q], bf[j][2 * q + 1]);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+        }
+      }
     }
     if (more) {
       la.store(nxt);
@@ -253,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles
     }
 }
 
-template <int BM, int BN, bool AK, bool BK>
+template <int BM, int BN, bool AK, bool BK, int MATH>
 hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
   const int tiles_m = (p.m + BM - 1) / BM, tiles_n = (p.n + BN - 1) / BN;
   const bool vec_a = ((uintptr_t)p.a % 16 == 0) && (p.lda % 16 == 0);
@@ -261,7 +316,7 @@ hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
   const dim3 grid(tiles_m * tiles_n), block(kThreads);
 #define FP8LIN_GEMM_CASE(FA, FB)                                                              \
   if (p.fmt_a == FA && p.fmt_b == FB) {                                                       \
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, FA, FB>), grid, block, 0, stream, p,      \
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, FA, FB, MATH>), grid, block, 0, stream, p, \
                        tiles_m, tiles_n, vec_a, vec_b);                                       \
     return hipGetLastError();                                                                 \
   }
@@ -275,7 +330,7 @@ hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
 
 // Fraction of the chip's workgroup slots doing useful work over all waves of
 // tiles, weighted by how much of each tile is inside the matrix.
-double tile_efficiency(int m, int n, int bm, int bn) {
+inline double tile_efficiency(int m, int n, int bm, int bn) {
   const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn, tiles = tm * tn;
   const int64_t slots = 256;
   const int64_t waves = (tiles + slots - 1) / slots;
@@ -286,15 +341,15 @@ double tile_efficiency(int m, int n, int bm, int bn) {
 
 // FP8LIN_GEMM_TILE=128 or 256 pins the tile size (tuning and tests);
 // otherwise it is chosen from the shape.
-int forced_tile() {
+inline int forced_tile() {
   const char* s = std::getenv("FP8LIN_GEMM_TILE");
   if (!s) return 0;
   const int v = std::atoi(s);
   return (v == 128 || v == 256) ? v : 0;
 }
 
-template <bool AK, bool BK>
-hipError_t launch_layout(const GemmProblem& p, hipStream_t stream) {
+template <bool AK, bool BK, int MATH>
+hipError_t launch_math(const GemmProblem& p, hipStream_t stream) {
   // The 256x256 tile does twice the MFMA work per byte of LDS and global
   // traffic of the 128x128 one; prefer it unless it leaves most CUs idle.
   int tile = forced_tile();
@@ -303,18 +358,16 @@ hipError_t launch_layout(const GemmProblem& p, hipStream_t stream) {
     const double e128 = tile_efficiency(p.m, p.n, 128, 128) * 0.75;
     tile = e256 >= e128 ? 256 : 128;
   }
-  if (tile == 256) return launch_tiles<256, 256, AK, BK>(p, stream);
-  return launch_tiles<128, 128, AK, BK>(p, stream);
+  if (tile == 256) return launch_tiles<256, 256, AK, BK, MATH>(p, stream);
+  return launch_tiles<128, 128, AK, BK, MATH>(p, stream);
 }
 
-}  // namespace
-
-hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream) {
+template <bool AK, bool BK>
+hipError_t launch_layout(const GemmProblem& p, hipStream_t stream) {
   if (p.m <= 0 || p.n <= 0) return hipSuccess;
-  if (p.a_kmajor && p.b_kmajor) return launch_layout<true, true>(p, stream);
-  if (p.a_kmajor && !p.b_kmajor) return launch_layout<true, false>(p, stream);
-  if (!p.a_kmajor && !p.b_kmajor) return launch_layout<false, false>(p, stream);
-  return launch_layout<false, true>(p, stream);
+  if (p.math == kMathNativeFp8) return launch_math<AK, BK, kMathNativeFp8>(p, stream);
+  return launch_math<AK, BK, kMathExact>(p, stream);
 }
 
+}  // namespace gemm_detail
 }  // namespace fp8lin

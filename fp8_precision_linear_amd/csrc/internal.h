@@ -15,6 +15,10 @@ hipError_t launch_bias(const float* amax, int fmt, int32_t margin, int32_t* bias
 hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias, int fmt,
                        uint8_t* y, hipStream_t stream);
 
+// Product arithmetic (the values of fp8_scaled_gemm's `math` argument).
+#define FP8LIN_MATH_EXACT FP8_GEMM_EXACT
+#define FP8LIN_MATH_NATIVE_FP8 FP8_GEMM_NATIVE_FP8
+
 // One FP8 product C[m][n] = 2^-(*bias_a + *bias_b) * sum_k A(m, k) * B(k, n).
 // A(m, k) lives at a[m * lda + k] when a_kmajor, else at a[k * lda + m];
 // B(k, n) lives at b[n * ldb + k] when b_kmajor, else at b[k * ldb + n].
@@ -32,8 +36,12 @@ struct GemmProblem {
   float* c;
   int64_t ldc;
   int m, n, k;
+  int math;
 };
 
-hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+// One launcher per operand layout (gemm_fwd.hip, gemm_dgrad.hip, gemm_wgrad.hip).
+hipError_t launch_gemm_fwd(const GemmProblem& p, hipStream_t stream);    // A, B contraction-contiguous
+hipError_t launch_gemm_dgrad(const GemmProblem& p, hipStream_t stream);  // B contraction-strided
+hipError_t launch_gemm_wgrad(const GemmProblem& p, hipStream_t stream);  // A, B contraction-strided
 
 }  // namespace fp8lin

@@ -31,7 +31,7 @@ def status(code):
 
 def test_every_declared_function_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 7
+    assert len(names) == 8
     for n in names:
         assert hasattr(L, n), n
         assert n in fl.SIGNATURES, n
@@ -113,3 +113,12 @@ def test_python_wrappers_reject_cpu_tensors():
     x = torch.zeros(16, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fl.amax(x)
+
+
+def test_generic_gemm_rejects_unknown_op_and_math():
+    assert L.fp8_scaled_gemm(3, 0, A16, 0, A32, A48, 0, A32, 8, 8, 8, A16, None) == status("FP8_ERR_OP")
+    assert L.fp8_scaled_gemm(0, 2, A16, 0, A32, A48, 0, A32, 8, 8, 8, A16, None) == status("FP8_ERR_OP")
+    assert L.fp8_scaled_gemm(0, -1, A16, 0, A32, A48, 0, A32, 8, 8, 8, A16, None) == status("FP8_ERR_OP")
+    for op in (0, 1, 2):
+        assert L.fp8_scaled_gemm(op, 1, A16, 5, A32, A48, 0, A32, 8, 8, 8, A16, None) == status("FP8_ERR_FORMAT")
+        assert L.fp8_scaled_gemm(op, 0, A16, 0, A32, A48, 0, A32, 8, 8, 8, None, None) == status("FP8_ERR_NULL")
