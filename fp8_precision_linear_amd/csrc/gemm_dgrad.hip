@@ -1,6 +1,6 @@
 // FP8 product kernels, data gradient: W8 read with the contraction as its slow index.
 // One translation unit per operand layout so the instantiations compile in parallel.
-#include "gemm_kernel.h"
+#include "gemm_pipe.h"
 
 namespace fp8lin {
 

@@ -1,6 +1,6 @@
 // FP8 product kernels, forward: both operands contraction-contiguous.
 // One translation unit per operand layout so the instantiations compile in parallel.
-#include "gemm_kernel.h"
+#include "gemm_pipe.h"
 
 namespace fp8lin {
 

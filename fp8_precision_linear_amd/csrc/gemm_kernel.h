@@ -72,15 +72,20 @@ __device__ __forceinline__ uint32_t byte_of(const uint4& v, int j) {
   return (word_of(v, j >> 2) >> (8 * (j & 3))) & 0xFFu;
 }
 
+// Loader interface: load(...) fetches one stage of the operand tile into
+// registers; store(lds) writes it into the LDS tile.  The stage is complete
+// in LDS once every lane has passed store() and a barrier.
+
 // Operand tile whose contraction index is contiguous in memory:
-// rows [row0, row0 + R) x bytes [k0, k0 + 128).
+// rows [row0, row0 + R) x bytes [k0, k0 + 128), through registers, with
+// zero fill past the edges (any contraction length).
 template <int R>
 struct KMajorLoader {
   static constexpr int kChunks = R * (kBK / 16) / kThreads;  // 16-byte chunks per lane
   uint4 v[kChunks];
 
   __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t ld, int row0,
-                                       int rows, int k0, int K, bool vec) {
+                                       int rows, int k0, int K, bool vec, uint8_t*) {
 #pragma unroll
     for (int p = 0; p < kChunks; ++p) {
       const int q = (int)threadIdx.x + kThreads * p, r = q >> 3, c = q & 7;
@@ -117,7 +122,7 @@ struct MNMajorLoader {
   uint4 v[KU];
 
   __device__ __forceinline__ void load(const uint8_t* __restrict__ base, int64_t ld, int mn0,
-                                       int mns, int k0, int K, bool vec) {
+                                       int mns, int k0, int K, bool vec, uint8_t*) {
     const int mu = (int)threadIdx.x % NU, kb = (int)threadIdx.x / NU;
     const int gmn = mn0 + mu * 16;
 #pragma unroll
@@ -191,6 +196,8 @@ __device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
   return __builtin_bit_cast(v8h, make_uint4(a.x, a.y, b.x, b.y));
 }
 
+// The general kernel: any shape and alignment (operands staged through
+// registers with zero fill at every edge, two LDS stages of 128 bytes).
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int FA, int FB, int MATH>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles_m, int tiles_n,
                                                         bool vec_a, bool vec_b) {
@@ -219,8 +226,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles
 
   const int nk = (p.k + kBK - 1) / kBK;
   if (nk > 0) {
-    la.load(p.a, p.lda, m0, p.m, 0, p.k, vec_a);
-    lb.load(p.b, p.ldb, n0, p.n, 0, p.k, vec_b);
+    la.load(p.a, p.lda, m0, p.m, 0, p.k, vec_a, smem);
+    lb.load(p.b, p.ldb, n0, p.n, 0, p.k, vec_b, smem + BM * kBK);
     la.store(smem);
     lb.store(smem + BM * kBK);
     __syncthreads();
@@ -232,8 +239,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles
     uint8_t* nxt = smem + ((kt + 1) & 1) * kStage;
     const bool more = kt + 1 < nk;
     if (more) {
-      la.load(p.a, p.lda, m0, p.m, (kt + 1) * kBK, p.k, vec_a);
-      lb.load(p.b, p.ldb, n0, p.n, (kt + 1) * kBK, p.k, vec_b);
+      la.load(p.a, p.lda, m0, p.m, (kt + 1) * kBK, p.k, vec_a, nxt);
+      lb.load(p.b, p.ldb, n0, p.n, (kt + 1) * kBK, p.k, vec_b, nxt + BM * kBK);
     }
     const uint8_t* As = cur;
     const uint8_t* Bs = cur + BM * kBK;
@@ -306,67 +313,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles
           p.c[(int64_t)row * p.ldc + col] = __builtin_ldexpf(acc[i][j][r], unscale);
       }
     }
-}
-
-template <int BM, int BN, bool AK, bool BK, int MATH>
-hipError_t launch_tiles(const GemmProblem& p, hipStream_t stream) {
-  const int tiles_m = (p.m + BM - 1) / BM, tiles_n = (p.n + BN - 1) / BN;
-  const bool vec_a = ((uintptr_t)p.a % 16 == 0) && (p.lda % 16 == 0);
-  const bool vec_b = ((uintptr_t)p.b % 16 == 0) && (p.ldb % 16 == 0);
-  const dim3 grid(tiles_m * tiles_n), block(kThreads);
-#define FP8LIN_GEMM_CASE(FA, FB)                                                              \
-  if (p.fmt_a == FA && p.fmt_b == FB) {                                                       \
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, FA, FB, MATH>), grid, block, 0, stream, p, \
-                       tiles_m, tiles_n, vec_a, vec_b);                                       \
-    return hipGetLastError();                                                                 \
-  }
-  FP8LIN_GEMM_CASE(FP8_E4M3, FP8_E4M3)
-  FP8LIN_GEMM_CASE(FP8_E5M2, FP8_E4M3)
-  FP8LIN_GEMM_CASE(FP8_E4M3, FP8_E5M2)
-  FP8LIN_GEMM_CASE(FP8_E5M2, FP8_E5M2)
-#undef FP8LIN_GEMM_CASE
-  return hipErrorInvalidValue;
-}
-
-// Fraction of the chip's workgroup slots doing useful work over all waves of
-// tiles, weighted by how much of each tile is inside the matrix.
-inline double tile_efficiency(int m, int n, int bm, int bn) {
-  const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn, tiles = tm * tn;
-  const int64_t slots = 256;
-  const int64_t waves = (tiles + slots - 1) / slots;
-  const double fill = (double)tiles / (double)(waves * slots);
-  const double inside = ((double)m * n) / ((double)tm * bm * tn * bn);
-  return fill * inside;
-}
-
-// FP8LIN_GEMM_TILE=128 or 256 pins the tile size (tuning and tests);
-// otherwise it is chosen from the shape.
-inline int forced_tile() {
-  const char* s = std::getenv("FP8LIN_GEMM_TILE");
-  if (!s) return 0;
-  const int v = std::atoi(s);
-  return (v == 128 || v == 256) ? v : 0;
-}
-
-template <bool AK, bool BK, int MATH>
-hipError_t launch_math(const GemmProblem& p, hipStream_t stream) {
-  // The 256x256 tile does twice the MFMA work per byte of LDS and global
-  // traffic of the 128x128 one; prefer it unless it leaves most CUs idle.
-  int tile = forced_tile();
-  if (tile == 0) {
-    const double e256 = tile_efficiency(p.m, p.n, 256, 256);
-    const double e128 = tile_efficiency(p.m, p.n, 128, 128) * 0.75;
-    tile = e256 >= e128 ? 256 : 128;
-  }
-  if (tile == 256) return launch_tiles<256, 256, AK, BK, MATH>(p, stream);
-  return launch_tiles<128, 128, AK, BK, MATH>(p, stream);
-}
-
-template <bool AK, bool BK>
-hipError_t launch_layout(const GemmProblem& p, hipStream_t stream) {
-  if (p.m <= 0 || p.n <= 0) return hipSuccess;
-  if (p.math == kMathNativeFp8) return launch_math<AK, BK, kMathNativeFp8>(p, stream);
-  return launch_math<AK, BK, kMathExact>(p, stream);
 }
 
 }  // namespace gemm_detail

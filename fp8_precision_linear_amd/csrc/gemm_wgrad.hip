@@ -1,6 +1,6 @@
 // FP8 product kernels, weight gradient: both operands read with the contraction as their slow index.
 // One translation unit per operand layout so the instantiations compile in parallel.
-#include "gemm_kernel.h"
+#include "gemm_pipe.h"
 
 namespace fp8lin {
 
