@@ -175,18 +175,20 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 // Four FP8 codes (one dword) as four fp16 values (two dwords), exactly.
 // E5M2 shares fp16's sign, exponent width and bias: its code is the high byte
 // of the fp16 with the same value (subnormals, inf and NaN included).  Every
-// E4M3 value is a normal fp16; it goes through v_cvt_pk_f32_fp8 (exact) and a
-// pack to fp16 that cannot round.
+// E4M3 value is a normal fp16; v_cvt_scalef32_pk_f16_fp8 with scale 1 converts
+// two codes (the low or the high 16-bit word of the dword) per instruction,
+// exactly for every finite code and NaN to NaN (measured over all 65536 code
+// pairs, both words).  Its result is taken as one 32-bit pattern: extracting
+// the two halves separately has been compiled into a repeat of the low half.
 template <int FMT>
 __device__ __forceinline__ uint2 fp8x4_to_f16(uint32_t w) {
   if constexpr (FMT == FP8_E5M2) {
     return make_uint2(((w & 0xFFu) << 8) | ((w & 0xFF00u) << 16),
                       ((w >> 8) & 0xFF00u) | (w & 0xFF000000u));
   } else {
-    const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-    const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
-    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo[0], lo[1])),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi[0], hi[1])));
+    return make_uint2(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
   }
 }
 

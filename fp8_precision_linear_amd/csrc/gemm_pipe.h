@@ -1,7 +1,7 @@
-// Pipelined FP8 product kernel for gfx950: every operand tile streams into LDS
-// through LDS DMA (global_load_lds_dwordx4) over a ring of four stages, so
-// three contraction stages are always in flight while the MFMAs consume the
-// fourth.  No operand byte passes through registers on its way into LDS.
+// Pipelined FP8 product kernels for gfx950: every operand tile streams into
+// LDS through LDS DMA (global_load_lds_dwordx4) over a ring of four stages, so
+// three contraction stages are in flight while the MFMAs consume the fourth.
+// No operand byte passes through registers on its way into LDS.
 //
 // Stage = 64 contraction bytes.  LDS tiles:
 //  * contraction-contiguous operand ("K-major", the weight and activation of
@@ -22,10 +22,24 @@
 // holds the stage's contraction bytes [32h, 32h + 32) in ascending order, in
 // both layouts.
 //
-// Ring: four separate __shared__ arrays and a loop unrolled over them, so the
-// compiler's LDS-DMA tracking sees that the DMA into one array does not touch
-// the array being read; the wait for a stage is an explicit vmcnt that leaves
-// the two younger stages in flight, then a bare s_barrier.
+// Two kernels share these pieces:
+//  * gemm_pp_kernel, 256x256 tiles, 8 waves in two groups of four ("ping-
+//    pong").  Each SIMD holds one wave of each group.  The groups are half a
+//    stage apart: while one group issues its MFMAs from fragments already in
+//    registers, the other reads the next stage's fragments from LDS and
+//    issues DMA, and a barrier swaps the roles.  A wave's MFMA phase is never
+//    interrupted by LDS latency, and the matrix core of each SIMD alternates
+//    between the two waves.  Group 0 computes tile rows [0, 128) and streams
+//    the A tile, group 1 rows [128, 256) and the B tile; wave w of a group
+//    computes 64 tile columns.
+//  * gemm_quad_kernel, 128x128 tiles, 4 waves (2 x 2) that read and multiply
+//    in the same phase; used where 256x256 tiles would leave CUs idle.
+//
+// Ring: one __shared__ array per operand holding its four stage tiles, and
+// main loops unrolled over the four slots, so every slot and fragment offset
+// is an instruction constant on top of a few per-lane base registers.  The
+// wait for a stage is an explicit vmcnt that leaves the two younger stages of
+// the wave's own DMA in flight, then a bare s_barrier.
 #pragma once
 
 #include "gemm_kernel.h"
@@ -46,7 +60,47 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt lgkmcnt(0) only: every LDS read this wave issued has returned.
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+// Wait until at most `younger` stages of this wave's DMA (D instructions per
+// stage) are still in flight.
+template <int D>
+__device__ __forceinline__ void wait_stages(int younger) {
+  if (younger >= 2) wait_vmcnt<2 * D>();
+  else if (younger == 1) wait_vmcnt<D>();
+  else wait_vmcnt<0>();
+}
+
+// A bare barrier: no memory access may move across it (asm "memory" clobber),
+// and it waits for nothing the explicit waits did not.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ int kswz(int r) { return (r >> 1) & 3; }
+
+// The wave's index in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+}
+
+// Opaque copies: the value is the same, but the compiler cannot hoist address
+// arithmetic built on it out of the main loop.  Without them it precomputes a
+// separate register for every (ring slot, fragment) address and spills.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ __forceinline__ int64_t opaque64(int64_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
 
 // One LDS-DMA load: 16 bytes per lane from `src` into LDS at
 // `lds_kb + 16 * lane` (lds_kb: the wave-uniform LDS byte address of the
@@ -55,211 +109,392 @@ __device__ __forceinline__ int kswz(int r) { return (r >> 1) & 3; }
 // protocol waits for it explicitly (wait_vmcnt + barrier).  Vector memory
 // operations complete in issue order, so the compiler's own vmcnt waits stay
 // correct (they can only wait longer).
-__device__ __forceinline__ void dma16(const uint8_t* src, const uint8_t* lds_kb) {
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)(
-      (__attribute__((address_space(3))) const uint8_t*)lds_kb);
+__device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds_kb) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
       "global_load_lds_dwordx4 %0, off"
       :
-      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_kb))
       : "memory", "m0");
 }
 
-// One stage of a K-major tile: rows [row0, row0 + R) x bytes [k0, k0 + 64).
-// A wave's DMA fills one KB = 16 rows; lane l lands at byte 16 l, i.e. row
-// 16 q + l / 4, physical chunk l % 4, so it fetches logical chunk
-// (l % 4) ^ kswz(row).  Rows past the edge re-read the last row (their
-// products feed outputs that are not stored).
-template <int R>
-__device__ __forceinline__ void dma_kmajor(const uint8_t* __restrict__ base, int64_t ld, int row0,
-                                           int rows, int k0, uint8_t* lds) {
-  const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
-#pragma unroll
-  for (int b = 0; b < R / 16 / 4; ++b) {
-    const int q = wave + 4 * b;
-    const int r = q * 16 + (lane >> 2);
-    const int gr = min(row0 + r, rows - 1);
-    const uint8_t* src = base + (int64_t)gr * ld + k0 + (((lane & 3) ^ kswz(r)) << 4);
-    dma16(src, lds + q * 1024);
-  }
-}
+// The DMA loads one wave issues per stage for an R-wide operand tile, shared
+// among NW waves (w = this wave's index among them).  One load fills one KB
+// of the stage tile: KB q = w + NW * b.
+//  * K-major, tile rows [mn0, mn0 + R) x bytes [k0, k0 + 64): KB q holds
+//    rows 16 q .. 16 q + 15; lane l lands at byte 16 l, i.e. row 16 q + l / 4,
+//    physical chunk l % 4, so it fetches logical chunk (l % 4) ^ kswz(row).
+//    Rows past the edge re-read the last row (their products feed outputs
+//    that are not stored).
+//  * MN-major, contraction rows [k0, k0 + 64) x bytes [mn0, mn0 + R): KB q
+//    holds 1024 / R rows; lane l lands at row q * (1024 / R) + l / (R / 16),
+//    physical chunk l % (R / 16), and fetches logical chunk
+//    (l % (R / 16)) ^ (row & 7).  Chunks past the edge re-read the last chunk
+//    of the row (mns is a multiple of 16).
+// off[b] is the lane's byte offset from the operand base for stage 0; stage
+// kt adds kt * 64 (K-major) or kt * 64 * ld (MN-major).
+template <int R, bool KMAJ, int NW>
+struct DmaPlan {
+  static constexpr int kRowsPerKB = KMAJ ? 16 : 1024 / R;
+  static constexpr int N = R * kPipeBK / 1024 / NW;  // the stage tile's KBs over NW waves
+  static_assert(N >= 1 && N * NW * 1024 == R * kPipeBK, "KB split");
+  int64_t off[N];
+  int w;
 
-// One stage of an MN-major tile: contraction rows [k0, k0 + 64) x bytes
-// [mn0, mn0 + R).  One KB holds 1024 / R rows; lane l lands at row
-// q * (1024 / R) + l / (R / 16), physical chunk l % (R / 16), and fetches
-// logical chunk (l % (R / 16)) ^ (row & 7).  Chunks past the edge re-read the
-// last chunk of the row (mns is a multiple of 16).
-template <int R>
-__device__ __forceinline__ void dma_mnmajor(const uint8_t* __restrict__ base, int64_t ld, int mn0,
-                                            int mns, int k0, uint8_t* lds) {
-  constexpr int kChunks = R / 16, kRowsPerKB = 1024 / R;
-  const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+  __device__ __forceinline__ void init(int64_t ld, int mn0, int mns, int wave, int lane) {
+    w = wave;
 #pragma unroll
-  for (int b = 0; b < 64 / kRowsPerKB / 4; ++b) {
-    const int q = wave + 4 * b;
-    const int r = q * kRowsPerKB + lane / kChunks;
-    const int c = (lane % kChunks) ^ (r & 7);
-    const int gmn = min(mn0 + c * 16, mns - 16);
-    const uint8_t* src = base + (int64_t)(k0 + r) * ld + gmn;
-    dma16(src, lds + q * 1024);
-  }
-}
-
-// The lane's 32 contraction bytes of the K-major fragment for tile row r.
-__device__ __forceinline__ v8i frag_kmajor(const uint8_t* tile, int r, int h) {
-  const uint8_t* row = tile + r * kPipeBK;
-  const uint4 x0 = *reinterpret_cast<const uint4*>(row + (((2 * h) ^ kswz(r)) << 4));
-  const uint4 x1 = *reinterpret_cast<const uint4*>(row + (((2 * h + 1) ^ kswz(r)) << 4));
-  return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-}
-
-// The lane's 32 contraction bytes of the MN-major fragment for the 32 tile
-// columns starting at c0 (lane l takes column c0 + l % 32), via four
-// transposing reads of 8 contraction rows each.
-template <int R>
-__device__ __forceinline__ v8i frag_mnmajor(const uint8_t* tile, int c0, int lane) {
-  const int i = lane & 15, h = lane >> 5;
-  const int col = c0 + 16 * ((lane >> 4) & 1) + 8 * (i & 1);
-  v8i f;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int row = 32 * h + 8 * t + (i >> 1);
-    const uint8_t* p = tile + row * R + ((((col >> 4) ^ (row & 7))) << 4) + (col & 15);
-    const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)p);
-    f[2 * t] = v[0];
-    f[2 * t + 1] = v[1];
-  }
-  return f;
-}
-
-template <int BM, int BN, bool AK, bool BK, int FA, int FB, int MATH>
-struct PipeCtx {
-  static constexpr int TM = BM / 64, TN = BN / 64;
-  static constexpr int kTileA = BM * kPipeBK;
-  // DMA instructions each lane issues per stage (both operands)
-  static constexpr int kDmaPerStage = (BM + BN) * kPipeBK / 1024 / 4;
-
-  const GemmProblem& p;
-  int m0, n0, nk, lane, wm, wn;
-  v16f (&acc)[TM][TN];
-
-  __device__ __forceinline__ void issue(int kt, uint8_t* stage) const {
-    const int k0 = kt * kPipeBK;
-    if constexpr (AK) dma_kmajor<BM>(p.a, p.lda, m0, p.m, k0, stage);
-    else dma_mnmajor<BM>(p.a, p.lda, m0, p.m, k0, stage);
-    if constexpr (BK) dma_kmajor<BN>(p.b, p.ldb, n0, p.n, k0, stage + kTileA);
-    else dma_mnmajor<BN>(p.b, p.ldb, n0, p.n, k0, stage + kTileA);
-  }
-
-  __device__ __forceinline__ void compute(const uint8_t* stage) const {
-    const uint8_t* As = stage;
-    const uint8_t* Bs = stage + kTileA;
-    const int h = lane >> 5, rl = lane & 31;
-    v8i af[TM], bf[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if constexpr (AK) af[i] = frag_kmajor(As, wm * (BM / 2) + i * 32 + rl, h);
-      else af[i] = frag_mnmajor<BM>(As, wm * (BM / 2) + i * 32, lane);
-    }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      if constexpr (BK) bf[j] = frag_kmajor(Bs, wn * (BN / 2) + j * 32 + rl, h);
-      else bf[j] = frag_mnmajor<BN>(Bs, wn * (BN / 2) + j * 32, lane);
-    }
-    if constexpr (MATH == kMathNativeFp8) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], FA,
-                                                                      FB, 0, 127, 0, 127);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v8h ah[TM], bh[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) ah[i] = fp8x8_to_f16<FA>(af[i][2 * q], af[i][2 * q + 1]);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bh[j] = fp8x8_to_f16<FB>(bf[j][2 * q], bf[j][2 * q + 1]);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+    for (int b = 0; b < N; ++b) {
+      const int q = w + NW * b;
+      if constexpr (KMAJ) {
+        const int r = q * 16 + (lane >> 2);
+        const int gr = min(mn0 + r, mns - 1);
+        off[b] = (int64_t)gr * ld + (((lane & 3) ^ kswz(r)) << 4);
+      } else {
+        constexpr int kChunks = R / 16;
+        const int r = q * kRowsPerKB + lane / kChunks;
+        const int c = (lane % kChunks) ^ (r & 7);
+        const int gmn = min(mn0 + c * 16, mns - 16);
+        off[b] = (int64_t)r * ld + gmn;
       }
     }
   }
 
-  // Stage kt lives in ring slot S (= kt % 4).  Wait for its DMA (leaving the
-  // younger in-flight stages alone), barrier, refill the slot freed by stage
-  // kt - 1 with stage kt + 3, then compute stage kt.
-  template <int S>
-  __device__ __forceinline__ void step(int kt, uint8_t* cur, uint8_t* refill) const {
-    if (kt >= nk) return;
-    if (kt + 2 < nk) wait_vmcnt<2 * kDmaPerStage>();
-    else if (kt + 1 < nk) wait_vmcnt<kDmaPerStage>();
-    else wait_vmcnt<0>();
-    // A bare barrier: no memory access may move across it (asm "memory"
-    // clobber), and it waits for nothing the vmcnt above did not.
-    asm volatile("s_barrier" ::: "memory");
-    if (kt + 3 < nk) issue(kt + 3, refill);
-    compute(cur);
+  // Stage kt into the stage tile at LDS address `lds_tile`.
+  __device__ __forceinline__ void issue(const uint8_t* base, int64_t ld, int kt,
+                                        uint32_t lds_tile) const {
+    const int64_t kofs = KMAJ ? (int64_t)kt * kPipeBK : (int64_t)kt * kPipeBK * ld;
+#pragma unroll
+    for (int b = 0; b < N; ++b) dma16(base + kofs + opaque64(off[b]), lds_tile + (w + NW * b) * 1024);
   }
 };
 
-template <int BM, int BN, bool AK, bool BK, int FA, int FB, int MATH>
-__global__ __launch_bounds__(kThreads) void gemm_pipe_kernel(GemmProblem p, int tiles_m,
-                                                             int tiles_n) {
-  constexpr int TM = BM / 64, TN = BN / 64;
-  constexpr int kStageBytes = (BM + BN) * kPipeBK;
-  __shared__ __attribute__((aligned(1024))) uint8_t s0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t s3[kStageBytes];
+// Where a wave's T fragments of an R-wide operand tile sit in LDS: the
+// fragment of the 32 rows (K-major) or columns (MN-major) first + 32 t.
+//  * K-major: lane l (row r = first + 32 t + l % 32, half h = l / 32) reads
+//    logical chunks 2h and 2h + 1 of row r with two ds_read_b128.  first is a
+//    multiple of 32, so the swizzle depends on l % 32 alone and the offsets of
+//    fragment t differ by the constant 32 t * 64.
+//  * MN-major: four ds_read_b64_tr_b8 of 8 contraction rows each (rows
+//    32h + 8u + (l % 16) / 2, u = 0..3, at a constant distance 8 R apart); even
+//    lanes address the first 8 columns of a 16-column block and odd lanes the
+//    next 8, so lane l receives the 8 contraction values of column
+//    first + 32 t + l % 32.
+// off[] holds the lane's LDS byte addresses in ring slot 0 (slot s adds the
+// constant s * R * 64).
+template <int R, bool KMAJ, int T>
+struct FragPlan {
+  static constexpr int N = KMAJ ? 2 : T;
+  uint32_t off[N];
 
-  int tm, tn;
-  tile_coords((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+  __device__ __forceinline__ void init(uint32_t tile0, int first, int lane) {
+    const int h = lane >> 5;
+    if constexpr (KMAJ) {
+      const int rl = lane & 31;
+      off[0] = tile0 + (first + rl) * kPipeBK + (((2 * h) ^ kswz(rl)) << 4);
+      off[1] = tile0 + (first + rl) * kPipeBK + (((2 * h + 1) ^ kswz(rl)) << 4);
+    } else {
+      const int i = lane & 15, lb = (lane >> 4) & 1;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        const int blk = ((first + 32 * t) >> 4) + lb;  // 16-byte column block
+        off[t] = tile0 + (32 * h + (i >> 1)) * R + ((blk ^ (i >> 1)) << 4) + 8 * (i & 1);
+      }
+    }
+  }
 
-  v16f acc[TM][TN];
+  template <int SLOT>
+  __device__ __forceinline__ v8i load(int t) const {
+    constexpr uint32_t kSlot = SLOT * R * kPipeBK;
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const v4i* lds_v4i;
+    typedef __attribute__((address_space(3))) v2i* lds_v2i;
+    if constexpr (KMAJ) {
+      const uint32_t kt = kSlot + t * 32 * kPipeBK;
+      const v4i x0 = *(lds_v4i)(uintptr_t)(opaque(off[0]) + kt);
+      const v4i x1 = *(lds_v4i)(uintptr_t)(opaque(off[1]) + kt);
+      return v8i{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    } else {
+      const uint32_t a = opaque(off[t]) + kSlot;
+      v8i f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i)(uintptr_t)(a + 8 * u * R));
+        f[2 * u] = v[0];
+        f[2 * u + 1] = v[1];
+      }
+      return f;
+    }
+  }
+};
+
+// Register fences: empty volatile asm that claims to rewrite the values.
+// Volatile asm keeps its order against the barrier asm, so an MFMA phase whose
+// inputs are fenced at its start and outputs at its end stays between the
+// barriers that delimit it (plain register arithmetic may otherwise be moved
+// across an s_barrier written as inline asm).
+template <int N>
+__device__ __forceinline__ void fence(v8i (&f)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
+}
+template <int TM, int TN>
+__device__ __forceinline__ void fence(v16f (&acc)[TM][TN]) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) asm volatile("" : "+v"(acc[i][j]));
+}
+
+// acc[i][j] += A-fragment i x B-fragment j over one 64-byte stage.
+template <int TM, int TN, int FA, int FB, int MATH>
+__device__ __forceinline__ void mma_stage(const v8i (&af)[TM], const v8i (&bf)[TN],
+                                          v16f (&acc)[TM][TN]) {
+  if constexpr (MATH == kMathNativeFp8) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], FA, FB,
+                                                                    0, 127, 0, 127);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v8h ah[TM], bh[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ah[i] = fp8x8_to_f16<FA>(af[i][2 * q], af[i][2 * q + 1]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bh[j] = fp8x8_to_f16<FB>(bf[j][2 * q], bf[j][2 * q + 1]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+    }
+  }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void zero_acc(v16f (&acc)[TM][TN]) {
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
 
-  const PipeCtx<BM, BN, AK, BK, FA, FB, MATH> ctx{p, tm * BM, tn * BN, p.k / kPipeBK,
-                                                  lane, wave >> 1, wave & 1, acc};
-  // prologue: stages 0, 1, 2 in flight
-  if (ctx.nk > 0) ctx.issue(0, s0);
-  if (ctx.nk > 1) ctx.issue(1, s1);
-  if (ctx.nk > 2) ctx.issue(2, s2);
-  for (int kt = 0; kt < ctx.nk; kt += kPipeStages) {
-    ctx.template step<0>(kt + 0, s0, s3);
-    ctx.template step<1>(kt + 1, s1, s0);
-    ctx.template step<2>(kt + 2, s2, s1);
-    ctx.template step<3>(kt + 3, s3, s2);
-  }
-
-  // 32x32 accumulator layout: register r of lane l holds row
-  // 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32 of the MFMA tile.
-  const int m0 = tm * BM, n0 = tn * BN, wm = wave >> 1, wn = wave & 1;
+// Unscale and store a wave's TM x TN block of 32x32 tiles whose top-left
+// output is (row0, col0).  32x32 accumulator layout: register r of lane l
+// holds row 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32.
+template <int TM, int TN>
+__device__ __forceinline__ void store_block(const GemmProblem& p, const v16f (&acc)[TM][TN],
+                                            int row0, int col0, int lane) {
   const int h = lane >> 5, rl = lane & 31;
   const int unscale = -(*p.bias_a + *p.bias_b);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * (BN / 2) + j * 32 + rl;
+      const int col = col0 + j * 32 + rl;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < p.m && col < p.n)
           p.c[(int64_t)row * p.ldc + col] = __builtin_ldexpf(acc[i][j][r], unscale);
       }
     }
+}
+
+// ------------------------------------------------------ ping-pong, 256 x 256
+
+// The work of one wave of group G (0 or 1) in the ping-pong kernel.
+//  * Fragments: A rows G * 128 + 32 i (i < 4), B columns 64 gw + 32 j (j < 2).
+//  * DMA: group 0 streams the A tile, group 1 the B tile, 16 KB per stage
+//    each, four loads per wave.
+//  * Stage kt: phase 2kt, group 0 reads stage kt while group 1 multiplies
+//    stage kt - 1; phase 2kt + 1, group 0 multiplies stage kt while group 1
+//    reads it.  A barrier separates the phases.  Before the first of them
+//    every wave waits for its own DMA of stage kt (the two younger stages stay
+//    in flight), so after it the whole stage is in LDS.  The refill of the
+//    slot stage kt - 1 used (with stage kt + 3) is issued in the read phase:
+//    both groups finished reading stage kt - 1 before phase 2kt.  A read
+//    phase ends with the wave's fragments in registers, so a slot is never
+//    overwritten while a read of it is outstanding.
+template <int G, bool AK, bool BK, int FA, int FB, int MATH>
+struct PingPongWave {
+  static constexpr int R = 256, TM = 4, TN = 2;
+  static constexpr bool SK = G == 0 ? AK : BK;  // layout of the streamed operand
+  using Dma = DmaPlan<R, SK, 4>;
+
+  const GemmProblem& p;
+  int nk;
+  uint32_t lds_mine;  // LDS address of slot 0 of the streamed operand's tile
+  const uint8_t* base;
+  int64_t ld;
+  Dma dma;
+  FragPlan<R, AK, TM> fa;
+  FragPlan<R, BK, TN> fb;
+  v8i af[TM], bf[TN];
+  v16f (&acc)[TM][TN];
+
+  __device__ __forceinline__ PingPongWave(const GemmProblem& p_, int m0, int n0, int gw, int lane,
+                                          uint32_t lds_a, uint32_t lds_b, v16f (&acc_)[TM][TN])
+      : p(p_), nk(p_.k / kPipeBK), acc(acc_) {
+    lds_mine = G == 0 ? lds_a : lds_b;
+    base = G == 0 ? p.a : p.b;
+    ld = G == 0 ? p.lda : p.ldb;
+    dma.init(ld, G == 0 ? m0 : n0, G == 0 ? p.m : p.n, gw, lane);
+    fa.init(lds_a, G * (R / 2), lane);
+    fb.init(lds_b, gw * (R / 4), lane);
+  }
+
+  template <int SLOT>
+  __device__ __forceinline__ void read(int kt) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = fa.template load<SLOT>(i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[j] = fb.template load<SLOT>(j);
+    if (kt + 3 < nk) dma.issue(base, ld, kt + 3, lds_mine + ((SLOT + 3) % 4) * R * kPipeBK);
+    wait_lgkm0();
+  }
+
+  __device__ __forceinline__ void mma() {
+    fence(af);
+    fence(bf);
+    mma_stage<TM, TN, FA, FB, MATH>(af, bf, acc);
+    fence(acc);
+  }
+
+  template <int SLOT>
+  __device__ __forceinline__ void step(int kt) {
+    if (kt >= nk) return;
+    wait_stages<Dma::N>(min(2, nk - 1 - kt));
+    bare_barrier();
+    if constexpr (G == 0) read<SLOT>(kt);
+    else if (kt > 0) mma();
+    bare_barrier();
+    if constexpr (G == 0) mma();
+    else read<SLOT>(kt);
+  }
+
+  __device__ __forceinline__ void run() {
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      if (s < nk) dma.issue(base, ld, s, lds_mine + s * R * kPipeBK);
+    for (int kt = 0; kt < nk; kt += kPipeStages) {
+      step<0>(kt + 0);
+      step<1>(kt + 1);
+      step<2>(kt + 2);
+      step<3>(kt + 3);
+    }
+    if (G == 1 && nk > 0) mma();  // group 1's last stage
+  }
+};
+
+template <bool AK, bool BK, int FA, int FB, int MATH>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, int tiles_m, int tiles_n) {
+  constexpr int R = 256;
+  // Ring of four stages per operand: slot s of A at sa + s * 16 KB, of B at
+  // sb + s * 16 KB (all fragment offsets stay below 64 KB of their base).
+  __shared__ __attribute__((aligned(1024))) uint8_t sa[kPipeStages * R * kPipeBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb[kPipeStages * R * kPipeBK];
+
+  int tm, tn;
+  tile_coords((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int lane = (int)threadIdx.x & 63, wave = wave_id();
+  const int g = wave >> 2, gw = wave & 3;
+  const int m0 = tm * R, n0 = tn * R;
+
+  v16f acc[4][2];
+  zero_acc(acc);
+  if (g == 0) {
+    PingPongWave<0, AK, BK, FA, FB, MATH> w(p, m0, n0, gw, lane, lds_addr(sa), lds_addr(sb), acc);
+    w.run();
+  } else {
+    PingPongWave<1, AK, BK, FA, FB, MATH> w(p, m0, n0, gw, lane, lds_addr(sa), lds_addr(sb), acc);
+    w.run();
+  }
+  store_block(p, acc, m0 + g * (R / 2), n0 + gw * (R / 4), lane);
+}
+
+// ---------------------------------------------------------- quad, 128 x 128
+
+// 4 waves in a 2 x 2 grid; wave (wm, wn) owns a 64 x 64 block and issues a
+// quarter of both operand tiles' DMA.  Each stage: wait for it, barrier,
+// refill the slot freed by stage kt - 1 with stage kt + 3, read, multiply.
+template <bool AK, bool BK, int FA, int FB, int MATH>
+struct QuadWave {
+  static constexpr int R = 128, TM = 2, TN = 2;
+  using DmaA = DmaPlan<R, AK, 4>;
+  using DmaB = DmaPlan<R, BK, 4>;
+
+  const GemmProblem& p;
+  int nk;
+  uint32_t lds_a, lds_b;
+  DmaA da;
+  DmaB db;
+  FragPlan<R, AK, TM> fa;
+  FragPlan<R, BK, TN> fb;
+  v16f (&acc)[TM][TN];
+
+  __device__ __forceinline__ QuadWave(const GemmProblem& p_, int m0, int n0, int wave, int lane,
+                                      uint32_t la, uint32_t lb, v16f (&acc_)[TM][TN])
+      : p(p_), nk(p_.k / kPipeBK), lds_a(la), lds_b(lb), acc(acc_) {
+    da.init(p.lda, m0, p.m, wave, lane);
+    db.init(p.ldb, n0, p.n, wave, lane);
+    fa.init(la, (wave >> 1) * (R / 2), lane);
+    fb.init(lb, (wave & 1) * (R / 2), lane);
+  }
+
+  __device__ __forceinline__ void issue(int kt, int slot) const {
+    da.issue(p.a, p.lda, kt, lds_a + slot * R * kPipeBK);
+    db.issue(p.b, p.ldb, kt, lds_b + slot * R * kPipeBK);
+  }
+
+  template <int SLOT>
+  __device__ __forceinline__ void step(int kt) {
+    if (kt >= nk) return;
+    wait_stages<DmaA::N + DmaB::N>(min(2, nk - 1 - kt));
+    bare_barrier();
+    if (kt + 3 < nk) issue(kt + 3, (SLOT + 3) % 4);
+    v8i af[TM], bf[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[i] = fa.template load<SLOT>(i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[j] = fb.template load<SLOT>(j);
+    mma_stage<TM, TN, FA, FB, MATH>(af, bf, acc);
+  }
+
+  __device__ __forceinline__ void run() {
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      if (s < nk) issue(s, s);
+    for (int kt = 0; kt < nk; kt += kPipeStages) {
+      step<0>(kt + 0);
+      step<1>(kt + 1);
+      step<2>(kt + 2);
+      step<3>(kt + 3);
+    }
+  }
+};
+
+template <bool AK, bool BK, int FA, int FB, int MATH>
+__global__ __launch_bounds__(256) void gemm_quad_kernel(GemmProblem p, int tiles_m, int tiles_n) {
+  constexpr int R = 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t sa[kPipeStages * R * kPipeBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb[kPipeStages * R * kPipeBK];
+
+  int tm, tn;
+  tile_coords((int)blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int lane = (int)threadIdx.x & 63, wave = wave_id();
+  const int m0 = tm * R, n0 = tn * R;
+
+  v16f acc[2][2];
+  zero_acc(acc);
+  QuadWave<AK, BK, FA, FB, MATH> w(p, m0, n0, wave, lane, lds_addr(sa), lds_addr(sb), acc);
+  w.run();
+  store_block(p, acc, m0 + (wave >> 1) * (R / 2), n0 + (wave & 1) * (R / 2), lane);
 }
 
 // ----------------------------------------------------------------- launch
@@ -270,22 +505,39 @@ inline dim3 tile_grid(const GemmProblem& p, int bm, int bn, int& tiles_m, int& t
   return dim3(tiles_m * tiles_n);
 }
 
-template <int BM, int BN, bool AK, bool BK, int MATH>
-hipError_t launch_pipe(const GemmProblem& p, hipStream_t stream) {
-  int tiles_m, tiles_n;
-  const dim3 grid = tile_grid(p, BM, BN, tiles_m, tiles_n), block(kThreads);
-#define FP8LIN_PIPE_CASE(FA, FB)                                                              \
-  if (p.fmt_a == FA && p.fmt_b == FB) {                                                       \
-    hipLaunchKernelGGL((gemm_pipe_kernel<BM, BN, AK, BK, FA, FB, MATH>), grid, block, 0,       \
-                       stream, p, tiles_m, tiles_n);                                          \
+// Instantiate KERNEL<AK, BK, FA, FB, MATH> for the operand formats of p.
+#define FP8LIN_FORMAT_DISPATCH(KERNEL, GRID, BLOCK)                                           \
+  do {                                                                                        \
+    if (p.fmt_a == FP8_E4M3 && p.fmt_b == FP8_E4M3) {                                         \
+      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E4M3, FP8_E4M3, MATH>), GRID, BLOCK, 0, stream,  \
+                         p, tiles_m, tiles_n);                                                \
+    } else if (p.fmt_a == FP8_E5M2 && p.fmt_b == FP8_E4M3) {                                  \
+      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E5M2, FP8_E4M3, MATH>), GRID, BLOCK, 0, stream,  \
+                         p, tiles_m, tiles_n);                                                \
+    } else if (p.fmt_a == FP8_E4M3 && p.fmt_b == FP8_E5M2) {                                  \
+      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E4M3, FP8_E5M2, MATH>), GRID, BLOCK, 0, stream,  \
+                         p, tiles_m, tiles_n);                                                \
+    } else if (p.fmt_a == FP8_E5M2 && p.fmt_b == FP8_E5M2) {                                  \
+      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E5M2, FP8_E5M2, MATH>), GRID, BLOCK, 0, stream,  \
+                         p, tiles_m, tiles_n);                                                \
+    } else {                                                                                  \
+      return hipErrorInvalidValue;                                                            \
+    }                                                                                         \
     return hipGetLastError();                                                                 \
-  }
-  FP8LIN_PIPE_CASE(FP8_E4M3, FP8_E4M3)
-  FP8LIN_PIPE_CASE(FP8_E5M2, FP8_E4M3)
-  FP8LIN_PIPE_CASE(FP8_E4M3, FP8_E5M2)
-  FP8LIN_PIPE_CASE(FP8_E5M2, FP8_E5M2)
-#undef FP8LIN_PIPE_CASE
-  return hipErrorInvalidValue;
+  } while (0)
+
+template <bool AK, bool BK, int MATH>
+hipError_t launch_pp(const GemmProblem& p, hipStream_t stream) {
+  int tiles_m, tiles_n;
+  const dim3 grid = tile_grid(p, 256, 256, tiles_m, tiles_n), block(512);
+  FP8LIN_FORMAT_DISPATCH(gemm_pp_kernel, grid, block);
+}
+
+template <bool AK, bool BK, int MATH>
+hipError_t launch_quad(const GemmProblem& p, hipStream_t stream) {
+  int tiles_m, tiles_n;
+  const dim3 grid = tile_grid(p, 128, 128, tiles_m, tiles_n), block(256);
+  FP8LIN_FORMAT_DISPATCH(gemm_quad_kernel, grid, block);
 }
 
 template <bool AK, bool BK, int MATH>
@@ -328,7 +580,7 @@ inline int forced_tile() {
   return (v == 128 || v == 256) ? v : 0;
 }
 
-// The pipelined kernel needs: a contraction that is a whole number of 64-byte
+// The pipelined kernels need: a contraction that is a whole number of 64-byte
 // stages; 16-byte aligned operand rows; and, for an operand read with the
 // contraction as its slow index, a row length (M or N) that is a multiple of
 // 16.  Anything else runs the general kernel.
@@ -353,8 +605,8 @@ hipError_t launch_math(const GemmProblem& p, hipStream_t stream) {
     const double e128 = tile_efficiency(p.m, p.n, 128, 128) * 0.75;
     tile = e256 >= e128 ? 256 : 128;
   }
-  if (tile == 256) return launch_pipe<256, 256, AK, BK, MATH>(p, stream);
-  return launch_pipe<128, 128, AK, BK, MATH>(p, stream);
+  if (tile == 256) return launch_pp<AK, BK, MATH>(p, stream);
+  return launch_quad<AK, BK, MATH>(p, stream);
 }
 
 template <bool AK, bool BK>
@@ -363,6 +615,8 @@ hipError_t launch_layout(const GemmProblem& p, hipStream_t stream) {
   if (p.math == kMathNativeFp8) return launch_math<AK, BK, kMathNativeFp8>(p, stream);
   return launch_math<AK, BK, kMathExact>(p, stream);
 }
+
+#undef FP8LIN_FORMAT_DISPATCH
 
 }  // namespace gemm_detail
 }  // namespace fp8lin
