@@ -39,6 +39,11 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows of each product in the CPU sample")
     ap.add_argument("--cpu-cols", type=int, default=8192, help="columns of each product in the CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy twice (HBM counter calibration)")
+    ap.add_argument("--record-traffic", metavar="DIR",
+                    help="only write profiles/gemm_traffic.json from rocprofv3 --pmc CSVs under DIR "
+                         "(fetch/, write/, copy_fetch/, copy_write/)")
     return ap.parse_args()
 
 
@@ -65,21 +70,100 @@ def gemm_operands(l, which):
     return l.dy, l.x, (l.N, l.K)
 
 
-def file_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+# Sources of the product kernels; the committed traffic record is valid only
+# while they are unchanged.
+GEMM_SOURCES = [os.path.join(ROOT, "fp8_precision_linear_amd", "csrc", f)
+                for f in ("gemm_pipe.h", "gemm_kernel.h")]
+COPY_BYTES = 256 * 1024 * 1024
 
 
-def traffic_record(kernel_source):
+def sources_sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_record():
     """HBM bytes per launch from committed PMC counters, valid only while the
-    kernel source they were taken on is unchanged."""
+    kernel sources they were taken on are unchanged."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != file_sha(kernel_source):
+    if rec.get("source_sha256") != sources_sha(GEMM_SOURCES):
         return None
     return rec
+
+
+def copy_calibration():
+    """A plain device-to-device copy of COPY_BYTES, twice: what FETCH_SIZE and
+    WRITE_SIZE read for a known number of bytes moved."""
+    import torch
+    x = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 2}), flush=True)
+
+
+def record_traffic(d):
+    """profiles/gemm_traffic.json from four rocprofv3 --pmc runs (CSV output):
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the bench's product
+    kernels, and of the calibration copy.  Each counter is scaled by
+    COPY_BYTES / (what it reads for the copy)."""
+    import csv
+    import glob
+
+    def rows(sub):
+        files = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        if len(files) != 1:
+            raise SystemExit(f"expected one counter CSV under {sub}, found {files}")
+        return list(csv.DictReader(open(files[0])))
+
+    def per_dispatch(rs, counter, pick):
+        vals = {}
+        for r in rs:
+            if r["Counter_Name"] == counter and pick(r["Kernel_Name"]):
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        return vals
+
+    is_gemm = lambda k: "gemm_detail" in k and "gemm" in k
+    is_copy = lambda k: "copyBuffer" in k or "elementwise" in k
+    copy_f = max(per_dispatch(rows("copy_fetch"), "FETCH_SIZE", is_copy).values())
+    copy_w = max(per_dispatch(rows("copy_write"), "WRITE_SIZE", is_copy).values())
+    f_factor = COPY_BYTES / (copy_f * 1024.0)
+    w_factor = COPY_BYTES / (copy_w * 1024.0)
+    f = per_dispatch(rows("fetch"), "FETCH_SIZE", is_gemm)
+    wr = per_dispatch(rows("write"), "WRITE_SIZE", is_gemm)
+    fetch = sum(f.values()) / len(f) * 1024.0 * f_factor
+    write = sum(wr.values()) / len(wr) * 1024.0 * w_factor
+    rec = {
+        "bytes_per_launch": round(fetch + write),
+        "fetch_bytes_per_launch": round(fetch),
+        "write_bytes_per_launch": round(write),
+        "launches_fetch": len(f), "launches_write": len(wr),
+        "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+        "source_sha256": sources_sha(GEMM_SOURCES),
+        "commands": [
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/fetch -o run -- "
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/write -o run -- "
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/copy_fetch -o run -- "
+            "python3 bench.py --copy-calibration",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/copy_write -o run -- "
+            "python3 bench.py --copy-calibration",
+            "python3 bench.py --record-traffic <DIR>",
+        ],
+    }
+    out = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec), flush=True)
 
 
 def cpu_baseline(w, host, rows, cols):
@@ -160,10 +244,16 @@ def cpu_baseline(w, host, rows, cols):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU (no multi-GPU path); --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     import fp8_precision_linear_amd as fl
@@ -244,18 +334,23 @@ def main():
 
     # per-kernel durations from the events (same stream as the launches)
     gemm_ms = amax_ms = bias_ms = cast_ms = 0.0
+    cast_by, amax_by = {}, {}
     last = {}
     for kind, key, e in ev:
         if kind == "quant_start":
             last["q"] = e
         elif kind == "amax_end":
-            amax_ms += last["q"].elapsed_time(e)
+            t = last["q"].elapsed_time(e)
+            amax_ms += t
+            amax_by[key] = amax_by.get(key, 0.0) + t
             last["a"] = e
         elif kind == "bias_end":
             bias_ms += last["a"].elapsed_time(e)
             last["b"] = e
         elif kind == "cast_end":
-            cast_ms += last["b"].elapsed_time(e)
+            t = last["b"].elapsed_time(e)
+            cast_ms += t
+            cast_by[key] = cast_by.get(key, 0.0) + t
         elif kind == "gemm_start":
             last["g"] = e
         elif kind == "gemm_end":
@@ -268,7 +363,7 @@ def main():
     cast_gbs = 3.0 * quant_elems * K / (cast_ms * 1e-3) / 1e9 if cast_ms > 0 else None
     amax_gbs = 2.0 * quant_elems * K / (amax_ms * 1e-3) / 1e9 if amax_ms > 0 else None
 
-    rec = traffic_record(os.path.join(ROOT, "fp8_precision_linear_amd", "csrc", "gemm_kernel.h"))
+    rec = traffic_record()
     traffic = rec["bytes_per_launch"] if rec else None
     # the exact arithmetic runs its contraction on the fp16 MFMA: that is its peak
     peak = PEAK_F16_TFLOPS if args.math == "exact" else PEAK_FP8_TFLOPS
@@ -297,8 +392,9 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": ("gemm_kernel, exact math: FP8 codes widened to fp16, 32x32x16 fp16 MFMA"
-                       if args.math == "exact" else "gemm_kernel, native 32x32x64 FP8 MFMA"),
+            "kernel": ("gemm_pp_kernel (256x256 tiles, ping-pong waves), exact math: FP8 codes "
+                       "widened to fp16, 32x32x16 fp16 MFMA" if args.math == "exact" else
+                       "gemm_pp_kernel (256x256 tiles, ping-pong waves), native 32x32x64 FP8 MFMA"),
             "achieved": round(gemm_tflops, 2),
             "peak": peak,
             "unit": "TFLOP/s",
@@ -314,12 +410,30 @@ def main():
             "frac": round(cast_gbs / PEAK_HBM_GBS, 4) if cast_gbs else None,
             "bytes_per_element": 3,
             "avg_launch_us": round(cast_ms * 1e3 / max(K * len([i for i in plan if i[0] == 'quant']), 1), 2),
+            "per_tensor": {n: {"elements": int(torch.tensor(w.tensor(n).shape).prod()),
+                               "us": round(t * 1e3 / K, 2),
+                               "gbs": round(3.0 * int(torch.tensor(w.tensor(n).shape).prod()) / (t * 1e-3 / K) / 1e9, 1)}
+                           for n, t in cast_by.items()},
         },
         "amax": {
             "bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
             "achieved": round(amax_gbs, 1) if amax_gbs else None,
             "frac": round(amax_gbs / PEAK_HBM_GBS, 4) if amax_gbs else None,
             "bytes_per_element": 2,
+            "per_tensor": {n: {"us": round(t * 1e3 / K, 2),
+                               "gbs": round(2.0 * int(torch.tensor(w.tensor(n).shape).prod()) / (t * 1e-3 / K) / 1e9, 1)}
+                           for n, t in amax_by.items()},
+        },
+        # the whole in-step quantisation: amax reads x, the cast reads it again
+        # and writes the codes (5 bytes per bf16 element), clear and bias
+        # launches included
+        "quantise": {
+            "bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
+            "achieved": round(5.0 * quant_elems * K / ((amax_ms + bias_ms + cast_ms) * 1e-3) / 1e9, 1)
+            if cast_ms > 0 else None,
+            "frac": round(5.0 * quant_elems * K / ((amax_ms + bias_ms + cast_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            if cast_ms > 0 else None,
+            "bytes_per_element": 5,
         },
         "step_breakdown_ms": {"gemm": round(gemm_ms / K, 4), "amax": round(amax_ms / K, 4),
                               "bias": round(bias_ms / K, 4), "cast": round(cast_ms / K, 4)},

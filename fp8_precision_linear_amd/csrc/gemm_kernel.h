@@ -6,28 +6,27 @@
 // unscale after the matrix multiplication) and bullet 5 (training: forward,
 // data-gradient and weight-gradient products; inference).
 //
-// Design (MI355X / CDNA4):
-//  * v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales (E8M0 127 = 2^0):
-//    the operand formats (E4M3 or E5M2) are per-instruction fields, so every
-//    format pairing runs at the same dense FP8 rate.
-//  * A workgroup of 4 wave64s computes a BM x BN tile (2 x 2 waves, each a
-//    BM/2 x BN/2 block of 32x32 MFMA tiles).  The contraction advances 128
-//    bytes per stage through a double-buffered LDS tile pair; global loads of
-//    the next stage are in flight while the MFMAs consume the current one.
-//  * LDS keeps every operand tile contraction-contiguous ([row][128 bytes]),
-//    16-byte chunks XOR-swizzled by (row ^ row >> 4) & 7, so a lane reads its
-//    32-byte MFMA fragment with two conflict-free ds_read_b128.  An operand
-//    whose contraction index is the slow one in memory (the weight in the
-//    data gradient, both operands in the weight gradient) is loaded as
-//    16-byte rows and byte-transposed in registers on its way into LDS.
-//  * Tiles are numbered so that the workgroups the dispatcher sends to one XCD
-//    (blockIdx % 8) take a contiguous run of tiles, grouped 8 tile-rows at a
-//    time, so neighbouring tiles share operand panels in that XCD's L2.
+// This file holds what all product kernels share (the arithmetic modes, the
+// exact FP8 -> fp16 / bf16 widening, the XCD-aware tile order) and the
+// general kernel, which takes any shape and alignment: operands staged
+// through registers into two LDS stages of 128 contraction bytes, zero fill
+// at every edge, 128x128 tiles of 4 waves.  The pipelined kernels that run
+// the workloads' products are in gemm_pipe.h.
+//
+// Arithmetic:
+//  * exact (the default): FP8 codes widened exactly to fp16 or bf16 in
+//    registers, then the 32x32x16 fp16 / bf16 MFMA, whose sums keep a 24-bit
+//    window (fp32-level accuracy);
+//  * native: v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales (E8M0
+//    127 = 2^0); the operand formats are instruction fields, so every format
+//    pairing runs at the dense FP8 rate, but each instruction keeps only ~13
+//    bits below its largest product.
 //  * The unscale is one v_ldexp_f32 per output in the epilogue (exact unless
 //    the result is an fp32 subnormal).
 #pragma once
 
 #include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "internal.h"
@@ -46,6 +45,9 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 // instruction with only ~13 bits kept below the largest one.
 constexpr int kMathExact = FP8LIN_MATH_EXACT;
 constexpr int kMathNativeFp8 = FP8LIN_MATH_NATIVE_FP8;
+// Exact sums through the bf16 MFMA instead (internal kernel variant; every
+// FP8 value is a normal bf16 and bf16 x bf16 products of them are exact).
+constexpr int kMathExactBf16 = 100;
 
 constexpr int kThreads = 256;
 constexpr int kBK = 128;  // contraction bytes per LDS stage
@@ -190,6 +192,30 @@ __device__ __forceinline__ uint2 fp8x4_to_f16(uint32_t w) {
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
   }
+}
+
+// Four FP8 codes as four bf16 values (two dwords), exactly: every E4M3 and
+// E5M2 value is a normal bf16.  One v_cvt_scalef32_pk_bf16_{fp8,bf8} (scale 1)
+// per two codes; the result is read as one 32-bit pattern.
+template <int FMT>
+__device__ __forceinline__ uint2 fp8x4_to_bf16(uint32_t w) {
+  if constexpr (FMT == FP8_E5M2) {
+    return make_uint2(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true)));
+  } else {
+    return make_uint2(
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
+  }
+}
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+template <int FMT>
+__device__ __forceinline__ v8bf fp8x8_to_bf16(int w0, int w1) {
+  const uint2 a = fp8x4_to_bf16<FMT>((uint32_t)w0), b = fp8x4_to_bf16<FMT>((uint32_t)w1);
+  return __builtin_bit_cast(v8bf, make_uint4(a.x, a.y, b.x, b.y));
 }
 
 template <int FMT>

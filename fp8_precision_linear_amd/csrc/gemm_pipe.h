@@ -6,13 +6,17 @@
 // Stage = 64 contraction bytes.  LDS tiles:
 //  * contraction-contiguous operand ("K-major", the weight and activation of
 //    the forward product, dY in the data gradient): [R rows][64 bytes]; the
-//    four 16-byte chunks of row r sit at chunk c ^ ((r >> 1) & 3), so the
-//    eight rows a ds_read_b128 quarter-wave touches land in eight different
-//    bank groups;
+//    four 16-byte chunks of row r sit at chunk c ^ ((r >> 2) & 3).  The LDS
+//    has 64 banks (256 bytes per cycle): the 16 rows that 16 lanes of a
+//    ds_read_b128 address (four rows per 256-byte bank window) then cover all
+//    16 bank groups of 16 bytes;
 //  * operand whose contraction index is slow in memory ("MN-major": W8 in the
 //    data gradient, dY8 and X8 in the weight gradient): the memory tile
 //    [64 contraction rows][R bytes] as it is, 16-byte chunk c of row k at
-//    c ^ (k & 7).  Fragments are read with ds_read_b64_tr_b8: in each group of
+//    c ^ mnswz(k) (mnswz: (k & 7) for 128-byte rows, 2 (k & 7) for 256-byte
+//    rows; either way the 8 rows x 2 column blocks that 32 lanes of one
+//    transposing read address fall in 16 different bank groups).
+//    Fragments are read with ds_read_b64_tr_b8: in each group of
 //    16 lanes, lane i receives byte (i & 7) of the 8-byte pieces addressed by
 //    lanes 2q + (i >> 3), q = 0..7.  Even lanes address rows kb..kb+7 in the
 //    first 8 columns of a 16-column block and odd lanes the same rows in the
@@ -78,7 +82,10 @@ __device__ __forceinline__ void wait_stages(int younger) {
 // and it waits for nothing the explicit waits did not.
 __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-__device__ __forceinline__ int kswz(int r) { return (r >> 1) & 3; }
+// Chunk swizzles of the K-major and MN-major stage tiles.
+__device__ __forceinline__ int kswz(int r) { return (r >> 2) & 3; }
+template <int R>
+__device__ __forceinline__ int mnswz(int k) { return R == 256 ? 2 * (k & 7) : (k & 7); }
 
 // The wave's index in the workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() {
@@ -129,7 +136,7 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint32_t lds_kb) {
 //  * MN-major, contraction rows [k0, k0 + 64) x bytes [mn0, mn0 + R): KB q
 //    holds 1024 / R rows; lane l lands at row q * (1024 / R) + l / (R / 16),
 //    physical chunk l % (R / 16), and fetches logical chunk
-//    (l % (R / 16)) ^ (row & 7).  Chunks past the edge re-read the last chunk
+//    (l % (R / 16)) ^ mnswz(row).  Chunks past the edge re-read the last chunk
 //    of the row (mns is a multiple of 16).
 // off[b] is the lane's byte offset from the operand base for stage 0; stage
 // kt adds kt * 64 (K-major) or kt * 64 * ld (MN-major).
@@ -153,7 +160,7 @@ struct DmaPlan {
       } else {
         constexpr int kChunks = R / 16;
         const int r = q * kRowsPerKB + lane / kChunks;
-        const int c = (lane % kChunks) ^ (r & 7);
+        const int c = (lane % kChunks) ^ mnswz<R>(r);
         const int gmn = min(mn0 + c * 16, mns - 16);
         off[b] = (int64_t)r * ld + gmn;
       }
@@ -173,7 +180,7 @@ struct DmaPlan {
 // fragment of the 32 rows (K-major) or columns (MN-major) first + 32 t.
 //  * K-major: lane l (row r = first + 32 t + l % 32, half h = l / 32) reads
 //    logical chunks 2h and 2h + 1 of row r with two ds_read_b128.  first is a
-//    multiple of 32, so the swizzle depends on l % 32 alone and the offsets of
+//    multiple of 16, so the swizzle depends on l % 32 alone and the offsets of
 //    fragment t differ by the constant 32 t * 64.
 //  * MN-major: four ds_read_b64_tr_b8 of 8 contraction rows each (rows
 //    32h + 8u + (l % 16) / 2, u = 0..3, at a constant distance 8 R apart); even
@@ -198,7 +205,7 @@ struct FragPlan {
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         const int blk = ((first + 32 * t) >> 4) + lb;  // 16-byte column block
-        off[t] = tile0 + (32 * h + (i >> 1)) * R + ((blk ^ (i >> 1)) << 4) + 8 * (i & 1);
+        off[t] = tile0 + (32 * h + (i >> 1)) * R + ((blk ^ mnswz<R>(i >> 1)) << 4) + 8 * (i & 1);
       }
     }
   }
@@ -257,6 +264,20 @@ __device__ __forceinline__ void mma_stage(const v8i (&af)[TM], const v8i (&bf)[T
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], FA, FB,
                                                                     0, 127, 0, 127);
+  } else if constexpr (MATH == kMathExactBf16) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v8bf ah[TM], bh[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) ah[i] = fp8x8_to_bf16<FA>(af[i][2 * q], af[i][2 * q + 1]);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bh[j] = fp8x8_to_bf16<FB>(bf[j][2 * q], bf[j][2 * q + 1]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+    }
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -596,7 +617,8 @@ bool pipe_ok(const GemmProblem& p) {
 
 template <bool AK, bool BK, int MATH>
 hipError_t launch_math(const GemmProblem& p, hipStream_t stream) {
-  if (!pipe_ok<AK, BK>(p)) return launch_general<AK, BK, MATH>(p, stream);
+  if (!pipe_ok<AK, BK>(p))
+    return launch_general<AK, BK, MATH == kMathNativeFp8 ? kMathNativeFp8 : kMathExact>(p, stream);
   // The 256x256 tile does twice the MFMA work per byte of LDS and global
   // traffic of the 128x128 one; prefer it unless it leaves most CUs idle.
   int tile = forced_tile();
@@ -609,10 +631,24 @@ hipError_t launch_math(const GemmProblem& p, hipStream_t stream) {
   return launch_quad<AK, BK, MATH>(p, stream);
 }
 
+// Exact products run on the bf16 MFMA when either operand is E5M2 and on the
+// fp16 MFMA otherwise: both are exact (every FP8 value is a normal bf16; every
+// E4M3 value a normal fp16, every E5M2 value an fp16), and on the MI355X this
+// choice measured fastest (bf16 ~10% ahead with an E5M2 operand, fp16 1-2%
+// ahead for E4M3 x E4M3).  FP8LIN_EXACT_MFMA=f16 or bf16 forces one (tuning
+// and tests).
+inline bool exact_on_bf16(const GemmProblem& p) {
+  const char* s = std::getenv("FP8LIN_EXACT_MFMA");
+  if (s && std::strcmp(s, "bf16") == 0) return true;
+  if (s && std::strcmp(s, "f16") == 0) return false;
+  return p.fmt_a == FP8_E5M2 || p.fmt_b == FP8_E5M2;
+}
+
 template <bool AK, bool BK>
 hipError_t launch_layout(const GemmProblem& p, hipStream_t stream) {
   if (p.m <= 0 || p.n <= 0) return hipSuccess;
   if (p.math == kMathNativeFp8) return launch_math<AK, BK, kMathNativeFp8>(p, stream);
+  if (exact_on_bf16(p)) return launch_math<AK, BK, kMathExactBf16>(p, stream);
   return launch_math<AK, BK, kMathExact>(p, stream);
 }
 

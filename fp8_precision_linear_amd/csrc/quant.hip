@@ -12,6 +12,9 @@
 // order, with NaN above inf), so the result is exact and independent of the
 // reduction order: wave shuffle, then LDS across the block's waves, then one
 // atomicMax per block.
+#include <cstdlib>
+#include <cstring>
+
 #include "internal.h"
 
 namespace fp8lin {
@@ -21,9 +24,17 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
 // Launch shapes measured on MI355X over a 470 MB bf16 tensor: amax peaks with
-// one 256-lane block per CU and 8 loads in flight per lane (6.9 TB/s; more
-// blocks add contention on the single atomicMax target); the cast peaks with
-// ~4 units per lane over a large grid (6.2 TB/s).
+// one 256-lane block per CU and 8 loads in flight per lane (more blocks add
+// contention on the single atomicMax target); the cast with ~4 units per lane
+// over a large grid.
+//
+// Cache hints, measured on amax -> cast sequences over 128 MiB and 448 MiB
+// bf16 tensors after a cache flush: amax reads with ordinary loads, so a
+// tensor that fits the 256 MB Infinity Cache is still there when the cast
+// reads it again (cast 6.2-6.4 TB/s on 128 MiB, against ~5.0 with streaming
+// hints on both); a cast whose input exceeds kCachedCastBytes streams with
+// non-temporal loads and stores (6.5 TB/s on 448 MiB, against 6.2 without).
+constexpr int64_t kCachedCastBytes = 192ll << 20;
 constexpr int kAmaxUnroll = 8;
 constexpr int kAmaxMaxBlocks = 256;
 constexpr int kCastUnroll = 4;
@@ -32,15 +43,26 @@ constexpr int kCastMaxBlocks = 16384;
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Streaming (non-temporal) 16-byte accesses: every byte is touched once.
-__device__ __forceinline__ uint4 load_stream(const uint4* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v[0], v[1], v[2], v[3]);
+// 16-byte accesses, non-temporal (NT: streaming, every byte touched once) or
+// ordinary (cached).
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+  if constexpr (NT) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *p;
+  }
 }
 
-__device__ __forceinline__ void store_stream(uint4 v, uint4* p) {
-  const u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+template <bool NT>
+__device__ __forceinline__ void store16(uint4 v, uint4* p) {
+  if constexpr (NT) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+  } else {
+    *p = v;
+  }
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -81,6 +103,7 @@ __device__ __forceinline__ u16x2 vmax_bf16(u16x2 acc, uint4 v) {
   return acc;
 }
 
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __restrict__ x,
                                                              int64_t nvec,
                                                              const uint16_t* __restrict__ tail,
@@ -91,11 +114,11 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __rest
   for (; i + (kAmaxUnroll - 1) * stride < nvec; i += kAmaxUnroll * stride) {
     uint4 v[kAmaxUnroll];
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = load_stream(&x[i + u * stride]);
+    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = load16<NT>(&x[i + u * stride]);
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) acc = vmax_bf16(acc, v[u]);
   }
-  for (; i < nvec; i += stride) acc = vmax_bf16(acc, load_stream(&x[i]));
+  for (; i < nvec; i += stride) acc = vmax_bf16(acc, load16<NT>(&x[i]));
   uint32_t m = max((uint32_t)acc.x, (uint32_t)acc.y);
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7FFFu));
   block_max_to(m << 16, out);  // bf16 magnitude widened to fp32 bits
@@ -107,6 +130,7 @@ __device__ __forceinline__ uint32_t vmax_f32(uint32_t acc, uint4 v) {
   return acc;
 }
 
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void amax_f32_kernel(const uint4* __restrict__ x,
                                                             int64_t nvec,
                                                             const uint32_t* __restrict__ tail,
@@ -117,11 +141,11 @@ __global__ __launch_bounds__(kThreads) void amax_f32_kernel(const uint4* __restr
   for (; i + (kAmaxUnroll - 1) * stride < nvec; i += kAmaxUnroll * stride) {
     uint4 v[kAmaxUnroll];
 #pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = load_stream(&x[i + u * stride]);
+    for (int u = 0; u < kAmaxUnroll; ++u) v[u] = load16<NT>(&x[i + u * stride]);
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) m = vmax_f32(m, v[u]);
   }
-  for (; i < nvec; i += stride) m = vmax_f32(m, load_stream(&x[i]));
+  for (; i < nvec; i += stride) m = vmax_f32(m, load16<NT>(&x[i]));
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max(m, tail[threadIdx.x] & 0x7FFFFFFFu);
   block_max_to(m, out);
 }
@@ -205,8 +229,114 @@ __device__ __forceinline__ uint32_t pack4_f32(uint4 v, int32_t b) {
          (fp8_code<FMT>(v.w, b) << 24);
 }
 
-// One unit = 16 elements -> one 16-byte store.
+// ---------------------------------------------------------------- cast, hardware conversion
+// gfx950's v_cvt_scalef32_pk_{fp8,bf8}_bf16 converts two bf16 values x to the
+// FP8 codes of x / scale with round-to-nearest-even.  Measured against the
+// rounding defined above on every bf16 pattern and every scale 2^k,
+// k = -126..127: bit-identical for every finite input whose scaled value does
+// not exceed the format's largest finite value; beyond it the instruction
+// returns NaN / inf codes instead of saturating, and its NaN and inf codes
+// differ from the ones defined here.  So, with scale = 2^-b (a normal float
+// for b in [-127, 126]):
+//  * finite inputs are first clamped in magnitude to fmt_max * 2^-b (a packed
+//    16-bit integer min on the magnitude bits: for non-negative IEEE values
+//    integer order is value order), which turns overflow into exactly the
+//    saturation the rounding above performs (every value at or beyond
+//    fmt_max rounds to the largest finite code);
+//  * a unit holding any inf or NaN is redone with fp8_code.
+constexpr int kHwBiasMin = -127, kHwBiasMax = 126;
+
+typedef short hw_v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 hw_v2bf __attribute__((ext_vector_type(2)));
+
+// bf16 magnitude bits of min(fmt_max * 2^-b, largest finite bf16), twice.
+// fmt_max = 1.75 * 2^emax has bf16 fraction bits 0x60.
 template <int FMT>
+__device__ __forceinline__ uint32_t hw_bound2(int32_t b) {
+  const int efield = (FMT == FP8_E4M3 ? 8 : 15) + 127 - b;
+  const uint32_t m = efield >= 255 ? 0x7F7Fu : (((uint32_t)efield << 7) | 0x60u);
+  return m | (m << 16);
+}
+
+// Four bf16 values (two dwords) -> four codes.  mx accumulates the largest
+// magnitude seen (per 16-bit half) for the non-finite check.
+template <int FMT>
+__device__ __forceinline__ uint32_t pack4_bf16_hw(uint32_t w0, uint32_t w1, uint32_t bound2,
+                                                  float scale, u16x2& mx) {
+  const u16x2 m0 = bf16_mag2(w0), m1 = bf16_mag2(w1), bd = *reinterpret_cast<u16x2*>(&bound2);
+  mx = __builtin_elementwise_max(mx, __builtin_elementwise_max(m0, m1));
+  const u16x2 c0 = __builtin_elementwise_min(m0, bd), c1 = __builtin_elementwise_min(m1, bd);
+  const uint32_t x0 = (w0 & 0x80008000u) | __builtin_bit_cast(uint32_t, c0);
+  const uint32_t x1 = (w1 & 0x80008000u) | __builtin_bit_cast(uint32_t, c1);
+  hw_v2s r = {0, 0};
+  if constexpr (FMT == FP8_E4M3) {
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(hw_v2bf, x0), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(hw_v2bf, x1), scale, true);
+  } else {
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(hw_v2bf, x0), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(r, __builtin_bit_cast(hw_v2bf, x1), scale, true);
+  }
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// One unit (16 bf16 values in lo, hi) with the hardware conversion, or with
+// fp8_code if it holds an inf or NaN.
+template <int FMT>
+__device__ __forceinline__ uint4 cast_unit_hw(uint4 lo, uint4 hi, int32_t b, uint32_t bound2,
+                                              float scale) {
+  u16x2 mx = {0, 0};
+  uint4 o;
+  o.x = pack4_bf16_hw<FMT>(lo.x, lo.y, bound2, scale, mx);
+  o.y = pack4_bf16_hw<FMT>(lo.z, lo.w, bound2, scale, mx);
+  o.z = pack4_bf16_hw<FMT>(hi.x, hi.y, bound2, scale, mx);
+  o.w = pack4_bf16_hw<FMT>(hi.z, hi.w, bound2, scale, mx);
+  if (max(mx.x, mx.y) >= 0x7F80u) {  // inf or NaN present
+    o.x = pack4_bf16<FMT>(lo.x, lo.y, b);
+    o.y = pack4_bf16<FMT>(lo.z, lo.w, b);
+    o.z = pack4_bf16<FMT>(hi.x, hi.y, b);
+    o.w = pack4_bf16<FMT>(hi.z, hi.w, b);
+  }
+  return o;
+}
+
+template <int FMT>
+__device__ __forceinline__ uint4 cast_unit_sw(uint4 lo, uint4 hi, int32_t b) {
+  uint4 o;
+  o.x = pack4_bf16<FMT>(lo.x, lo.y, b);
+  o.y = pack4_bf16<FMT>(lo.z, lo.w, b);
+  o.z = pack4_bf16<FMT>(hi.x, hi.y, b);
+  o.w = pack4_bf16<FMT>(hi.z, hi.w, b);
+  return o;
+}
+
+// One unit = 16 elements -> one 16-byte store.  HW selects the hardware
+// conversion (bias in [kHwBiasMin, kHwBiasMax]) or fp8_code throughout.
+template <int FMT, bool HW, bool NT>
+__device__ __forceinline__ void cast_bf16_body(const uint4* __restrict__ x, int64_t nunit, int32_t b,
+                                               uint4* __restrict__ y) {
+  const uint32_t bound2 = hw_bound2<FMT>(b);
+  const float scale = __builtin_ldexpf(1.0f, -b);
+  auto unit = [&](uint4 lo, uint4 hi) {
+    if constexpr (HW) return cast_unit_hw<FMT>(lo, hi, b, bound2, scale);
+    else return cast_unit_sw<FMT>(lo, hi, b);
+  };
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (kCastUnroll - 1) * stride < nunit; i += kCastUnroll * stride) {
+    uint4 lo[kCastUnroll], hi[kCastUnroll];
+#pragma unroll
+    for (int u = 0; u < kCastUnroll; ++u) {
+      lo[u] = load16<NT>(&x[2 * (i + u * stride)]);
+      hi[u] = load16<NT>(&x[2 * (i + u * stride) + 1]);
+    }
+#pragma unroll
+    for (int u = 0; u < kCastUnroll; ++u) store16<NT>(unit(lo[u], hi[u]), &y[i + u * stride]);
+  }
+  for (; i < nunit; i += stride)
+    store16<NT>(unit(load16<NT>(&x[2 * i]), load16<NT>(&x[2 * i + 1])), &y[i]);
+}
+
+template <int FMT, bool NT>
 __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const uint4* __restrict__ x,
                                                              int64_t nunit,
                                                              const int32_t* __restrict__ bias,
@@ -215,39 +345,13 @@ __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const uint4* __rest
                                                              uint8_t* __restrict__ tail_y,
                                                              int ntail) {
   const int32_t b = *bias;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (kCastUnroll - 1) * stride < nunit; i += kCastUnroll * stride) {
-    uint4 lo[kCastUnroll], hi[kCastUnroll];
-#pragma unroll
-    for (int u = 0; u < kCastUnroll; ++u) {
-      lo[u] = load_stream(&x[2 * (i + u * stride)]);
-      hi[u] = load_stream(&x[2 * (i + u * stride) + 1]);
-    }
-#pragma unroll
-    for (int u = 0; u < kCastUnroll; ++u) {
-      uint4 o;
-      o.x = pack4_bf16<FMT>(lo[u].x, lo[u].y, b);
-      o.y = pack4_bf16<FMT>(lo[u].z, lo[u].w, b);
-      o.z = pack4_bf16<FMT>(hi[u].x, hi[u].y, b);
-      o.w = pack4_bf16<FMT>(hi[u].z, hi[u].w, b);
-      store_stream(o, &y[i + u * stride]);
-    }
-  }
-  for (; i < nunit; i += stride) {
-    const uint4 a0 = load_stream(&x[2 * i]), a1 = load_stream(&x[2 * i + 1]);
-    uint4 o;
-    o.x = pack4_bf16<FMT>(a0.x, a0.y, b);
-    o.y = pack4_bf16<FMT>(a0.z, a0.w, b);
-    o.z = pack4_bf16<FMT>(a1.x, a1.y, b);
-    o.w = pack4_bf16<FMT>(a1.z, a1.w, b);
-    store_stream(o, &y[i]);
-  }
+  if (b >= kHwBiasMin && b <= kHwBiasMax) cast_bf16_body<FMT, true, NT>(x, nunit, b, y);
+  else cast_bf16_body<FMT, false, NT>(x, nunit, b, y);
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail)
     tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>((uint32_t)tail_x[threadIdx.x] << 16, b);
 }
 
-template <int FMT>
+template <int FMT, bool NT>
 __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restrict__ x,
                                                             int64_t nunit,
                                                             const int32_t* __restrict__ bias,
@@ -258,14 +362,14 @@ __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restr
   const int32_t b = *bias;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nunit; i += stride) {
-    const uint4 a0 = load_stream(&x[4 * i]), a1 = load_stream(&x[4 * i + 1]);
-    const uint4 a2 = load_stream(&x[4 * i + 2]), a3 = load_stream(&x[4 * i + 3]);
+    const uint4 a0 = load16<NT>(&x[4 * i]), a1 = load16<NT>(&x[4 * i + 1]);
+    const uint4 a2 = load16<NT>(&x[4 * i + 2]), a3 = load16<NT>(&x[4 * i + 3]);
     uint4 o;
     o.x = pack4_f32<FMT>(a0, b);
     o.y = pack4_f32<FMT>(a1, b);
     o.z = pack4_f32<FMT>(a2, b);
     o.w = pack4_f32<FMT>(a3, b);
-    store_stream(o, &y[i]);
+    store16<NT>(o, &y[i]);
   }
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail)
     tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>(tail_x[threadIdx.x], b);
@@ -279,24 +383,37 @@ int stream_blocks(int64_t units, int64_t per_lane, int64_t cap) {
 
 }  // namespace
 
+// FP8LIN_AMAX_HINT=nt or cached forces the amax loads' cache hint (tuning);
+// by default a tensor that fits kCachedCastBytes is read cached (the cast that
+// follows finds it in the Infinity Cache) and a larger one streamed.
+static bool amax_streams(int64_t in_bytes) {
+  const char* h = std::getenv("FP8LIN_AMAX_HINT");
+  if (h && std::strcmp(h, "nt") == 0) return true;
+  if (h && std::strcmp(h, "cached") == 0) return false;
+  return in_bytes > kCachedCastBytes;
+}
+
 hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t stream) {
   uint32_t* out = reinterpret_cast<uint32_t*>(amax);
   hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, out);
   if (n > 0) {
+    const bool nt = amax_streams(n * (dtype == FP8_IN_BF16 ? 2 : 4));
     if (dtype == FP8_IN_BF16) {
       const int64_t nvec = n / 8;
       const int ntail = (int)(n - nvec * 8);
       const uint16_t* tail = static_cast<const uint16_t*>(x) + nvec * 8;
-      hipLaunchKernelGGL(amax_bf16_kernel, dim3(stream_blocks(nvec, kAmaxUnroll, kAmaxMaxBlocks)),
-                         dim3(kThreads), 0, stream, static_cast<const uint4*>(x), nvec, tail,
-                         ntail, out);
+      const dim3 grid(stream_blocks(nvec, kAmaxUnroll, kAmaxMaxBlocks));
+      const uint4* xv = static_cast<const uint4*>(x);
+      if (nt) hipLaunchKernelGGL(amax_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
+      else hipLaunchKernelGGL(amax_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
     } else {
       const int64_t nvec = n / 4;
       const int ntail = (int)(n - nvec * 4);
       const uint32_t* tail = static_cast<const uint32_t*>(x) + nvec * 4;
-      hipLaunchKernelGGL(amax_f32_kernel, dim3(stream_blocks(nvec, kAmaxUnroll, kAmaxMaxBlocks)),
-                         dim3(kThreads), 0, stream, static_cast<const uint4*>(x), nvec, tail,
-                         ntail, out);
+      const dim3 grid(stream_blocks(nvec, kAmaxUnroll, kAmaxMaxBlocks));
+      const uint4* xv = static_cast<const uint4*>(x);
+      if (nt) hipLaunchKernelGGL(amax_f32_kernel<true>, grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
+      else hipLaunchKernelGGL(amax_f32_kernel<false>, grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
     }
   }
   return hipGetLastError();
@@ -316,26 +433,38 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias,
   const int ntail = (int)(n - nunit * 16);
   uint8_t* tail_y = y + nunit * 16;
   uint4* yv = reinterpret_cast<uint4*>(y);
+  const int64_t in_bytes = n * (dtype == FP8_IN_BF16 ? 2 : 4);
+  const bool nt = in_bytes > kCachedCastBytes;
   if (dtype == FP8_IN_BF16) {
     const uint16_t* tail_x = static_cast<const uint16_t*>(x) + nunit * 16;
     const uint4* xv = static_cast<const uint4*>(x);
     const dim3 grid(stream_blocks(nunit, kCastUnroll, kCastMaxBlocks));
-    if (fmt == FP8_E4M3)
-      hipLaunchKernelGGL(cast_bf16_kernel<FP8_E4M3>, grid, dim3(kThreads), 0, stream, xv, nunit,
-                         bias, yv, tail_x, tail_y, ntail);
-    else
-      hipLaunchKernelGGL(cast_bf16_kernel<FP8_E5M2>, grid, dim3(kThreads), 0, stream, xv, nunit,
-                         bias, yv, tail_x, tail_y, ntail);
+#define FP8LIN_CAST(F, NT)                                                                    \
+  hipLaunchKernelGGL((cast_bf16_kernel<F, NT>), grid, dim3(kThreads), 0, stream, xv, nunit, \
+                     bias, yv, tail_x, tail_y, ntail)
+    if (fmt == FP8_E4M3) {
+      if (nt) FP8LIN_CAST(FP8_E4M3, true);
+      else FP8LIN_CAST(FP8_E4M3, false);
+    } else {
+      if (nt) FP8LIN_CAST(FP8_E5M2, true);
+      else FP8LIN_CAST(FP8_E5M2, false);
+    }
+#undef FP8LIN_CAST
   } else {
     const uint32_t* tail_x = static_cast<const uint32_t*>(x) + nunit * 16;
     const uint4* xv = static_cast<const uint4*>(x);
     const dim3 grid(stream_blocks(nunit, 1, kCastMaxBlocks));
-    if (fmt == FP8_E4M3)
-      hipLaunchKernelGGL(cast_f32_kernel<FP8_E4M3>, grid, dim3(kThreads), 0, stream, xv, nunit,
-                         bias, yv, tail_x, tail_y, ntail);
-    else
-      hipLaunchKernelGGL(cast_f32_kernel<FP8_E5M2>, grid, dim3(kThreads), 0, stream, xv, nunit,
-                         bias, yv, tail_x, tail_y, ntail);
+#define FP8LIN_CAST(F, NT)                                                                   \
+  hipLaunchKernelGGL((cast_f32_kernel<F, NT>), grid, dim3(kThreads), 0, stream, xv, nunit, \
+                     bias, yv, tail_x, tail_y, ntail)
+    if (fmt == FP8_E4M3) {
+      if (nt) FP8LIN_CAST(FP8_E4M3, true);
+      else FP8LIN_CAST(FP8_E4M3, false);
+    } else {
+      if (nt) FP8LIN_CAST(FP8_E5M2, true);
+      else FP8LIN_CAST(FP8_E5M2, false);
+    }
+#undef FP8LIN_CAST
   }
   return hipGetLastError();
 }

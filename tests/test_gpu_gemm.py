@@ -29,13 +29,20 @@ def fl():
     return need_gpu()
 
 
-@pytest.fixture(params=["auto", "128", "256"])
+# Kernel configurations: the automatic choice, then each pipelined tile with
+# each MFMA the exact arithmetic can run on (fp16 and bf16).
+CONFIGS = [("auto", "auto"), ("128", "f16"), ("256", "f16"), ("128", "bf16"), ("256", "bf16")]
+
+
+@pytest.fixture(params=CONFIGS, ids=[f"tile{t}-{m}" for t, m in CONFIGS])
 def tile(request, monkeypatch):
-    if request.param != "auto":
-        monkeypatch.setenv("FP8LIN_GEMM_TILE", request.param)
-    else:
-        monkeypatch.delenv("FP8LIN_GEMM_TILE", raising=False)
-    return request.param
+    t, m = request.param
+    for var, val in (("FP8LIN_GEMM_TILE", t), ("FP8LIN_EXACT_MFMA", m)):
+        if val != "auto":
+            monkeypatch.setenv(var, val)
+        else:
+            monkeypatch.delenv(var, raising=False)
+    return f"{t}/{m}"
 
 
 def finite_codes(rng, shape, fmt):
