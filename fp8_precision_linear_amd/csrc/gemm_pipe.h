@@ -212,7 +212,11 @@ struct FragPlan {
 
   template <int SLOT>
   __device__ __forceinline__ v8i load(int t) const {
-    constexpr uint32_t kSlot = SLOT * R * kPipeBK;
+    return load_at(SLOT * R * kPipeBK, t);
+  }
+
+  // Fragment t of the ring slot that starts kSlot bytes after slot 0.
+  __device__ __forceinline__ v8i load_at(uint32_t kSlot, int t) const {
     typedef int v4i __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) const v4i* lds_v4i;
     typedef __attribute__((address_space(3))) v2i* lds_v2i;
