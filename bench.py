@@ -8,12 +8,14 @@ workload is the Llama-2-70B-shaped single-layer inference (8192 tokens,
 hidden 8192, QKV 8192->10240, O 8192->8192, gate/up 8192->28672, down
 28672->8192).
 
-Prints one JSON line: whole-step TFLOP/s (amax + bias + cast included), the
-roofline of the dominant kernel (the FP8 GEMM) measured with HIP events on the
-launch stream, the cast's HBM throughput, and the CPU oracle timed on a
-bounded sample of the same step.
+Prints one JSON line: whole-step TFLOP/s (amax + bias + cast included) from
+K timed steps; the roofline of the dominant kernel (the FP8 GEMM) and the
+amax / cast HBM throughput from HIP events on the launch stream in K further
+steps; amax and cast of each in-step tensor again with a flushed cache
+("cold"); and the CPU oracle timed on a bounded sample of the same step.
 """
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -39,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows of each product in the CPU sample")
     ap.add_argument("--cpu-cols", type=int, default=8192, help="columns of each product in the CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold (cache-flushed) amax and cast measurement")
+    ap.add_argument("--cold-reps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy twice (HBM counter calibration)")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -85,16 +90,88 @@ def sources_sha(paths):
     return h.hexdigest()
 
 
-def traffic_record():
-    """HBM bytes per launch from committed PMC counters, valid only while the
-    kernel sources they were taken on are unchanged."""
+def traffic_record(workload):
+    """HBM bytes per launch from committed PMC counters, valid only for the
+    workload and kernel sources they were taken on."""
     path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != sources_sha(GEMM_SOURCES):
+    if rec.get("source_sha256") != sources_sha(GEMM_SOURCES) or rec.get("workload") != workload:
         return None
     return rec
+
+
+COLD_FLUSH_BYTES = 768 << 20   # > the 256 MB Infinity Cache
+COLD_CLEAN_BYTES = 512 << 20
+
+
+def cold_quant(fl, w, plan, q, x, reps):
+    """amax (with its clear) and cast of every in-step quantised tensor, each
+    timed alone after flushing the Infinity Cache (outside the timing); median
+    over `reps`, HIP events on the launch stream.  Two flushes:
+      * clean: a 768 MiB scratch write, then a read of another 512 MiB buffer,
+        so that the scratch's dirty lines are written back before the kernel
+        runs and the cache holds nothing of use to it;
+      * dirty: the scratch write alone; the timed kernel then also pays for
+        writing those dirty lines back as its reads evict them."""
+    import statistics
+
+    import torch
+    scratch = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    clean = torch.ones(COLD_CLEAN_BYTES // 4, dtype=torch.int32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, dirty=False):
+        # flush, start event, kernel, end event queued back to back on the
+        # launch stream: the flush ends before the start event on the GPU, and
+        # no host-side launch latency falls between the two events
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            scratch.zero_()
+            if not dirty:
+                clean.sum()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    per, amax_b = {}, 0.0
+    tot = {"amax_ms": 0.0, "cast_ms": 0.0, "elems": 0}
+    for item in plan:
+        if item[0] != "quant":
+            continue
+        n = item[1]
+        codes, bias, amax, fmt = q[n]
+        elems = x[n].numel()
+        ta = timed(lambda: fl.amax(x[n], out=amax))
+        tc = timed(lambda: fl.scale_cast(x[n], bias, fmt, out=codes))
+        tad = timed(lambda: fl.amax(x[n], out=amax), dirty=True)
+        tcd = timed(lambda: fl.scale_cast(x[n], bias, fmt, out=codes), dirty=True)
+        per[n] = {"elements": elems, "amax_us": round(ta * 1e3, 2), "cast_us": round(tc * 1e3, 2),
+                  "amax_gbs": round(2.0 * elems / (ta * 1e-3) / 1e9, 1),
+                  "cast_gbs": round(3.0 * elems / (tc * 1e-3) / 1e9, 1),
+                  "dirty_amax_gbs": round(2.0 * elems / (tad * 1e-3) / 1e9, 1),
+                  "dirty_cast_gbs": round(3.0 * elems / (tcd * 1e-3) / 1e9, 1)}
+        for k, t in (("amax_ms", ta), ("cast_ms", tc), ("dirty_amax_ms", tad), ("dirty_cast_ms", tcd)):
+            tot[k] = tot.get(k, 0.0) + t
+        tot["elems"] += elems
+    del scratch, clean
+    if not per:
+        return None
+    gbs = lambda b, ms: 1.0 * b * tot["elems"] / (ms * 1e-3) / 1e9
+    cast_gbs, amax_gbs = gbs(3, tot["cast_ms"]), gbs(2, tot["amax_ms"])
+    return {"method": f"each kernel alone after a {COLD_FLUSH_BYTES >> 20} MiB scratch write and a "
+                      f"{COLD_CLEAN_BYTES >> 20} MiB read of another buffer (dirty_*: the write alone), "
+                      f"median of {reps}, HIP events",
+            "cast_gbs": round(cast_gbs, 1), "cast_frac": round(cast_gbs / PEAK_HBM_GBS, 4),
+            "amax_gbs": round(amax_gbs, 1), "amax_frac": round(amax_gbs / PEAK_HBM_GBS, 4),
+            "dirty_cast_gbs": round(gbs(3, tot["dirty_cast_ms"]), 1),
+            "dirty_amax_gbs": round(gbs(2, tot["dirty_amax_ms"]), 1),
+            "per_tensor": per}
 
 
 def copy_calibration():
@@ -141,7 +218,9 @@ def record_traffic(d):
     wr = per_dispatch(rows("write"), "WRITE_SIZE", is_gemm)
     fetch = sum(f.values()) / len(f) * 1024.0 * f_factor
     write = sum(wr.values()) / len(wr) * 1024.0 * w_factor
+    import synth
     rec = {
+        "workload": synth.WORKLOADS[5].name,
         "bytes_per_launch": round(fetch + write),
         "fetch_bytes_per_launch": round(fetch),
         "write_bytes_per_launch": round(write),
@@ -150,9 +229,9 @@ def record_traffic(d):
         "source_sha256": sources_sha(GEMM_SOURCES),
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/fetch -o run -- "
-            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/write -o run -- "
-            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/copy_fetch -o run -- "
             "python3 bench.py --copy-calibration",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/copy_write -o run -- "
@@ -234,6 +313,8 @@ def cpu_baseline(w, host, rows, cols):
         "value": step_flops / t_step / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.threads(),
+        "host_cpu_count": os.cpu_count(),
+        "host_affinity": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"first {rows} rows of each in-step quantisation (amax+bias+cast, 1 thread) and a "
                    f"{rows}x{cols} output block of every product (OpenMP over rows); each part scaled "
@@ -322,15 +403,26 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps, wall clock, synchronised on both sides
-    ev = []
+    # timed region: K steps, wall clock, synchronised on both sides; no
+    # per-kernel events and no Python garbage collection inside it
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(ev)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-kernel durations: K more steps with HIP events around every launch
+    ev = []
+    for _ in range(args.steps):
+        step(ev)
+    torch.cuda.synchronize()
+    gc.enable()
+
+    cold = None if args.no_cold else cold_quant(fl, w, plan, q, x, args.cold_reps)
 
     # per-kernel durations from the events (same stream as the launches)
     gemm_ms = amax_ms = bias_ms = cast_ms = 0.0
@@ -363,7 +455,7 @@ def main():
     cast_gbs = 3.0 * quant_elems * K / (cast_ms * 1e-3) / 1e9 if cast_ms > 0 else None
     amax_gbs = 2.0 * quant_elems * K / (amax_ms * 1e-3) / 1e9 if amax_ms > 0 else None
 
-    rec = traffic_record()
+    rec = traffic_record(w.name)
     traffic = rec["bytes_per_launch"] if rec else None
     # the exact arithmetic runs its contraction on the fp16 MFMA: that is its peak
     peak = PEAK_F16_TFLOPS if args.math == "exact" else PEAK_FP8_TFLOPS
@@ -387,6 +479,7 @@ def main():
             "products": [f"{l.name}:{p}:{l.M}x{l.N}x{l.K}" for l in w.linears for p in l.passes],
             "in_step_quantised": [i[1] for i in plan if i[0] == "quant"],
             "accumulate": "f32",
+            "input_sha256": {t.name: synth.sha256(host[t.name]) for t in w.tensors},
             "math": args.math,
             "parallelism": "single-gpu",
         },
@@ -435,6 +528,7 @@ def main():
             if cast_ms > 0 else None,
             "bytes_per_element": 5,
         },
+        "cold": cold,
         "step_breakdown_ms": {"gemm": round(gemm_ms / K, 4), "amax": round(amax_ms / K, 4),
                               "bias": round(bias_ms / K, 4), "cast": round(cast_ms / K, 4)},
     }

@@ -23,22 +23,27 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 
-// Launch shapes measured on MI355X over a 470 MB bf16 tensor: amax peaks with
-// one 256-lane block per CU and 8 loads in flight per lane (more blocks add
-// contention on the single atomicMax target); the cast with ~4 units per lane
-// over a large grid.
-//
-// Cache hints, measured on amax -> cast sequences over 128 MiB and 448 MiB
-// bf16 tensors after a cache flush: amax reads with ordinary loads, so a
-// tensor that fits the 256 MB Infinity Cache is still there when the cast
-// reads it again (cast 6.2-6.4 TB/s on 128 MiB, against ~5.0 with streaming
-// hints on both); a cast whose input exceeds kCachedCastBytes streams with
-// non-temporal loads and stores (6.5 TB/s on 448 MiB, against 6.2 without).
-constexpr int64_t kCachedCastBytes = 192ll << 20;
+// Launch shapes and cache hints measured on MI355X over 128 MiB and 448 MiB
+// bf16 tensors, both cold (after a cache flush) and right after amax:
+//  * amax peaks with one 256-lane block per CU and 8 loads in flight per lane
+//    (more blocks add contention on the single atomicMax target);
+//  * the cast peaks with one 16-element unit per lane per iteration over a
+//    grid of up to 32768 blocks (every lane's two loads in flight at once):
+//    6.2 TB/s cold and 6.6 TB/s warm on 128 MiB, 6.4 / 6.8 TB/s on 448 MiB,
+//    against 4.7-5.4 cold with four units per lane over 4096 blocks;
+//  * amax and cast read with non-temporal loads, which do not allocate in the
+//    Infinity Cache: when the cache holds dirty lines (as after a GEMM has
+//    written its fp32 output) ordinary loads pay for writing them back (amax
+//    2.4 against 5.5 TB/s on 128 MiB), and in the full inference step this
+//    choice gives the shortest amax + bias + cast of all the combinations
+//    measured; the FP8 codes are stored ordinarily (faster than streaming
+//    stores in every case measured).
+//  FP8LIN_AMAX_HINT / FP8LIN_CAST_HINT = cached | nt override the load hint
+//  (tuning).
 constexpr int kAmaxUnroll = 8;
 constexpr int kAmaxMaxBlocks = 256;
-constexpr int kCastUnroll = 4;
-constexpr int kCastMaxBlocks = 16384;
+constexpr int kCastUnitsPerLane = 1;  // launch shape: units per lane
+constexpr int kCastMaxBlocks = 32768;
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -309,31 +314,36 @@ __device__ __forceinline__ uint4 cast_unit_sw(uint4 lo, uint4 hi, int32_t b) {
   return o;
 }
 
-// One unit = 16 elements -> one 16-byte store.  HW selects the hardware
-// conversion (bias in [kHwBiasMin, kHwBiasMax]) or fp8_code throughout.
-template <int FMT, bool HW, bool NT>
-__device__ __forceinline__ void cast_bf16_body(const uint4* __restrict__ x, int64_t nunit, int32_t b,
+// One unit = 16 elements -> one 16-byte store.  The data loads do not depend
+// on the bias, so they are issued before the bias load has returned; the
+// choice between the hardware conversion (bias in [kHwBiasMin, kHwBiasMax])
+// and fp8_code is a wave-uniform branch per unit after them.
+template <int FMT, bool NT>
+__device__ __forceinline__ void cast_bf16_body(const uint4* __restrict__ x, int64_t nunit,
+                                               const int32_t* __restrict__ bias,
                                                uint4* __restrict__ y) {
-  const uint32_t bound2 = hw_bound2<FMT>(b);
-  const float scale = __builtin_ldexpf(1.0f, -b);
-  auto unit = [&](uint4 lo, uint4 hi) {
-    if constexpr (HW) return cast_unit_hw<FMT>(lo, hi, b, bound2, scale);
-    else return cast_unit_sw<FMT>(lo, hi, b);
-  };
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + (kCastUnroll - 1) * stride < nunit; i += kCastUnroll * stride) {
-    uint4 lo[kCastUnroll], hi[kCastUnroll];
-#pragma unroll
-    for (int u = 0; u < kCastUnroll; ++u) {
-      lo[u] = load16<NT>(&x[2 * (i + u * stride)]);
-      hi[u] = load16<NT>(&x[2 * (i + u * stride) + 1]);
+  if (i >= nunit) return;
+  uint4 lo = load16<NT>(&x[2 * i]), hi = load16<NT>(&x[2 * i + 1]);
+  const int32_t b = *bias;
+  const bool hw = b >= kHwBiasMin && b <= kHwBiasMax;
+  const uint32_t bound2 = hw_bound2<FMT>(b);
+  const float scale = __builtin_ldexpf(1.0f, hw ? -b : 0);
+  for (;;) {
+    const int64_t next = i + stride;
+    uint4 nlo = lo, nhi = hi;
+    if (next < nunit) {  // the next unit's loads in flight during this one's conversion
+      nlo = load16<NT>(&x[2 * next]);
+      nhi = load16<NT>(&x[2 * next + 1]);
     }
-#pragma unroll
-    for (int u = 0; u < kCastUnroll; ++u) store16<NT>(unit(lo[u], hi[u]), &y[i + u * stride]);
+    store16<false>(hw ? cast_unit_hw<FMT>(lo, hi, b, bound2, scale) : cast_unit_sw<FMT>(lo, hi, b),
+                   &y[i]);
+    if (next >= nunit) break;
+    i = next;
+    lo = nlo;
+    hi = nhi;
   }
-  for (; i < nunit; i += stride)
-    store16<NT>(unit(load16<NT>(&x[2 * i]), load16<NT>(&x[2 * i + 1])), &y[i]);
 }
 
 template <int FMT, bool NT>
@@ -344,11 +354,9 @@ __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const uint4* __rest
                                                              const uint16_t* __restrict__ tail_x,
                                                              uint8_t* __restrict__ tail_y,
                                                              int ntail) {
-  const int32_t b = *bias;
-  if (b >= kHwBiasMin && b <= kHwBiasMax) cast_bf16_body<FMT, true, NT>(x, nunit, b, y);
-  else cast_bf16_body<FMT, false, NT>(x, nunit, b, y);
+  cast_bf16_body<FMT, NT>(x, nunit, bias, y);
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail)
-    tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>((uint32_t)tail_x[threadIdx.x] << 16, b);
+    tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>((uint32_t)tail_x[threadIdx.x] << 16, *bias);
 }
 
 template <int FMT, bool NT>
@@ -369,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restr
     o.y = pack4_f32<FMT>(a1, b);
     o.z = pack4_f32<FMT>(a2, b);
     o.w = pack4_f32<FMT>(a3, b);
-    store16<NT>(o, &y[i]);
+    store16<false>(o, &y[i]);
   }
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail)
     tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>(tail_x[threadIdx.x], b);
@@ -383,21 +391,18 @@ int stream_blocks(int64_t units, int64_t per_lane, int64_t cap) {
 
 }  // namespace
 
-// FP8LIN_AMAX_HINT=nt or cached forces the amax loads' cache hint (tuning);
-// by default a tensor that fits kCachedCastBytes is read cached (the cast that
-// follows finds it in the Infinity Cache) and a larger one streamed.
-static bool amax_streams(int64_t in_bytes) {
-  const char* h = std::getenv("FP8LIN_AMAX_HINT");
-  if (h && std::strcmp(h, "nt") == 0) return true;
-  if (h && std::strcmp(h, "cached") == 0) return false;
-  return in_bytes > kCachedCastBytes;
+// Load hint of amax and cast: non-temporal unless the environment variable
+// says "cached" (tuning).
+static bool streams(const char* var) {
+  const char* h = std::getenv(var);
+  return !(h && std::strcmp(h, "cached") == 0);
 }
 
 hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t stream) {
   uint32_t* out = reinterpret_cast<uint32_t*>(amax);
   hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, out);
   if (n > 0) {
-    const bool nt = amax_streams(n * (dtype == FP8_IN_BF16 ? 2 : 4));
+    const bool nt = streams("FP8LIN_AMAX_HINT");
     if (dtype == FP8_IN_BF16) {
       const int64_t nvec = n / 8;
       const int ntail = (int)(n - nvec * 8);
@@ -433,12 +438,11 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias,
   const int ntail = (int)(n - nunit * 16);
   uint8_t* tail_y = y + nunit * 16;
   uint4* yv = reinterpret_cast<uint4*>(y);
-  const int64_t in_bytes = n * (dtype == FP8_IN_BF16 ? 2 : 4);
-  const bool nt = in_bytes > kCachedCastBytes;
+  const bool nt = streams("FP8LIN_CAST_HINT");
   if (dtype == FP8_IN_BF16) {
     const uint16_t* tail_x = static_cast<const uint16_t*>(x) + nunit * 16;
     const uint4* xv = static_cast<const uint4*>(x);
-    const dim3 grid(stream_blocks(nunit, kCastUnroll, kCastMaxBlocks));
+    const dim3 grid(stream_blocks(nunit, kCastUnitsPerLane, kCastMaxBlocks));
 #define FP8LIN_CAST(F, NT)                                                                    \
   hipLaunchKernelGGL((cast_bf16_kernel<F, NT>), grid, dim3(kThreads), 0, stream, xv, nunit, \
                      bias, yv, tail_x, tail_y, ntail)

@@ -134,3 +134,44 @@ def test_workload_tensors_bit_exact(fl, wl):
         ref = oracle.scale_cast(words.reshape(-1), b_ref, t.fmt)
         assert np.array_equal(got, ref), f"{t.name}: {np.count_nonzero(got != ref)} codes differ"
         del codes, x
+
+
+def test_cast_mixes_non_finite_values_into_finite_units(fl):
+    """The cast converts 16-element units on the hardware path unless a unit
+    holds an inf or NaN; here every unit mixes a few of them into finite
+    values (including ones that saturate), at biases on both paths."""
+    rng = np.random.default_rng(5)
+    n = 16 * 4096 + 7
+    v = (rng.standard_normal(n) * 300).astype(np.float32)
+    words = synth.bf16_words(synth.to_bf16(v)).copy()
+    specials = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81], dtype=np.uint16)
+    pos = rng.integers(0, n, n // 5)
+    words[pos] = specials[rng.integers(0, specials.size, pos.size)]
+    x = bf16_dev(words)
+    for fmt in (E4M3, E5M2):
+        for b in (-130, -4, 0, 3, 12, 126, 127):
+            say("cast mixed non-finite", "fmt", fmt, "bias", b)
+            got = fl.scale_cast(x, i32_dev(b), fmt).cpu().numpy()
+            ref = oracle.scale_cast(words, b, fmt)
+            assert np.array_equal(got, ref), f"fmt {fmt} bias {b}: {np.count_nonzero(got != ref)} codes differ"
+
+
+def test_gradient_underflow_control(fl):
+    """The 13B backward workload's gradients (~N(0,1) x 1e-6) cast to E5M2:
+    with bias 0 every value lies below the smallest E5M2 subnormal's half, so
+    every code is a signed zero; with the AMAX bias the codes carry the
+    values (the underflow the per-tensor scale avoids)."""
+    w = synth.WORKLOADS[4]
+    dy = synth.workload_tensor(w, "dY_down")
+    words = synth.bf16_words(dy).ravel()
+    x = bf16_dev(words)
+    say("underflow control dY_down", words.size)
+    zero = fl.scale_cast(x, i32_dev(0), E5M2).cpu().numpy()
+    assert np.all((zero & 0x7F) == 0)
+    amax = fl.amax(x)
+    bias = fl.compute_bias(amax, E5M2, 0)
+    b = int(bias.cpu().item())
+    assert b == oracle.compute_bias(oracle.amax_bits(words), E5M2, 0)
+    codes = fl.scale_cast(x, bias, E5M2).cpu().numpy()
+    assert np.array_equal(codes, oracle.scale_cast(words, b, E5M2))
+    assert np.count_nonzero(codes & 0x7F) > 0.99 * codes.size
