@@ -102,6 +102,53 @@ def traffic_record(workload):
     return rec
 
 
+def epilogue_amax(fl, w, plan, q, outs, math, op_of, reps=9):
+    """The largest product of the step three ways (interleaved, median of
+    `reps`, HIP events): alone; with the amax of its fp32 output folded in its epilogue
+    (fp8_scaled_gemm_amax); and followed by a separate fp8_amax pass over
+    that output, which is what quantising the output next would otherwise
+    need."""
+    import statistics
+
+    import torch
+    gemms = [i for i in plan if i[0] == "gemm"]
+    if not gemms:
+        return None
+    _, l, which = max(gemms, key=lambda i: i[1].M * i[1].N * i[1].K)
+    an, bn, _ = gemm_operands(l, which)
+    a8, ba, _, fa = q[an]
+    b8, bb, _, fb = q[bn]
+    out = outs[(l.name, which)]
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def once(fn):
+        torch.cuda.synchronize()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    plain = lambda: fl.scaled_gemm(op_of[which], a8, fa, ba, b8, fb, bb, math=math, out=out)
+    fused = lambda: fl.scaled_gemm(op_of[which], a8, fa, ba, b8, fb, bb, math=math, out=out, amax=amax)
+
+    def separate():
+        plain()
+        fl.amax(out.reshape(-1), out=amax)
+
+    # the three variants interleaved, so that clock drift affects them alike
+    ts = {"plain": [], "fused": [], "separate": []}
+    for _ in range(reps):
+        for k, fn in (("plain", plain), ("fused", fused), ("separate", separate)):
+            ts[k].append(once(fn))
+    t_plain, t_fused, t_sep = (statistics.median(ts[k]) for k in ("plain", "fused", "separate"))
+    return {"product": f"{l.name}:{which}:{l.M}x{l.N}x{l.K}",
+            "gemm_us": round(t_plain, 1), "gemm_with_epilogue_amax_us": round(t_fused, 1),
+            "gemm_then_amax_pass_us": round(t_sep, 1),
+            "saved_us": round(t_sep - t_fused, 1)}
+
+
 COLD_FLUSH_BYTES = 768 << 20   # > the 256 MB Infinity Cache
 COLD_CLEAN_BYTES = 512 << 20
 
@@ -423,6 +470,7 @@ def main():
     gc.enable()
 
     cold = None if args.no_cold else cold_quant(fl, w, plan, q, x, args.cold_reps)
+    epi = epilogue_amax(fl, w, plan, q, outs, math, op_of)
 
     # per-kernel durations from the events (same stream as the launches)
     gemm_ms = amax_ms = bias_ms = cast_ms = 0.0
@@ -529,6 +577,7 @@ def main():
             "bytes_per_element": 5,
         },
         "cold": cold,
+        "epilogue_amax": epi,
         "step_breakdown_ms": {"gemm": round(gemm_ms / K, 4), "amax": round(amax_ms / K, 4),
                               "bias": round(bias_ms / K, 4), "cast": round(cast_ms / K, 4)},
     }

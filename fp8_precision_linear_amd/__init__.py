@@ -41,6 +41,7 @@ SIGNATURES = {
     "fp8_compute_bias": (_ci, [_vp, _ci, _i32, _vp, _vp]),
     "fp8_scale_cast": (_ci, [_vp, _ci, _i64, _vp, _ci, _vp, _vp]),
     "fp8_scaled_gemm": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "fp8_scaled_gemm_amax": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_fwd": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_dgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_wgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
@@ -171,10 +172,12 @@ def scaled_gemm_wgrad(dy8, fdy, bdy, x8, fx, bx, out=None, stream=None):
     return out
 
 
-def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=None):
+def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=None, amax=None):
     """Any of the three products with a chosen arithmetic (fp8_scaled_gemm).
     op: OP_FWD (a = X8[M, K], b = W8[N, K]), OP_DGRAD (a = dY8[M, N], b = W8[N, K])
-    or OP_WGRAD (a = dY8[M, N], b = X8[M, K]); math: MATH_EXACT or MATH_NATIVE_FP8."""
+    or OP_WGRAD (a = dY8[M, N], b = X8[M, K]); math: MATH_EXACT or MATH_NATIVE_FP8.
+    amax: optional float32[1] device tensor that receives max |out|, computed
+    in the product's epilogue (fp8_scaled_gemm_amax)."""
     _need_cuda(a8, b8, ba, bb)
     if op == OP_FWD:
         (M, K), (N, K2) = a8.shape, b8.shape
@@ -190,7 +193,14 @@ def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=No
     if not ok:
         raise ValueError("contraction sizes differ")
     out = torch.empty(shape, dtype=torch.float32, device=a8.device) if out is None else out
-    _check("fp8_scaled_gemm",
-           lib.fp8_scaled_gemm(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8), int(fb),
-                               _ptr(bb), M, N, K, _ptr(out), _stream(stream)))
+    if amax is None:
+        _check("fp8_scaled_gemm",
+               lib.fp8_scaled_gemm(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8), int(fb),
+                                   _ptr(bb), M, N, K, _ptr(out), _stream(stream)))
+    else:
+        _need_cuda(amax)
+        _check("fp8_scaled_gemm_amax",
+               lib.fp8_scaled_gemm_amax(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8),
+                                        int(fb), _ptr(bb), M, N, K, _ptr(out), _ptr(amax),
+                                        _stream(stream)))
     return out

@@ -96,43 +96,75 @@ int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* b
   return hip_status(fp8lin::launch_cast(x, dtype, n, bias, fmt, y, (hipStream_t)stream));
 }
 
-int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
-                    const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
-                    int64_t M, int64_t N, int64_t K, float* out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The three products; out_amax (optional) receives max |out|.  Every argument
+// is checked before any HIP call; on error nothing is written.
+int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, const int32_t* ba,
+                const uint8_t* b, fp8_format_t fb, const int32_t* bb, int64_t M, int64_t N,
+                int64_t K, float* out, float* out_amax, hipStream_t st) {
   if (math != FP8_GEMM_EXACT && math != FP8_GEMM_NATIVE_FP8) return FP8_ERR_OP;
-  hipStream_t st = (hipStream_t)stream;
+  fp8lin::GemmProblem p{};
+  bool empty = false;
   switch (op) {
-    case FP8_GEMM_FWD: {
+    case FP8_GEMM_FWD:
       // Y[M x N]: X8 and W8 both contraction (K) contiguous.
       if (int s = gemm_checks(a, fa, ba, b, fb, bb, M, N, K, out, M * K, N * K)) return s;
-      if (M == 0 || N == 0) return FP8_OK;
-      if (int s = device_ok()) return s;
-      fp8lin::GemmProblem p{a, K, true, fa, ba, b, K, true, fb, bb, out, N,
-                            (int)M, (int)N, (int)K, math};
-      return hip_status(fp8lin::launch_gemm_fwd(p, st));
-    }
-    case FP8_GEMM_DGRAD: {
+      empty = M == 0 || N == 0;
+      p = fp8lin::GemmProblem{a, K, true, fa, ba, b, K, true, fb, bb, out, N,
+                              (int)M, (int)N, (int)K, math, nullptr};
+      break;
+    case FP8_GEMM_DGRAD:
       // dX[M x K]: rows of dY8 (contraction N contiguous) times W8 read as
       // [contraction N][K] (the contraction is its slow index).
       if (int s = gemm_checks(a, fa, ba, b, fb, bb, M, K, N, out, M * N, N * K)) return s;
-      if (M == 0 || K == 0) return FP8_OK;
-      if (int s = device_ok()) return s;
-      fp8lin::GemmProblem p{a, N, true, fa, ba, b, K, false, fb, bb, out, K,
-                            (int)M, (int)K, (int)N, math};
-      return hip_status(fp8lin::launch_gemm_dgrad(p, st));
-    }
-    case FP8_GEMM_WGRAD: {
+      empty = M == 0 || K == 0;
+      p = fp8lin::GemmProblem{a, N, true, fa, ba, b, K, false, fb, bb, out, K,
+                              (int)M, (int)K, (int)N, math, nullptr};
+      break;
+    case FP8_GEMM_WGRAD:
       // dW[N x K]: dY8 read as [contraction M][N] times X8 read as [contraction M][K].
       if (int s = gemm_checks(a, fa, ba, b, fb, bb, N, K, M, out, M * N, M * K)) return s;
-      if (N == 0 || K == 0) return FP8_OK;
-      if (int s = device_ok()) return s;
-      fp8lin::GemmProblem p{a, N, false, fa, ba, b, K, false, fb, bb, out, K,
-                            (int)N, (int)K, (int)M, math};
-      return hip_status(fp8lin::launch_gemm_wgrad(p, st));
-    }
+      empty = N == 0 || K == 0;
+      p = fp8lin::GemmProblem{a, N, false, fa, ba, b, K, false, fb, bb, out, K,
+                              (int)N, (int)K, (int)M, math, nullptr};
+      break;
     default:
       return FP8_ERR_OP;
   }
+  if (empty && !out_amax) return FP8_OK;
+  if (int s = device_ok()) return s;
+  if (out_amax) {
+    p.amax = reinterpret_cast<uint32_t*>(out_amax);
+    if (int s = hip_status(fp8lin::launch_clear_u32(p.amax, st))) return s;
+  }
+  if (empty) return FP8_OK;
+  switch (op) {
+    case FP8_GEMM_FWD: return hip_status(fp8lin::launch_gemm_fwd(p, st));
+    case FP8_GEMM_DGRAD: return hip_status(fp8lin::launch_gemm_dgrad(p, st));
+    default: return hip_status(fp8lin::launch_gemm_wgrad(p, st));
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
+                    const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
+                    int64_t M, int64_t N, int64_t K, float* out, void* stream) {
+  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, nullptr, (hipStream_t)stream);
+}
+
+int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
+                         const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
+                         int64_t M, int64_t N, int64_t K, float* out, float* out_amax,
+                         void* stream) {
+  if (!out_amax) return FP8_ERR_NULL;
+  if (((uintptr_t)out_amax & 3u) != 0) return FP8_ERR_ALIGN;
+  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, out_amax, (hipStream_t)stream);
 }
 
 int fp8_scaled_gemm_fwd(const uint8_t* x8, fp8_format_t fx, const int32_t* bx,

@@ -224,6 +224,15 @@ __device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
   return __builtin_bit_cast(v8h, make_uint4(a.x, a.y, b.x, b.y));
 }
 
+// Fold this lane's largest output magnitude (fp32 bits, sign cleared) into
+// *amax: wave maximum by shuffles, then one atomicMax per wave.  Every lane of
+// the wave must reach it.
+__device__ __forceinline__ void amax_fold(uint32_t m, uint32_t* amax) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(amax, m);
+}
+
 // The general kernel: any shape and alignment (operands staged through
 // registers with zero fill at every edge, two LDS stages of 128 bytes).
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int FA, int FB, int MATH>
@@ -329,6 +338,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles
   // 32x32 accumulator layout: register r of lane l holds row
   // 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32 of the MFMA tile.
   const int unscale = -(*p.bias_a + *p.bias_b);
+  uint32_t mx = 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -337,10 +347,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < p.m && col < p.n)
-          p.c[(int64_t)row * p.ldc + col] = __builtin_ldexpf(acc[i][j][r], unscale);
+        if (row < p.m && col < p.n) {
+          const float v = __builtin_ldexpf(acc[i][j][r], unscale);
+          p.c[(int64_t)row * p.ldc + col] = v;
+          mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu);
+        }
       }
     }
+  if (p.amax) amax_fold(mx, p.amax);
 }
 
 }  // namespace gemm_detail

@@ -311,12 +311,14 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[TM][TN]) {
 
 // Unscale and store a wave's TM x TN block of 32x32 tiles whose top-left
 // output is (row0, col0).  32x32 accumulator layout: register r of lane l
-// holds row 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32.
-template <int TM, int TN>
-__device__ __forceinline__ void store_block(const GemmProblem& p, const v16f (&acc)[TM][TN],
-                                            int row0, int col0, int lane) {
+// holds row 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32.  With
+// AMAX the largest stored magnitude is folded into *p.amax.
+template <bool AMAX, int TM, int TN>
+__device__ __forceinline__ void store_block_as(const GemmProblem& p, const v16f (&acc)[TM][TN],
+                                               int row0, int col0, int lane) {
   const int h = lane >> 5, rl = lane & 31;
   const int unscale = -(*p.bias_a + *p.bias_b);
+  uint32_t mx = 0;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -325,10 +327,21 @@ __device__ __forceinline__ void store_block(const GemmProblem& p, const v16f (&a
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < p.m && col < p.n)
-          p.c[(int64_t)row * p.ldc + col] = __builtin_ldexpf(acc[i][j][r], unscale);
+        if (row < p.m && col < p.n) {
+          const float v = __builtin_ldexpf(acc[i][j][r], unscale);
+          p.c[(int64_t)row * p.ldc + col] = v;
+          if constexpr (AMAX) mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu);
+        }
       }
     }
+  if constexpr (AMAX) amax_fold(mx, p.amax);
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void store_block(const GemmProblem& p, const v16f (&acc)[TM][TN],
+                                            int row0, int col0, int lane) {
+  if (p.amax) store_block_as<true>(p, acc, row0, col0, lane);
+  else store_block_as<false>(p, acc, row0, col0, lane);
 }
 
 // ------------------------------------------------------ ping-pong, 256 x 256

@@ -14,6 +14,8 @@ hipError_t launch_bias(const float* amax, int fmt, int32_t margin, int32_t* bias
                        hipStream_t stream);
 hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias, int fmt,
                        uint8_t* y, hipStream_t stream);
+// *p = 0 (one lane).
+hipError_t launch_clear_u32(uint32_t* p, hipStream_t stream);
 
 // Product arithmetic (the values of fp8_scaled_gemm's `math` argument).
 #define FP8LIN_MATH_EXACT FP8_GEMM_EXACT
@@ -37,6 +39,9 @@ struct GemmProblem {
   int64_t ldc;
   int m, n, k;
   int math;
+  // optional: fold max |C[m][n]| (as fp32 magnitude bits) into *amax with
+  // atomicMax; nullptr for none
+  uint32_t* amax;
 };
 
 // One launcher per operand layout (gemm_fwd.hip, gemm_dgrad.hip, gemm_wgrad.hip).

@@ -424,6 +424,11 @@ hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStre
   return hipGetLastError();
 }
 
+hipError_t launch_clear_u32(uint32_t* p, hipStream_t stream) {
+  hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_bias(const float* amax, int fmt, int32_t margin, int32_t* bias,
                        hipStream_t stream) {
   hipLaunchKernelGGL(bias_kernel, dim3(1), dim3(1), 0, stream,

@@ -113,8 +113,9 @@ int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* b
  *
  * Arithmetic: every product of two FP8 values is exact in fp32 and the sums
  * are formed with fp32 accuracy (FP8_GEMM_EXACT): the FP8 codes are widened
- * exactly to fp16 in registers and multiplied on the fp16 MFMA, whose
- * products are summed with a 24-bit window.  The native FP8 MFMA of gfx950 is
+ * exactly to fp16 (both operands E4M3) or bf16 (an E5M2 operand) in registers
+ * and multiplied on the 16-bit MFMA, whose products are summed with a 24-bit
+ * window.  The native FP8 MFMA of gfx950 is
  * twice as fast but keeps only about 13 bits below the largest of the 64
  * products each instruction sums (an error near 1e-4 of sum|a||b| per
  * instruction); it is available through fp8_scaled_gemm with
@@ -135,6 +136,21 @@ typedef enum {
 int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
                     const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
                     int64_t M, int64_t N, int64_t K, float* out, void* stream);
+
+/* fp8_scaled_gemm that also returns the per-tensor amax of its output (the
+ * "Proposed method" bullet-1 statistic of the tensor the product produces),
+ * computed in the product's own epilogue, so that quantising the output next
+ * needs no separate amax pass over it (fp8_compute_bias takes it directly).
+ *   out_amax  device, one float, 4-byte aligned, written: max |out| over all
+ *             written outputs (0 when there are none; NaN if an output is
+ *             NaN), bit-identical to fp8_amax over the fp32 output.
+ * Launches a one-lane clear of out_amax, then the product.  Returns
+ * FP8_ERR_NULL / FP8_ERR_ALIGN for a null or misaligned out_amax, otherwise
+ * as fp8_scaled_gemm. */
+int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
+                         const int32_t* ba, const uint8_t* b, fp8_format_t fb,
+                         const int32_t* bb, int64_t M, int64_t N, int64_t K, float* out,
+                         float* out_amax, void* stream);
 
 /* Forward: Y[M x N] = 2^-(bx+bw) * X8[M x K] . W8[N x K]^T */
 int fp8_scaled_gemm_fwd(const uint8_t* x8, fp8_format_t fx, const int32_t* bx,

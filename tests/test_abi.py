@@ -31,7 +31,7 @@ def status(code):
 
 def test_every_declared_function_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(L, n), n
         assert n in fl.SIGNATURES, n
@@ -122,3 +122,26 @@ def test_generic_gemm_rejects_unknown_op_and_math():
     for op in (0, 1, 2):
         assert L.fp8_scaled_gemm(op, 1, A16, 5, A32, A48, 0, A32, 8, 8, 8, A16, None) == status("FP8_ERR_FORMAT")
         assert L.fp8_scaled_gemm(op, 0, A16, 0, A32, A48, 0, A32, 8, 8, 8, None, None) == status("FP8_ERR_NULL")
+
+
+def test_gemm_amax_argument_checks():
+    """fp8_scaled_gemm_amax checks its amax output first, then everything
+    fp8_scaled_gemm checks, all before any HIP call."""
+    f = L.fp8_scaled_gemm_amax
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 8, 8, 8, A16, None, None) == status("FP8_ERR_NULL")
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 8, 8, 8, A16, P(18), None) == status("FP8_ERR_ALIGN")
+    assert f(3, 0, A16, 0, A32, A48, 0, A32, 8, 8, 8, A16, A32, None) == status("FP8_ERR_OP")
+    assert f(0, 2, A16, 0, A32, A48, 0, A32, 8, 8, 8, A16, A32, None) == status("FP8_ERR_OP")
+    for op in (0, 1, 2):
+        assert f(op, 0, A16, 7, A32, A48, 0, A32, 8, 8, 8, A16, A32, None) == status("FP8_ERR_FORMAT")
+        assert f(op, 0, A16, 0, A32, A48, 0, A32, 8, 8, 8, None, A32, None) == status("FP8_ERR_NULL")
+        assert f(op, 0, MIS, 0, A32, A48, 0, A32, 8, 8, 8, A16, A32, None) == status("FP8_ERR_ALIGN")
+        assert f(op, 0, A16, 0, A32, A48, 0, A32, -1, 8, 8, A16, A32, None) == status("FP8_ERR_SIZE")
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
+def test_gemm_amax_without_a_device_reports_no_device():
+    """Even an empty product must clear its amax output, so it needs the device."""
+    f = L.fp8_scaled_gemm_amax
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 0, 8, 8, A16, A32, None) == status("FP8_ERR_DEVICE")
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 64, 64, 64, A16, A32, None) == status("FP8_ERR_DEVICE")

@@ -210,3 +210,44 @@ def test_workload_products(fl, wl):
                 ref, bound = at(a8, fa, ba, b8, fb, bb, rows, cols)
                 check_gemm(got[rows, cols], ref, bound, f"wl{wl} {l.name} {which}")
             del got
+
+
+@pytest.mark.parametrize("which", ["fwd", "dgrad", "wgrad"])
+def test_epilogue_amax_is_the_amax_of_the_output(fl, tile, which):
+    """fp8_scaled_gemm_amax: the product's output is the same as without it,
+    and the amax its epilogue folds is bit-identical to max |out| of that
+    output (and to fp8_amax over it).  An empty product leaves amax 0."""
+    rng = np.random.default_rng(77)
+    op = {"fwd": fl.OP_FWD, "dgrad": fl.OP_DGRAD, "wgrad": fl.OP_WGRAD}[which]
+    for (M, N, K) in [(300, 520, 392), (257, 129, 1000), (512, 512, 128), (64, 64, 0), (1, 17, 1), (0, 8, 8)]:
+        a8, b8 = operands(rng, which, M, N, K, E5M2, E4M3)
+        A, B, BA, BB = u8_dev(a8), u8_dev(b8), i32_dev(3), i32_dev(-2)
+        say("epilogue amax", which, "tile", tile, "MNK", M, N, K)
+        plain = fl.scaled_gemm(op, A, E5M2, BA, B, E4M3, BB)
+        amax = torch.full((1,), 12345.0, dtype=torch.float32, device="cuda")
+        got = fl.scaled_gemm(op, A, E5M2, BA, B, E4M3, BB, amax=amax)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int32), plain.view(torch.int32))
+        bits = got.view(torch.int32).cpu().numpy().astype(np.uint32) & 0x7FFFFFFF
+        want = int(bits.max()) if bits.size else 0
+        assert int(amax.view(torch.int32).cpu().item()) == want
+        if got.numel():
+            assert torch.equal(fl.amax(got.reshape(-1)).view(torch.int32), amax.view(torch.int32))
+
+
+def test_epilogue_amax_drives_the_next_quantisation(fl):
+    """Quantising a product's fp32 output with the bias from its epilogue
+    amax gives the oracle's codes for that output (amax, bias and cast
+    bit-exact, "Proposed method" bullets 1-4)."""
+    rng = np.random.default_rng(78)
+    M, N, K = 384, 640, 512
+    a8, b8 = operands(rng, "fwd", M, N, K, E4M3, E4M3)
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    y = fl.scaled_gemm(fl.OP_FWD, u8_dev(a8), E4M3, i32_dev(4), u8_dev(b8), E4M3, i32_dev(5), amax=amax)
+    for fmt in (E4M3, E5M2):
+        bias = fl.compute_bias(amax, fmt, 1)
+        codes = fl.scale_cast(y.reshape(-1), bias, fmt).cpu().numpy()
+        words = y.reshape(-1).view(torch.int32).cpu().numpy().view(np.uint32)
+        b = oracle.compute_bias(oracle.amax_bits(words), fmt, 1)
+        assert int(bias.cpu().item()) == b
+        assert np.array_equal(codes, oracle.scale_cast(words, b, fmt))

@@ -175,3 +175,31 @@ def test_gradient_underflow_control(fl):
     codes = fl.scale_cast(x, bias, E5M2).cpu().numpy()
     assert np.array_equal(codes, oracle.scale_cast(words, b, E5M2))
     assert np.count_nonzero(codes & 0x7F) > 0.99 * codes.size
+
+
+def test_fixed_and_delayed_scaling(fl):
+    """FP8-CSCALE and delayed scaling use the same cast with a bias the
+    caller chooses ("Proposed method": the fixed-scale baseline the pages
+    compare AMAX against): a bias written to device memory by the caller, or
+    the bias of an earlier tensor reused on a new one.  Here a tensor that has
+    grown 8x since its bias was taken saturates under the stale bias exactly
+    as the rounding rule says, and not under its own AMAX bias."""
+    rng = np.random.default_rng(31)
+    old = synth.bf16_words(synth.to_bf16((rng.standard_normal(1 << 20) * 2.0).astype(np.float32)))
+    new = synth.bf16_words(synth.to_bf16((rng.standard_normal(1 << 20) * 16.0).astype(np.float32)))
+    for fmt in (E4M3, E5M2):
+        say("fixed / delayed scaling", "fmt", fmt)
+        # fixed scale: bias chosen by the caller
+        for b in (-3, 0, 5):
+            got = fl.scale_cast(bf16_dev(new), i32_dev(b), fmt).cpu().numpy()
+            assert np.array_equal(got, oracle.scale_cast(new, b, fmt))
+        # delayed scale: the old tensor's AMAX bias, kept on the device
+        stale = fl.compute_bias(fl.amax(bf16_dev(old)), fmt, 0)
+        b_old = int(stale.cpu().item())
+        got = fl.scale_cast(bf16_dev(new), stale, fmt).cpu().numpy()
+        assert np.array_equal(got, oracle.scale_cast(new, b_old, fmt))
+        top = 0x7E if fmt == E4M3 else 0x7B
+        assert np.count_nonzero((got & 0x7F) == top) > 100          # saturated under the stale bias
+        fresh = fl.compute_bias(fl.amax(bf16_dev(new)), fmt, 0)
+        got = fl.scale_cast(bf16_dev(new), fresh, fmt).cpu().numpy()
+        assert np.count_nonzero((got & 0x7F) == top) <= 2           # only the largest values reach the top code
