@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold (cache-flushed) amax and cast measurement")
     ap.add_argument("--cold-reps", type=int, default=5)
+    ap.add_argument("--no-epilogue-amax", action="store_true",
+                    help="skip the epilogue-amax measurement on the largest product")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy twice (HBM counter calibration)")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -276,9 +278,9 @@ def record_traffic(d):
         "source_sha256": sources_sha(GEMM_SOURCES),
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/fetch -o run -- "
-            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold",
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/write -o run -- "
-            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold",
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/copy_fetch -o run -- "
             "python3 bench.py --copy-calibration",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/copy_write -o run -- "
@@ -470,7 +472,7 @@ def main():
     gc.enable()
 
     cold = None if args.no_cold else cold_quant(fl, w, plan, q, x, args.cold_reps)
-    epi = epilogue_amax(fl, w, plan, q, outs, math, op_of)
+    epi = None if args.no_epilogue_amax else epilogue_amax(fl, w, plan, q, outs, math, op_of)
 
     # per-kernel durations from the events (same stream as the launches)
     gemm_ms = amax_ms = bias_ms = cast_ms = 0.0

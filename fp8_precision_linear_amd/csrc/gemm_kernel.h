@@ -225,12 +225,17 @@ __device__ __forceinline__ v8h fp8x8_to_f16(int w0, int w1) {
 }
 
 // Fold this lane's largest output magnitude (fp32 bits, sign cleared) into
-// *amax: wave maximum by shuffles, then one atomicMax per wave.  Every lane of
-// the wave must reach it.
+// *amax: wave maximum by shuffles, then one atomicMax per wave -- skipped when
+// *amax already holds at least as much.  Every wave of a product reaches this
+// at about the same time, and atomics on one address serialise; the value only
+// grows, so a stale read can cost an unneeded atomic but never a wrong result.
+// Every lane of the wave must reach it.
 __device__ __forceinline__ void amax_fold(uint32_t m, uint32_t* amax) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(amax, m);
+  if ((threadIdx.x & 63) == 0 &&
+      m > __hip_atomic_load(amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+    atomicMax(amax, m);
 }
 
 // The general kernel: any shape and alignment (operands staged through
