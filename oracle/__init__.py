@@ -27,8 +27,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 BF16, F32 = 0, 1
-E4M3, E5M2 = 0, 1
-FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
+E4M3, E5M2, E3M4 = 0, 1, 2
+FMT_MAX = {E4M3: 448.0, E5M2: 57344.0, E3M4: 30.0}
 
 
 def build():

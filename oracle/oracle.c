@@ -20,6 +20,11 @@
  * Readings where the page is silent (each is listed in the design notes):
  *   - FP8_E4 / FP8_E5 are the OCP 8-bit formats E4M3 (max 448, no infinity,
  *     NaN = S.1111.111) and E5M2 (max 57344, IEEE-style inf and NaN);
+ *   - E3M4, the third format of the post-training quantisation study ("Efficient
+ *     post-training quantization with FP8 formats", summary page), is named
+ *     there without its encoding; it is read here as built like OCP E4M3:
+ *     exponent bias 3, 4 mantissa bits, subnormals, no infinity, NaN only at
+ *     S.111.1111, so max 30 = S.111.1110 and the smallest subnormal 2^-6;
  *   - bias = floor(log2(fmt_max / amax)) - margin, an integer, so the scale
  *     2^bias is a power of two and amax * 2^bias <= fmt_max when margin >= 0;
  *   - amax that is 0, inf or NaN gives bias 0 and the margin is not applied;
@@ -49,6 +54,7 @@
 #define ORACLE_F32 1
 #define ORACLE_E4M3 0
 #define ORACLE_E5M2 1
+#define ORACLE_E3M4 2
 
 /* Threads the OpenMP loops below may use (1 without OpenMP). */
 int oracle_threads(void) {
@@ -164,8 +170,10 @@ static fmt_t format_params(int fmt) {
   fmt_t f;
   if (fmt == ORACLE_E4M3) {
     f.mbits = 3; f.emin = -6; f.emax = 8; f.fmt_max = 448.0; f.maxcode = 0x7E;
-  } else {
+  } else if (fmt == ORACLE_E5M2) {
     f.mbits = 2; f.emin = -14; f.emax = 15; f.fmt_max = 57344.0; f.maxcode = 0x7B;
+  } else {
+    f.mbits = 4; f.emin = -2; f.emax = 4; f.fmt_max = 30.0; f.maxcode = 0x7E;
   }
   return f;
 }
@@ -198,6 +206,10 @@ double oracle_decode_fp8(uint8_t c, int fmt) {
     int E = (c >> 3) & 15, M = c & 7;
     if (E == 15 && M == 7) return NAN;
     v = (E == 0) ? ldexp((double)M, -9) : ldexp((double)(8 + M), E - 10);
+  } else if (fmt == ORACLE_E3M4) {
+    int E = (c >> 4) & 7, M = c & 15;
+    if (E == 7 && M == 15) return NAN;
+    v = (E == 0) ? ldexp((double)M, -6) : ldexp((double)(16 + M), E - 7);
   } else {
     int E = (c >> 2) & 31, M = c & 3;
     if (E == 31) return M ? NAN : (s ? -INFINITY : INFINITY);

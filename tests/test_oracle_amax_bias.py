@@ -20,9 +20,10 @@ import pytest
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-E4M3, E5M2 = 0, 1
-FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
-FMT_NAME = {"E4M3": E4M3, "E5M2": E5M2}
+E4M3, E5M2, E3M4 = 0, 1, 2
+ALL_FMTS = [E4M3, E5M2, E3M4]
+FMT_MAX = {E4M3: 448.0, E5M2: 57344.0, E3M4: 30.0}   # E3M4: the reading of the oracle's header
+FMT_NAME = {"E4M3": E4M3, "E5M2": E5M2, "E3M4": E3M4}
 
 
 def f32_of_bits(b):
@@ -122,7 +123,7 @@ def test_bias_golden_values(orc):
         assert got == int(expected), (fmt_s, bits, margin, got, expected)
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_bias_every_positive_finite_bf16(orc, fmt):
     words = np.arange(1, 0x7F80, dtype=np.uint32)       # +subnormals .. +max finite
     assert words.size == 32639
@@ -135,10 +136,10 @@ def test_bias_every_positive_finite_bf16(orc, fmt):
         assert bad.size == 0, (margin, vals[bad[:5]], got[bad[:5]], ref[bad[:5]])
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_bias_fp32_thresholds_and_random(orc, fmt):
     rng = np.random.default_rng(9)
-    mants = [0, 1, 0x5FFFFF, 0x600000, 0x600001, 0x7FFFFF, 0x400000]
+    mants = [0, 1, 0x5FFFFF, 0x600000, 0x600001, 0x6FFFFF, 0x700000, 0x700001, 0x7FFFFF, 0x400000]
     bits = [(e << 23) | m for e in range(0, 255) for m in mants if (e, m) != (0, 0)]
     bits += rng.integers(1, 0x7F800000, 30_000).tolist()
     for k in range(-150, 112):  # fmt_max * 2^k and its fp32 neighbours
@@ -155,7 +156,7 @@ def test_bias_fp32_thresholds_and_random(orc, fmt):
         assert orc.compute_bias(b, fmt, 0) == bias_bruteforce(a, FMT_MAX[fmt], 0), hex(b)
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_bias_next_float_above_power_of_two_multiple_drops_by_one(orc, fmt):
     for k in range(-20, 20):
         a = np.float32(math.ldexp(FMT_MAX[fmt], -k))
@@ -164,7 +165,7 @@ def test_bias_next_float_above_power_of_two_multiple_drops_by_one(orc, fmt):
         assert orc.compute_bias(bits_of_f32(up), fmt, 0) == k - 1
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_bias_invariants(orc, fmt):
     words = np.arange(1, 0x7F80, dtype=np.uint32)
     bits = (words << 16).astype(np.uint32)
@@ -182,7 +183,7 @@ def test_bias_invariants(orc, fmt):
         assert np.array_equal(bm, b0[::97] - m)
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_bias_of_zero_inf_nan_is_zero(orc, fmt):
     for bits in (0x00000000, 0x80000000, 0x7F800000, 0x7FC00000, 0x7FFFFFFF):
         for m in (-3, 0, 2):

@@ -6,8 +6,17 @@ before the FP8 cast; E4 for weights/activations, E5 for gradients).  Rounding
 to nearest with ties to the even code, saturation, kept subnormals, signed
 zero and NaN -> 0x7F|sign are the readings this library takes.
 
+E3M4, the third format of "Efficient post-training quantization with FP8
+formats" (summary page), is named there without its encoding; the reading
+taken is OCP E4M3's construction with 3 exponent bits (bias 3) and 4 mantissa
+bits: subnormals, no infinity, NaN only at S.111.1111, max 30, smallest
+subnormal 2^-6.  torch has no such dtype, so its grid is enumerated here as a
+set of values (subnormal multiples of 2^-6 and 16 values per binade
+2^-2 .. 2^4), sorted, and pinned by hand-worked values.
+
 Independent references used here, none of which shares code with the oracle:
   * torch's float8_e4m3fn / float8_e5m2 decode of all 256 codes;
+  * the enumerated E3M4 grid above;
   * torch's float32 -> float8 conversion (round-to-nearest-even, no saturation)
     after clamping to +-fmt_max, on values that are exact in float32;
   * a brute-force nearest-code search over the sorted non-negative finite code
@@ -21,17 +30,41 @@ import pytest
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-E4M3, E5M2 = 0, 1
+E4M3, E5M2, E3M4 = 0, 1, 2
+ALL_FMTS = [E4M3, E5M2, E3M4]
 TORCH_FMT = {E4M3: torch.float8_e4m3fn, E5M2: torch.float8_e5m2}
-FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
-MAXCODE = {E4M3: 0x7E, E5M2: 0x7B}
-QUANTUM = {E4M3: 2.0 ** -9, E5M2: 2.0 ** -16}   # smallest subnormal
-FMT_NAME = {"E4M3": E4M3, "E5M2": E5M2}
+FMT_MAX = {E4M3: 448.0, E5M2: 57344.0, E3M4: 30.0}
+MAXCODE = {E4M3: 0x7E, E5M2: 0x7B, E3M4: 0x7E}
+MBITS = {E4M3: 3, E5M2: 2, E3M4: 4}
+QUANTUM = {E4M3: 2.0 ** -9, E5M2: 2.0 ** -16, E3M4: 2.0 ** -6}   # smallest subnormal
+FMT_NAME = {"E4M3": E4M3, "E5M2": E5M2, "E3M4": E3M4}
 
 
 def torch_code_values(fmt):
     """float64 value of each of the 256 codes, decoded by torch."""
     return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(TORCH_FMT[fmt]).to(torch.float64).numpy()
+
+
+def e3m4_grid():
+    """The non-negative finite E3M4 values in increasing order: 16 subnormal
+    multiples of 2^-6 (zero included), then 16 values (1 + j/16) * 2^e for each
+    binade e = -2 .. 4, less the top one of the last binade (the NaN slot)."""
+    vals = {k * 2.0 ** -6 for k in range(16)}
+    vals |= {(1 + j / 16) * 2.0 ** e for e in range(-2, 5) for j in range(16)}
+    vals.discard(31.0)
+    return np.array(sorted(vals), dtype=np.float64)
+
+
+def code_values(fmt):
+    """float64 value of each of the 256 codes: torch's decode for E4M3 and
+    E5M2; for E3M4 the enumerated grid, codes in value order (sign-magnitude
+    layout), 0x7F / 0xFF NaN, the upper half the negated lower half."""
+    if fmt != E3M4:
+        return torch_code_values(fmt)
+    g = e3m4_grid()
+    assert g.size == 127
+    pos = np.concatenate([g, [np.nan]])
+    return np.concatenate([pos, -pos])
 
 
 def bf16_values(words):
@@ -43,7 +76,7 @@ def nearest_code_bruteforce(v, fmt):
     """Code nearest to each float64 v (exact), ties to the even code,
     saturating at fmt_max, NaN -> 0x7F|sign.  Independent of the oracle's
     shift-and-round: it searches the sorted table of code values."""
-    table = torch_code_values(fmt)
+    table = code_values(fmt)
     mags = table[: MAXCODE[fmt] + 1]            # codes 0..maxcode, increasing values
     assert np.all(np.diff(mags) > 0)
     sign = np.signbit(v)
@@ -101,9 +134,9 @@ def test_decode_then_encode_is_identity(orc, fmt):
     assert np.array_equal(orc.scale_cast(words, 0, fmt), finite.astype(np.uint8))
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_nan_and_infinite_codes(orc, fmt):
-    vals = torch_code_values(fmt)
+    vals = code_values(fmt)
     # every NaN code decodes to NaN and re-encodes to 0x7F|sign
     nan_codes = np.where(np.isnan(vals))[0]
     words = vals[nan_codes].astype(np.float32)
@@ -116,9 +149,9 @@ def test_nan_and_infinite_codes(orc, fmt):
     assert list(orc.scale_cast(inf, -50, fmt)) == [MAXCODE[fmt], MAXCODE[fmt] | 0x80]
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_midpoints_go_to_even_code_and_neighbours_to_nearer(orc, fmt):
-    vals = torch_code_values(fmt)[: MAXCODE[fmt] + 1]
+    vals = code_values(fmt)[: MAXCODE[fmt] + 1]
     mids = (vals[:-1] + vals[1:]) / 2                  # exact in fp32 (<= 5 significant bits)
     m32 = mids.astype(np.float32)
     assert np.array_equal(m32.astype(np.float64), mids)
@@ -130,8 +163,8 @@ def test_midpoints_go_to_even_code_and_neighbours_to_nearer(orc, fmt):
     dn = np.nextafter(m32, np.float32(0))
     assert np.array_equal(orc.scale_cast(up, 0, fmt), (lo + 1).astype(np.uint8))
     assert np.array_equal(orc.scale_cast(dn, 0, fmt), lo.astype(np.uint8))
-    # the midpoint above fmt_max and beyond saturates
-    top = np.float32(vals[-1] * (1 + 2.0 ** -(4 if fmt == E4M3 else 3)))
+    # the midpoint between fmt_max and the next grid value, and beyond, saturate
+    top = np.float32(vals[-1] + (vals[-1] - vals[-2]) / 2)
     big = np.array([top, np.nextafter(top, np.float32(np.inf)), 3.0e38], dtype=np.float32)
     assert list(orc.scale_cast(big, 0, fmt)) == [MAXCODE[fmt]] * 3
 
@@ -153,7 +186,7 @@ def test_every_bf16_times_bias_sweep_matches_torch(orc, fmt):
             raise AssertionError(f"bias {b}: words {words[bad]} ours {ours[bad]} torch {ref[bad]}")
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_every_bf16_matches_bruteforce_nearest(orc, fmt):
     words = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     x = bf16_values(words)
@@ -166,7 +199,7 @@ def test_every_bf16_matches_bruteforce_nearest(orc, fmt):
             raise AssertionError(f"bias {b}: words {words[bad]} ours {ours[bad]} brute {ref[bad]}")
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_random_fp32_words_match_bruteforce(orc, fmt):
     rng = np.random.default_rng(7)
     words = rng.integers(0, 2 ** 32, 400_000, dtype=np.uint64).astype(np.uint32)
@@ -200,7 +233,7 @@ def test_golden_closed_form_codes(orc):
         assert got == int(expected, 16), (fmt_s, bits, bias, hex(got), expected)
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_underflow_invariant(orc, fmt):
     q = QUANTUM[fmt]
     rng = np.random.default_rng(11)
@@ -217,7 +250,7 @@ def test_underflow_invariant(orc, fmt):
     assert np.all(orc.scale_cast(-b, 0, fmt) == 0x81)
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_power_of_two_identity(orc, fmt):
     """cast(x, b) == cast(x * 2^k, b - k) whenever x * 2^k is exact; and
     deq(cast(x, b)) * 2^-b == x when x * 2^b lies on the FP8 grid."""
@@ -228,7 +261,7 @@ def test_power_of_two_identity(orc, fmt):
         assert np.array_equal(xk.astype(np.float64), x.astype(np.float64) * 2.0 ** k)
         for b in (0, 4, 9):
             assert np.array_equal(orc.scale_cast(x, b, fmt), orc.scale_cast(xk, b - k, fmt))
-    vals = torch_code_values(fmt)
+    vals = code_values(fmt)
     grid = vals[np.isfinite(vals)]
     for b in (-12, 0, 5, 40):
         xg = (grid * 2.0 ** -b).astype(np.float32)
@@ -237,7 +270,7 @@ def test_power_of_two_identity(orc, fmt):
         assert np.array_equal(back, grid * 2.0 ** -b)
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_saturation_invariant_with_amax_bias(orc, fmt):
     """With margin >= 0 nothing needs clamping: the largest element's code
     sits in the top two binades and no code is the saturated one unless the
@@ -256,7 +289,7 @@ def test_saturation_invariant_with_amax_bias(orc, fmt):
             # amax * 2^b lies in (fmt_max / 2^(margin+1), fmt_max / 2^margin], so
             # the largest code's exponent field is one of the top two (shifted
             # down by the margin); rounding up cannot leave that pair
-            mb = 3 if fmt == E4M3 else 2
+            mb = MBITS[fmt]
             top_binade = (MAXCODE[fmt] >> mb)
             assert (top >> mb) in (top_binade - margin, top_binade - margin - 1)
             assert np.all(codes <= MAXCODE[fmt])
@@ -276,3 +309,39 @@ def test_gradient_underflow_control_on_the_13b_backward_workload(orc):
     assert 30 <= b <= 36
     codes = orc.scale_cast(words, b, 1)
     assert np.count_nonzero(codes & 0x7F) > 0.99 * codes.size
+
+
+def test_e3m4_grid_hand_values(orc):
+    """The E3M4 reading: codes 0x01, 0x0F, 0x10, 0x30, 0x6F, 0x70, 0x7E are
+    2^-6, 15 * 2^-6, 2^-2 (smallest normal), 1, 15.5, 16 and 30 (largest)."""
+    g = code_values(E3M4)
+    hand = {0x00: 0.0, 0x01: 2.0 ** -6, 0x0F: 15 * 2.0 ** -6, 0x10: 0.25, 0x11: 0.25 + 2.0 ** -6,
+            0x30: 1.0, 0x31: 1.0625, 0x6F: 15.5, 0x70: 16.0, 0x7D: 29.0, 0x7E: 30.0}
+    for c, v in hand.items():
+        assert g[c] == v, (hex(c), g[c], v)
+        assert g[c | 0x80] == -v and np.signbit(g[c | 0x80])
+    assert np.isnan(g[0x7F]) and np.isnan(g[0xFF])
+    # steps: 2^-6 through the subnormals and the first normal binade, then
+    # doubling per binade of 16 codes
+    steps = np.diff(g[:0x7F])
+    for c in range(0x7E):
+        e = max(c >> 4, 1)
+        assert steps[c] == 2.0 ** (e - 7), hex(c)
+
+
+def test_e3m4_decode_matches_grid(orc):
+    ours = orc.decode_fp8(np.arange(256), E3M4)
+    ref = code_values(E3M4)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(ours[m], ref[m])
+    assert np.array_equal(np.signbit(ours[m]), np.signbit(ref[m]))
+
+
+def test_e3m4_decode_then_encode_is_identity(orc):
+    vals = code_values(E3M4)
+    finite = np.where(np.isfinite(vals))[0]
+    f32 = vals[finite].astype(np.float32)
+    assert np.array_equal(orc.scale_cast(f32, 0, E3M4), finite.astype(np.uint8))
+    words = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.scale_cast(words, 0, E3M4), finite.astype(np.uint8))
