@@ -163,7 +163,9 @@ def cold_quant(fl, w, plan, q, x, reps):
         so that the scratch's dirty lines are written back before the kernel
         runs and the cache holds nothing of use to it;
       * dirty: the scratch write alone; the timed kernel then also pays for
-        writing those dirty lines back as its reads evict them."""
+        writing those dirty lines back as its reads evict them.
+    Each E4M3 tensor is also cast to E3M4 (its own bias, fmt_max 30), clean
+    flush: that format has no hardware conversion and takes the integer path."""
     import statistics
 
     import torch
@@ -189,7 +191,7 @@ def cold_quant(fl, w, plan, q, x, reps):
         return statistics.median(ts)
 
     per, amax_b = {}, 0.0
-    tot = {"amax_ms": 0.0, "cast_ms": 0.0, "elems": 0}
+    tot = {"amax_ms": 0.0, "cast_ms": 0.0, "elems": 0, "e3m4_ms": 0.0, "e3m4_elems": 0}
     for item in plan:
         if item[0] != "quant":
             continue
@@ -208,6 +210,14 @@ def cold_quant(fl, w, plan, q, x, reps):
         for k, t in (("amax_ms", ta), ("cast_ms", tc), ("dirty_amax_ms", tad), ("dirty_cast_ms", tcd)):
             tot[k] = tot.get(k, 0.0) + t
         tot["elems"] += elems
+        if fmt == fl.E4M3:
+            b3 = fl.compute_bias(amax, fl.E3M4, w.tensor(n).margin)
+            c3 = torch.empty_like(codes)
+            t3 = timed(lambda: fl.scale_cast(x[n], b3, fl.E3M4, out=c3))
+            per[n]["e3m4_cast_gbs"] = round(3.0 * elems / (t3 * 1e-3) / 1e9, 1)
+            tot["e3m4_ms"] += t3
+            tot["e3m4_elems"] += elems
+            del c3
     del scratch, clean
     if not per:
         return None
@@ -220,6 +230,10 @@ def cold_quant(fl, w, plan, q, x, reps):
             "amax_gbs": round(amax_gbs, 1), "amax_frac": round(amax_gbs / PEAK_HBM_GBS, 4),
             "dirty_cast_gbs": round(gbs(3, tot["dirty_cast_ms"]), 1),
             "dirty_amax_gbs": round(gbs(2, tot["dirty_amax_ms"]), 1),
+            "e3m4_cast_gbs": round(3.0 * tot["e3m4_elems"] / (tot["e3m4_ms"] * 1e-3) / 1e9, 1)
+            if tot["e3m4_ms"] > 0 else None,
+            "e3m4_cast_frac": round(3.0 * tot["e3m4_elems"] / (tot["e3m4_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            if tot["e3m4_ms"] > 0 else None,
             "per_tensor": per}
 
 

@@ -20,9 +20,10 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfp8lin.so")
 
-E4M3, E5M2 = 0, 1
+# E3M4: quantisation only (no product takes it).
+E4M3, E5M2, E3M4 = 0, 1, 2
 BF16, FP32 = 0, 1
-FMT_MAX = {E4M3: 448.0, E5M2: 57344.0}
+FMT_MAX = {E4M3: 448.0, E5M2: 57344.0, E3M4: 30.0}
 MAX_MARGIN = 64
 
 STATUS = {0: "FP8_OK", -1: "FP8_ERR_NULL", -2: "FP8_ERR_SIZE", -3: "FP8_ERR_FORMAT",

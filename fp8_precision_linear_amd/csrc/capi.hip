@@ -13,7 +13,9 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
-bool bad_format(int f) { return f != FP8_E4M3 && f != FP8_E5M2; }
+// E3M4 has no MFMA operand type: quantisation only.
+bool bad_format(int f) { return f != FP8_E4M3 && f != FP8_E5M2 && f != FP8_E3M4; }
+bool bad_operand_format(int f) { return f != FP8_E4M3 && f != FP8_E5M2; }
 bool bad_dtype(int d) { return d != FP8_IN_BF16 && d != FP8_IN_FP32; }
 bool bad_dim(int64_t v) { return v < 0 || v > (int64_t)0x7FFFFFFF; }
 
@@ -38,7 +40,7 @@ int gemm_checks(const uint8_t* a, int fa, const int32_t* ba, const uint8_t* b, i
                 const int32_t* bb, int64_t M, int64_t N, int64_t K, const float* out,
                 int64_t a_elems, int64_t b_elems) {
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8_ERR_SIZE;
-  if (bad_format(fa) || bad_format(fb)) return FP8_ERR_FORMAT;
+  if (bad_operand_format(fa) || bad_operand_format(fb)) return FP8_ERR_FORMAT;
   if (M == 0 || N == 0) return FP8_OK;
   if (!out || !ba || !bb) return FP8_ERR_NULL;
   if ((a_elems > 0 && !a) || (b_elems > 0 && !b)) return FP8_ERR_NULL;

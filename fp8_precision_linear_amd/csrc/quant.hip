@@ -156,10 +156,11 @@ __global__ __launch_bounds__(kThreads) void amax_f32_kernel(const uint4* __restr
 }
 
 // ---------------------------------------------------------------- bias
-// floor(log2(fmt_max / A)) - margin with fmt_max = 1.75 * 2^emax.  Writing
-// A = (1 + f) * 2^e with f in [0, 1): fmt_max / A = 1.75 / (1 + f) * 2^(emax - e)
-// and 1.75 / (1 + f) lies in (0.875, 1.75], so its floor(log2) is 0 when
-// 1 + f <= 1.75 (fraction field <= 0x600000) and -1 otherwise.
+// floor(log2(fmt_max / A)) - margin with fmt_max = t * 2^emax, t = 1.75 for
+// E4M3 (448) and E5M2 (57344), 1.875 for E3M4 (30).  Writing A = (1 + f) * 2^e
+// with f in [0, 1): fmt_max / A = t / (1 + f) * 2^(emax - e) and t / (1 + f)
+// lies in (t / 2, t], so its floor(log2) is 0 when 1 + f <= t (fraction field
+// <= 0x600000, resp. 0x700000) and -1 otherwise.
 __device__ __forceinline__ int32_t bias_from_amax_bits(uint32_t a, int fmt, int32_t margin) {
   if (a == 0u || a >= 0x7F800000u) return 0;  // zero, inf, NaN (or a negative input)
   int e;
@@ -172,8 +173,9 @@ __device__ __forceinline__ int32_t bias_from_amax_bits(uint32_t a, int fmt, int3
     e = (int)(a >> 23) - 127;
     frac = a & 0x7FFFFFu;
   }
-  const int emax = fmt == FP8_E4M3 ? 8 : 15;
-  return emax - e - (frac > 0x600000u ? 1 : 0) - margin;
+  const int emax = fmt == FP8_E4M3 ? 8 : (fmt == FP8_E5M2 ? 15 : 4);
+  const uint32_t tfrac = fmt == FP8_E3M4 ? 0x700000u : 0x600000u;
+  return emax - e - (frac > tfrac ? 1 : 0) - margin;
 }
 
 __global__ void bias_kernel(const uint32_t* __restrict__ amax, int fmt, int32_t margin,
@@ -207,13 +209,21 @@ __device__ __forceinline__ uint32_t fp8_code(uint32_t xbits, int32_t b) {
     const uint32_t sub = __float_as_uint(__uint_as_float(a) + 16384.0f) - 0x46800000u;
     code = a < 0x3C800000u ? sub : nrm;
     code = min(code, 0x7Eu);
-  } else {
+  } else if constexpr (FMT == FP8_E5M2) {
     // normal: code = (fp32 exponent - 112) * 4 + top 2 fraction bits, rounded
     const uint32_t nrm = (a + (0xFFFFFu - 0x38000000u) + ((a >> 21) & 1u)) >> 21;
     // subnormal (|v| < 2^-14): the ulp of 2^7 in fp32 is 2^-16
     const uint32_t sub = __float_as_uint(__uint_as_float(a) + 128.0f) - 0x43000000u;
     code = a < 0x38800000u ? sub : nrm;
     code = min(code, 0x7Bu);
+  } else {
+    static_assert(FMT == FP8_E3M4, "unknown format");
+    // normal: code = (fp32 exponent - 124) * 16 + top 4 fraction bits, rounded
+    const uint32_t nrm = (a + (0x3FFFFu - 0x3E000000u) + ((a >> 19) & 1u)) >> 19;
+    // subnormal (|v| < 2^-2): the ulp of 2^17 in fp32 is 2^-6
+    const uint32_t sub = __float_as_uint(__uint_as_float(a) + 131072.0f) - 0x48000000u;
+    code = a < 0x3E800000u ? sub : nrm;
+    code = min(code, 0x7Eu);  // 30; the code above it is NaN
   }
   code = a > 0x7F800000u ? 0x7Fu : code;
   return code | ((vb >> 24) & 0x80u);
@@ -249,7 +259,10 @@ __device__ __forceinline__ uint32_t pack4_f32(uint4 v, int32_t b) {
 //    saturation the rounding above performs (every value at or beyond
 //    fmt_max rounds to the largest finite code);
 //  * a unit holding any inf or NaN is redone with fp8_code.
+// E3M4 has no such conversion and always takes fp8_code.
 constexpr int kHwBiasMin = -127, kHwBiasMax = 126;
+template <int FMT>
+constexpr bool kHwConvert = FMT == FP8_E4M3 || FMT == FP8_E5M2;
 
 typedef short hw_v2s __attribute__((ext_vector_type(2)));
 typedef __bf16 hw_v2bf __attribute__((ext_vector_type(2)));
@@ -258,6 +271,7 @@ typedef __bf16 hw_v2bf __attribute__((ext_vector_type(2)));
 // fmt_max = 1.75 * 2^emax has bf16 fraction bits 0x60.
 template <int FMT>
 __device__ __forceinline__ uint32_t hw_bound2(int32_t b) {
+  static_assert(kHwConvert<FMT>, "no hardware conversion for this format");
   const int efield = (FMT == FP8_E4M3 ? 8 : 15) + 127 - b;
   const uint32_t m = efield >= 255 ? 0x7F7Fu : (((uint32_t)efield << 7) | 0x60u);
   return m | (m << 16);
@@ -316,8 +330,8 @@ __device__ __forceinline__ uint4 cast_unit_sw(uint4 lo, uint4 hi, int32_t b) {
 
 // One unit = 16 elements -> one 16-byte store.  The data loads do not depend
 // on the bias, so they are issued before the bias load has returned; the
-// choice between the hardware conversion (bias in [kHwBiasMin, kHwBiasMax])
-// and fp8_code is a wave-uniform branch per unit after them.
+// choice between the hardware conversion (bias in [kHwBiasMin, kHwBiasMax],
+// E4M3 and E5M2) and fp8_code is a wave-uniform branch per unit after them.
 template <int FMT, bool NT>
 __device__ __forceinline__ void cast_bf16_body(const uint4* __restrict__ x, int64_t nunit,
                                                const int32_t* __restrict__ bias,
@@ -327,8 +341,9 @@ __device__ __forceinline__ void cast_bf16_body(const uint4* __restrict__ x, int6
   if (i >= nunit) return;
   uint4 lo = load16<NT>(&x[2 * i]), hi = load16<NT>(&x[2 * i + 1]);
   const int32_t b = *bias;
-  const bool hw = b >= kHwBiasMin && b <= kHwBiasMax;
-  const uint32_t bound2 = hw_bound2<FMT>(b);
+  const bool hw = kHwConvert<FMT> && b >= kHwBiasMin && b <= kHwBiasMax;
+  uint32_t bound2 = 0;
+  if constexpr (kHwConvert<FMT>) bound2 = hw_bound2<FMT>(b);
   const float scale = __builtin_ldexpf(1.0f, hw ? -b : 0);
   for (;;) {
     const int64_t next = i + stride;
@@ -337,8 +352,12 @@ __device__ __forceinline__ void cast_bf16_body(const uint4* __restrict__ x, int6
       nlo = load16<NT>(&x[2 * next]);
       nhi = load16<NT>(&x[2 * next + 1]);
     }
-    store16<false>(hw ? cast_unit_hw<FMT>(lo, hi, b, bound2, scale) : cast_unit_sw<FMT>(lo, hi, b),
-                   &y[i]);
+    uint4 o;
+    if constexpr (kHwConvert<FMT>)
+      o = hw ? cast_unit_hw<FMT>(lo, hi, b, bound2, scale) : cast_unit_sw<FMT>(lo, hi, b);
+    else
+      o = cast_unit_sw<FMT>(lo, hi, b);
+    store16<false>(o, &y[i]);
     if (next >= nunit) break;
     i = next;
     lo = nlo;
@@ -436,6 +455,23 @@ hipError_t launch_bias(const float* amax, int fmt, int32_t margin, int32_t* bias
   return hipGetLastError();
 }
 
+// FP8LIN_CAST(format, non-temporal) for each format the cast produces.
+#define FP8LIN_CAST_FORMATS(fmt, nt)                                      \
+  switch (fmt) {                                                          \
+    case FP8_E4M3:                                                        \
+      if (nt) FP8LIN_CAST(FP8_E4M3, true);                                \
+      else FP8LIN_CAST(FP8_E4M3, false);                                  \
+      break;                                                              \
+    case FP8_E5M2:                                                        \
+      if (nt) FP8LIN_CAST(FP8_E5M2, true);                                \
+      else FP8LIN_CAST(FP8_E5M2, false);                                  \
+      break;                                                              \
+    default:                                                              \
+      if (nt) FP8LIN_CAST(FP8_E3M4, true);                                \
+      else FP8LIN_CAST(FP8_E3M4, false);                                  \
+      break;                                                              \
+  }
+
 hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias, int fmt,
                        uint8_t* y, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
@@ -451,13 +487,7 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias,
 #define FP8LIN_CAST(F, NT)                                                                    \
   hipLaunchKernelGGL((cast_bf16_kernel<F, NT>), grid, dim3(kThreads), 0, stream, xv, nunit, \
                      bias, yv, tail_x, tail_y, ntail)
-    if (fmt == FP8_E4M3) {
-      if (nt) FP8LIN_CAST(FP8_E4M3, true);
-      else FP8LIN_CAST(FP8_E4M3, false);
-    } else {
-      if (nt) FP8LIN_CAST(FP8_E5M2, true);
-      else FP8LIN_CAST(FP8_E5M2, false);
-    }
+    FP8LIN_CAST_FORMATS(fmt, nt);
 #undef FP8LIN_CAST
   } else {
     const uint32_t* tail_x = static_cast<const uint32_t*>(x) + nunit * 16;
@@ -466,16 +496,11 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias,
 #define FP8LIN_CAST(F, NT)                                                                   \
   hipLaunchKernelGGL((cast_f32_kernel<F, NT>), grid, dim3(kThreads), 0, stream, xv, nunit, \
                      bias, yv, tail_x, tail_y, ntail)
-    if (fmt == FP8_E4M3) {
-      if (nt) FP8LIN_CAST(FP8_E4M3, true);
-      else FP8LIN_CAST(FP8_E4M3, false);
-    } else {
-      if (nt) FP8LIN_CAST(FP8_E5M2, true);
-      else FP8LIN_CAST(FP8_E5M2, false);
-    }
+    FP8LIN_CAST_FORMATS(fmt, nt);
 #undef FP8LIN_CAST
   }
   return hipGetLastError();
 }
+#undef FP8LIN_CAST_FORMATS
 
 }  // namespace fp8lin

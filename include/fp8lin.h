@@ -36,10 +36,17 @@
 extern "C" {
 #endif
 
-/* FP8 encodings (OCP 8-bit floating point): the page's FP8_E4 and FP8_E5. */
+/* FP8 encodings.  E4M3 and E5M2 are the OCP 8-bit formats, the review page's
+ * FP8_E4 and FP8_E5.  E3M4 is the third format of the post-training
+ * quantisation study ("Efficient post-training quantization with FP8
+ * formats", summary page), which names it without an encoding; it is built
+ * here like OCP E4M3.  E3M4 is accepted by fp8_compute_bias and
+ * fp8_scale_cast only: gfx950's MFMA has no E3M4 operand, so the products
+ * reject it with FP8_ERR_FORMAT. */
 typedef enum {
   FP8_E4M3 = 0, /* 1-4-3, exponent bias 7, max 448, no infinity, NaN = S.1111.111 */
-  FP8_E5M2 = 1  /* 1-5-2, exponent bias 15, max 57344, inf = S.11111.00 (never produced) */
+  FP8_E5M2 = 1, /* 1-5-2, exponent bias 15, max 57344, inf = S.11111.00 (never produced) */
+  FP8_E3M4 = 2  /* 1-3-4, exponent bias 3, max 30, no infinity, NaN = S.111.1111 */
 } fp8_format_t;
 
 /* Element type of a high-precision input tensor. */
@@ -52,7 +59,7 @@ typedef enum {
 #define FP8_OK 0
 #define FP8_ERR_NULL (-1)   /* a required pointer is NULL */
 #define FP8_ERR_SIZE (-2)   /* a size is negative or too large */
-#define FP8_ERR_FORMAT (-3) /* format is not an fp8_format_t */
+#define FP8_ERR_FORMAT (-3) /* format is not an fp8_format_t (or E3M4 given to a product) */
 #define FP8_ERR_DTYPE (-4)  /* dtype is not an fp8_dtype_t */
 #define FP8_ERR_ALIGN (-5)  /* a pointer that must be 16-byte aligned is not */
 #define FP8_ERR_MARGIN (-6) /* |margin| > FP8_MAX_MARGIN */
@@ -80,7 +87,7 @@ int fp8_amax(const void* x, fp8_dtype_t dtype, int64_t n, float* amax, void* str
  * Scaling bias ("Proposed method", bullet 2): the largest integer b with
  * amax * 2^b <= fmt_max, minus `margin`, i.e. floor(log2(fmt_max/amax)) - margin,
  * evaluated exactly from the exponent and mantissa fields.  fmt_max is 448
- * (E4M3) or 57344 (E5M2).  An amax of 0, inf or NaN gives b = 0 and the margin
+ * (E4M3), 57344 (E5M2) or 30 (E3M4).  An amax of 0, inf or NaN gives b = 0 and the margin
  * is not applied.
  *   amax  device, one float (normally the output of fp8_amax).
  *   bias  device, one int32, written.
@@ -106,7 +113,8 @@ int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* b
 /*
  * The three FP8 x FP8 products with fp32 accumulation, unscaled after the
  * matmul ("Proposed method", bullets 3 and 5).  Each output is overwritten
- * (no accumulation into it).  Operands may use either format in any pairing.
+ * (no accumulation into it).  Operands may be E4M3 or E5M2 in any pairing
+ * (E3M4: FP8_ERR_FORMAT).
  * All pointers are device memory; byte operands and outputs must be 16-byte
  * aligned.  M, N, K >= 0 (K == 0 writes zeros; M == 0 or N == 0 is a no-op).
  * bx, bw, bdy: device, one int32 each -- the operands' scaling biases.

@@ -52,7 +52,7 @@ def test_amax_argument_checks():
 
 
 def test_bias_argument_checks():
-    assert L.fp8_compute_bias(A16, 2, 0, A32, None) == status("FP8_ERR_FORMAT")
+    assert L.fp8_compute_bias(A16, 3, 0, A32, None) == status("FP8_ERR_FORMAT")
     assert L.fp8_compute_bias(A16, 0, 65, A32, None) == status("FP8_ERR_MARGIN")
     assert L.fp8_compute_bias(A16, 1, -65, A32, None) == status("FP8_ERR_MARGIN")
     assert L.fp8_compute_bias(None, 0, 0, A32, None) == status("FP8_ERR_NULL")
@@ -63,6 +63,7 @@ def test_cast_argument_checks():
     assert L.fp8_scale_cast(A16, 0, -5, A32, 0, A48, None) == status("FP8_ERR_SIZE")
     assert L.fp8_scale_cast(A16, 3, 5, A32, 0, A48, None) == status("FP8_ERR_DTYPE")
     assert L.fp8_scale_cast(A16, 0, 5, A32, -1, A48, None) == status("FP8_ERR_FORMAT")
+    assert L.fp8_scale_cast(A16, 0, 5, A32, 3, A48, None) == status("FP8_ERR_FORMAT")
     assert L.fp8_scale_cast(A16, 0, 5, None, 0, A48, None) == status("FP8_ERR_NULL")
     assert L.fp8_scale_cast(A16, 0, 5, A32, 0, None, None) == status("FP8_ERR_NULL")
     assert L.fp8_scale_cast(MIS, 0, 5, A32, 0, A48, None) == status("FP8_ERR_ALIGN")
@@ -85,7 +86,9 @@ def test_gemm_argument_checks(fn):
 
     assert call(M=-1) == status("FP8_ERR_SIZE")
     assert call(K=1 << 31) == status("FP8_ERR_SIZE")
-    assert call(fa=2) == status("FP8_ERR_FORMAT")
+    assert call(fa=2) == status("FP8_ERR_FORMAT")     # E3M4: no product takes it
+    assert call(fb=2) == status("FP8_ERR_FORMAT")
+    assert call(fa=3) == status("FP8_ERR_FORMAT")
     assert call(fb=-1) == status("FP8_ERR_FORMAT")
     assert call(out=None) == status("FP8_ERR_NULL")
     assert call(ba=None) == status("FP8_ERR_NULL")

@@ -2,7 +2,9 @@
 
 All three must match bit for bit ("Training and inference of large language
 models using 8-bit floating point", review page, "Proposed method", bullets
-1-4).  Every call goes through the C ABI (the ctypes binding).
+1-4), and so must the E3M4 cast (the third format of "Efficient post-training
+quantization with FP8 formats", summary page, under the encoding the oracle's
+header states).  Every call goes through the C ABI (the ctypes binding).
 """
 import numpy as np
 import pytest
@@ -13,7 +15,8 @@ import synth
 from gpu_util import bf16_dev, f32_dev, i32_dev, need_gpu, say, words_of
 
 pytestmark = pytest.mark.gpu
-E4M3, E5M2 = 0, 1
+E4M3, E5M2, E3M4 = 0, 1, 2
+ALL_FMTS = [E4M3, E5M2, E3M4]
 
 
 @pytest.fixture(scope="module")
@@ -21,7 +24,7 @@ def fl():
     return need_gpu()
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_cast_every_bf16_word_for_every_bias(fl, fmt):
     words = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     x = bf16_dev(words)
@@ -38,7 +41,7 @@ def test_cast_every_bf16_word_for_every_bias(fl, fmt):
             raise AssertionError(f"fmt {fmt} bias {b}: words {words[bad]} gpu {got[r][bad]} oracle {ref[bad]}")
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_cast_fp32_words(fl, fmt):
     rng = np.random.default_rng(21)
     words = rng.integers(0, 2 ** 32, 2_000_003, dtype=np.uint64).astype(np.uint32)
@@ -67,7 +70,7 @@ def test_amax_and_cast_ragged_sizes(fl, n, dtype):
     say("ragged", dtype, "n", n)
     a = fl.amax(x)
     assert int(words_of(a)[0]) == oracle.amax_bits(words)
-    for fmt, margin in ((E4M3, 0), (E5M2, 2), (E4M3, -1)):
+    for fmt, margin in ((E4M3, 0), (E5M2, 2), (E4M3, -1), (E3M4, 1)):
         b = fl.compute_bias(a, fmt, margin)
         assert int(b.item()) == oracle.compute_bias(oracle.amax_bits(words), fmt, margin)
         y = fl.scale_cast(x, b, fmt).cpu().numpy()
@@ -97,7 +100,7 @@ def test_amax_special_values_anywhere(fl):
     assert a.item() == 0.0
 
 
-@pytest.mark.parametrize("fmt", [E4M3, E5M2])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_bias_every_positive_bf16_amax(fl, fmt):
     words = np.arange(1, 0x7F80, dtype=np.uint32)
     step = 1 if fmt == E4M3 else 5
@@ -111,7 +114,8 @@ def test_bias_every_positive_bf16_amax(fl, fmt):
     ref = np.array([oracle.compute_bias(int(b), fmt, 0) for b in bits])
     assert np.array_equal(got, ref)
     # margins and special amax values
-    specials = [0, 0x80000000, 0x7F800000, 0x7FC00000, 1, 0x7F7FFFFF, 0x43E00000, 0x43E00001]
+    specials = [0, 0x80000000, 0x7F800000, 0x7FC00000, 1, 0x7F7FFFFF, 0x43E00000, 0x43E00001,
+                0x41F00000, 0x41F00001, 0x41EFFFFF]
     for s in specials:
         for m in (-64, -3, 0, 1, 64):
             b = fl.compute_bias(f32_dev(np.array([s], np.uint32)), fmt, m)
@@ -136,6 +140,30 @@ def test_workload_tensors_bit_exact(fl, wl):
         del codes, x
 
 
+@pytest.mark.parametrize("wl", [1, 3, 5])
+def test_e3m4_quantisation_of_workload_activations(fl, wl):
+    """The workload's E4M3 tensors (activations and weights) quantised to E3M4
+    instead: amax, bias (fmt_max 30) and codes bit-exact, margins 0 and 1."""
+    w = synth.WORKLOADS[wl]
+    for t in w.tensors:
+        if t.fmt != E4M3:
+            continue
+        x = synth.workload_tensor(w, t.name)
+        words = synth.bf16_words(x)
+        a_ref = oracle.amax_bits(words)
+        for margin in (0, 1):
+            say("E3M4 workload", wl, t.name, tuple(t.shape), "margin", margin)
+            codes, bias, amax = fl.quantize(x.cuda(), E3M4, margin)
+            b_ref = oracle.compute_bias(a_ref, E3M4, margin)
+            assert int(words_of(amax)[0]) == a_ref, t.name
+            assert int(bias.item()) == b_ref, t.name
+            got = codes.cpu().numpy().reshape(-1)
+            ref = oracle.scale_cast(words.reshape(-1), b_ref, E3M4)
+            assert np.array_equal(got, ref), f"{t.name}: {np.count_nonzero(got != ref)} codes differ"
+            del codes
+        del x
+
+
 def test_cast_mixes_non_finite_values_into_finite_units(fl):
     """The cast converts 16-element units on the hardware path unless a unit
     holds an inf or NaN; here every unit mixes a few of them into finite
@@ -148,7 +176,7 @@ def test_cast_mixes_non_finite_values_into_finite_units(fl):
     pos = rng.integers(0, n, n // 5)
     words[pos] = specials[rng.integers(0, specials.size, pos.size)]
     x = bf16_dev(words)
-    for fmt in (E4M3, E5M2):
+    for fmt in ALL_FMTS:
         for b in (-130, -4, 0, 3, 12, 126, 127):
             say("cast mixed non-finite", "fmt", fmt, "bias", b)
             got = fl.scale_cast(x, i32_dev(b), fmt).cpu().numpy()
