@@ -69,6 +69,10 @@ def lib():
             f = getattr(L, name)
             f.restype = None
             f.argtypes = [vp, ci, i32, vp, ci, i32, i64, i64, i64, vp, vp, i64, vp, vp]
+        L.oracle_swiglu_fwd.restype = None
+        L.oracle_swiglu_fwd.argtypes = [vp, i64, i64, vp]
+        L.oracle_swiglu_bwd.restype = None
+        L.oracle_swiglu_bwd.argtypes = [vp, vp, i64, i64, vp]
         _lib = L
     return _lib
 
@@ -193,3 +197,30 @@ def gemm_wgrad_at(dy8, fdy, bdy, x8, fx, bx, rows, cols):
     dy8, x8 = _u8(dy8), _u8(x8)
     (M, N), (_, K) = dy8.shape, x8.shape
     return _at(lib().oracle_gemm_wgrad_at, dy8, fdy, bdy, x8, fx, bx, M, N, K, rows, cols)
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float32:
+        raise TypeError("SwiGLU inputs are float32 arrays")
+    return a
+
+
+def swiglu_fwd(h):
+    """a = silu(g) * u in float64, h = [g | u] of shape (rows, 2f) (oracle.c, step 5)."""
+    h = _f32(h)
+    rows, f2 = h.shape
+    assert f2 % 2 == 0
+    a = np.empty((rows, f2 // 2))
+    lib().oracle_swiglu_fwd(_ptr(h), rows, f2 // 2, _ptr(a))
+    return a
+
+
+def swiglu_bwd(h, da):
+    """dh = [da * u * silu'(g) | da * silu(g)] in float64 (oracle.c, step 5)."""
+    h, da = _f32(h), _f32(da)
+    rows, f2 = h.shape
+    assert f2 % 2 == 0 and da.shape == (rows, f2 // 2)
+    dh = np.empty((rows, f2))
+    lib().oracle_swiglu_bwd(_ptr(h), _ptr(da), rows, f2 // 2, _ptr(dh))
+    return dh

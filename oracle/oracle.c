@@ -34,7 +34,11 @@
  *   - amax of a tensor holding NaN is the NaN whose magnitude bits are largest;
  *     amax of an empty tensor is 0;
  *   - the matmul result is sum_k a_k * b_k over the decoded FP8 values times
- *     2^-(bias_a + bias_b); here it is formed in fp64, in ascending k.
+ *     2^-(bias_a + bias_b); here it is formed in fp64, in ascending k;
+ *   - the activation between the products of a chained MLP is Llama 2's gated
+ *     SwiGLU (the pages train Llama 2 models, "Main findings", but do not
+ *     spell the activation out): a = silu(g) * u with silu(g) = g * sigmoid(g),
+ *     where g and u are the two halves of the up-projection's output.
  *
  * Every finite input is decoded into an exact triple (sign, integer
  * significand S, power-of-two exponent q) with value (-1)^sign * S * 2^q, so
@@ -415,4 +419,47 @@ void oracle_gemm_wgrad_at(const uint8_t* dy8, int fdy, int32_t bdy, const uint8_
     out[t] = ldexp(acc, unscale);
     if (bound) bound[t] = ldexp(mag, unscale);
   }
+}
+
+/* ------------------------------------------------------------------------
+ * Step 5: the gated activation between the two products of a chained MLP
+ * (SwiGLU, the reading in the header), in fp64.
+ *   h:  rows x 2f fp32, row t = [g_t0 .. g_t(f-1) | u_t0 .. u_t(f-1)]
+ *   forward   a[t][j]        = silu(g) * u
+ *   backward  dh[t][j]       = da * u * silu'(g)   (d a / d g)
+ *             dh[t][f + j]   = da * silu(g)        (d a / d u)
+ * with sigmoid(g) = 1 / (1 + e^-g), silu(g) = g * sigmoid(g) and
+ * silu'(g) = sigmoid(g) * (1 + g * (1 - sigmoid(g))).  sigmoid and
+ * 1 - sigmoid are taken from e^-|g| (e / (1 + e) and 1 / (1 + e)), the same
+ * values without forming 1 - sigmoid by subtraction.
+ * ---------------------------------------------------------------------- */
+static void sigmoid_pair(double g, double* s, double* sc) {
+  if (g < 0.0) {
+    double e = exp(g);
+    *s = e / (1.0 + e);
+    *sc = 1.0 / (1.0 + e);
+  } else {
+    double e = exp(-g);
+    *s = 1.0 / (1.0 + e);
+    *sc = e / (1.0 + e);
+  }
+}
+
+void oracle_swiglu_fwd(const float* h, int64_t rows, int64_t f, double* a) {
+  for (int64_t t = 0; t < rows; ++t)
+    for (int64_t j = 0; j < f; ++j) {
+      double g = h[t * 2 * f + j], u = h[t * 2 * f + f + j], s, sc;
+      sigmoid_pair(g, &s, &sc);
+      a[t * f + j] = g * s * u;
+    }
+}
+
+void oracle_swiglu_bwd(const float* h, const float* da, int64_t rows, int64_t f, double* dh) {
+  for (int64_t t = 0; t < rows; ++t)
+    for (int64_t j = 0; j < f; ++j) {
+      double g = h[t * 2 * f + j], u = h[t * 2 * f + f + j], d = da[t * f + j], s, sc;
+      sigmoid_pair(g, &s, &sc);
+      dh[t * 2 * f + j] = d * u * (s * (1.0 + g * sc));
+      dh[t * 2 * f + f + j] = d * (g * s);
+    }
 }
