@@ -46,6 +46,8 @@ SIGNATURES = {
     "fp8_scaled_gemm_fwd": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_dgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_wgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "fp8_swiglu_fwd": (_ci, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_swiglu_bwd": (_ci, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
 }
 
 
@@ -204,4 +206,39 @@ def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=No
                lib.fp8_scaled_gemm_amax(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8),
                                         int(fb), _ptr(bb), M, N, K, _ptr(out), _ptr(amax),
                                         _stream(stream)))
+    return out
+
+
+def swiglu_fwd(h, out=None, amax=None, stream=None):
+    """a = silu(g) * u as a bf16 tensor [rows, f], h = [g | u] float32 [rows, 2f]
+    (fp8_swiglu_fwd).  amax: optional float32[1] device tensor that receives
+    max |a|."""
+    _need_cuda(h)
+    if h.dtype != torch.float32 or h.dim() != 2 or h.shape[1] % 2:
+        raise ValueError("h must be a float32 [rows, 2f] tensor")
+    rows, f = h.shape[0], h.shape[1] // 2
+    out = torch.empty((rows, f), dtype=torch.bfloat16, device=h.device) if out is None else out
+    _need_cuda(out, amax)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (rows, f):
+        raise ValueError("out must be a bfloat16 [rows, f] tensor")
+    _check("fp8_swiglu_fwd", lib.fp8_swiglu_fwd(_ptr(h), rows, f, _ptr(out), _ptr(amax), _stream(stream)))
+    return out
+
+
+def swiglu_bwd(h, da, out=None, amax=None, stream=None):
+    """dh = [da * u * silu'(g) | da * silu(g)] as a bf16 tensor [rows, 2f]
+    (fp8_swiglu_bwd); da float32 [rows, f].  amax: optional float32[1] device
+    tensor that receives max |dh|."""
+    _need_cuda(h, da)
+    if h.dtype != torch.float32 or h.dim() != 2 or h.shape[1] % 2:
+        raise ValueError("h must be a float32 [rows, 2f] tensor")
+    rows, f = h.shape[0], h.shape[1] // 2
+    if da.dtype != torch.float32 or tuple(da.shape) != (rows, f):
+        raise ValueError("da must be a float32 [rows, f] tensor")
+    out = torch.empty((rows, 2 * f), dtype=torch.bfloat16, device=h.device) if out is None else out
+    _need_cuda(out, amax)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (rows, 2 * f):
+        raise ValueError("out must be a bfloat16 [rows, 2f] tensor")
+    _check("fp8_swiglu_bwd", lib.fp8_swiglu_bwd(_ptr(h), _ptr(da), rows, f, _ptr(out), _ptr(amax),
+                                                _stream(stream)))
     return out

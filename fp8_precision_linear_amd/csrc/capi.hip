@@ -190,3 +190,42 @@ int fp8_scaled_gemm_wgrad(const uint8_t* dy8, fp8_format_t fdy, const int32_t* b
 }
 
 }  // extern "C"
+
+namespace {
+
+int swiglu_checks(const void* h, const void* da, bool need_da, int64_t rows, int64_t f,
+                  const void* out, const float* out_amax) {
+  if (rows < 0 || f < 0 || rows > (int64_t)0x7FFFFFFF || f > (int64_t)0x3FFFFFFF)
+    return FP8_ERR_SIZE;
+  if (fp8lin::swiglu_blocks(rows, f) > (int64_t)0x7FFFFFFF) return FP8_ERR_SIZE;
+  if (out_amax && ((uintptr_t)out_amax & 3u) != 0) return FP8_ERR_ALIGN;
+  if (rows == 0 || f == 0) return FP8_OK;
+  if (!h || !out || (need_da && !da)) return FP8_ERR_NULL;
+  if (misaligned(h) || misaligned(out) || (need_da && misaligned(da))) return FP8_ERR_ALIGN;
+  return FP8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8_swiglu_fwd(const float* h, int64_t rows, int64_t f, uint16_t* a, float* out_amax,
+                   void* stream) {
+  if (int s = swiglu_checks(h, nullptr, false, rows, f, a, out_amax)) return s;
+  if ((rows == 0 || f == 0) && !out_amax) return FP8_OK;
+  if (int s = device_ok()) return s;
+  return hip_status(fp8lin::launch_swiglu_fwd(h, rows, f, a, reinterpret_cast<uint32_t*>(out_amax),
+                                              (hipStream_t)stream));
+}
+
+int fp8_swiglu_bwd(const float* h, const float* da, int64_t rows, int64_t f, uint16_t* dh,
+                   float* out_amax, void* stream) {
+  if (int s = swiglu_checks(h, da, true, rows, f, dh, out_amax)) return s;
+  if ((rows == 0 || f == 0) && !out_amax) return FP8_OK;
+  if (int s = device_ok()) return s;
+  return hip_status(fp8lin::launch_swiglu_bwd(h, da, rows, f, dh,
+                                              reinterpret_cast<uint32_t*>(out_amax),
+                                              (hipStream_t)stream));
+}
+
+}  // extern "C"

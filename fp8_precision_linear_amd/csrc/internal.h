@@ -17,6 +17,15 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias,
 // *p = 0 (one lane).
 hipError_t launch_clear_u32(uint32_t* p, hipStream_t stream);
 
+// SwiGLU between the products of a chained MLP (swiglu.hip).  amax: optional,
+// cleared then folded with max |output| (fp32 magnitude bits).
+hipError_t launch_swiglu_fwd(const float* h, int64_t rows, int64_t f, uint16_t* a, uint32_t* amax,
+                             hipStream_t stream);
+hipError_t launch_swiglu_bwd(const float* h, const float* da, int64_t rows, int64_t f, uint16_t* dh,
+                             uint32_t* amax, hipStream_t stream);
+// Blocks the SwiGLU launches use for a rows x f output (must fit a 32-bit grid).
+int64_t swiglu_blocks(int64_t rows, int64_t f);
+
 // Product arithmetic (the values of fp8_scaled_gemm's `math` argument).
 #define FP8LIN_MATH_EXACT FP8_GEMM_EXACT
 #define FP8LIN_MATH_NATIVE_FP8 FP8_GEMM_NATIVE_FP8

@@ -160,6 +160,33 @@ int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_forma
                          const int32_t* bb, int64_t M, int64_t N, int64_t K, float* out,
                          float* out_amax, void* stream);
 
+/*
+ * The gated activation between the two products of a chained FP8 MLP: Llama
+ * 2's SwiGLU (the review page trains Llama 2 models, "Main findings", without
+ * naming the activation).  The up-projection is one fused product whose
+ * output h [rows x 2f] (fp32, row-major) holds the gate columns g then the up
+ * columns u of each row.  With sigmoid(g) = 1 / (1 + e^-g), evaluated in fp32:
+ *   fp8_swiglu_fwd:  a[t][j] = g * sigmoid(g) * u                 a: rows x f
+ *   fp8_swiglu_bwd:  dh[t][j]     = da * u * sigmoid(g) * (1 + g * (1 - sigmoid(g)))
+ *                    dh[t][f + j] = da * g * sigmoid(g)           dh: rows x 2f
+ * (g = h[t][j], u = h[t][f + j], da = da[t][j]).  Outputs are bf16 words,
+ * rounded to nearest even from the fp32 result (within one bf16 unit in the
+ * last place of the exact value, up to fp32 rounding near a midpoint).
+ * Non-finite inputs follow IEEE arithmetic of these formulas (g = -inf gives
+ * NaN).
+ *   out_amax  device float, optional (NULL: not computed), 4-byte aligned:
+ *             written with max |output| over the whole output, bit-identical
+ *             to fp8_amax over it, so fp8_compute_bias can follow directly
+ *             ("Proposed method", bullet 1); 0 for an empty output.
+ * h, da, a, dh: device, 16-byte aligned.  rows, f >= 0 (either 0: nothing but
+ * the amax clear is launched).  Returns FP8_ERR_SIZE when rows * ceil(f / 1024)
+ * exceeds 2^31 - 1.
+ */
+int fp8_swiglu_fwd(const float* h, int64_t rows, int64_t f, uint16_t* a, float* out_amax,
+                   void* stream);
+int fp8_swiglu_bwd(const float* h, const float* da, int64_t rows, int64_t f, uint16_t* dh,
+                   float* out_amax, void* stream);
+
 /* Forward: Y[M x N] = 2^-(bx+bw) * X8[M x K] . W8[N x K]^T */
 int fp8_scaled_gemm_fwd(const uint8_t* x8, fp8_format_t fx, const int32_t* bx,
                         const uint8_t* w8, fp8_format_t fw, const int32_t* bw,

@@ -144,6 +144,50 @@ WORKLOADS = {w.index: w for w in (_single_linear(), _gpt111m(), _llama7b_mlp(),
                                   _llama13b_bwd(), _llama70b_infer())}
 
 
+@dataclass(frozen=True)
+class ChainedMLP:
+    """A gated MLP trained with FP8 products end to end (forward and backward
+    through the SwiGLU between them): x [tokens, d] bf16, w1 = [W_gate; W_up]
+    [2f, d] and w2 = W_down [d, f] as float32 master weights, and g = dL/dy
+    [tokens, d] float32, the upstream gradient of the synthetic loss
+    L = sum(y * g)."""
+    index: int
+    name: str
+    tokens: int
+    d: int
+    f: int
+    x_dist: str = "t3_outliers"
+    x_sigma: float = 1.0
+    w_sigma: float = 0.02
+    g_sigma: float = 1e-6
+
+    ORDER = ("X", "W1", "W2", "G")
+
+    def seed(self, name):
+        return 1000 * self.index + self.ORDER.index(name)
+
+    def shape(self, name):
+        return {"X": (self.tokens, self.d), "W1": (2 * self.f, self.d), "W2": (self.d, self.f),
+                "G": (self.tokens, self.d)}[name]
+
+    def flops(self):
+        """Six products per step (three forward-shaped, each with a data and a
+        weight gradient): 18 * tokens * f * d."""
+        return 18 * self.tokens * self.f * self.d
+
+
+def chained_mlp_tensor(m, name):
+    """CPU tensor `name` of chained MLP `m`: X bf16, the rest float32."""
+    if name == "X":
+        return draw_bf16(m.seed(name), m.shape(name), m.x_dist, m.x_sigma)
+    sigma = m.w_sigma if name in ("W1", "W2") else m.g_sigma
+    return torch.from_numpy(draw_f32(m.seed(name), m.shape(name), "normal", sigma))
+
+
+# Llama-2-7B's MLP (hidden 4096, intermediate 11008) over 4096 tokens.
+CHAINED_MLPS = {6: ChainedMLP(6, "llama2-7b-mlp-chained-fwd-bwd-tokens4096", 4096, 4096, 11008)}
+
+
 def draw_f32(seed, shape, dist, sigma):
     """float32 numpy array of the given distribution (see module docstring)."""
     rng = np.random.default_rng(seed)

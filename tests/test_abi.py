@@ -31,7 +31,7 @@ def status(code):
 
 def test_every_declared_function_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), n
         assert n in fl.SIGNATURES, n
@@ -148,3 +148,30 @@ def test_gemm_amax_without_a_device_reports_no_device():
     f = L.fp8_scaled_gemm_amax
     assert f(0, 0, A16, 0, A32, A48, 0, A32, 0, 8, 8, A16, A32, None) == status("FP8_ERR_DEVICE")
     assert f(0, 0, A16, 0, A32, A48, 0, A32, 64, 64, 64, A16, A32, None) == status("FP8_ERR_DEVICE")
+
+
+def test_swiglu_argument_checks():
+    fwd, bwd = L.fp8_swiglu_fwd, L.fp8_swiglu_bwd
+    assert fwd(A16, -1, 4, A32, None, None) == status("FP8_ERR_SIZE")
+    assert fwd(A16, 4, -4, A32, None, None) == status("FP8_ERR_SIZE")
+    assert fwd(A16, 1 << 31, 4, A32, None, None) == status("FP8_ERR_SIZE")
+    assert fwd(A16, (1 << 31) - 1, 1 << 29, A32, None, None) == status("FP8_ERR_SIZE")   # grid too large
+    assert fwd(None, 4, 4, A32, None, None) == status("FP8_ERR_NULL")
+    assert fwd(A16, 4, 4, None, None, None) == status("FP8_ERR_NULL")
+    assert fwd(MIS, 4, 4, A32, None, None) == status("FP8_ERR_ALIGN")
+    assert fwd(A16, 4, 4, MIS, None, None) == status("FP8_ERR_ALIGN")
+    assert fwd(A16, 4, 4, A32, P(18), None) == status("FP8_ERR_ALIGN")
+    assert bwd(A16, None, 4, 4, A32, None, None) == status("FP8_ERR_NULL")
+    assert bwd(A16, MIS, 4, 4, A32, None, None) == status("FP8_ERR_ALIGN")
+    assert bwd(A16, A48, -4, 4, A32, None, None) == status("FP8_ERR_SIZE")
+    # empty without an amax: nothing to do, no device needed
+    assert fwd(None, 0, 4, None, None, None) == 0
+    assert bwd(None, None, 4, 0, None, None, None) == 0
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
+def test_swiglu_without_a_device_reports_no_device():
+    assert L.fp8_swiglu_fwd(A16, 4, 4, A32, None, None) == status("FP8_ERR_DEVICE")
+    assert L.fp8_swiglu_bwd(A16, A48, 4, 4, A32, A16, None) == status("FP8_ERR_DEVICE")
+    assert L.fp8_swiglu_fwd(None, 0, 4, None, A16, None) == status("FP8_ERR_DEVICE")   # the amax clear
+
