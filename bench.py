@@ -8,6 +8,10 @@ workload is the Llama-2-70B-shaped single-layer inference (8192 tokens,
 hidden 8192, QKV 8192->10240, O 8192->8192, gate/up 8192->28672, down
 28672->8192).
 
+Workload 6 is the chained FP8 MLP instead (Llama-2-7B MLP, 4096 tokens): one
+step = the autograd Function's forward and backward (six quantisations, six
+products, SwiGLU forward and backward), see bench_mlp.
+
 Prints one JSON line: whole-step TFLOP/s (amax + bias + cast included) from
 K timed steps; the roofline of the dominant kernel (the FP8 GEMM) and the
 amax / cast HBM throughput from HIP events on the launch stream in K further
@@ -35,7 +39,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=5, help="1..5 (see synth.WORKLOADS)")
+    ap.add_argument("--workload", type=int, default=5,
+                    help="1..5 (synth.WORKLOADS) or 6 (synth.CHAINED_MLPS: the chained FP8 MLP)")
+    ap.add_argument("--bias-steps", type=int, default=20,
+                    help="chained MLP: untimed Adam steps whose per-tensor biases are logged")
+    ap.add_argument("--cpu-tokens", type=int, default=16,
+                    help="chained MLP: tokens of the CPU oracle's sample")
     ap.add_argument("--math", choices=["exact", "native-fp8"], default="exact",
                     help="product arithmetic: exact (fp16 MFMA on exactly widened FP8) or the native FP8 MFMA")
     ap.add_argument("--cpu-rows", type=int, default=256, help="rows of each product in the CPU sample")
@@ -386,6 +395,185 @@ def cpu_baseline(w, host, rows, cols):
     }
 
 
+def cpu_baseline_mlp(m, host, tokens):
+    """The oracle, as it stands, on a bounded sample of the chained MLP's step:
+    the first `tokens` tokens through the forward and backward (every
+    quantisation, product and SwiGLU; the weights quantised whole, as each
+    step does), scaled to the step: the quantisations of the weights are
+    whole-step work, everything else scales with the tokens."""
+    import numpy as np
+    import oracle
+    import synth
+
+    T, d, f = m.tokens, m.d, m.f
+    t = min(tokens, T)
+    x = synth.bf16_words(host["X"])[:t]
+    w1 = host["W1"].numpy().view(np.uint32)
+    w2 = host["W2"].numpy().view(np.uint32)
+    g = host["G"].numpy()[:t].copy().view(np.uint32)
+    E4, E5 = 0, 1
+
+    def bf16_words_of(v):
+        import torch
+        return synth.bf16_words(torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16))
+
+    t0 = time.perf_counter()
+    _, bw1, w1_8 = oracle.quantize(w1, E4)
+    _, bw2, w2_8 = oracle.quantize(w2, E4)
+    t_weights = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    _, bx, x8 = oracle.quantize(x, E4)
+    h, _ = oracle.gemm_fwd(x8, E4, bx, w1_8, E4, bw1)
+    a = bf16_words_of(oracle.swiglu_fwd(h.astype(np.float32)))
+    _, ba, a8 = oracle.quantize(a, E4)
+    oracle.gemm_fwd(a8, E4, ba, w2_8, E4, bw2)
+    _, bdy, dy8 = oracle.quantize(g, E5)
+    da, _ = oracle.gemm_dgrad(dy8, E5, bdy, w2_8, E4, bw2)
+    oracle.gemm_wgrad(dy8, E5, bdy, a8, E4, ba)
+    dh = bf16_words_of(oracle.swiglu_bwd(h.astype(np.float32), da.astype(np.float32)))
+    _, bdh, dh8 = oracle.quantize(dh, E5)
+    oracle.gemm_dgrad(dh8, E5, bdh, w1_8, E4, bw1)
+    oracle.gemm_wgrad(dh8, E5, bdh, x8, E4, bx)
+    t_tokens = time.perf_counter() - t0
+    t_step = t_weights + t_tokens * (T / t)
+    return {"value": round(m.flops() / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"the first {t} of {T} tokens through the whole forward and backward "
+                      f"(weights quantised whole); token work scaled by {T / t:.0f}",
+            "seconds": round(t_weights + t_tokens, 2), "host_cpu_count": os.cpu_count(),
+            "host_affinity": len(os.sched_getaffinity(0))}
+
+
+def bench_mlp(args, m):
+    """The chained FP8 MLP: x [T, d] bf16, fp32 master weights w1 [2F, d] and
+    w2 [d, F], upstream gradient g [T, d] (the synthetic loss L = sum(y * g)).
+    One step = FP8MLPFunction forward + backward through autograd; every
+    product, quantisation and SwiGLU runs in libfp8lin (dx is computed and
+    handed to autograd, which drops it: x is a leaf that needs no gradient).
+    Weights are re-quantised every step, as training does.  No optimizer step
+    in the timed region (the weight update is not part of the layer)."""
+    import torch
+
+    import fp8_precision_linear_amd as fl
+    from fp8_precision_linear_amd import mlp
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    host = {n: synth.chained_mlp_tensor(m, n) for n in m.ORDER}
+    x = host["X"].cuda()
+    w1 = host["W1"].cuda().requires_grad_()
+    w2 = host["W2"].cuda().requires_grad_()
+    g = host["G"].cuda()
+    math = fl.MATH_EXACT if args.math == "exact" else fl.MATH_NATIVE_FP8
+    cfg = mlp.MLPConfig(math=math)
+
+    def step():
+        w1.grad = None
+        w2.grad = None
+        y = mlp.FP8MLPFunction.apply(x, w1, w2, cfg)
+        y.backward(g)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # per-kernel durations: K more steps with events around every launch group
+    cfg.events = []
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    gc.enable()
+    K = args.steps
+    by = {}
+    for kind, name, e0, e1 in cfg.events:
+        by[(kind, name)] = by.get((kind, name), 0.0) + e0.elapsed_time(e1) / K
+    cfg.events = None
+    T, d, f = m.tokens, m.d, m.f
+    gemm_flops = {"fwd h": 2 * T * 2 * f * d, "fwd y": 2 * T * d * f, "dgrad da": 2 * T * d * f,
+                  "wgrad dw2": 2 * T * d * f, "dgrad dx": 2 * T * 2 * f * d, "wgrad dw1": 2 * T * 2 * f * d}
+    gemm_ms = sum(v for (k, _), v in by.items() if k == "gemm")
+    gemm_tflops = sum(gemm_flops.values()) / (gemm_ms * 1e-3) / 1e12
+    peak = PEAK_F16_TFLOPS if args.math == "exact" else PEAK_FP8_TFLOPS
+    # HBM bytes per group: amax reads the input, the cast reads it again and
+    # writes one byte per element; SwiGLU fwd reads g, u (fp32) and writes a
+    # (bf16), bwd reads g, u, da and writes dg, du
+    quant_bytes = {"x": (2 + 2 + 1) * T * d, "w1": (4 + 4 + 1) * 2 * f * d, "a": (2 + 1) * T * f,
+                   "w2": (4 + 4 + 1) * d * f, "dy": (4 + 4 + 1) * T * d, "dh": (2 + 1) * T * 2 * f}
+    sw_bytes = {"fwd": (8 + 2) * T * f, "bwd": (12 + 4) * T * f}
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
+
+    hist = None
+    if args.bias_steps > 0:
+        # untimed: Adam on a regression towards a fixed target, so that the
+        # tensors (and with them the biases) move as in training
+        log = mlp.BiasLog()
+        tcfg = mlp.MLPConfig(math=math, log=log)
+        p1 = w1.detach().clone().requires_grad_()
+        p2 = w2.detach().clone().requires_grad_()
+        with torch.no_grad():
+            target = mlp.mlp_forward(x, w1.detach() * 3, w2.detach() * 3, mlp.MLPConfig(math=math))[0]
+        opt = torch.optim.Adam([p1, p2], lr=1e-3)
+        losses = []
+        for _ in range(args.bias_steps):
+            y = mlp.FP8MLPFunction.apply(x, p1, p2, tcfg)
+            loss = ((y - target) ** 2).mean()
+            opt.zero_grad()
+            loss.backward()
+            opt.step()
+            losses.append(loss.detach())
+        hist = {"per_tensor_bias": log.history(),
+                "loss": [round(float(v), 6) for v in torch.stack(losses).cpu()],
+                "method": f"{args.bias_steps} untimed Adam steps (lr 1e-3) on mean((y - y_t)^2), "
+                          f"y_t the same MLP with weights x3"}
+        del p1, p2, opt, target
+
+    line = {
+        "metric": "chained FP8 MLP fwd+bwd TFLOP/s (six FP8-AMAX products, quantisations and SwiGLU included)",
+        "value": round(m.flops() / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": m.name, "tokens": T, "d": d, "f": f, "math": args.math,
+                   "weights": "fp32 masters, re-quantised each step", "accumulate": "f32",
+                   "input_sha256": {n: synth.sha256(host[n]) for n in m.ORDER},
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "kernel": "the six products (gemm_pp_kernel)",
+                     "achieved": round(gemm_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / peak, 4),
+                     "frac_of_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": None,
+                     "per_product_us": {n: round(by[("gemm", n)] * 1e3, 1) for n in gemm_flops}},
+        "swiglu": {n: {"us": round(by[("swiglu", n)] * 1e3, 1),
+                       "gbs": round(gbs(b, by[("swiglu", n)]), 1),
+                       "frac": round(gbs(b, by[("swiglu", n)]) / PEAK_HBM_GBS, 4)}
+                   for n, b in sw_bytes.items()},
+        "quantise": {n: {"us": round(by[("quant", n)] * 1e3, 1),
+                         "gbs": round(gbs(b, by[("quant", n)]), 1),
+                         "frac": round(gbs(b, by[("quant", n)]) / PEAK_HBM_GBS, 4)}
+                     for n, b in quant_bytes.items()},
+        "step_breakdown_ms": {k: round(sum(v for (kk, _), v in by.items() if kk == k), 4)
+                              for k in ("gemm", "quant", "swiglu")},
+        "bias_history": hist,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_mlp(m, host, args.cpu_tokens)
+        line["cpu_baseline"]["vs_gpu"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -403,6 +591,9 @@ def main():
     import fp8_precision_linear_amd as fl
     import synth
 
+    if args.workload in synth.CHAINED_MLPS:
+        bench_mlp(args, synth.CHAINED_MLPS[args.workload])
+        return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     w = synth.WORKLOADS[args.workload]

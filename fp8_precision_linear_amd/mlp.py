@@ -27,6 +27,7 @@ The fused gate-up weight is one tensor with one scale, and so is its gradient
 no host synchronisation; this module only allocates outputs and orders the
 calls.  Gradients come back in fp32 (autograd converts dx to x's dtype).
 """
+from contextlib import contextmanager
 from dataclasses import dataclass, field
 
 import torch
@@ -63,10 +64,25 @@ class BiasLog:
 @dataclass
 class MLPConfig:
     """Margins per quantised tensor (compute_bias's margin), the product
-    arithmetic, and an optional bias log."""
+    arithmetic, an optional bias log, and an optional list that receives
+    (kind, name, start event, end event) around every group of launches
+    (kind: "quant", "gemm" or "swiglu"), for per-kernel timing."""
     margins: dict = field(default_factory=lambda: {n: 0 for n in TENSORS})
     math: int = MATH_EXACT
     log: BiasLog = None
+    events: list = None
+
+
+@contextmanager
+def _span(cfg, kind, name):
+    if cfg.events is None:
+        yield
+        return
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    yield
+    e1.record()
+    cfg.events.append((kind, name, e0, e1))
 
 
 def _shapes(x, w1, w2):
@@ -87,15 +103,22 @@ def mlp_forward(x, w1, w2, cfg=None):
     cfg = cfg or MLPConfig()
     _shapes(x, w1, w2)
     m = cfg.margins
-    x8, bx, _ = quantize(x, E4M3, m["x"])
-    w1_8, bw1, _ = quantize(w1, E4M3, m["w1"])
-    h = scaled_gemm(OP_FWD, x8, E4M3, bx, w1_8, E4M3, bw1, math=cfg.math)
     a_amax = torch.empty(1, dtype=torch.float32, device=x.device)
-    a = swiglu_fwd(h, amax=a_amax)
-    ba = compute_bias(a_amax, E4M3, m["a"])
-    a8 = scale_cast(a, ba, E4M3)
-    w2_8, bw2, _ = quantize(w2, E4M3, m["w2"])
-    y = scaled_gemm(OP_FWD, a8, E4M3, ba, w2_8, E4M3, bw2, math=cfg.math)
+    with _span(cfg, "quant", "x"):
+        x8, bx, _ = quantize(x, E4M3, m["x"])
+    with _span(cfg, "quant", "w1"):
+        w1_8, bw1, _ = quantize(w1, E4M3, m["w1"])
+    with _span(cfg, "gemm", "fwd h"):
+        h = scaled_gemm(OP_FWD, x8, E4M3, bx, w1_8, E4M3, bw1, math=cfg.math)
+    with _span(cfg, "swiglu", "fwd"):
+        a = swiglu_fwd(h, amax=a_amax)
+    with _span(cfg, "quant", "a"):
+        ba = compute_bias(a_amax, E4M3, m["a"])
+        a8 = scale_cast(a, ba, E4M3)
+    with _span(cfg, "quant", "w2"):
+        w2_8, bw2, _ = quantize(w2, E4M3, m["w2"])
+    with _span(cfg, "gemm", "fwd y"):
+        y = scaled_gemm(OP_FWD, a8, E4M3, ba, w2_8, E4M3, bw2, math=cfg.math)
     if cfg.log is not None:
         for n, b in (("x", bx), ("w1", bw1), ("a", ba), ("w2", bw2)):
             cfg.log.record(n, b)
@@ -108,15 +131,22 @@ def mlp_backward(saved, dy, cfg=None):
     cfg = cfg or MLPConfig()
     m = cfg.margins
     dy = dy.contiguous()
-    dy8, bdy, _ = quantize(dy, E5M2, m["dy"])
-    da = scaled_gemm(OP_DGRAD, dy8, E5M2, bdy, saved["w2_8"], E4M3, saved["bw2"], math=cfg.math)
-    dw2 = scaled_gemm(OP_WGRAD, dy8, E5M2, bdy, saved["a8"], E4M3, saved["ba"], math=cfg.math)
     dh_amax = torch.empty(1, dtype=torch.float32, device=dy.device)
-    dh = swiglu_bwd(saved["h"], da, amax=dh_amax)
-    bdh = compute_bias(dh_amax, E5M2, m["dh"])
-    dh8 = scale_cast(dh, bdh, E5M2)
-    dx = scaled_gemm(OP_DGRAD, dh8, E5M2, bdh, saved["w1_8"], E4M3, saved["bw1"], math=cfg.math)
-    dw1 = scaled_gemm(OP_WGRAD, dh8, E5M2, bdh, saved["x8"], E4M3, saved["bx"], math=cfg.math)
+    with _span(cfg, "quant", "dy"):
+        dy8, bdy, _ = quantize(dy, E5M2, m["dy"])
+    with _span(cfg, "gemm", "dgrad da"):
+        da = scaled_gemm(OP_DGRAD, dy8, E5M2, bdy, saved["w2_8"], E4M3, saved["bw2"], math=cfg.math)
+    with _span(cfg, "gemm", "wgrad dw2"):
+        dw2 = scaled_gemm(OP_WGRAD, dy8, E5M2, bdy, saved["a8"], E4M3, saved["ba"], math=cfg.math)
+    with _span(cfg, "swiglu", "bwd"):
+        dh = swiglu_bwd(saved["h"], da, amax=dh_amax)
+    with _span(cfg, "quant", "dh"):
+        bdh = compute_bias(dh_amax, E5M2, m["dh"])
+        dh8 = scale_cast(dh, bdh, E5M2)
+    with _span(cfg, "gemm", "dgrad dx"):
+        dx = scaled_gemm(OP_DGRAD, dh8, E5M2, bdh, saved["w1_8"], E4M3, saved["bw1"], math=cfg.math)
+    with _span(cfg, "gemm", "wgrad dw1"):
+        dw1 = scaled_gemm(OP_WGRAD, dh8, E5M2, bdh, saved["x8"], E4M3, saved["bx"], math=cfg.math)
     if cfg.log is not None:
         cfg.log.record("dy", bdy)
         cfg.log.record("dh", bdh)
