@@ -318,6 +318,38 @@ __device__ __forceinline__ uint4 cast_unit_hw(uint4 lo, uint4 hi, int32_t b, uin
   return o;
 }
 
+// fp32 magnitude bits of min(fmt_max * 2^-b, largest finite fp32); fmt_max =
+// 1.75 * 2^emax has fp32 fraction bits 0x600000.
+template <int FMT>
+__device__ __forceinline__ uint32_t hw_bound_f32(int32_t b) {
+  static_assert(kHwConvert<FMT>, "no hardware conversion for this format");
+  const int efield = (FMT == FP8_E4M3 ? 8 : 15) + 127 - b;
+  return efield >= 255 ? 0x7F7FFFFFu : (((uint32_t)efield << 23) | 0x600000u);
+}
+
+// Four fp32 values -> four codes with v_cvt_scalef32_pk_{fp8,bf8}_f32, the
+// magnitudes clamped to fmt_max * 2^-b first (as for bf16 inputs); mx keeps
+// the largest magnitude seen, for the non-finite check.
+template <int FMT>
+__device__ __forceinline__ uint32_t pack4_f32_hw(uint4 v, uint32_t bound, float scale, uint32_t& mx) {
+  const uint32_t m0 = v.x & 0x7FFFFFFFu, m1 = v.y & 0x7FFFFFFFu;
+  const uint32_t m2 = v.z & 0x7FFFFFFFu, m3 = v.w & 0x7FFFFFFFu;
+  mx = max(mx, max(max(m0, m1), max(m2, m3)));
+  const float c0 = __uint_as_float((v.x & 0x80000000u) | min(m0, bound));
+  const float c1 = __uint_as_float((v.y & 0x80000000u) | min(m1, bound));
+  const float c2 = __uint_as_float((v.z & 0x80000000u) | min(m2, bound));
+  const float c3 = __uint_as_float((v.w & 0x80000000u) | min(m3, bound));
+  hw_v2s r = {0, 0};
+  if constexpr (FMT == FP8_E4M3) {
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c0, c1, scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c2, c3, scale, true);
+  } else {
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, c0, c1, scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, c2, c3, scale, true);
+  }
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 template <int FMT>
 __device__ __forceinline__ uint4 cast_unit_sw(uint4 lo, uint4 hi, int32_t b) {
   uint4 o;
@@ -378,28 +410,55 @@ __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const uint4* __rest
     tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>((uint32_t)tail_x[threadIdx.x] << 16, *bias);
 }
 
+// fp32 input: a wave takes chunks of kF32Chunk consecutive elements; load k
+// of lane l reads elements [256k + 4l, +4) of the chunk, so every load
+// instruction covers 1 KiB of consecutive bytes (16 bytes per lane, lane-
+// contiguous 64-byte runs left each instruction striding and measured 4.2 TB/s
+// on MI355X over 90M elements, against 6.4 TB/s this way), and the four codes
+// go out as one dword at the same position of the output.  Groups of four
+// holding an inf or NaN take fp8_code.  Elements past the last whole chunk
+// (fewer than kF32Chunk) are cast one per lane by block 0.
+constexpr int kF32Loads = 4;
+constexpr int64_t kF32Chunk = 256 * kF32Loads;
+
+template <int FMT>
+__device__ __forceinline__ uint32_t cast4_f32(uint4 v, bool hw, int32_t b, uint32_t bound, float scale) {
+  if constexpr (kHwConvert<FMT>) {
+    if (hw) {
+      uint32_t mx = 0;
+      const uint32_t o = pack4_f32_hw<FMT>(v, bound, scale, mx);
+      if (mx < 0x7F800000u) return o;
+    }
+  }
+  return pack4_f32<FMT>(v, b);
+}
+
 template <int FMT, bool NT>
 __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restrict__ x,
-                                                            int64_t nunit,
+                                                            int64_t nchunk,
                                                             const int32_t* __restrict__ bias,
-                                                            uint4* __restrict__ y,
+                                                            uint32_t* __restrict__ y,
                                                             const uint32_t* __restrict__ tail_x,
                                                             uint8_t* __restrict__ tail_y,
                                                             int ntail) {
   const int32_t b = *bias;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nunit; i += stride) {
-    const uint4 a0 = load16<NT>(&x[4 * i]), a1 = load16<NT>(&x[4 * i + 1]);
-    const uint4 a2 = load16<NT>(&x[4 * i + 2]), a3 = load16<NT>(&x[4 * i + 3]);
-    uint4 o;
-    o.x = pack4_f32<FMT>(a0, b);
-    o.y = pack4_f32<FMT>(a1, b);
-    o.z = pack4_f32<FMT>(a2, b);
-    o.w = pack4_f32<FMT>(a3, b);
-    store16<false>(o, &y[i]);
+  const bool hw = kHwConvert<FMT> && b >= kHwBiasMin && b <= kHwBiasMax;
+  uint32_t bound = 0;
+  if constexpr (kHwConvert<FMT>) bound = hw_bound_f32<FMT>(b);
+  const float scale = __builtin_ldexpf(1.0f, hw ? -b : 0);
+  const int lane = threadIdx.x & 63;
+  const int64_t wstride = (int64_t)gridDim.x * (kThreads / 64);
+  for (int64_t w = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); w < nchunk; w += wstride) {
+    const int64_t q = w * (kF32Chunk / 4);  // the chunk's first 16-byte group
+    uint4 v[kF32Loads];
+#pragma unroll
+    for (int k = 0; k < kF32Loads; ++k) v[k] = load16<NT>(&x[q + 64 * k + lane]);
+#pragma unroll
+    for (int k = 0; k < kF32Loads; ++k) y[q + 64 * k + lane] = cast4_f32<FMT>(v[k], hw, b, bound, scale);
   }
-  if (blockIdx.x == 0 && (int)threadIdx.x < ntail)
-    tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>(tail_x[threadIdx.x], b);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < ntail; i += kThreads)
+      tail_y[i] = (uint8_t)fp8_code<FMT>(tail_x[i], b);
 }
 
 // Grid size: `per_lane` units of work per lane, between 1 and `cap` blocks.
@@ -490,12 +549,18 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias,
     FP8LIN_CAST_FORMATS(fmt, nt);
 #undef FP8LIN_CAST
   } else {
-    const uint32_t* tail_x = static_cast<const uint32_t*>(x) + nunit * 16;
+    const int64_t nchunk = n / kF32Chunk;
+    const int nrest = (int)(n - nchunk * kF32Chunk);
+    const uint32_t* rest_x = static_cast<const uint32_t*>(x) + nchunk * kF32Chunk;
+    uint8_t* rest_y = y + nchunk * kF32Chunk;
+    uint32_t* yw = reinterpret_cast<uint32_t*>(y);
     const uint4* xv = static_cast<const uint4*>(x);
-    const dim3 grid(stream_blocks(nunit, 1, kCastMaxBlocks));
-#define FP8LIN_CAST(F, NT)                                                                   \
-  hipLaunchKernelGGL((cast_f32_kernel<F, NT>), grid, dim3(kThreads), 0, stream, xv, nunit, \
-                     bias, yv, tail_x, tail_y, ntail)
+    // one chunk per wave, four waves per block, at least one block (the rest)
+    const int64_t want = (nchunk + kThreads / 64 - 1) / (kThreads / 64);
+    const dim3 grid((uint32_t)(want < 1 ? 1 : (want > kCastMaxBlocks ? kCastMaxBlocks : want)));
+#define FP8LIN_CAST(F, NT)                                                                    \
+  hipLaunchKernelGGL((cast_f32_kernel<F, NT>), grid, dim3(kThreads), 0, stream, xv, nchunk, \
+                     bias, yw, rest_x, rest_y, nrest)
     FP8LIN_CAST_FORMATS(fmt, nt);
 #undef FP8LIN_CAST
   }

@@ -179,8 +179,9 @@ int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_forma
  *             to fp8_amax over it, so fp8_compute_bias can follow directly
  *             ("Proposed method", bullet 1); 0 for an empty output.
  * h, da, a, dh: device, 16-byte aligned.  rows, f >= 0 (either 0: nothing but
- * the amax clear is launched).  Returns FP8_ERR_SIZE when rows * ceil(f / 1024)
- * exceeds 2^31 - 1.
+ * the amax clear is launched).  Returns FP8_ERR_SIZE when the launch would need
+ * more than 2^31 - 1 blocks: rows * ceil(f / 1024) when f is a multiple of 4,
+ * rows * ceil(f / 256) otherwise.
  */
 int fp8_swiglu_fwd(const float* h, int64_t rows, int64_t f, uint16_t* a, float* out_amax,
                    void* stream);

@@ -56,6 +56,33 @@ def test_cast_fp32_words(fl, fmt):
         assert np.array_equal(got, ref), f"bias {b}: {np.count_nonzero(got != ref)} codes differ"
 
 
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+def test_cast_fp32_midpoints_and_neighbours(fl, fmt):
+    """fp32 inputs at every midpoint between neighbouring FP8 values (and the
+    one above the largest), at every FP8 value, and one fp32 ulp either side of
+    each, both signs, scaled by 2^-b for biases across the range; plus the
+    saturation bound fmt_max * 2^-b and its neighbours."""
+    vals = oracle.decode_fp8(np.arange(128), fmt)
+    vals = vals[np.isfinite(vals)]
+    top = vals[-1] + (vals[-1] - vals[-2]) / 2
+    pts = np.concatenate([vals, (vals[:-1] + vals[1:]) / 2, [top]])
+    fmax = {E4M3: 448.0, E5M2: 57344.0, E3M4: 30.0}[fmt]
+    for b in (-127, -100, -60, -20, -9, -1, 0, 1, 7, 20, 60, 100, 126, 127, 140):
+        with np.errstate(over="ignore"):
+            x = np.concatenate([pts, [fmax]]) * 2.0 ** -b
+            x32 = x.astype(np.float32)
+        x32 = x32[np.isfinite(x32) & (x32.astype(np.float64) == x)]
+        near = np.concatenate([x32, np.nextafter(x32, np.float32(np.inf)), np.nextafter(x32, np.float32(0))])
+        near = near[np.isfinite(near)]
+        words = np.concatenate([near, -near]).astype(np.float32).view(np.uint32)
+        say("cast fp32 midpoints", "fmt", fmt, "bias", b, "n", words.size)
+        got = fl.scale_cast(f32_dev(words), i32_dev(b), fmt).cpu().numpy()
+        ref = oracle.scale_cast(words, b, fmt)
+        if not np.array_equal(got, ref):
+            bad = np.where(got != ref)[0][:6]
+            raise AssertionError(f"fmt {fmt} bias {b}: words {[hex(w) for w in words[bad]]} gpu {got[bad]} oracle {ref[bad]}")
+
+
 @pytest.mark.parametrize("n", [1, 7, 8, 9, 15, 16, 17, 31, 33, 255, 4097, 1_000_003])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_amax_and_cast_ragged_sizes(fl, n, dtype):
@@ -182,6 +209,18 @@ def test_cast_mixes_non_finite_values_into_finite_units(fl):
             got = fl.scale_cast(x, i32_dev(b), fmt).cpu().numpy()
             ref = oracle.scale_cast(words, b, fmt)
             assert np.array_equal(got, ref), f"fmt {fmt} bias {b}: {np.count_nonzero(got != ref)} codes differ"
+    # the same with fp32 inputs (their own NaN payloads included)
+    w32 = v.view(np.uint32).copy()
+    spec32 = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001, 0x7F800001, 0x7F7FFFFF],
+                      dtype=np.uint32)
+    w32[pos] = spec32[rng.integers(0, spec32.size, pos.size)]
+    x32 = f32_dev(w32)
+    for fmt in ALL_FMTS:
+        for b in (-130, -4, 0, 3, 12, 126, 127):
+            say("cast mixed non-finite fp32", "fmt", fmt, "bias", b)
+            got = fl.scale_cast(x32, i32_dev(b), fmt).cpu().numpy()
+            ref = oracle.scale_cast(w32, b, fmt)
+            assert np.array_equal(got, ref), f"fp32 fmt {fmt} bias {b}: {np.count_nonzero(got != ref)} codes differ"
 
 
 def test_gradient_underflow_control(fl):
