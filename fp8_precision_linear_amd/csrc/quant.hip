@@ -534,12 +534,13 @@ hipError_t launch_bias(const float* amax, int fmt, int32_t margin, int32_t* bias
 hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias, int fmt,
                        uint8_t* y, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  const int64_t nunit = n / 16;
-  const int ntail = (int)(n - nunit * 16);
-  uint8_t* tail_y = y + nunit * 16;
-  uint4* yv = reinterpret_cast<uint4*>(y);
   const bool nt = streams("FP8LIN_CAST_HINT");
   if (dtype == FP8_IN_BF16) {
+    // 16-element units, one per lane; the last n % 16 elements by block 0
+    const int64_t nunit = n / 16;
+    const int ntail = (int)(n - nunit * 16);
+    uint8_t* tail_y = y + nunit * 16;
+    uint4* yv = reinterpret_cast<uint4*>(y);
     const uint16_t* tail_x = static_cast<const uint16_t*>(x) + nunit * 16;
     const uint4* xv = static_cast<const uint4*>(x);
     const dim3 grid(stream_blocks(nunit, kCastUnitsPerLane, kCastMaxBlocks));
