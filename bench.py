@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--cold-reps", type=int, default=5)
     ap.add_argument("--no-epilogue-amax", action="store_true",
                     help="skip the epilogue-amax measurement on the largest product")
+    ap.add_argument("--no-delayed", action="store_true",
+                    help="skip the delayed-scaling (cast with its amax folded in) measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy twice (HBM counter calibration)")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -158,6 +160,55 @@ def epilogue_amax(fl, w, plan, q, outs, math, op_of, reps=9):
             "gemm_us": round(t_plain, 1), "gemm_with_epilogue_amax_us": round(t_fused, 1),
             "gemm_then_amax_pass_us": round(t_sep, 1),
             "saved_us": round(t_sep - t_fused, 1)}
+
+
+def delayed_quant(fl, w, plan, q, x, reps=9):
+    """Delayed scaling on the step's in-step tensors: the cast with the amax of
+    its own input folded in (fp8_scale_cast_amax) after a bias from the amax a
+    previous call returned, against the current-step chain amax -> bias ->
+    cast; each timed alone with HIP events, interleaved, median of `reps`."""
+    import statistics
+
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    prev = torch.empty(1, dtype=torch.float32, device="cuda")
+
+    def once(fn):
+        torch.cuda.synchronize()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    per, t_chain, t_fused, elems = {}, 0.0, 0.0, 0
+    for item in plan:
+        if item[0] != "quant":
+            continue
+        n = item[1]
+        codes, bias, amax, fmt = q[n]
+        margin = w.tensor(n).margin
+        fl.amax(x[n], out=prev)
+        chain, fused = [], []
+        for _ in range(reps):
+            chain.append(once(lambda: (fl.amax(x[n], out=amax), fl.compute_bias(amax, fmt, margin, out=bias),
+                                       fl.scale_cast(x[n], bias, fmt, out=codes))))
+            fused.append(once(lambda: (fl.compute_bias(prev, fmt, margin, out=bias),
+                                       fl.scale_cast(x[n], bias, fmt, out=codes, amax=prev))))
+        tc, tf = statistics.median(chain), statistics.median(fused)
+        k = x[n].numel()
+        per[n] = {"chain_us": round(tc * 1e3, 1), "fused_us": round(tf * 1e3, 1),
+                  "fused_gbs": round(3.0 * k / (tf * 1e-3) / 1e9, 1)}
+        t_chain, t_fused, elems = t_chain + tc, t_fused + tf, elems + k
+    if not per:
+        return None
+    gbs = 3.0 * elems / (t_fused * 1e-3) / 1e9
+    return {"method": f"bias from the previous call's amax + cast with its input's amax folded in "
+                      f"(3 B per element) vs amax -> bias -> cast (5 B); each alone, HIP events, "
+                      f"median of {reps}",
+            "chain_us": round(t_chain * 1e3, 1), "fused_us": round(t_fused * 1e3, 1),
+            "fused_gbs": round(gbs, 1), "fused_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "per_tensor": per}
 
 
 COLD_FLUSH_BYTES = 768 << 20   # > the 256 MB Infinity Cache
@@ -678,6 +729,7 @@ def main():
 
     cold = None if args.no_cold else cold_quant(fl, w, plan, q, x, args.cold_reps)
     epi = None if args.no_epilogue_amax else epilogue_amax(fl, w, plan, q, outs, math, op_of)
+    delayed = None if args.no_delayed else delayed_quant(fl, w, plan, q, x)
 
     # per-kernel durations from the events (same stream as the launches)
     gemm_ms = amax_ms = bias_ms = cast_ms = 0.0
@@ -785,6 +837,7 @@ def main():
         },
         "cold": cold,
         "epilogue_amax": epi,
+        "delayed_scaling": delayed,
         "step_breakdown_ms": {"gemm": round(gemm_ms / K, 4), "amax": round(amax_ms / K, 4),
                               "bias": round(bias_ms / K, 4), "cast": round(cast_ms / K, 4)},
     }

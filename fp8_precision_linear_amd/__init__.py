@@ -41,6 +41,7 @@ SIGNATURES = {
     "fp8_amax": (_ci, [_vp, _ci, _i64, _vp, _vp]),
     "fp8_compute_bias": (_ci, [_vp, _ci, _i32, _vp, _vp]),
     "fp8_scale_cast": (_ci, [_vp, _ci, _i64, _vp, _ci, _vp, _vp]),
+    "fp8_scale_cast_amax": (_ci, [_vp, _ci, _i64, _vp, _ci, _vp, _vp, _vp]),
     "fp8_scaled_gemm": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_amax": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_fwd": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
@@ -117,12 +118,20 @@ def compute_bias(amax_t, fmt, margin=0, out=None, stream=None):
     return out
 
 
-def scale_cast(x, bias, fmt, out=None, stream=None):
-    """uint8 device tensor of FP8 codes of x * 2^bias, same shape as x (fp8_scale_cast)."""
+def scale_cast(x, bias, fmt, out=None, stream=None, amax=None):
+    """uint8 device tensor of FP8 codes of x * 2^bias, same shape as x (fp8_scale_cast).
+    amax: optional float32[1] device tensor that receives max |x|, folded in the
+    same pass (fp8_scale_cast_amax; for delayed scaling)."""
     _need_cuda(x, bias)
     out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
-    _check("fp8_scale_cast", lib.fp8_scale_cast(_ptr(x), _dtype_code(x), x.numel(), _ptr(bias),
-                                                int(fmt), _ptr(out), _stream(stream)))
+    if amax is None:
+        _check("fp8_scale_cast", lib.fp8_scale_cast(_ptr(x), _dtype_code(x), x.numel(), _ptr(bias),
+                                                    int(fmt), _ptr(out), _stream(stream)))
+    else:
+        _need_cuda(amax)
+        _check("fp8_scale_cast_amax",
+               lib.fp8_scale_cast_amax(_ptr(x), _dtype_code(x), x.numel(), _ptr(bias), int(fmt),
+                                       _ptr(out), _ptr(amax), _stream(stream)))
     return out
 
 

@@ -95,7 +95,23 @@ int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* b
   if (!x || !y || !bias) return FP8_ERR_NULL;
   if (misaligned(x) || misaligned(y)) return FP8_ERR_ALIGN;
   if (int s = device_ok()) return s;
-  return hip_status(fp8lin::launch_cast(x, dtype, n, bias, fmt, y, (hipStream_t)stream));
+  return hip_status(fp8lin::launch_cast(x, dtype, n, bias, fmt, y, nullptr, (hipStream_t)stream));
+}
+
+int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* bias,
+                        fp8_format_t fmt, uint8_t* y, float* x_amax, void* stream) {
+  if (n < 0) return FP8_ERR_SIZE;
+  if (bad_dtype(dtype)) return FP8_ERR_DTYPE;
+  if (bad_format(fmt)) return FP8_ERR_FORMAT;
+  if (!x_amax) return FP8_ERR_NULL;
+  if (((uintptr_t)x_amax & 3u) != 0) return FP8_ERR_ALIGN;
+  if (n > 0) {
+    if (!x || !y || !bias) return FP8_ERR_NULL;
+    if (misaligned(x) || misaligned(y)) return FP8_ERR_ALIGN;
+  }
+  if (int s = device_ok()) return s;
+  return hip_status(fp8lin::launch_cast(x, dtype, n, bias, fmt, y,
+                                        reinterpret_cast<uint32_t*>(x_amax), (hipStream_t)stream));
 }
 
 }  // extern "C"

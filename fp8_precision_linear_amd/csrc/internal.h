@@ -12,8 +12,9 @@ namespace fp8lin {
 hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t stream);
 hipError_t launch_bias(const float* amax, int fmt, int32_t margin, int32_t* bias,
                        hipStream_t stream);
+// amax: optional; when given, cleared, then max |x| (fp32 bits) folded in.
 hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias, int fmt,
-                       uint8_t* y, hipStream_t stream);
+                       uint8_t* y, uint32_t* amax, hipStream_t stream);
 // *p = 0 (one lane).
 hipError_t launch_clear_u32(uint32_t* p, hipStream_t stream);
 

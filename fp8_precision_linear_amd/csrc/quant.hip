@@ -15,6 +15,8 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace fp8lin {
@@ -88,6 +90,24 @@ __device__ __forceinline__ void block_max_to(uint32_t v, uint32_t* out) {
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) m = max(m, part[w]);
     atomicMax(out, m);
+  }
+}
+
+// The same, for grids of many blocks: the atomic is skipped when the stored
+// value is already at least as large, so that few of the blocks touch the one
+// address (atomics on it cost more than the loads: reading the value when the
+// block starts instead, which lets more blocks through, was slower).
+__device__ __forceinline__ void block_max_fold(uint32_t v, uint32_t* out) {
+  __shared__ uint32_t part[kWaves];
+  v = wave_max_u32(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) part[wave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = part[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) m = max(m, part[w]);
+    if (m > __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(out, m);
   }
 }
 
@@ -364,13 +384,15 @@ __device__ __forceinline__ uint4 cast_unit_sw(uint4 lo, uint4 hi, int32_t b) {
 // on the bias, so they are issued before the bias load has returned; the
 // choice between the hardware conversion (bias in [kHwBiasMin, kHwBiasMax],
 // E4M3 and E5M2) and fp8_code is a wave-uniform branch per unit after them.
-template <int FMT, bool NT>
-__device__ __forceinline__ void cast_bf16_body(const uint4* __restrict__ x, int64_t nunit,
-                                               const int32_t* __restrict__ bias,
-                                               uint4* __restrict__ y) {
+// With AMAX the lane's largest input magnitude (bf16 bits) is returned too.
+template <int FMT, bool NT, bool AMAX>
+__device__ __forceinline__ uint32_t cast_bf16_body(const uint4* __restrict__ x, int64_t nunit,
+                                                   const int32_t* __restrict__ bias,
+                                                   uint4* __restrict__ y) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (i >= nunit) return;
+  if (i >= nunit) return 0u;
+  u16x2 acc = {0, 0};
   uint4 lo = load16<NT>(&x[2 * i]), hi = load16<NT>(&x[2 * i + 1]);
   const int32_t b = *bias;
   const bool hw = kHwConvert<FMT> && b >= kHwBiasMin && b <= kHwBiasMax;
@@ -390,24 +412,31 @@ __device__ __forceinline__ void cast_bf16_body(const uint4* __restrict__ x, int6
     else
       o = cast_unit_sw<FMT>(lo, hi, b);
     store16<false>(o, &y[i]);
+    if constexpr (AMAX) acc = vmax_bf16(vmax_bf16(acc, lo), hi);
     if (next >= nunit) break;
     i = next;
     lo = nlo;
     hi = nhi;
   }
+  return max((uint32_t)acc.x, (uint32_t)acc.y);
 }
 
-template <int FMT, bool NT>
+// AMAX: also fold max |x| (fp32 bits) into *amax, once per block.
+template <int FMT, bool NT, bool AMAX>
 __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const uint4* __restrict__ x,
                                                              int64_t nunit,
                                                              const int32_t* __restrict__ bias,
                                                              uint4* __restrict__ y,
                                                              const uint16_t* __restrict__ tail_x,
                                                              uint8_t* __restrict__ tail_y,
-                                                             int ntail) {
-  cast_bf16_body<FMT, NT>(x, nunit, bias, y);
-  if (blockIdx.x == 0 && (int)threadIdx.x < ntail)
-    tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>((uint32_t)tail_x[threadIdx.x] << 16, *bias);
+                                                             int ntail, uint32_t* amax) {
+  uint32_t m = cast_bf16_body<FMT, NT, AMAX>(x, nunit, bias, y);
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) {
+    const uint32_t w = tail_x[threadIdx.x];
+    tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>(w << 16, *bias);
+    m = max(m, w & 0x7FFFu);
+  }
+  if constexpr (AMAX) block_max_fold(m << 16, amax);
 }
 
 // fp32 input: a wave takes chunks of kF32Chunk consecutive elements; load k
@@ -433,14 +462,14 @@ __device__ __forceinline__ uint32_t cast4_f32(uint4 v, bool hw, int32_t b, uint3
   return pack4_f32<FMT>(v, b);
 }
 
-template <int FMT, bool NT>
+template <int FMT, bool NT, bool AMAX>
 __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restrict__ x,
                                                             int64_t nchunk,
                                                             const int32_t* __restrict__ bias,
                                                             uint32_t* __restrict__ y,
                                                             const uint32_t* __restrict__ tail_x,
                                                             uint8_t* __restrict__ tail_y,
-                                                            int ntail) {
+                                                            int ntail, uint32_t* amax) {
   const int32_t b = *bias;
   const bool hw = kHwConvert<FMT> && b >= kHwBiasMin && b <= kHwBiasMax;
   uint32_t bound = 0;
@@ -448,17 +477,24 @@ __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restr
   const float scale = __builtin_ldexpf(1.0f, hw ? -b : 0);
   const int lane = threadIdx.x & 63;
   const int64_t wstride = (int64_t)gridDim.x * (kThreads / 64);
+  uint32_t m = 0;
   for (int64_t w = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); w < nchunk; w += wstride) {
     const int64_t q = w * (kF32Chunk / 4);  // the chunk's first 16-byte group
     uint4 v[kF32Loads];
 #pragma unroll
     for (int k = 0; k < kF32Loads; ++k) v[k] = load16<NT>(&x[q + 64 * k + lane]);
 #pragma unroll
-    for (int k = 0; k < kF32Loads; ++k) y[q + 64 * k + lane] = cast4_f32<FMT>(v[k], hw, b, bound, scale);
+    for (int k = 0; k < kF32Loads; ++k) {
+      y[q + 64 * k + lane] = cast4_f32<FMT>(v[k], hw, b, bound, scale);
+      if constexpr (AMAX) m = vmax_f32(m, v[k]);
+    }
   }
   if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < ntail; i += kThreads)
+    for (int i = threadIdx.x; i < ntail; i += kThreads) {
       tail_y[i] = (uint8_t)fp8_code<FMT>(tail_x[i], b);
+      m = max(m, tail_x[i] & 0x7FFFFFFFu);
+    }
+  if constexpr (AMAX) block_max_fold(m, amax);
 }
 
 // Grid size: `per_lane` units of work per lane, between 1 and `cap` blocks.
@@ -474,6 +510,20 @@ int stream_blocks(int64_t units, int64_t per_lane, int64_t cap) {
 static bool streams(const char* var) {
   const char* h = std::getenv(var);
   return !(h && std::strcmp(h, "cached") == 0);
+}
+
+// Units of work per lane of the cast that also folds its input's amax: each
+// block ends with (at most) one atomic on the single amax word, so this
+// variant runs fewer, longer-lived blocks than the plain cast (the body loops,
+// loading the next unit during the current one).  Measured on MI355X, bias +
+// cast-with-amax against amax -> bias -> cast, 128 / 448 MiB bf16: 80 / 150 us
+// with 1 unit per lane, 57 / 142 with 16, against 65 / 187; 16 to 32 were
+// within noise of each other.  FP8LIN_CAST_AMAX_UNITS overrides it (tuning).
+constexpr int kCastAmaxUnitsPerLane = 16;
+static int cast_amax_units() {
+  const char* v = std::getenv("FP8LIN_CAST_AMAX_UNITS");
+  const int u = v ? std::atoi(v) : kCastAmaxUnitsPerLane;
+  return u < 1 ? 1 : (u > 64 ? 64 : u);
 }
 
 hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t stream) {
@@ -514,26 +564,29 @@ hipError_t launch_bias(const float* amax, int fmt, int32_t margin, int32_t* bias
   return hipGetLastError();
 }
 
-// FP8LIN_CAST(format, non-temporal) for each format the cast produces.
-#define FP8LIN_CAST_FORMATS(fmt, nt)                                      \
-  switch (fmt) {                                                          \
-    case FP8_E4M3:                                                        \
-      if (nt) FP8LIN_CAST(FP8_E4M3, true);                                \
-      else FP8LIN_CAST(FP8_E4M3, false);                                  \
-      break;                                                              \
-    case FP8_E5M2:                                                        \
-      if (nt) FP8LIN_CAST(FP8_E5M2, true);                                \
-      else FP8LIN_CAST(FP8_E5M2, false);                                  \
-      break;                                                              \
-    default:                                                              \
-      if (nt) FP8LIN_CAST(FP8_E3M4, true);                                \
-      else FP8LIN_CAST(FP8_E3M4, false);                                  \
-      break;                                                              \
+// Calls fn(format, non-temporal, amax) with each as a std::integral_constant,
+// so that one launch statement covers every kernel variant.
+template <typename Fn>
+void with_cast_variant(int fmt, bool nt, bool amax, Fn&& fn) {
+  auto by_amax = [&](auto f, auto n) {
+    if (amax) fn(f, n, std::true_type{});
+    else fn(f, n, std::false_type{});
+  };
+  auto by_nt = [&](auto f) {
+    if (nt) by_amax(f, std::true_type{});
+    else by_amax(f, std::false_type{});
+  };
+  switch (fmt) {
+    case FP8_E4M3: by_nt(std::integral_constant<int, FP8_E4M3>{}); break;
+    case FP8_E5M2: by_nt(std::integral_constant<int, FP8_E5M2>{}); break;
+    default: by_nt(std::integral_constant<int, FP8_E3M4>{}); break;
   }
+}
 
 hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias, int fmt,
-                       uint8_t* y, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
+                       uint8_t* y, uint32_t* amax, hipStream_t stream) {
+  if (amax) hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, amax);
+  if (n <= 0) return hipGetLastError();
   const bool nt = streams("FP8LIN_CAST_HINT");
   if (dtype == FP8_IN_BF16) {
     // 16-element units, one per lane; the last n % 16 elements by block 0
@@ -543,12 +596,12 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias,
     uint4* yv = reinterpret_cast<uint4*>(y);
     const uint16_t* tail_x = static_cast<const uint16_t*>(x) + nunit * 16;
     const uint4* xv = static_cast<const uint4*>(x);
-    const dim3 grid(stream_blocks(nunit, kCastUnitsPerLane, kCastMaxBlocks));
-#define FP8LIN_CAST(F, NT)                                                                    \
-  hipLaunchKernelGGL((cast_bf16_kernel<F, NT>), grid, dim3(kThreads), 0, stream, xv, nunit, \
-                     bias, yv, tail_x, tail_y, ntail)
-    FP8LIN_CAST_FORMATS(fmt, nt);
-#undef FP8LIN_CAST
+    const dim3 grid(stream_blocks(nunit, amax ? cast_amax_units() : kCastUnitsPerLane, kCastMaxBlocks));
+    with_cast_variant(fmt, nt, amax != nullptr, [&](auto f, auto t, auto a) {
+      hipLaunchKernelGGL((cast_bf16_kernel<decltype(f)::value, decltype(t)::value, decltype(a)::value>),
+                         grid, dim3(kThreads), 0, stream, xv, nunit, bias, yv, tail_x, tail_y, ntail,
+                         amax);
+    });
   } else {
     const int64_t nchunk = n / kF32Chunk;
     const int nrest = (int)(n - nchunk * kF32Chunk);
@@ -556,17 +609,18 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias,
     uint8_t* rest_y = y + nchunk * kF32Chunk;
     uint32_t* yw = reinterpret_cast<uint32_t*>(y);
     const uint4* xv = static_cast<const uint4*>(x);
-    // one chunk per wave, four waves per block, at least one block (the rest)
-    const int64_t want = (nchunk + kThreads / 64 - 1) / (kThreads / 64);
+    // one chunk per wave (cast_amax_units() with the amax), four waves per
+    // block, at least one block (the rest)
+    const int64_t per_block = (int64_t)(kThreads / 64) * (amax ? cast_amax_units() : 1);
+    const int64_t want = (nchunk + per_block - 1) / per_block;
     const dim3 grid((uint32_t)(want < 1 ? 1 : (want > kCastMaxBlocks ? kCastMaxBlocks : want)));
-#define FP8LIN_CAST(F, NT)                                                                    \
-  hipLaunchKernelGGL((cast_f32_kernel<F, NT>), grid, dim3(kThreads), 0, stream, xv, nchunk, \
-                     bias, yw, rest_x, rest_y, nrest)
-    FP8LIN_CAST_FORMATS(fmt, nt);
-#undef FP8LIN_CAST
+    with_cast_variant(fmt, nt, amax != nullptr, [&](auto f, auto t, auto a) {
+      hipLaunchKernelGGL((cast_f32_kernel<decltype(f)::value, decltype(t)::value, decltype(a)::value>),
+                         grid, dim3(kThreads), 0, stream, xv, nchunk, bias, yw, rest_x, rest_y, nrest,
+                         amax);
+    });
   }
   return hipGetLastError();
 }
-#undef FP8LIN_CAST_FORMATS
 
 }  // namespace fp8lin

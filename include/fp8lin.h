@@ -111,6 +111,21 @@ int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* b
                    fp8_format_t fmt, uint8_t* y, void* stream);
 
 /*
+ * fp8_scale_cast that also returns max |x| of its own input, folded in the
+ * same pass ("Proposed method", bullet 1, fused with the cast): with delayed
+ * scaling -- this call's bias computed from the amax that the previous call
+ * on the previous step's tensor returned -- every quantisation reads its
+ * input once (3 bytes per bf16 element instead of amax + cast's 5).
+ *   x_amax  device, one float, 4-byte aligned, written: bit-identical to
+ *           fp8_amax over x (0 for n == 0).
+ * The codes are those of fp8_scale_cast.  Launches a one-lane clear of
+ * x_amax, then the cast.  Returns FP8_ERR_NULL / FP8_ERR_ALIGN for a null or
+ * misaligned x_amax, otherwise as fp8_scale_cast.
+ */
+int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* bias,
+                        fp8_format_t fmt, uint8_t* y, float* x_amax, void* stream);
+
+/*
  * The three FP8 x FP8 products with fp32 accumulation, unscaled after the
  * matmul ("Proposed method", bullets 3 and 5).  Each output is overwritten
  * (no accumulation into it).  Operands may be E4M3 or E5M2 in any pairing

@@ -31,7 +31,7 @@ def status(code):
 
 def test_every_declared_function_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), n
         assert n in fl.SIGNATURES, n
@@ -174,4 +174,25 @@ def test_swiglu_without_a_device_reports_no_device():
     assert L.fp8_swiglu_fwd(A16, 4, 4, A32, None, None) == status("FP8_ERR_DEVICE")
     assert L.fp8_swiglu_bwd(A16, A48, 4, 4, A32, A16, None) == status("FP8_ERR_DEVICE")
     assert L.fp8_swiglu_fwd(None, 0, 4, None, A16, None) == status("FP8_ERR_DEVICE")   # the amax clear
+
+
+def test_scale_cast_amax_argument_checks():
+    f = L.fp8_scale_cast_amax
+    assert f(A16, 0, -5, A32, 0, A48, A16, None) == status("FP8_ERR_SIZE")
+    assert f(A16, 3, 5, A32, 0, A48, A16, None) == status("FP8_ERR_DTYPE")
+    assert f(A16, 0, 5, A32, 3, A48, A16, None) == status("FP8_ERR_FORMAT")
+    assert f(A16, 0, 5, A32, 0, A48, None, None) == status("FP8_ERR_NULL")
+    assert f(A16, 0, 5, A32, 0, A48, P(18), None) == status("FP8_ERR_ALIGN")
+    assert f(None, 0, 5, A32, 0, A48, A16, None) == status("FP8_ERR_NULL")
+    assert f(A16, 0, 5, None, 0, A48, A16, None) == status("FP8_ERR_NULL")
+    assert f(A16, 0, 5, A32, 0, None, A16, None) == status("FP8_ERR_NULL")
+    assert f(MIS, 0, 5, A32, 0, A48, A16, None) == status("FP8_ERR_ALIGN")
+    assert f(A16, 1, 5, A32, 0, MIS, A16, None) == status("FP8_ERR_ALIGN")
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
+def test_scale_cast_amax_without_a_device_reports_no_device():
+    # even n == 0 clears the amax output, so it needs the device
+    assert L.fp8_scale_cast_amax(None, 0, 0, None, 0, None, A16, None) == status("FP8_ERR_DEVICE")
+    assert L.fp8_scale_cast_amax(A16, 0, 5, A32, 2, A48, A16, None) == status("FP8_ERR_DEVICE")
 

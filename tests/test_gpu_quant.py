@@ -270,3 +270,61 @@ def test_fixed_and_delayed_scaling(fl):
         fresh = fl.compute_bias(fl.amax(bf16_dev(new)), fmt, 0)
         got = fl.scale_cast(bf16_dev(new), fresh, fmt).cpu().numpy()
         assert np.count_nonzero((got & 0x7F) == top) <= 2           # only the largest values reach the top code
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_cast_with_fused_amax(fl, dtype):
+    """fp8_scale_cast_amax: the codes of fp8_scale_cast and max |x| of the
+    input from the same pass, both bit-exact, over ragged sizes, every format,
+    biases on both conversion paths, and non-finite values anywhere."""
+    rng = np.random.default_rng(17)
+    for n in (1, 15, 16, 17, 1023, 1024, 1025, 4096 * 3 + 5, 300_001):
+        v = (rng.standard_normal(n) * 40).astype(np.float32)
+        if dtype == "bf16":
+            words = synth.bf16_words(synth.to_bf16(v)).copy()
+            specials = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC1], dtype=np.uint16)
+            x = bf16_dev
+        else:
+            words = v.view(np.uint32).copy()
+            specials = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00001], dtype=np.uint32)
+            x = f32_dev
+        for with_special in (False, True):
+            w = words.copy()
+            if with_special:
+                w[rng.integers(0, n)] = specials[rng.integers(0, specials.size)]
+            xd = x(w)
+            for fmt in ALL_FMTS:
+                for b in (-130, 0, 5, 127):
+                    say("cast+amax", dtype, n, "special", with_special, "fmt", fmt, "bias", b)
+                    am = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+                    got = fl.scale_cast(xd, i32_dev(b), fmt, amax=am).cpu().numpy()
+                    assert np.array_equal(got, oracle.scale_cast(w, b, fmt)), (n, fmt, b)
+                    assert int(words_of(am)[0]) == oracle.amax_bits(w), (n, fmt, b)
+    # n == 0: the amax output is cleared, nothing else happens
+    am = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    assert fl.lib.fp8_scale_cast_amax(None, 0, 0, None, 0, None, am.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert am.item() == 0.0
+
+
+def test_delayed_scaling_with_the_fused_cast(fl):
+    """Delayed scaling: step t casts with the bias computed from the amax the
+    step t-1 cast returned (bias 0 at t = 0), and returns its own amax; every
+    step's codes and amax equal the oracle's on that schedule."""
+    rng = np.random.default_rng(23)
+    scales = [1.0, 3.0, 0.25, 40.0, 40.0, 1e-3]
+    bias = i32_dev(0)
+    prev_bits = None
+    for t, sc in enumerate(scales):
+        v = (rng.standard_normal(65536 + 7) * sc).astype(np.float32)
+        words = synth.bf16_words(synth.to_bf16(v)).copy()
+        say("delayed scaling step", t)
+        am = torch.empty(1, dtype=torch.float32, device="cuda")
+        codes = fl.scale_cast(bf16_dev(words), bias, E4M3, amax=am).cpu().numpy()
+        b_ref = 0 if prev_bits is None else oracle.compute_bias(prev_bits, E4M3, 0)
+        assert int(bias.item()) == b_ref, t
+        assert np.array_equal(codes, oracle.scale_cast(words, b_ref, E4M3)), t
+        prev_bits = oracle.amax_bits(words)
+        assert int(words_of(am)[0]) == prev_bits, t
+        bias = fl.compute_bias(am, E4M3, 0)
+
