@@ -26,6 +26,11 @@
  *    A launch failure returns FP8_ERR_HIP; a fault during execution surfaces at
  *    the caller's next synchronisation.
  *  - Calls are thread-safe.  Calls that write the same output must not overlap.
+ *  - Tuning only (read at each call, never needed for correct results):
+ *    FP8LIN_GEMM_TILE=128|256 forces the products' tile, FP8LIN_EXACT_MFMA=
+ *    f16|bf16 the 16-bit MFMA of the exact arithmetic, FP8LIN_AMAX_HINT /
+ *    FP8LIN_CAST_HINT=cached ordinary instead of streaming loads, and
+ *    FP8LIN_CAST_AMAX_UNITS=n the units per lane of fp8_scale_cast_amax.
  */
 #ifndef FP8LIN_H
 #define FP8LIN_H
