@@ -4,7 +4,10 @@
 // point", review page, "Proposed method", bullets 1-4: a per-tensor maximum
 // absolute value, a power-of-two bias from log2(format max / amax) with a
 // margin, and a cast of the scaled tensor to E4M3 (weights, activations) or
-// E5M2 (gradients).
+// E5M2 (gradients); also E3M4, the third format of "Efficient post-training
+// quantization with FP8 formats" (summary page), cast only.  Inputs are bf16
+// or fp32.  The cast can also fold its own input's amax (for delayed scaling,
+// where the bias comes from the previous step's amax).
 //
 // All three are HBM-streaming kernels: 16-byte loads and stores per lane,
 // grid-stride loops, several loads in flight per lane.  amax reduces on the
