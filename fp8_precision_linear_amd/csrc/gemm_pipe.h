@@ -598,17 +598,6 @@ hipError_t launch_general(const GemmProblem& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-// Fraction of the chip's workgroup slots doing useful work over all waves of
-// tiles, weighted by how much of each tile is inside the matrix.
-inline double tile_efficiency(int m, int n, int bm, int bn) {
-  const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn, tiles = tm * tn;
-  const int64_t slots = 256;
-  const int64_t waves = (tiles + slots - 1) / slots;
-  const double fill = (double)tiles / (double)(waves * slots);
-  const double inside = ((double)m * n) / ((double)tm * bm * tn * bn);
-  return fill * inside;
-}
-
 // FP8LIN_GEMM_TILE=128 or 256 pins the pipelined kernel's tile (tuning and
 // tests); otherwise it is chosen from the shape.
 inline int forced_tile() {
@@ -632,19 +621,89 @@ bool pipe_ok(const GemmProblem& p) {
   return true;
 }
 
+// How an output is cut into launches.  The 256x256 tile does twice the MFMA
+// work per byte of LDS and global traffic of the 128x128 one, but a launch
+// whose tile count is not a multiple of the chip's 256 workgroup slots runs
+// its last wave of tiles part-empty.  Candidates: everything in 256x256
+// tiles; everything in 128x128 tiles; or a leading block of whole rows
+// (split_m) or columns (split_n), a multiple of 256, in 256x256 tiles and the
+// rest in 128x128 tiles, as two launches.  The cost is the number of waves of
+// tiles, a 128x128 wave counting a third of a 256x256 one (a quarter of the
+// work at ~75% of the rate).
+struct TilePlan {
+  int tile;     // 256 or 128: the tile of the whole output, when not split
+  int split_m;  // > 0: rows [0, split_m) in 256x256 tiles, the rest in 128x128
+  int split_n;  // > 0: columns [0, split_n) likewise
+};
+
+inline double plan_waves(int64_t m, int64_t n, int bm) {
+  const int64_t tiles = ((m + bm - 1) / bm) * ((n + bm - 1) / bm);
+  const double waves = (double)((tiles + 255) / 256);
+  return bm == 256 ? waves : waves / 3.0;
+}
+
+// For each whole number w of 256x256 waves below the unsplit count, the head
+// is the most whole tile-rows (or tile-columns) that fit in w waves.  Past 64
+// waves the last wave's idle slots are under 2% of the work: no split.
+inline TilePlan plan_tiles(int m, int n) {
+  TilePlan best{256, 0, 0};
+  double cost = plan_waves(m, n, 256);
+  const double c128 = plan_waves(m, n, 128);
+  if (c128 < cost) {
+    best = TilePlan{128, 0, 0};
+    cost = c128;
+  }
+  const int64_t tm = (m + 255) / 256, tn = (n + 255) / 256, waves = (tm * tn + 255) / 256;
+  if (waves > 64) return best;
+  for (int64_t w = 1; w < waves; ++w) {
+    const int64_t rows = w * 256 / tn, cols = w * 256 / tm;  // whole tile-rows / -columns
+    if (rows >= 1 && rows < tm) {
+      const double c = plan_waves(rows * 256, n, 256) + plan_waves(m - rows * 256, n, 128);
+      if (c < cost - 1e-9) {
+        best = TilePlan{256, (int)(rows * 256), 0};
+        cost = c;
+      }
+    }
+    if (cols >= 1 && cols < tn) {
+      const double c = plan_waves(m, cols * 256, 256) + plan_waves(m, n - cols * 256, 128);
+      if (c < cost - 1e-9) {
+        best = TilePlan{256, 0, (int)(cols * 256)};
+        cost = c;
+      }
+    }
+  }
+  return best;
+}
+
 template <bool AK, bool BK, int MATH>
 hipError_t launch_math(const GemmProblem& p, hipStream_t stream) {
   if (!pipe_ok<AK, BK>(p))
     return launch_general<AK, BK, MATH == kMathNativeFp8 ? kMathNativeFp8 : kMathExact>(p, stream);
-  // The 256x256 tile does twice the MFMA work per byte of LDS and global
-  // traffic of the 128x128 one; prefer it unless it leaves most CUs idle.
-  int tile = forced_tile();
-  if (tile == 0) {
-    const double e256 = tile_efficiency(p.m, p.n, 256, 256);
-    const double e128 = tile_efficiency(p.m, p.n, 128, 128) * 0.75;
-    tile = e256 >= e128 ? 256 : 128;
+  const int forced = forced_tile();
+  const TilePlan plan = forced ? TilePlan{forced, 0, 0} : plan_tiles(p.m, p.n);
+  if (plan.split_m > 0 || plan.split_n > 0) {
+    // Two launches on the stream, the second on the remaining rows or
+    // columns: the same problem with its operand and output pointers moved
+    // on (offsets are multiples of 256 elements or rows, so every alignment
+    // pipe_ok checked still holds, as does m % 16 and n % 16).
+    GemmProblem head = p, rest = p;
+    if (plan.split_m > 0) {
+      const int64_t s = plan.split_m;
+      head.m = plan.split_m;
+      rest.m = p.m - plan.split_m;
+      rest.a = AK ? p.a + s * p.lda : p.a + s;
+      rest.c = p.c + s * p.ldc;
+    } else {
+      const int64_t s = plan.split_n;
+      head.n = plan.split_n;
+      rest.n = p.n - plan.split_n;
+      rest.b = BK ? p.b + s * p.ldb : p.b + s;
+      rest.c = p.c + s;
+    }
+    if (hipError_t e = launch_pp<AK, BK, MATH>(head, stream)) return e;
+    return launch_quad<AK, BK, MATH>(rest, stream);
   }
-  if (tile == 256) return launch_pp<AK, BK, MATH>(p, stream);
+  if (plan.tile == 256) return launch_pp<AK, BK, MATH>(p, stream);
   return launch_quad<AK, BK, MATH>(p, stream);
 }
 

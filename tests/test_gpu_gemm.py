@@ -251,3 +251,46 @@ def test_epilogue_amax_drives_the_next_quantisation(fl):
         b = oracle.compute_bias(oracle.amax_bits(words), fmt, 1)
         assert int(bias.cpu().item()) == b
         assert np.array_equal(codes, oracle.scale_cast(words, b, fmt))
+
+
+# Output shapes whose 256x256 tiling leaves a part-empty last wave, so the
+# launch takes a block of whole waves in 256x256 tiles and the rest of the
+# rows (row split) or columns (column split) in 128x128 tiles; the sampled
+# outputs include every row / column next to the split and the last ones.
+SPLIT_SHAPES = [  # (product, output rows, output cols, contraction, expected split)
+    ("fwd", 4096, 5120, 128, "columns at 4096"),
+    ("dgrad", 4096, 5120, 64, "columns at 4096"),
+    ("wgrad", 13824, 5120, 64, "rows at 13056"),
+    ("fwd", 4096, 22016, 64, "columns at 20480"),
+    ("dgrad", 4096, 13824, 64, "rows at 3584"),
+]
+
+
+@pytest.mark.parametrize("which,R,C,Kc,split", SPLIT_SHAPES)
+def test_two_launch_split_of_the_output(fl, which, R, C, Kc, split):
+    rng = np.random.default_rng(R + C + Kc)
+    fa, fb = (E4M3, E4M3) if which == "fwd" else (E5M2, E4M3)
+    # problem sizes (M, N, K) of each product for an R x C output
+    M, N, K = {"fwd": (R, C, Kc), "dgrad": (R, Kc, C), "wgrad": (Kc, R, C)}[which]
+    a8, b8 = operands(rng, which, M, N, K, fa, fb)
+    say("split launch", which, R, C, Kc, split)
+    am = torch.empty(1, dtype=torch.float32, device="cuda")
+    op = {"fwd": fl.OP_FWD, "dgrad": fl.OP_DGRAD, "wgrad": fl.OP_WGRAD}[which]
+    out = fl.scaled_gemm(op, u8_dev(a8), fa, i32_dev(2), u8_dev(b8), fb, i32_dev(-1), amax=am)
+    got = out.cpu().numpy()
+    at = {"fwd": oracle.gemm_fwd_at, "dgrad": oracle.gemm_dgrad_at, "wgrad": oracle.gemm_wgrad_at}[which]
+    b_at = int(split.split()[-1])
+    rows = np.concatenate([rng.integers(0, R, 3000), np.repeat(np.arange(R - 3, R), 40)])
+    cols = np.concatenate([rng.integers(0, C, 3000), rng.integers(0, C, 120)])
+    if split.startswith("rows"):
+        band = np.repeat(np.arange(b_at - 8, b_at + 8), 64)
+        rows = np.concatenate([rows, band])
+        cols = np.concatenate([cols, rng.integers(0, C, band.size)])
+    else:
+        band = np.repeat(np.arange(b_at - 8, b_at + 8), 64)
+        cols = np.concatenate([cols, band])
+        rows = np.concatenate([rows, rng.integers(0, R, band.size)])
+    ref, bound = at(a8, fa, 2, b8, fb, -1, rows, cols)
+    check_gemm(got[rows, cols], ref, bound, f"split {which} {R}x{C} ({split})")
+    # the epilogue amax covers both launches
+    assert int(am.view(torch.int32).item()) & 0xFFFFFFFF == int((got.view(np.uint32) & 0x7FFFFFFF).max())
