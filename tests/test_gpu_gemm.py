@@ -266,8 +266,9 @@ SPLIT_SHAPES = [  # (product, output rows, output cols, contraction, expected sp
 ]
 
 
+@pytest.mark.parametrize("math", ["exact", "native"])
 @pytest.mark.parametrize("which,R,C,Kc,split", SPLIT_SHAPES)
-def test_two_launch_split_of_the_output(fl, which, R, C, Kc, split):
+def test_two_launch_split_of_the_output(fl, which, R, C, Kc, split, math):
     rng = np.random.default_rng(R + C + Kc)
     fa, fb = (E4M3, E4M3) if which == "fwd" else (E5M2, E4M3)
     # problem sizes (M, N, K) of each product for an R x C output
@@ -276,7 +277,8 @@ def test_two_launch_split_of_the_output(fl, which, R, C, Kc, split):
     say("split launch", which, R, C, Kc, split)
     am = torch.empty(1, dtype=torch.float32, device="cuda")
     op = {"fwd": fl.OP_FWD, "dgrad": fl.OP_DGRAD, "wgrad": fl.OP_WGRAD}[which]
-    out = fl.scaled_gemm(op, u8_dev(a8), fa, i32_dev(2), u8_dev(b8), fb, i32_dev(-1), amax=am)
+    mth = fl.MATH_EXACT if math == "exact" else fl.MATH_NATIVE_FP8
+    out = fl.scaled_gemm(op, u8_dev(a8), fa, i32_dev(2), u8_dev(b8), fb, i32_dev(-1), math=mth, amax=am)
     got = out.cpu().numpy()
     at = {"fwd": oracle.gemm_fwd_at, "dgrad": oracle.gemm_dgrad_at, "wgrad": oracle.gemm_wgrad_at}[which]
     b_at = int(split.split()[-1])
@@ -291,6 +293,8 @@ def test_two_launch_split_of_the_output(fl, which, R, C, Kc, split):
         cols = np.concatenate([cols, band])
         rows = np.concatenate([rows, rng.integers(0, R, band.size)])
     ref, bound = at(a8, fa, 2, b8, fb, -1, rows, cols)
-    check_gemm(got[rows, cols], ref, bound, f"split {which} {R}x{C} ({split})")
+    # the native FP8 MFMA's own bound (test_native_fp8_math_within_its_bound)
+    rel = 1e-5 if math == "exact" else 2.0 ** -7 + (Kc / 64 + 1) * 2.0 ** -24
+    check_gemm(got[rows, cols], ref, bound, f"split {which} {R}x{C} ({split}) {math}", rel=rel)
     # the epilogue amax covers both launches
     assert int(am.view(torch.int32).item()) & 0xFFFFFFFF == int((got.view(np.uint32) & 0x7FFFFFFF).max())
