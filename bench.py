@@ -539,12 +539,39 @@ def bench_mlp(args, m):
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
+    events, cfg.events = cfg.events, None
+    # the same step captured once into a HIP graph and replayed K times (no
+    # host-side launch or autograd work per step); fresh leaf weights, so that
+    # their gradient nodes are made on the warm-up stream, not the default one
+    gw1 = w1.detach().clone().requires_grad_()
+    gw2 = w2.detach().clone().requires_grad_()
+
+    def gstep():
+        gw1.grad = None
+        gw2.grad = None
+        mlp.FP8MLPFunction.apply(x, gw1, gw2, cfg).backward(g)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gstep()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        gstep()
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    del graph, gw1, gw2
     gc.enable()
     K = args.steps
     by = {}
-    for kind, name, e0, e1 in cfg.events:
+    for kind, name, e0, e1 in events:
         by[(kind, name)] = by.get((kind, name), 0.0) + e0.elapsed_time(e1) / K
-    cfg.events = None
     T, d, f = m.tokens, m.d, m.f
     gemm_flops = {"fwd h": 2 * T * 2 * f * d, "fwd y": 2 * T * d * f, "dgrad da": 2 * T * d * f,
                   "wgrad dw2": 2 * T * d * f, "dgrad dx": 2 * T * 2 * f * d, "wgrad dw1": 2 * T * 2 * f * d}
@@ -617,6 +644,10 @@ def bench_mlp(args, m):
                      for n, b in quant_bytes.items()},
         "step_breakdown_ms": {k: round(sum(v for (kk, _), v in by.items() if kk == k), 4)
                               for k in ("gemm", "quant", "swiglu")},
+        "hip_graph": {"ms_per_step": round(graph_ms, 4),
+                      "value": round(m.flops() / (graph_ms * 1e-3) / 1e12, 2),
+                      "method": "the same forward + backward captured once with torch.cuda.graph, "
+                                f"{K} replays timed"},
         "bias_history": hist,
     }
     if not args.no_cpu_baseline:

@@ -316,3 +316,57 @@ def test_bias_log_over_training_steps(fl):
     for step in range(8):
         assert hist["w1"][step] == oracle.compute_bias(oracle.amax_bits(w1_words[step]), E4M3, 0)
     print("bias history", hist)
+
+
+def test_mlp_step_replays_in_a_hip_graph(fl):
+    """The chained MLP's forward + backward captured once into a HIP graph
+    (torch.cuda.CUDAGraph) and replayed: every replay, with eager work and
+    synchronisations between replays and the inputs changed in place, equals
+    the eager step bit for bit (the library's clears are kernels, not memsets,
+    and nothing in the step synchronises with the host)."""
+    from fp8_precision_linear_amd import mlp
+    t = small_mlp(256, 256, 192, 8)
+    x = t["X"].cuda()
+    w1 = t["W1"].cuda().requires_grad_()
+    w2 = t["W2"].cuda().requires_grad_()
+    g = t["G"].cuda()
+    cfg = mlp.MLPConfig()
+
+    def step():
+        w1.grad = None
+        w2.grad = None
+        y = mlp.FP8MLPFunction.apply(x, w1, w2, cfg)
+        y.backward(g)
+        return y
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    say("mlp graph capture")
+    with torch.cuda.graph(graph, stream=side):
+        y_g = step()
+    dw1_g, dw2_g = w1.grad, w2.grad
+    rng = np.random.default_rng(9)
+    for r in range(4):
+        # new inputs, in place (the graph reads these buffers)
+        with torch.no_grad():
+            x.copy_(synth.to_bf16((rng.standard_normal(tuple(x.shape)) * (1 + r)).astype(np.float32)).cuda())
+            w1.mul_(0.9)
+            g.mul_(2.0)
+        say("mlp graph replay", r)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = (y_g.clone(), dw1_g.clone(), dw2_g.clone())
+        # eager step on the same inputs, with other eager work in between (on
+        # the warm-up stream, where the weights' gradient nodes were made)
+        _ = torch.randn(1000, device="cuda").sum()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            y_e = step()
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], y_e.detach()), r
+        assert torch.equal(got[1], w1.grad) and torch.equal(got[2], w2.grad), r
