@@ -40,6 +40,8 @@ int gemm_checks(const uint8_t* a, int fa, const int32_t* ba, const uint8_t* b, i
                 const int32_t* bb, int64_t M, int64_t N, int64_t K, const float* out,
                 int64_t a_elems, int64_t b_elems) {
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8_ERR_SIZE;
+  // the launch grid (at most one block per 128 x 128 output tile) is 32-bit
+  if (((M + 127) / 128) * ((N + 127) / 128) > (int64_t)0x7FFFFFFF) return FP8_ERR_SIZE;
   if (bad_operand_format(fa) || bad_operand_format(fb)) return FP8_ERR_FORMAT;
   if (M == 0 || N == 0) return FP8_OK;
   if (!out || !ba || !bb) return FP8_ERR_NULL;

@@ -136,7 +136,9 @@ int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32
  * (no accumulation into it).  Operands may be E4M3 or E5M2 in any pairing
  * (E3M4: FP8_ERR_FORMAT).
  * All pointers are device memory; byte operands and outputs must be 16-byte
- * aligned.  M, N, K >= 0 (K == 0 writes zeros; M == 0 or N == 0 is a no-op).
+ * aligned.  M, N, K >= 0 (K == 0 writes zeros; M == 0 or N == 0 is a no-op);
+ * FP8_ERR_SIZE for a dimension above 2^31 - 1 or an output of more than
+ * 2^31 - 1 tiles of 128 x 128.
  * bx, bw, bdy: device, one int32 each -- the operands' scaling biases.
  *
  * Arithmetic: every product of two FP8 values is exact in fp32 and the sums

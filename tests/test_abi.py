@@ -86,6 +86,10 @@ def test_gemm_argument_checks(fn):
 
     assert call(M=-1) == status("FP8_ERR_SIZE")
     assert call(K=1 << 31) == status("FP8_ERR_SIZE")
+    # an output of more than 2^31 - 1 tiles of 128 x 128 (each side fits)
+    out_rows, out_cols = {"fp8_scaled_gemm_fwd": ("M", "N"), "fp8_scaled_gemm_dgrad": ("M", "K"),
+                          "fp8_scaled_gemm_wgrad": ("N", "K")}[fn]
+    assert call(**{out_rows: (1 << 31) - 1, out_cols: (1 << 31) - 1}) == status("FP8_ERR_SIZE")
     assert call(fa=2) == status("FP8_ERR_FORMAT")     # E3M4: no product takes it
     assert call(fb=2) == status("FP8_ERR_FORMAT")
     assert call(fa=3) == status("FP8_ERR_FORMAT")
