@@ -1,0 +1,111 @@
+"""The FP8-AMAX linear layer as a PyTorch autograd Function and module.
+
+"Training and inference of large language models using 8-bit floating point",
+review page, "Proposed method": the input, the weight and the output gradient
+each get a per-tensor power-of-two scale from their amax (bullets 1-2), are
+cast to E4M3 (input, weight) or E5M2 (gradient) (bullet 4), and the three
+products run in FP8 and are unscaled afterwards (bullet 3), in training
+(bullet 5):
+    forward   y  = x8 . w8^T            (fp8_scaled_gemm_fwd)
+    backward  dx = dy8 . w8             (fp8_scaled_gemm_dgrad)
+              dw = dy8^T . x8           (fp8_scaled_gemm_wgrad)
+x may have any leading dimensions ([..., K]); w is [N, K].  Outputs and
+gradients are fp32 (autograd converts dx to x's dtype).
+
+Scaling modes (ScalingState):
+  * "current": every quantisation is amax -> compute_bias -> cast on the
+    tensor itself, as the method states;
+  * "delayed": the bias of a tensor comes from the amax its previous step's
+    cast returned, and the cast (fp8_scale_cast_amax) returns this step's
+    amax in the same pass, so each quantisation reads its input once; the
+    first step of each tensor uses "current".  Values beyond the previous
+    step's scale saturate: the pages' delayed / infrequent bias update trades
+    that for the skipped amax pass.
+Every bias is logged per tensor (BiasLog), without a host synchronisation.
+"""
+import torch
+
+from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, compute_bias, quantize,
+               scale_cast, scaled_gemm)
+from .mlp import BiasLog
+
+ROLES = ("x", "w", "dy")
+FORMATS = {"x": E4M3, "w": E4M3, "dy": E5M2}
+
+
+class ScalingState:
+    """Per-tensor scaling of one linear layer: margins, the mode ("current" or
+    "delayed"), each role's amax from its last quantisation (device
+    float32[1]), and an optional BiasLog."""
+
+    def __init__(self, mode="current", margins=None, math=MATH_EXACT, log=None):
+        if mode not in ("current", "delayed"):
+            raise ValueError(f"mode is 'current' or 'delayed', got {mode!r}")
+        self.mode = mode
+        self.margins = {r: 0 for r in ROLES}
+        self.margins.update(margins or {})
+        self.math = math
+        self.log = log
+        self.amax = {}
+
+    def quantise(self, role, t):
+        """(codes, bias) of tensor t for `role`."""
+        fmt, margin = FORMATS[role], self.margins[role]
+        prev = self.amax.get(role)
+        if self.mode == "delayed" and prev is not None:
+            bias = compute_bias(prev, fmt, margin)
+            amax = torch.empty(1, dtype=torch.float32, device=t.device)
+            codes = scale_cast(t, bias, fmt, amax=amax)
+        else:
+            codes, bias, amax = quantize(t, fmt, margin)
+        self.amax[role] = amax
+        if self.log is not None:
+            self.log.record(role, bias)
+        return codes, bias
+
+
+def _flat(t):
+    return t.contiguous().reshape(-1, t.shape[-1])
+
+
+class FP8LinearFunction(torch.autograd.Function):
+    """y = x . w^T with FP8-AMAX products; gradients for x and w."""
+
+    @staticmethod
+    def forward(ctx, x, w, state):
+        if w.dim() != 2 or x.shape[-1] != w.shape[1]:
+            raise ValueError(f"x [..., K] and w [N, K] do not match: {tuple(x.shape)}, {tuple(w.shape)}")
+        x2 = _flat(x)
+        x8, bx = state.quantise("x", x2)
+        w8, bw = state.quantise("w", w.contiguous())
+        y = scaled_gemm(OP_FWD, x8, E4M3, bx, w8, E4M3, bw, math=state.math)
+        ctx.saved = (x8, bx, w8, bw)
+        ctx.state = state
+        ctx.x_shape = x.shape
+        return y.reshape(*x.shape[:-1], w.shape[0])
+
+    @staticmethod
+    def backward(ctx, dy):
+        x8, bx, w8, bw = ctx.saved
+        state = ctx.state
+        dy8, bdy = state.quantise("dy", _flat(dy))
+        dx = scaled_gemm(OP_DGRAD, dy8, E5M2, bdy, w8, E4M3, bw, math=state.math)
+        dw = scaled_gemm(OP_WGRAD, dy8, E5M2, bdy, x8, E4M3, bx, math=state.math)
+        ctx.saved = None
+        return dx.reshape(ctx.x_shape), dw, None
+
+
+class FP8Linear(torch.nn.Module):
+    """Linear layer without bias whose three products are FP8-AMAX scaled
+    GEMMs; the weight (out_features x in_features) is an fp32 master by
+    default."""
+
+    def __init__(self, in_features, out_features, mode="current", margins=None, math=MATH_EXACT,
+                 log=None, device=None, dtype=torch.float32, std=0.02):
+        super().__init__()
+        self.state = ScalingState(mode, margins, math, log)
+        self.weight = torch.nn.Parameter(torch.randn(out_features, in_features, device=device,
+                                                     dtype=dtype) * std)
+
+    def forward(self, x):
+        return FP8LinearFunction.apply(x, self.weight, self.state)

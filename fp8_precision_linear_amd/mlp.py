@@ -52,8 +52,11 @@ class BiasLog:
         self._events.append((name, bias))
 
     def history(self):
-        """{tensor name: [bias per call]} (one host read of all of them)."""
-        out = {n: [] for n in TENSORS}
+        """{tensor name: [bias per call]}, names in order of first use (one
+        host read of all of them)."""
+        out = {}
+        for n, _ in self._events:
+            out.setdefault(n, [])
         if self._events:
             vals = torch.cat([b for _, b in self._events]).cpu().tolist()
             for (n, _), v in zip(self._events, vals):
