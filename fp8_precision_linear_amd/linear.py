@@ -22,6 +22,8 @@ Scaling modes (ScalingState):
     step's scale saturate: the pages' delayed / infrequent bias update trades
     that for the skipped amax pass.
 Every bias is logged per tensor (BiasLog), without a host synchronisation.
+For post-training-quantised inference (bullet 5) FP8Linear.freeze_weight()
+quantises the weight once; later calls reuse its codes and bias.
 """
 import torch
 
@@ -47,9 +49,21 @@ class ScalingState:
         self.math = math
         self.log = log
         self.amax = {}
+        self.frozen = {}   # role -> (codes, bias) reused instead of quantising
+
+    def freeze(self, role, t):
+        """Quantise t for `role` once (current scaling); later quantise()
+        calls for that role return these codes and bias."""
+        self.frozen.pop(role, None)
+        self.frozen[role] = self.quantise(role, t)
+
+    def unfreeze(self, role):
+        self.frozen.pop(role, None)
 
     def quantise(self, role, t):
         """(codes, bias) of tensor t for `role`."""
+        if role in self.frozen:
+            return self.frozen[role]
         fmt, margin = FORMATS[role], self.margins[role]
         prev = self.amax.get(role)
         if self.mode == "delayed" and prev is not None:
@@ -109,3 +123,17 @@ class FP8Linear(torch.nn.Module):
 
     def forward(self, x):
         return FP8LinearFunction.apply(x, self.weight, self.state)
+
+    @torch.no_grad()
+    def freeze_weight(self):
+        """Post-training quantisation: the weight's codes and bias are made
+        now, from its current values, and reused by every later call until
+        unfreeze_weight() (the weight gradient is still computed)."""
+        mode, self.state.mode = self.state.mode, "current"
+        try:
+            self.state.freeze("w", self.weight.detach().contiguous())
+        finally:
+            self.state.mode = mode
+
+    def unfreeze_weight(self):
+        self.state.unfreeze("w")

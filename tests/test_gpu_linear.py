@@ -121,3 +121,32 @@ def test_linear_end_to_end_against_unquantised_fp64(fl):
     print("relative errors (y, dx, dw)", errs)
     assert all(e < 0.1 for e in errs), errs
     assert rel(y.detach(), yr.detach().T.contiguous().T.flip(0)) > 0.8
+
+
+def test_linear_frozen_weight_for_inference(fl):
+    """freeze_weight(): the weight is quantised once; later calls reuse its
+    codes (one logged weight bias over several calls, outputs identical to an
+    unfrozen layer's on the same weight), even after the weight changes."""
+    from fp8_precision_linear_amd import linear, mlp
+    x, w, _ = tensors((128, 256), 192, 21)
+    log = mlp.BiasLog()
+    lin = linear.FP8Linear(256, 192, log=log, device="cuda")
+    ref = linear.FP8Linear(256, 192, device="cuda")
+    with torch.no_grad():
+        lin.weight.copy_(w)
+        ref.weight.copy_(w)
+    lin.freeze_weight()
+    xd = x.cuda()
+    with torch.no_grad():
+        y_ref = ref(xd)
+        outs = [lin(xd) for _ in range(3)]
+        lin.weight.mul_(4.0)                 # ignored while frozen
+        outs.append(lin(xd))
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, y_ref)
+    hist = log.history()
+    assert len(hist["w"]) == 1 and len(hist["x"]) == 4
+    lin.unfreeze_weight()
+    with torch.no_grad():
+        assert not torch.equal(lin(xd), y_ref)
