@@ -9,6 +9,10 @@ floating point" (Perez, Zhang et al., 2023), review page, "Proposed method":
 per-tensor amax -> compute_bias -> scale and cast to E4M3 (weights,
 activations) or E5M2 (gradients) -> FP8 matmul, unscaled afterwards.
 
+Layers built on these calls: ``fp8_precision_linear_amd.linear`` (FP8Linear,
+the layer with current or delayed scaling) and ``fp8_precision_linear_amd.mlp``
+(the chained FP8 MLP with SwiGLU).
+
 Importing this module loads the library and raises ImportError if it is not
 built; build it with ``python fp8_precision_linear_amd/build.py``.
 """
