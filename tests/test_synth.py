@@ -39,3 +39,19 @@ def test_distributions():
     assert np.median(np.abs(t)) < 1.0
     bf = synth.to_bf16(np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8], dtype=np.float32))
     assert bf.float().tolist() == [1.0, 1.0 + 2 ** -6]   # nearest-even to 7 fraction bits
+
+
+def test_chained_mlp_workload():
+    m = synth.CHAINED_MLPS[6]
+    assert (m.tokens, m.d, m.f) == (4096, 4096, 11008)
+    assert m.shape("W1") == (2 * 11008, 4096) and m.shape("W2") == (4096, 11008)
+    assert m.flops() == 18 * 4096 * 11008 * 4096          # 3 forward-shaped products x 3 passes
+    assert [m.seed(n) for n in m.ORDER] == [6000, 6001, 6002, 6003]
+    small = synth.ChainedMLP(77, "t", 8, 16, 12)
+    x = synth.chained_mlp_tensor(small, "X")
+    w1 = synth.chained_mlp_tensor(small, "W1")
+    g = synth.chained_mlp_tensor(small, "G")
+    assert x.dtype == torch.bfloat16 and x.shape == (8, 16)
+    assert w1.dtype == torch.float32 and w1.shape == (24, 16)
+    assert g.dtype == torch.float32 and abs(float(g.std()) - 1e-6) < 5e-7
+    assert synth.sha256(x) == synth.sha256(synth.chained_mlp_tensor(small, "X"))
