@@ -328,3 +328,44 @@ def test_delayed_scaling_with_the_fused_cast(fl):
         assert int(words_of(am)[0]) == prev_bits, t
         bias = fl.compute_bias(am, E4M3, 0)
 
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_degenerate_tensors(fl, dtype):
+    """Tensors the method meets at its edges: all +0, all -0, mixed zeros,
+    all NaN, all inf, one NaN among zeros, a constant, a single element, only
+    subnormal inputs, the largest finite value.  amax (separate and folded in
+    the cast), bias at three margins and codes, every format, all bit-exact."""
+    n = 4099
+    if dtype == "bf16":
+        mk = lambda v: np.full(n, v, dtype=np.uint16)
+        pz, nz, nan, inf, one, sub, big = 0x0000, 0x8000, 0x7FC0, 0x7F80, 0x3F80, 0x0001, 0x7F7F
+        dev = bf16_dev
+    else:
+        mk = lambda v: np.full(n, v, dtype=np.uint32)
+        pz, nz, nan, inf, one, sub, big = 0x0, 0x80000000, 0x7FC00000, 0x7F800000, 0x3F800000, 0x1, 0x7F7FFFFF
+        dev = f32_dev
+    cases = {"+0": mk(pz), "-0": mk(nz), "constant 1": mk(one), "all NaN": mk(nan), "all inf": mk(inf),
+             "subnormal": mk(sub), "largest finite": mk(big)}
+    mixed = mk(pz)
+    mixed[::2] = nz
+    cases["mixed zeros"] = mixed
+    lone = mk(pz)
+    lone[n // 3] = nan
+    cases["one NaN"] = lone
+    cases["single"] = mk(one)[:1].copy()
+    for name, words in cases.items():
+        x = dev(words)
+        a_ref = oracle.amax_bits(words)
+        assert int(words_of(fl.amax(x))[0]) == a_ref, name
+        for fmt in ALL_FMTS:
+            for margin in (-3, 0, 2):
+                say("degenerate", dtype, name, "fmt", fmt, "margin", margin)
+                codes, bias, amax = fl.quantize(x, fmt, margin)
+                b_ref = oracle.compute_bias(a_ref, fmt, margin)
+                assert int(bias.item()) == b_ref, (name, fmt, margin)
+                ref = oracle.scale_cast(words, b_ref, fmt)
+                assert np.array_equal(codes.cpu().numpy(), ref), (name, fmt, margin)
+                am = torch.empty(1, dtype=torch.float32, device="cuda")
+                fused = fl.scale_cast(x, bias, fmt, amax=am).cpu().numpy()
+                assert np.array_equal(fused, ref) and int(words_of(am)[0]) == a_ref, (name, fmt, margin)
