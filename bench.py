@@ -439,13 +439,16 @@ def cpu_baseline(w, host, rows, cols):
         "host_affinity": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"every in-step quantisation at full size (amax+bias+cast, 1 thread, "
-                   f"{t_quant:.1f} s) and a {rows}x{cols} output block of every product (OpenMP over "
-                   f"rows, {t_gemm:.1f} s), the products extrapolated to their full size by the "
-                   f"sampled fraction of the flops"),
+                   f"{t_quant:.1f} s) and "
+                   + (f"the full output of every product (OpenMP over rows, {t_gemm:.1f} s)"
+                      if flops_sample == step_flops else
+                      f"a {rows}x{cols} output block of every product (OpenMP over rows, "
+                      f"{t_gemm:.1f} s), the products extrapolated to their full size by the "
+                      f"sampled fraction of the flops")),
         "seconds_sampled": round(t_quant + t_gemm, 3),
         "quant_seconds_full_size": round(t_quant, 3),
         "gemm_seconds_sampled": round(t_gemm, 3),
-        "gemm_extrapolated": True,
+        "gemm_extrapolated": flops_sample != step_flops,
     }
 
 
@@ -884,7 +887,10 @@ def main():
                               "bias": round(bias_ms / K, 4), "cast": round(cast_ms / K, 4)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, host, args.cpu_rows, args.cpu_cols)
+        # small workloads (at most 200 GFLOP a step): the products' full outputs
+        full = w.flops() <= 2e11
+        line["cpu_baseline"] = cpu_baseline(w, host, 1 << 31 if full else args.cpu_rows,
+                                            1 << 31 if full else args.cpu_cols)
         line["cpu_baseline"]["vs_gpu"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
     print(json.dumps(line), flush=True)
 
