@@ -1,0 +1,50 @@
+"""The C ABI from a plain C program (tests/c/abi_client.c, built with gcc
+against include/fp8lin.h and libfp8lin.so; no Python in the client).  Without
+a GPU it checks the argument errors and status strings; on the GPU it
+quantises a seeded bf16 vector and runs a forward product, and its output
+files are compared with the oracle (amax, bias and codes bit-exact; the
+product within 1e-5 * 2^-(ba+bb) * sum |a||b|)."""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check_gemm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIBDIR = os.path.join(ROOT, "fp8_precision_linear_amd")
+
+
+@pytest.fixture(scope="module")
+def client(tmp_path_factory):
+    exe = str(tmp_path_factory.mktemp("c") / "abi_client")
+    cmd = ["gcc", "-O1", "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c", "abi_client.c"), "-o", exe,
+           "-L", LIBDIR, "-lfp8lin", "-L", "/opt/rocm/lib", "-lamdhip64",
+           f"-Wl,-rpath,{LIBDIR}", "-Wl,-rpath,/opt/rocm/lib"]
+    subprocess.run(cmd, check=True)
+    return exe
+
+
+def test_c_client_argument_checks(client):
+    r = subprocess.run([client, "checks"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+@pytest.mark.gpu
+def test_c_client_quantise_and_product(client, tmp_path):
+    n = 64 * 128 + 4099
+    r = subprocess.run([client, "run", str(tmp_path), str(n)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    rd = lambda name, dt: np.fromfile(str(tmp_path / name), dtype=dt)
+    x, w = rd("x.bf16", np.uint16), rd("w.e4m3", np.uint8).reshape(48, 128)
+    a_bits = oracle.amax_bits(x)
+    b = oracle.compute_bias(a_bits, 0, 0)
+    assert int(rd("amax.f32", np.uint32)[0]) == a_bits
+    assert int(rd("bias.i32", np.int32)[0]) == b
+    codes = oracle.scale_cast(x, b, 0)
+    assert np.array_equal(rd("codes.u8", np.uint8), codes)
+    ref, bound = oracle.gemm_fwd(codes[:64 * 128].reshape(64, 128), 0, b, w, 0, 3)
+    check_gemm(rd("y.f32", np.float32).reshape(64, 48), ref, bound, "C client product")
