@@ -61,7 +61,7 @@ const char* fp8_status_string(int status) {
     case FP8_ERR_SIZE: return "a size is negative or too large";
     case FP8_ERR_FORMAT: return "unknown FP8 format";
     case FP8_ERR_DTYPE: return "unknown input dtype";
-    case FP8_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case FP8_ERR_ALIGN: return "a pointer is misaligned (16 bytes for tensors, 4 for amax outputs)";
     case FP8_ERR_MARGIN: return "margin out of range";
     case FP8_ERR_DEVICE: return "no gfx950 HIP device is current";
     case FP8_ERR_HIP: return "a HIP launch failed";

@@ -66,7 +66,7 @@ typedef enum {
 #define FP8_ERR_SIZE (-2)   /* a size is negative or too large */
 #define FP8_ERR_FORMAT (-3) /* format is not an fp8_format_t (or E3M4 given to a product) */
 #define FP8_ERR_DTYPE (-4)  /* dtype is not an fp8_dtype_t */
-#define FP8_ERR_ALIGN (-5)  /* a pointer that must be 16-byte aligned is not */
+#define FP8_ERR_ALIGN (-5)  /* a pointer is misaligned: tensors need 16 bytes, amax outputs 4 */
 #define FP8_ERR_MARGIN (-6) /* |margin| > FP8_MAX_MARGIN */
 #define FP8_ERR_DEVICE (-7) /* no HIP device, or the current device is not gfx950 */
 #define FP8_ERR_HIP (-8)    /* a HIP launch failed */
