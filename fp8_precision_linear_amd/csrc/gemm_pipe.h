@@ -312,7 +312,9 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[TM][TN]) {
 // Unscale and store a wave's TM x TN block of 32x32 tiles whose top-left
 // output is (row0, col0).  32x32 accumulator layout: register r of lane l
 // holds row 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32.  With
-// AMAX the largest stored magnitude is folded into *p.amax.
+// AMAX the largest stored magnitude is folded into *p.amax.  The stores are
+// non-temporal: the output is not read back by the product, and a wave of
+// tiles writes about twice an XCD's L2 in outputs (measured: 0.2-1% faster).
 template <bool AMAX, int TM, int TN>
 __device__ __forceinline__ void store_block_as(const GemmProblem& p, const v16f (&acc)[TM][TN],
                                                int row0, int col0, int lane) {
@@ -329,7 +331,7 @@ __device__ __forceinline__ void store_block_as(const GemmProblem& p, const v16f 
         const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < p.m && col < p.n) {
           const float v = __builtin_ldexpf(acc[i][j][r], unscale);
-          p.c[(int64_t)row * p.ldc + col] = v;
+          __builtin_nontemporal_store(v, &p.c[(int64_t)row * p.ldc + col]);
           if constexpr (AMAX) mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu);
         }
       }
