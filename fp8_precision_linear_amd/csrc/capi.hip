@@ -13,6 +13,8 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+// amax and bias words: their natural 4-byte alignment (atomics need it)
+bool misaligned_word(const void* p) { return ((uintptr_t)p & 3u) != 0; }
 // E3M4 has no MFMA operand type: quantisation only.
 bool bad_format(int f) { return f != FP8_E4M3 && f != FP8_E5M2 && f != FP8_E3M4; }
 bool bad_operand_format(int f) { return f != FP8_E4M3 && f != FP8_E5M2; }
@@ -36,10 +38,13 @@ int device_ok() {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
 
+// The operands are a_rows x a_cols and b_rows x b_cols, each of those one of
+// M, N, K: the products are formed only after the range check.
 int gemm_checks(const uint8_t* a, int fa, const int32_t* ba, const uint8_t* b, int fb,
                 const int32_t* bb, int64_t M, int64_t N, int64_t K, const float* out,
-                int64_t a_elems, int64_t b_elems) {
+                int64_t a_rows, int64_t a_cols, int64_t b_rows, int64_t b_cols) {
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8_ERR_SIZE;
+  const int64_t a_elems = a_rows * a_cols, b_elems = b_rows * b_cols;
   // the launch grid (at most one block per 128 x 128 output tile) is 32-bit
   if (((M + 127) / 128) * ((N + 127) / 128) > (int64_t)0x7FFFFFFF) return FP8_ERR_SIZE;
   if (bad_operand_format(fa) || bad_operand_format(fb)) return FP8_ERR_FORMAT;
@@ -47,6 +52,7 @@ int gemm_checks(const uint8_t* a, int fa, const int32_t* ba, const uint8_t* b, i
   if (!out || !ba || !bb) return FP8_ERR_NULL;
   if ((a_elems > 0 && !a) || (b_elems > 0 && !b)) return FP8_ERR_NULL;
   if (misaligned(out) || (a && misaligned(a)) || (b && misaligned(b))) return FP8_ERR_ALIGN;
+  if (misaligned_word(ba) || misaligned_word(bb)) return FP8_ERR_ALIGN;
   return FP8_OK;
 }
 
@@ -74,7 +80,7 @@ int fp8_amax(const void* x, fp8_dtype_t dtype, int64_t n, float* amax, void* str
   if (n < 0) return FP8_ERR_SIZE;
   if (bad_dtype(dtype)) return FP8_ERR_DTYPE;
   if (!amax || (n > 0 && !x)) return FP8_ERR_NULL;
-  if (n > 0 && misaligned(x)) return FP8_ERR_ALIGN;
+  if ((n > 0 && misaligned(x)) || misaligned_word(amax)) return FP8_ERR_ALIGN;
   if (int s = device_ok()) return s;
   return hip_status(fp8lin::launch_amax(x, dtype, n, amax, (hipStream_t)stream));
 }
@@ -84,6 +90,7 @@ int fp8_compute_bias(const float* amax, fp8_format_t fmt, int32_t margin, int32_
   if (bad_format(fmt)) return FP8_ERR_FORMAT;
   if (margin > FP8_MAX_MARGIN || margin < -FP8_MAX_MARGIN) return FP8_ERR_MARGIN;
   if (!amax || !bias) return FP8_ERR_NULL;
+  if (misaligned_word(amax) || misaligned_word(bias)) return FP8_ERR_ALIGN;
   if (int s = device_ok()) return s;
   return hip_status(fp8lin::launch_bias(amax, fmt, margin, bias, (hipStream_t)stream));
 }
@@ -95,7 +102,7 @@ int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* b
   if (bad_format(fmt)) return FP8_ERR_FORMAT;
   if (n == 0) return FP8_OK;
   if (!x || !y || !bias) return FP8_ERR_NULL;
-  if (misaligned(x) || misaligned(y)) return FP8_ERR_ALIGN;
+  if (misaligned(x) || misaligned(y) || misaligned_word(bias)) return FP8_ERR_ALIGN;
   if (int s = device_ok()) return s;
   return hip_status(fp8lin::launch_cast(x, dtype, n, bias, fmt, y, nullptr, (hipStream_t)stream));
 }
@@ -106,10 +113,10 @@ int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32
   if (bad_dtype(dtype)) return FP8_ERR_DTYPE;
   if (bad_format(fmt)) return FP8_ERR_FORMAT;
   if (!x_amax) return FP8_ERR_NULL;
-  if (((uintptr_t)x_amax & 3u) != 0) return FP8_ERR_ALIGN;
+  if (misaligned_word(x_amax)) return FP8_ERR_ALIGN;
   if (n > 0) {
     if (!x || !y || !bias) return FP8_ERR_NULL;
-    if (misaligned(x) || misaligned(y)) return FP8_ERR_ALIGN;
+    if (misaligned(x) || misaligned(y) || misaligned_word(bias)) return FP8_ERR_ALIGN;
   }
   if (int s = device_ok()) return s;
   return hip_status(fp8lin::launch_cast(x, dtype, n, bias, fmt, y,
@@ -131,7 +138,7 @@ int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, c
   switch (op) {
     case FP8_GEMM_FWD:
       // Y[M x N]: X8 and W8 both contraction (K) contiguous.
-      if (int s = gemm_checks(a, fa, ba, b, fb, bb, M, N, K, out, M * K, N * K)) return s;
+      if (int s = gemm_checks(a, fa, ba, b, fb, bb, M, N, K, out, M, K, N, K)) return s;
       empty = M == 0 || N == 0;
       p = fp8lin::GemmProblem{a, K, true, fa, ba, b, K, true, fb, bb, out, N,
                               (int)M, (int)N, (int)K, math, nullptr};
@@ -139,14 +146,14 @@ int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, c
     case FP8_GEMM_DGRAD:
       // dX[M x K]: rows of dY8 (contraction N contiguous) times W8 read as
       // [contraction N][K] (the contraction is its slow index).
-      if (int s = gemm_checks(a, fa, ba, b, fb, bb, M, K, N, out, M * N, N * K)) return s;
+      if (int s = gemm_checks(a, fa, ba, b, fb, bb, M, K, N, out, M, N, N, K)) return s;
       empty = M == 0 || K == 0;
       p = fp8lin::GemmProblem{a, N, true, fa, ba, b, K, false, fb, bb, out, K,
                               (int)M, (int)K, (int)N, math, nullptr};
       break;
     case FP8_GEMM_WGRAD:
       // dW[N x K]: dY8 read as [contraction M][N] times X8 read as [contraction M][K].
-      if (int s = gemm_checks(a, fa, ba, b, fb, bb, N, K, M, out, M * N, M * K)) return s;
+      if (int s = gemm_checks(a, fa, ba, b, fb, bb, N, K, M, out, M, N, M, K)) return s;
       empty = N == 0 || K == 0;
       p = fp8lin::GemmProblem{a, N, false, fa, ba, b, K, false, fb, bb, out, K,
                               (int)N, (int)K, (int)M, math, nullptr};
@@ -183,7 +190,7 @@ int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_forma
                          int64_t M, int64_t N, int64_t K, float* out, float* out_amax,
                          void* stream) {
   if (!out_amax) return FP8_ERR_NULL;
-  if (((uintptr_t)out_amax & 3u) != 0) return FP8_ERR_ALIGN;
+  if (misaligned_word(out_amax)) return FP8_ERR_ALIGN;
   return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, out_amax, (hipStream_t)stream);
 }
 
@@ -216,7 +223,7 @@ int swiglu_checks(const void* h, const void* da, bool need_da, int64_t rows, int
   if (rows < 0 || f < 0 || rows > (int64_t)0x7FFFFFFF || f > (int64_t)0x3FFFFFFF)
     return FP8_ERR_SIZE;
   if (fp8lin::swiglu_blocks(rows, f) > (int64_t)0x7FFFFFFF) return FP8_ERR_SIZE;
-  if (out_amax && ((uintptr_t)out_amax & 3u) != 0) return FP8_ERR_ALIGN;
+  if (out_amax && misaligned_word(out_amax)) return FP8_ERR_ALIGN;
   if (rows == 0 || f == 0) return FP8_OK;
   if (!h || !out || (need_da && !da)) return FP8_ERR_NULL;
   if (misaligned(h) || misaligned(out) || (need_da && misaligned(da))) return FP8_ERR_ALIGN;

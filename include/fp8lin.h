@@ -80,7 +80,7 @@ const char* fp8_status_string(int status);
 /*
  * Per-tensor maximum absolute value ("Proposed method", bullet 1).
  *   x     device, n elements of `dtype`, 16-byte aligned.
- *   amax  device, one float: written with max_i |x_i|.  The result is exact
+ *   amax  device, one float, 4-byte aligned: written with max_i |x_i|.  The result is exact
  *         (a bf16 value widens to float without rounding).  Any NaN element
  *         makes it the NaN with the largest magnitude bits; otherwise any
  *         infinity makes it +inf; n == 0 gives +0.
@@ -94,8 +94,8 @@ int fp8_amax(const void* x, fp8_dtype_t dtype, int64_t n, float* amax, void* str
  * evaluated exactly from the exponent and mantissa fields.  fmt_max is 448
  * (E4M3), 57344 (E5M2) or 30 (E3M4).  An amax of 0, inf or NaN gives b = 0 and the margin
  * is not applied.
- *   amax  device, one float (normally the output of fp8_amax).
- *   bias  device, one int32, written.
+ *   amax  device, one float, 4-byte aligned (normally the output of fp8_amax).
+ *   bias  device, one int32, 4-byte aligned, written.
  *   |margin| <= FP8_MAX_MARGIN; a positive margin leaves headroom below
  *   fmt_max, a negative one makes the largest values saturate.
  */
@@ -109,7 +109,8 @@ int fp8_compute_bias(const float* amax, fp8_format_t fmt, int32_t margin, int32_
  * finite code; FP8 subnormals are produced; zero and underflow keep the sign
  * (-0 is 0x80); NaN becomes 0x7F | sign.
  *   x     device, n elements of `dtype`, 16-byte aligned.
- *   bias  device, one int32 (normally the output of fp8_compute_bias).
+ *   bias  device, one int32, 4-byte aligned (normally the output of
+ *         fp8_compute_bias).
  *   y     device, n bytes, 16-byte aligned, written.
  */
 int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* bias,
@@ -139,7 +140,8 @@ int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32
  * aligned.  M, N, K >= 0 (K == 0 writes zeros; M == 0 or N == 0 is a no-op);
  * FP8_ERR_SIZE for a dimension above 2^31 - 1 or an output of more than
  * 2^31 - 1 tiles of 128 x 128.
- * bx, bw, bdy: device, one int32 each -- the operands' scaling biases.
+ * bx, bw, bdy: device, one int32 each, 4-byte aligned -- the operands'
+ * scaling biases.
  *
  * Arithmetic: every product of two FP8 values is exact in fp32 and the sums
  * are formed with fp32 accuracy (FP8_GEMM_EXACT): the FP8 codes are widened

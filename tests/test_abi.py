@@ -49,6 +49,8 @@ def test_amax_argument_checks():
     assert L.fp8_amax(None, 0, 10, A32, None) == status("FP8_ERR_NULL")
     assert L.fp8_amax(A16, 0, 10, None, None) == status("FP8_ERR_NULL")
     assert L.fp8_amax(MIS, 1, 10, A32, None) == status("FP8_ERR_ALIGN")
+    assert L.fp8_amax(A16, 0, 10, P(18), None) == status("FP8_ERR_ALIGN")   # amax word
+    assert L.fp8_amax(None, 0, 0, P(18), None) == status("FP8_ERR_ALIGN")   # also when empty
 
 
 def test_bias_argument_checks():
@@ -57,6 +59,8 @@ def test_bias_argument_checks():
     assert L.fp8_compute_bias(A16, 1, -65, A32, None) == status("FP8_ERR_MARGIN")
     assert L.fp8_compute_bias(None, 0, 0, A32, None) == status("FP8_ERR_NULL")
     assert L.fp8_compute_bias(A16, 0, 0, None, None) == status("FP8_ERR_NULL")
+    assert L.fp8_compute_bias(P(18), 0, 0, A32, None) == status("FP8_ERR_ALIGN")
+    assert L.fp8_compute_bias(A16, 0, 0, P(34), None) == status("FP8_ERR_ALIGN")
 
 
 def test_cast_argument_checks():
@@ -68,6 +72,7 @@ def test_cast_argument_checks():
     assert L.fp8_scale_cast(A16, 0, 5, A32, 0, None, None) == status("FP8_ERR_NULL")
     assert L.fp8_scale_cast(MIS, 0, 5, A32, 0, A48, None) == status("FP8_ERR_ALIGN")
     assert L.fp8_scale_cast(A16, 0, 5, A32, 0, MIS, None) == status("FP8_ERR_ALIGN")
+    assert L.fp8_scale_cast(A16, 0, 5, P(33), 0, A48, None) == status("FP8_ERR_ALIGN")   # bias word
     # n == 0 is a no-op: nothing is checked further and nothing is launched
     assert L.fp8_scale_cast(None, 0, 0, None, 0, None, None) == 0
 
@@ -100,6 +105,10 @@ def test_gemm_argument_checks(fn):
     assert call(b=None) == status("FP8_ERR_NULL")
     assert call(a=MIS) == status("FP8_ERR_ALIGN")
     assert call(out=MIS) == status("FP8_ERR_ALIGN")
+    assert call(ba=P(34)) == status("FP8_ERR_ALIGN")
+    assert call(bb=P(35)) == status("FP8_ERR_ALIGN")
+    # sizes whose element counts overflow int64 are rejected by the range check
+    assert call(M=1 << 62, K=1 << 62) == status("FP8_ERR_SIZE")
     # an empty output is a no-op whatever the pointers are; an empty
     # contraction still writes the (zero) output, so it needs the pointers
     out_dim, contraction = {"fp8_scaled_gemm_fwd": ("M", "K"), "fp8_scaled_gemm_dgrad": ("M", "N"),
