@@ -57,6 +57,10 @@ def parse():
                     help="skip the epilogue-amax measurement on the largest product")
     ap.add_argument("--no-delayed", action="store_true",
                     help="skip the delayed-scaling (cast with its amax folded in) measurement")
+    ap.add_argument("--quant", choices=["one-call", "three-calls"], default="one-call",
+                    help="how the timed steps quantise each activation: fp8_quantize, or "
+                         "fp8_amax -> fp8_compute_bias -> fp8_scale_cast (the steps with per-kernel "
+                         "events always make the three calls, to time each kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy twice (HBM counter calibration)")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -213,6 +217,47 @@ def delayed_quant(fl, w, plan, q, x, reps=9):
 
 COLD_FLUSH_BYTES = 768 << 20   # > the 256 MB Infinity Cache
 COLD_CLEAN_BYTES = 512 << 20
+
+
+def one_call_quant(fl, w, plan, q, x, reps=9):
+    """Each in-step quantisation two ways (interleaved, median of `reps`, HIP
+    events around the calls on the launch stream): fp8_quantize, and the
+    three calls amax -> compute_bias -> scale_cast.  Same outputs bit for bit
+    (checked here on the last repetition)."""
+    import statistics
+
+    import torch
+
+    def once(fn):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) * 1e3
+
+    per, chain_sum, one_sum = {}, 0.0, 0.0
+    for item in plan:
+        if item[0] != "quant":
+            continue
+        n = item[1]
+        codes, bias, amax, fmt = q[n]
+        margin = w.tensor(n).margin
+        c2, b2, a2 = torch.empty_like(codes), torch.empty_like(bias), torch.empty_like(amax)
+        chain, one = [], []
+        for _ in range(reps):
+            chain.append(once(lambda: (fl.amax(x[n], out=amax), fl.compute_bias(amax, fmt, margin, out=bias),
+                                       fl.scale_cast(x[n], bias, fmt, out=codes))))
+            one.append(once(lambda: fl.quantize(x[n], fmt, margin, out=c2, bias=b2, amax=a2)))
+        assert torch.equal(codes, c2) and torch.equal(bias, b2) and torch.equal(amax.view(torch.int32),
+                                                                               a2.view(torch.int32)), n
+        cm, om = statistics.median(chain), statistics.median(one)
+        chain_sum += cm
+        one_sum += om
+        per[n] = {"elements": x[n].numel(), "three_calls_us": round(cm, 2), "one_call_us": round(om, 2)}
+    return {"method": "fp8_quantize vs fp8_amax -> fp8_compute_bias -> fp8_scale_cast, each tensor alone, "
+                      "HIP events, median of %d; outputs identical" % reps,
+            "three_calls_us": round(chain_sum, 2), "one_call_us": round(one_sum, 2), "per_tensor": per}
 
 
 def cold_quant(fl, w, plan, q, x, reps):
@@ -713,6 +758,9 @@ def main():
                 n = item[1]
                 codes, bias, amax, fmt = q[n]
                 t = w.tensor(n)
+                if ev is None and args.quant == "one-call":
+                    fl.quantize(x[n], fmt, t.margin, out=codes, bias=bias, amax=amax)
+                    continue
                 if ev is not None:
                     ev.append(("quant_start", n, torch.cuda.Event(enable_timing=True)))
                     ev[-1][2].record()
@@ -774,6 +822,7 @@ def main():
     cold = None if args.no_cold else cold_quant(fl, w, plan, q, x, args.cold_reps)
     epi = None if args.no_epilogue_amax else epilogue_amax(fl, w, plan, q, outs, math, op_of)
     delayed = None if args.no_delayed else delayed_quant(fl, w, plan, q, x)
+    one_call = None if args.no_delayed else one_call_quant(fl, w, plan, q, x)
 
     # per-kernel durations from the events (same stream as the launches)
     gemm_ms = amax_ms = bias_ms = cast_ms = 0.0
@@ -833,6 +882,9 @@ def main():
             "accumulate": "f32",
             "input_sha256": {t.name: synth.sha256(host[t.name]) for t in w.tensors},
             "math": args.math,
+            "quantisation": ("fp8_quantize per activation (one call: one workgroup up to 256 KiB, "
+                             "else clear, amax and a cast deriving the bias)" if args.quant == "one-call"
+                             else "fp8_amax -> fp8_compute_bias -> fp8_scale_cast per activation"),
             "parallelism": "single-gpu",
         },
         "roofline": {
@@ -883,6 +935,7 @@ def main():
         "cold": cold,
         "epilogue_amax": epi,
         "delayed_scaling": delayed,
+        "one_call_quantisation": one_call,
         "step_breakdown_ms": {"gemm": round(gemm_ms / K, 4), "amax": round(amax_ms / K, 4),
                               "bias": round(bias_ms / K, 4), "cast": round(cast_ms / K, 4)},
     }

@@ -46,6 +46,7 @@ SIGNATURES = {
     "fp8_compute_bias": (_ci, [_vp, _ci, _i32, _vp, _vp]),
     "fp8_scale_cast": (_ci, [_vp, _ci, _i64, _vp, _ci, _vp, _vp]),
     "fp8_scale_cast_amax": (_ci, [_vp, _ci, _i64, _vp, _ci, _vp, _vp, _vp]),
+    "fp8_quantize": (_ci, [_vp, _ci, _i64, _ci, _i32, _vp, _vp, _vp, _vp]),
     "fp8_scaled_gemm": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_amax": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_fwd": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
@@ -139,8 +140,22 @@ def scale_cast(x, bias, fmt, out=None, stream=None, amax=None):
     return out
 
 
-def quantize(x, fmt, margin=0, stream=None):
-    """(codes, bias, amax) of a tensor: the three quantisation calls in order."""
+def quantize(x, fmt, margin=0, out=None, bias=None, amax=None, stream=None):
+    """(codes, bias, amax) of a tensor in one call (fp8_quantize): the results of
+    amax -> compute_bias -> scale_cast, in one launch for small tensors and three
+    for large ones.  out / bias / amax: optional preallocated device tensors."""
+    _need_cuda(x)
+    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    bias = torch.empty(1, dtype=torch.int32, device=x.device) if bias is None else bias
+    amax = torch.empty(1, dtype=torch.float32, device=x.device) if amax is None else amax
+    _need_cuda(out, bias, amax)
+    _check("fp8_quantize", lib.fp8_quantize(_ptr(x), _dtype_code(x), x.numel(), int(fmt), int(margin),
+                                            _ptr(out), _ptr(amax), _ptr(bias), _stream(stream)))
+    return out, bias, amax
+
+
+def quantize_chain(x, fmt, margin=0, stream=None):
+    """(codes, bias, amax) of a tensor through the three separate calls in order."""
     a = amax(x, stream=stream)
     b = compute_bias(a, fmt, margin, stream=stream)
     return scale_cast(x, b, fmt, stream=stream), b, a

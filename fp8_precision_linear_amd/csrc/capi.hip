@@ -107,6 +107,20 @@ int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* b
   return hip_status(fp8lin::launch_cast(x, dtype, n, bias, fmt, y, nullptr, (hipStream_t)stream));
 }
 
+int fp8_quantize(const void* x, fp8_dtype_t dtype, int64_t n, fp8_format_t fmt, int32_t margin,
+                 uint8_t* y, float* amax, int32_t* bias, void* stream) {
+  if (n < 0) return FP8_ERR_SIZE;
+  if (bad_dtype(dtype)) return FP8_ERR_DTYPE;
+  if (bad_format(fmt)) return FP8_ERR_FORMAT;
+  if (margin > FP8_MAX_MARGIN || margin < -FP8_MAX_MARGIN) return FP8_ERR_MARGIN;
+  if (!amax || !bias || (n > 0 && (!x || !y))) return FP8_ERR_NULL;
+  if (misaligned_word(amax) || misaligned_word(bias)) return FP8_ERR_ALIGN;
+  if (n > 0 && (misaligned(x) || misaligned(y))) return FP8_ERR_ALIGN;
+  if (int s = device_ok()) return s;
+  return hip_status(fp8lin::launch_quantize(x, dtype, n, fmt, margin, y, amax, bias,
+                                            (hipStream_t)stream));
+}
+
 int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* bias,
                         fp8_format_t fmt, uint8_t* y, float* x_amax, void* stream) {
   if (n < 0) return FP8_ERR_SIZE;

@@ -17,6 +17,11 @@ hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias,
                        uint8_t* y, uint32_t* amax, hipStream_t stream);
 // *p = 0 (one lane).
 hipError_t launch_clear_u32(uint32_t* p, hipStream_t stream);
+// amax -> bias -> cast of one tensor, results bit-identical to launch_amax,
+// launch_bias and launch_cast in turn: one launch for small tensors, three
+// (clear, amax, a cast that derives the bias itself) for the rest.
+hipError_t launch_quantize(const void* x, int dtype, int64_t n, int fmt, int32_t margin, uint8_t* y,
+                           float* amax, int32_t* bias, hipStream_t stream);
 
 // SwiGLU between the products of a chained MLP (swiglu.hip).  amax: optional,
 // cleared then folded with max |output| (fp32 magnitude bits).

@@ -117,6 +117,23 @@ int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* b
                    fp8_format_t fmt, uint8_t* y, void* stream);
 
 /*
+ * The whole per-tensor quantisation ("Proposed method", bullets 1-4):
+ * fp8_amax, fp8_compute_bias and fp8_scale_cast in one call, with the same
+ * results bit for bit, in fewer launches.  Inputs of up to 256 KiB (131072
+ * bf16 or 65536 fp32 elements) take one launch of one workgroup; larger ones
+ * three (a one-lane clear of amax, the amax reduction, and the cast, every
+ * block of which derives the bias from the amax itself).
+ *   x      device, n elements of `dtype`, 16-byte aligned.
+ *   y      device, n bytes, 16-byte aligned, written with the codes.
+ *   amax   device, one float, 4-byte aligned, written as by fp8_amax.
+ *   bias   device, one int32, 4-byte aligned, written as by fp8_compute_bias.
+ *   |margin| <= FP8_MAX_MARGIN (FP8_ERR_MARGIN otherwise).
+ * n == 0 writes amax = 0 and bias = 0.  Errors as for the three calls.
+ */
+int fp8_quantize(const void* x, fp8_dtype_t dtype, int64_t n, fp8_format_t fmt, int32_t margin,
+                 uint8_t* y, float* amax, int32_t* bias, void* stream);
+
+/*
  * fp8_scale_cast that also returns max |x| of its own input, folded in the
  * same pass ("Proposed method", bullet 1, fused with the cast): with delayed
  * scaling -- this call's bias computed from the amax that the previous call

@@ -369,3 +369,55 @@ def test_degenerate_tensors(fl, dtype):
                 am = torch.empty(1, dtype=torch.float32, device="cuda")
                 fused = fl.scale_cast(x, bias, fmt, amax=am).cpu().numpy()
                 assert np.array_equal(fused, ref) and int(words_of(am)[0]) == a_ref, (name, fmt, margin)
+
+
+def _quantize_inputs(dtype, n, scale, special, seed):
+    """Words of a seeded normal tensor times `scale`, with an optional planted
+    NaN, inf or largest-magnitude element."""
+    rng = np.random.default_rng(seed)
+    v = (rng.standard_normal(n) * scale).astype(np.float32)
+    if dtype == "bf16":
+        words = (torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)).copy()
+        nan, inf = 0xFFC1, 0x7F80
+    else:
+        words = v.view(np.uint32).copy()
+        nan, inf = 0x7FC00123, 0xFF800000
+    if n and special == "nan":
+        words[n // 2] = nan
+    elif n and special == "inf":
+        words[n - 1] = inf
+    return words
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_in_one_call(fl, dtype, monkeypatch):
+    """fp8_quantize against the oracle and against amax -> compute_bias ->
+    scale_cast, bit for bit, on both of its paths (one workgroup; clear, amax
+    and a cast deriving the bias itself), each forced over every size:
+    ragged sizes on both sides of the 256 KiB threshold, all three
+    formats, margins, biases outside the hardware conversion's range (tiny
+    and huge scales) and planted NaN / inf."""
+    dev = bf16_dev if dtype == "bf16" else f32_dev
+    sizes = [0, 1, 7, 15, 16, 17, 1023, 4099, 16389, 65536, 65537, 131072, 131073, 1_000_003]
+    for si, n in enumerate(sizes):
+        for scale, special in ((1.0, None), (1e-37, None), (3e4, "inf"), (0.02, "nan")):
+            words = _quantize_inputs(dtype, n, scale, special, 100 + si)
+            x = dev(words)
+            for fmt, margin in ((E4M3, 0), (E5M2, 1), (E3M4, -2), (E4M3, 64)):
+                a_ref, b_ref, c_ref = oracle.quantize(words, fmt, margin)
+                cc, cb, ca = fl.quantize_chain(x, fmt, margin)
+                for path, small in (("one workgroup", "2000000000"), ("three launches", "0"),
+                                    ("default choice", None)):
+                    if small is None:
+                        monkeypatch.delenv("FP8LIN_QUANT_SMALL", raising=False)
+                    else:
+                        monkeypatch.setenv("FP8LIN_QUANT_SMALL", small)
+                    say("quantize", dtype, "n", n, "scale", scale, special, "fmt", fmt, "margin", margin, path)
+                    codes, bias, amax = fl.quantize(x, fmt, margin)
+                    what = (dtype, n, scale, special, fmt, margin, path)
+                    assert int(words_of(amax)[0]) == a_ref, what
+                    assert int(bias.item()) == b_ref, what
+                    got = codes.cpu().numpy()
+                    assert np.array_equal(got, c_ref), what
+                    assert np.array_equal(got, cc.cpu().numpy()), what
+                    assert int(words_of(ca)[0]) == a_ref and int(cb.item()) == b_ref, what
