@@ -47,6 +47,7 @@ static int checks(void) {
   bad += expect("gemm E3M4", fp8_scaled_gemm_fwd((uint8_t*)p, FP8_E3M4, (int32_t*)p, (uint8_t*)p, FP8_E4M3, (int32_t*)p, 8, 8, 8, (float*)p, NULL), FP8_ERR_FORMAT);
   bad += expect("gemm op", fp8_scaled_gemm((fp8_gemm_op_t)5, FP8_GEMM_EXACT, (uint8_t*)p, FP8_E4M3, (int32_t*)p, (uint8_t*)p, FP8_E4M3, (int32_t*)p, 8, 8, 8, (float*)p, NULL), FP8_ERR_OP);
   bad += expect("swiglu size", fp8_swiglu_fwd((float*)p, -2, 4, (uint16_t*)p, NULL, NULL), FP8_ERR_SIZE);
+  bad += expect("quantize margin", fp8_quantize(p, FP8_IN_BF16, 8, FP8_E4M3, -FP8_MAX_MARGIN - 1, (uint8_t*)p, (float*)p, (int32_t*)p, NULL), FP8_ERR_MARGIN);
   if (strlen(fp8_status_string(FP8_ERR_ALIGN)) == 0) bad++;
   return bad;
 }
@@ -110,21 +111,34 @@ static int run(const char* dir, int64_t n) {
   TRY(fp8_scale_cast(dx, FP8_IN_BF16, n, (const int32_t*)dbias, FP8_E4M3, (uint8_t*)dy, st));
   TRY(fp8_scaled_gemm_fwd((const uint8_t*)dy, FP8_E4M3, (const int32_t*)dbias, (const uint8_t*)dw,
                           FP8_E4M3, (const int32_t*)dbw, M, N, K, (float*)dout, st));
+  /* the same quantisation in one call, into separate buffers */
+  void *dy1, *damax1, *dbias1;
+  if (hipMalloc(&dy1, (size_t)n) || hipMalloc(&damax1, 4) || hipMalloc(&dbias1, 4)) return 3;
+  TRY(fp8_quantize(dx, FP8_IN_BF16, n, FP8_E4M3, 0, (uint8_t*)dy1, (float*)damax1, (int32_t*)dbias1, st));
   if (hipStreamSynchronize(st)) return 4;
-  float amax;
-  int32_t bias;
+  float amax, amax1;
+  int32_t bias, bias1;
   uint8_t* codes = malloc((size_t)n);
+  uint8_t* codes1 = malloc((size_t)n);
+  if (hipMemcpy(&amax1, damax1, 4, D2H) || hipMemcpy(&bias1, dbias1, 4, D2H) ||
+      hipMemcpy(codes1, dy1, (size_t)n, D2H))
+    return 4;
   float* out = malloc((size_t)(M * N) * 4);
   if (hipMemcpy(&amax, damax, 4, D2H) || hipMemcpy(&bias, dbias, 4, D2H) ||
       hipMemcpy(codes, dy, (size_t)n, D2H) || hipMemcpy(out, dout, (size_t)(M * N) * 4, D2H))
     return 4;
+  if (memcmp(&amax, &amax1, 4) != 0 || bias != bias1 || memcmp(codes, codes1, (size_t)n) != 0) {
+    fprintf(stderr, "fp8_quantize differs from amax -> compute_bias -> scale_cast\n");
+    return 6;
+  }
   int bad = write_file(dir, "x.bf16", x, (size_t)n * 2) + write_file(dir, "w.e4m3", w, (size_t)(N * K)) +
             write_file(dir, "amax.f32", &amax, 4) + write_file(dir, "bias.i32", &bias, 4) +
             write_file(dir, "codes.u8", codes, (size_t)n) +
             write_file(dir, "y.f32", out, (size_t)(M * N) * 4);
   hipFree(dx); hipFree(dy); hipFree(damax); hipFree(dbias); hipFree(dw); hipFree(dbw); hipFree(dout);
+  hipFree(dy1); hipFree(damax1); hipFree(dbias1);
   hipStreamDestroy(st);
-  free(x); free(w); free(codes); free(out);
+  free(x); free(w); free(codes); free(codes1); free(out);
   return bad ? 5 : 0;
 }
 
