@@ -57,6 +57,8 @@ def parse():
                     help="skip the epilogue-amax measurement on the largest product")
     ap.add_argument("--no-delayed", action="store_true",
                     help="skip the delayed-scaling (cast with its amax folded in) measurement")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the step captured as a HIP graph and replayed")
     ap.add_argument("--quant", choices=["one-call", "three-calls"], default="one-call",
                     help="how the timed steps quantise each activation: fp8_quantize, or "
                          "fp8_amax -> fp8_compute_bias -> fp8_scale_cast (the steps with per-kernel "
@@ -217,6 +219,61 @@ def delayed_quant(fl, w, plan, q, x, reps=9):
 
 COLD_FLUSH_BYTES = 768 << 20   # > the 256 MB Infinity Cache
 COLD_CLEAN_BYTES = 512 << 20
+
+
+def graph_replay(step, q, outs, steps):
+    """The timed step captured once as a HIP graph (on a side stream: the
+    library launches on torch's current stream, which capture redirects) and
+    replayed `steps` times back to back, wall clock; every output (codes,
+    biases, amaxes, products) compared bit for bit with the eager step's after
+    the first replay, after the timed replays, and after one more replay that
+    follows an eager step.  No host launch work per step: what launch-bound
+    workloads would run at when a caller replays its step."""
+    import torch
+
+    def snapshot():
+        snap = {}
+        for n, (codes, bias, amax, _) in q.items():
+            snap[n] = (codes.clone(), bias.clone(), amax.view(torch.int32).clone())
+        for k, o in outs.items():
+            snap[k] = o.view(torch.int32).clone()
+        return snap
+
+    torch.cuda.synchronize()
+    step()
+    torch.cuda.synchronize()
+    eager = snapshot()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    def same_as_eager():
+        got = snapshot()
+        return all(all(torch.equal(a, b) for a, b in zip(eager[k], got[k])) if isinstance(eager[k], tuple)
+                   else torch.equal(eager[k], got[k]) for k in eager)
+
+    graph.replay()
+    torch.cuda.synchronize()
+    checks = [same_as_eager()]
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    checks.append(same_as_eager())
+    # eager work in between, then one more replay
+    step()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    checks.append(same_as_eager())
+    same = all(checks)
+    del graph
+    return {"ms_per_step": round(ms, 4), "replays": steps, "outputs_identical_to_eager": bool(same)}
 
 
 def one_call_quant(fl, w, plan, q, x, reps=9):
@@ -819,6 +876,7 @@ def main():
     import statistics
     step_median_ms = statistics.median(a.elapsed_time(b) for a, b in step_ev)
 
+    graph_info = None if args.no_graph else graph_replay(step, q, outs, args.steps)
     cold = None if args.no_cold else cold_quant(fl, w, plan, q, x, args.cold_reps)
     epi = None if args.no_epilogue_amax else epilogue_amax(fl, w, plan, q, outs, math, op_of)
     delayed = None if args.no_delayed else delayed_quant(fl, w, plan, q, x)
@@ -936,6 +994,8 @@ def main():
         "epilogue_amax": epi,
         "delayed_scaling": delayed,
         "one_call_quantisation": one_call,
+        "hip_graph": None if graph_info is None else dict(
+            graph_info, tflops=round(step_flops / (graph_info["ms_per_step"] * 1e-3) / 1e12, 2)),
         "step_breakdown_ms": {"gemm": round(gemm_ms / K, 4), "amax": round(amax_ms / K, 4),
                               "bias": round(bias_ms / K, 4), "cast": round(cast_ms / K, 4)},
     }

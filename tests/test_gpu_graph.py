@@ -1,0 +1,64 @@
+"""fp8_quantize (both of its paths) and a product captured as a HIP graph:
+every replay, with the inputs rewritten in place and eager work between the
+replays, gives the eager calls' outputs bit for bit.  The library launches on
+torch's current stream, so capture records its kernels (no memset nodes: the
+amax word is cleared by a kernel)."""
+import pytest
+import torch
+
+from gpu_util import need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fl():
+    return need_gpu()
+
+
+@pytest.mark.parametrize("n_rows", [96, 4096])   # 48 KiB (one workgroup) and 2 MiB (three launches) of bf16 x
+def test_quantize_and_product_replayed_from_a_graph(fl, n_rows):
+    K, N = 256, 192
+    g = torch.Generator(device="cuda").manual_seed(n_rows)
+    x = torch.empty(n_rows, K, dtype=torch.bfloat16, device="cuda")
+    w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    x8 = torch.empty(n_rows, K, dtype=torch.uint8, device="cuda")
+    w8 = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    bx, bw = (torch.empty(1, dtype=torch.int32, device="cuda") for _ in range(2))
+    ax, aw = (torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(2))
+    y = torch.empty(n_rows, N, dtype=torch.float32, device="cuda")
+
+    def step():
+        fl.quantize(x, fl.E4M3, 0, out=x8, bias=bx, amax=ax)
+        fl.quantize(w, fl.E4M3, 1, out=w8, bias=bw, amax=aw)
+        fl.scaled_gemm_fwd(x8, fl.E4M3, bx, w8, fl.E4M3, bw, out=y)
+
+    def outputs():
+        return [t.clone() for t in (x8, w8, bx, bw, ax.view(torch.int32), aw.view(torch.int32), y.view(torch.int32))]
+
+    def fill(seed):
+        x.copy_((torch.randn(n_rows, K, device="cuda", generator=torch.Generator(device="cuda").manual_seed(seed))
+                 * (1 + seed)).to(torch.bfloat16))
+
+    fill(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    for r in range(4):
+        say("graph replay", "rows", n_rows, "replay", r)
+        fill(r + 1)
+        step()                      # eager reference for this input
+        torch.cuda.synchronize()
+        ref = outputs()
+        for t in (x8, w8, bx, bw, ax, aw, y):   # clobber what the replay must rewrite
+            t.fill_(7)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = outputs()
+        for i, (a, b) in enumerate(zip(ref, got)):
+            assert torch.equal(a, b), (n_rows, r, i)
