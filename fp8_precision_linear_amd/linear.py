@@ -14,7 +14,8 @@ gradients are fp32 (autograd converts dx to x's dtype).
 
 Scaling modes (ScalingState):
   * "current": every quantisation is amax -> compute_bias -> cast on the
-    tensor itself, as the method states;
+    tensor itself, as the method states (one fp8_quantize call, which makes
+    them in one launch for small tensors and three for large ones);
   * "delayed": the bias of a tensor comes from the amax its previous step's
     cast returned, and the cast (fp8_scale_cast_amax) returns this step's
     amax in the same pass, so each quantisation reads its input once; the
