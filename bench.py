@@ -454,9 +454,9 @@ def record_traffic(d):
         "source_sha256": sources_sha(GEMM_SOURCES),
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/fetch -o run -- "
-            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax --no-delayed",
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax --no-delayed --no-graph",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/write -o run -- "
-            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax --no-delayed",
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax --no-delayed --no-graph",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/copy_fetch -o run -- "
             "python3 bench.py --copy-calibration",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/copy_write -o run -- "

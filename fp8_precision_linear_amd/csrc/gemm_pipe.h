@@ -321,41 +321,6 @@ __device__ __forceinline__ void store_block_as(const GemmProblem& p, const v16f 
   const int h = lane >> 5, rl = lane & 31;
   const int unscale = -(*p.bias_a + *p.bias_b);
   uint32_t mx = 0;
-  if (row0 + 32 * TM <= p.m && col0 + 32 * TN <= p.n && p.ldc < (int64_t)1 << 22) {
-    // Interior block (the common case): no bounds checks, and each address is
-    // the block's wave-uniform base plus a 32-bit offset (the block spans
-    // fewer than 2^32 bytes) summed from row multiples of ldc computed once,
-    // instead of a 64-bit row * ldc product per store.
-    float* base = p.c + (int64_t)row0 * p.ldc + col0;
-    const uint32_t ld = (uint32_t)p.ldc;
-    const uint32_t lane_off = 4u * (uint32_t)h * ld + (uint32_t)rl;
-    uint32_t o_r3[4], o_q[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      o_r3[t] = opaque((uint32_t)t * ld + lane_off);  // rows r % 4, plus the lane's own
-      o_q[t] = opaque((uint32_t)(8 * t) * ld);        // rows 8 (r / 4)
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const uint32_t o_i = opaque((uint32_t)(32 * i) * ld);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t o_iq = o_i + o_q[q];
-#pragma unroll
-        for (int r3 = 0; r3 < 4; ++r3) {
-          float* rowp = base + (o_iq + o_r3[r3]);
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            const float v = __builtin_ldexpf(acc[i][j][4 * q + r3], unscale);
-            __builtin_nontemporal_store(v, rowp + 32 * j);
-            if constexpr (AMAX) mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu);
-          }
-        }
-      }
-    }
-    if constexpr (AMAX) amax_fold(mx, p.amax);
-    return;
-  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
