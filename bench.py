@@ -109,10 +109,10 @@ def sources_sha(paths):
     return h.hexdigest()
 
 
-def traffic_record(workload):
+def traffic_record(workload, path=None):
     """HBM bytes per launch from committed PMC counters, valid only for the
     workload and kernel sources they were taken on."""
-    path = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    path = path or os.path.join(ROOT, "profiles", "gemm_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -412,7 +412,7 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 2}), flush=True)
 
 
-def record_traffic(d):
+def record_traffic(d, out=None):
     """profiles/gemm_traffic.json from four rocprofv3 --pmc runs (CSV output):
     FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the bench's product
     kernels, and of the calibration copy.  Each counter is scaled by
@@ -464,7 +464,7 @@ def record_traffic(d):
             "python3 bench.py --record-traffic <DIR>",
         ],
     }
-    out = os.path.join(ROOT, "profiles", "gemm_traffic.json")
+    out = out or os.path.join(ROOT, "profiles", "gemm_traffic.json")
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec), flush=True)
