@@ -746,7 +746,7 @@ static int64_t small_quant_max(int dtype) {
 hipError_t launch_quantize(const void* x, int dtype, int64_t n, int fmt, int32_t margin, uint8_t* y,
                            float* amax, int32_t* bias, hipStream_t stream) {
   uint32_t* a = reinterpret_cast<uint32_t*>(amax);
-  if (n <= small_quant_max(dtype)) {
+  if (n == 0 || n <= small_quant_max(dtype)) {  // an empty tensor still writes amax and bias
     const uint4* xv = static_cast<const uint4*>(x);
     if (dtype == FP8_IN_BF16) {
       const int64_t nunit = n / 16;

@@ -406,7 +406,7 @@ def test_quantize_in_one_call(fl, dtype, monkeypatch):
             for fmt, margin in ((E4M3, 0), (E5M2, 1), (E3M4, -2), (E4M3, 64)):
                 a_ref, b_ref, c_ref = oracle.quantize(words, fmt, margin)
                 cc, cb, ca = fl.quantize_chain(x, fmt, margin)
-                for path, small in (("one workgroup", "2000000000"), ("three launches", "0"),
+                for path, small in (("one workgroup", "2000000000"), ("three launches", "-1"),
                                     ("default choice", None)):
                     if small is None:
                         monkeypatch.delenv("FP8LIN_QUANT_SMALL", raising=False)
