@@ -57,6 +57,8 @@ def parse():
                     help="skip the epilogue-amax measurement on the largest product")
     ap.add_argument("--no-delayed", action="store_true",
                     help="skip the delayed-scaling (cast with its amax folded in) measurement")
+    ap.add_argument("--no-split", action="store_true",
+                    help="products never split along the contraction (no workspace)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the step captured as a HIP graph and replayed")
     ap.add_argument("--quant", choices=["one-call", "three-calls"], default="one-call",
@@ -808,6 +810,18 @@ def main():
             outs[(l.name, which)] = torch.empty(gemm_operands(l, which)[2], dtype=torch.float32, device=dev)
     math = fl.MATH_EXACT if args.math == "exact" else fl.MATH_NATIVE_FP8
     op_of = {"fwd": fl.OP_FWD, "dgrad": fl.OP_DGRAD, "wgrad": fl.OP_WGRAD}
+    # products whose outputs have too few tiles to fill the chip run split
+    # along the contraction in a workspace allocated here, once (the library
+    # allocates nothing); None where a product is not split
+    ws_of, ws = {}, None
+    if not args.no_split:
+        for item in plan:
+            if item[0] == "gemm":
+                _, l, which = item
+                ws_of[(l.name, which)] = fl.gemm_workspace_bytes(op_of[which], l.M, l.N, l.K)
+        need = max(ws_of.values(), default=0)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+    split_products = [f"{k[0]}:{k[1]}" for k, v in ws_of.items() if v > 0]
 
     def step(ev=None):
         for item in plan:
@@ -841,7 +855,8 @@ def main():
                 if ev is not None:
                     ev.append(("gemm_start", (l.name, which), torch.cuda.Event(enable_timing=True)))
                     ev[-1][2].record()
-                fl.scaled_gemm(op_of[which], a8, fa, ba, b8, fb, bb, math=math, out=outs[(l.name, which)])
+                fl.scaled_gemm(op_of[which], a8, fa, ba, b8, fb, bb, math=math, out=outs[(l.name, which)],
+                               workspace=ws if ws_of.get((l.name, which), 0) > 0 else None)
                 if ev is not None:
                     ev.append(("gemm_end", (l.name, which), torch.cuda.Event(enable_timing=True)))
                     ev[-1][2].record()
@@ -940,6 +955,7 @@ def main():
             "accumulate": "f32",
             "input_sha256": {t.name: synth.sha256(host[t.name]) for t in w.tensors},
             "math": args.math,
+            "split_along_contraction": split_products,
             "quantisation": ("fp8_quantize per activation (one call: one workgroup up to 256 KiB, "
                              "else clear, amax and a cast deriving the bias)" if args.quant == "one-call"
                              else "fp8_amax -> fp8_compute_bias -> fp8_scale_cast per activation"),

@@ -49,6 +49,8 @@ SIGNATURES = {
     "fp8_quantize": (_ci, [_vp, _ci, _i64, _ci, _i32, _vp, _vp, _vp, _vp]),
     "fp8_scaled_gemm": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_amax": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_scaled_gemm_workspace_bytes": (_i64, [_ci, _i64, _i64, _i64]),
+    "fp8_scaled_gemm_ws": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp]),
     "fp8_scaled_gemm_fwd": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_dgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_wgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
@@ -203,12 +205,25 @@ def scaled_gemm_wgrad(dy8, fdy, bdy, x8, fx, bx, out=None, stream=None):
     return out
 
 
-def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=None, amax=None):
+def gemm_workspace_bytes(op, M, N, K):
+    """Workspace bytes scaled_gemm(..., workspace=...) needs for this product
+    (0: it is not split along the contraction) (fp8_scaled_gemm_workspace_bytes)."""
+    v = lib.fp8_scaled_gemm_workspace_bytes(int(op), int(M), int(N), int(K))
+    if v < 0:
+        raise Fp8Error("fp8_scaled_gemm_workspace_bytes", v)
+    return v
+
+
+def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=None, amax=None,
+                workspace=None):
     """Any of the three products with a chosen arithmetic (fp8_scaled_gemm).
     op: OP_FWD (a = X8[M, K], b = W8[N, K]), OP_DGRAD (a = dY8[M, N], b = W8[N, K])
     or OP_WGRAD (a = dY8[M, N], b = X8[M, K]); math: MATH_EXACT or MATH_NATIVE_FP8.
     amax: optional float32[1] device tensor that receives max |out|, computed
-    in the product's epilogue (fp8_scaled_gemm_amax)."""
+    in the product's epilogue (fp8_scaled_gemm_amax).
+    workspace: optional device tensor of at least gemm_workspace_bytes(op, M, N, K)
+    bytes; with it an output of few tiles is computed split along the
+    contraction (fp8_scaled_gemm_ws).  Not combined with amax."""
     _need_cuda(a8, b8, ba, bb)
     if op == OP_FWD:
         (M, K), (N, K2) = a8.shape, b8.shape
@@ -224,7 +239,16 @@ def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=No
     if not ok:
         raise ValueError("contraction sizes differ")
     out = torch.empty(shape, dtype=torch.float32, device=a8.device) if out is None else out
-    if amax is None:
+    if workspace is not None:
+        if amax is not None:
+            raise ValueError("a workspace and an output amax are not combined")
+        _need_cuda(workspace)
+        nbytes = workspace.numel() * workspace.element_size()
+        _check("fp8_scaled_gemm_ws",
+               lib.fp8_scaled_gemm_ws(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8), int(fb),
+                                      _ptr(bb), M, N, K, _ptr(out), _ptr(workspace), nbytes,
+                                      _stream(stream)))
+    elif amax is None:
         _check("fp8_scaled_gemm",
                lib.fp8_scaled_gemm(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8), int(fb),
                                    _ptr(bb), M, N, K, _ptr(out), _stream(stream)))

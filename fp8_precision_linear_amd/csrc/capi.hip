@@ -143,9 +143,22 @@ namespace {
 
 // The three products; out_amax (optional) receives max |out|.  Every argument
 // is checked before any HIP call; on error nothing is written.
+// The product's output as rows x cols with contraction `depth`, for each op.
+bool out_shape(fp8_gemm_op_t op, int64_t M, int64_t N, int64_t K, int64_t& rows, int64_t& cols,
+               int64_t& depth) {
+  switch (op) {
+    case FP8_GEMM_FWD: rows = M; cols = N; depth = K; return true;
+    case FP8_GEMM_DGRAD: rows = M; cols = K; depth = N; return true;
+    case FP8_GEMM_WGRAD: rows = N; cols = K; depth = M; return true;
+    default: return false;
+  }
+}
+
+// with_ws: the fp8_scaled_gemm_ws form (ws / ws_bytes checked here).
 int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, const int32_t* ba,
                 const uint8_t* b, fp8_format_t fb, const int32_t* bb, int64_t M, int64_t N,
-                int64_t K, float* out, float* out_amax, hipStream_t st) {
+                int64_t K, float* out, float* out_amax, bool with_ws, void* ws, int64_t ws_bytes,
+                hipStream_t st) {
   if (math != FP8_GEMM_EXACT && math != FP8_GEMM_NATIVE_FP8) return FP8_ERR_OP;
   fp8lin::GemmProblem p{};
   bool empty = false;
@@ -175,6 +188,16 @@ int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, c
     default:
       return FP8_ERR_OP;
   }
+  bool split = false;
+  if (with_ws && !empty) {
+    const int64_t need = fp8lin::gemm_split_workspace_bytes(p.m, p.n, p.k);
+    if (need > 0) {
+      if (!ws) return FP8_ERR_NULL;
+      if (misaligned(ws)) return FP8_ERR_ALIGN;
+      if (ws_bytes < need) return FP8_ERR_SIZE;
+      split = true;
+    }
+  }
   if (empty && !out_amax) return FP8_OK;
   if (int s = device_ok()) return s;
   if (out_amax) {
@@ -182,6 +205,14 @@ int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, c
     if (int s = hip_status(fp8lin::launch_clear_u32(p.amax, st))) return s;
   }
   if (empty) return FP8_OK;
+  if (split) {
+    float* w = static_cast<float*>(ws);
+    switch (op) {
+      case FP8_GEMM_FWD: return hip_status(fp8lin::launch_gemm_fwd_ws(p, w, st));
+      case FP8_GEMM_DGRAD: return hip_status(fp8lin::launch_gemm_dgrad_ws(p, w, st));
+      default: return hip_status(fp8lin::launch_gemm_wgrad_ws(p, w, st));
+    }
+  }
   switch (op) {
     case FP8_GEMM_FWD: return hip_status(fp8lin::launch_gemm_fwd(p, st));
     case FP8_GEMM_DGRAD: return hip_status(fp8lin::launch_gemm_dgrad(p, st));
@@ -196,7 +227,24 @@ extern "C" {
 int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
                     const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
                     int64_t M, int64_t N, int64_t K, float* out, void* stream) {
-  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, nullptr, (hipStream_t)stream);
+  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, nullptr, false, nullptr, 0,
+                     (hipStream_t)stream);
+}
+
+int64_t fp8_scaled_gemm_workspace_bytes(fp8_gemm_op_t op, int64_t M, int64_t N, int64_t K) {
+  if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8_ERR_SIZE;
+  int64_t rows, cols, depth;
+  if (!out_shape(op, M, N, K, rows, cols, depth)) return FP8_ERR_OP;
+  return fp8lin::gemm_split_workspace_bytes(rows, cols, depth);
+}
+
+int fp8_scaled_gemm_ws(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
+                       const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
+                       int64_t M, int64_t N, int64_t K, float* out, void* ws, int64_t ws_bytes,
+                       void* stream) {
+  if (ws_bytes < 0) return FP8_ERR_SIZE;
+  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, nullptr, true, ws, ws_bytes,
+                     (hipStream_t)stream);
 }
 
 int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
@@ -205,7 +253,8 @@ int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_forma
                          void* stream) {
   if (!out_amax) return FP8_ERR_NULL;
   if (misaligned_word(out_amax)) return FP8_ERR_ALIGN;
-  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, out_amax, (hipStream_t)stream);
+  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, out_amax, false, nullptr, 0,
+                     (hipStream_t)stream);
 }
 
 int fp8_scaled_gemm_fwd(const uint8_t* x8, fp8_format_t fx, const int32_t* bx,

@@ -12,6 +12,9 @@ products run in FP8 and are unscaled afterwards (bullet 3), in training
 x may have any leading dimensions ([..., K]); w is [N, K].  Outputs and
 gradients are fp32 (autograd converts dx to x's dtype).
 
+Products whose outputs have too few tiles to fill the GPU (a small batch of
+tokens) run split along the contraction (fp8_scaled_gemm_ws).
+
 Scaling modes (ScalingState):
   * "current": every quantisation is amax -> compute_bias -> cast on the
     tensor itself, as the method states (one fp8_quantize call, which makes
@@ -28,8 +31,8 @@ quantises the weight once; later calls reuse its codes and bias.
 """
 import torch
 
-from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, compute_bias, quantize,
-               scale_cast, scaled_gemm)
+from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, compute_bias, gemm_workspace_bytes,
+               quantize, scale_cast, scaled_gemm)
 from .mlp import BiasLog
 
 ROLES = ("x", "w", "dy")
@@ -83,6 +86,14 @@ def _flat(t):
     return t.contiguous().reshape(-1, t.shape[-1])
 
 
+def _product(op, a8, fa, ba, b8, fb, bb, math, M, N, K):
+    """One product; an output of too few tiles to fill the GPU runs split
+    along the contraction in a workspace from torch's caching allocator."""
+    nbytes = gemm_workspace_bytes(op, M, N, K)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=a8.device) if nbytes > 0 else None
+    return scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=math, workspace=ws)
+
+
 class FP8LinearFunction(torch.autograd.Function):
     """y = x . w^T with FP8-AMAX products; gradients for x and w."""
 
@@ -93,7 +104,8 @@ class FP8LinearFunction(torch.autograd.Function):
         x2 = _flat(x)
         x8, bx = state.quantise("x", x2)
         w8, bw = state.quantise("w", w.contiguous())
-        y = scaled_gemm(OP_FWD, x8, E4M3, bx, w8, E4M3, bw, math=state.math)
+        M, K = x8.shape
+        y = _product(OP_FWD, x8, E4M3, bx, w8, E4M3, bw, state.math, M, w8.shape[0], K)
         ctx.saved = (x8, bx, w8, bw)
         ctx.state = state
         ctx.x_shape = x.shape
@@ -104,8 +116,9 @@ class FP8LinearFunction(torch.autograd.Function):
         x8, bx, w8, bw = ctx.saved
         state = ctx.state
         dy8, bdy = state.quantise("dy", _flat(dy))
-        dx = scaled_gemm(OP_DGRAD, dy8, E5M2, bdy, w8, E4M3, bw, math=state.math)
-        dw = scaled_gemm(OP_WGRAD, dy8, E5M2, bdy, x8, E4M3, bx, math=state.math)
+        (M, N), K = dy8.shape, w8.shape[1]
+        dx = _product(OP_DGRAD, dy8, E5M2, bdy, w8, E4M3, bw, state.math, M, N, K)
+        dw = _product(OP_WGRAD, dy8, E5M2, bdy, x8, E4M3, bx, state.math, M, N, K)
         ctx.saved = None
         return dx.reshape(ctx.x_shape), dw, None
 

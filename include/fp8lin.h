@@ -186,6 +186,37 @@ int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t f
                     const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
                     int64_t M, int64_t N, int64_t K, float* out, void* stream);
 
+/*
+ * Products whose output has too few 128 x 128 tiles to occupy the chip (a
+ * small batch of tokens; an output with a short side) run faster split along
+ * the contraction: each slice's sum goes to a caller-provided workspace, then
+ * the slices are added in slice order and unscaled once, so equal inputs give
+ * equal bits on every call.  These two entry points are for callers who can
+ * provide that workspace; fp8_scaled_gemm never splits.
+ *
+ * fp8_scaled_gemm_workspace_bytes: the workspace bytes fp8_scaled_gemm_ws
+ * needs for this product and shape (0: it is not split and needs none), or
+ * FP8_ERR_SIZE / FP8_ERR_OP for a bad size or op.  A pure function of
+ * (op, M, N, K); no device is touched.
+ *
+ * fp8_scaled_gemm_ws: fp8_scaled_gemm with a workspace.
+ *   ws        device, 16-byte aligned, at least
+ *             fp8_scaled_gemm_workspace_bytes(op, M, N, K) bytes (the
+ *             caller's; the call overwrites it and keeps no pointer).  May be
+ *             NULL when that is 0.
+ *   ws_bytes  its size.
+ * Returns FP8_ERR_NULL / FP8_ERR_ALIGN / FP8_ERR_SIZE for a missing,
+ * misaligned or too small workspace the product needs, otherwise as
+ * fp8_scaled_gemm.  Results are within the same bound as fp8_scaled_gemm's
+ * (the sums are formed in another order, so the bits may differ from its
+ * bits); an unsplit product is fp8_scaled_gemm itself.
+ */
+int64_t fp8_scaled_gemm_workspace_bytes(fp8_gemm_op_t op, int64_t M, int64_t N, int64_t K);
+int fp8_scaled_gemm_ws(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
+                       const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
+                       int64_t M, int64_t N, int64_t K, float* out, void* ws, int64_t ws_bytes,
+                       void* stream);
+
 /* fp8_scaled_gemm that also returns the per-tensor amax of its output (the
  * "Proposed method" bullet-1 statistic of the tensor the product produces),
  * computed in the product's own epilogue, so that quantising the output next

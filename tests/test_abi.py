@@ -31,7 +31,7 @@ def status(code):
 
 def test_every_declared_function_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
         assert n in fl.SIGNATURES, n
@@ -234,3 +234,47 @@ def test_quantize_argument_checks():
 def test_quantize_without_a_device_reports_no_device():
     assert L.fp8_quantize(A16, 0, 10, 0, 0, A48, A32, A32, None) == status("FP8_ERR_DEVICE")
     assert L.fp8_quantize(None, 1, 0, 2, 3, None, A32, A32, None) == status("FP8_ERR_DEVICE")
+
+
+def test_gemm_workspace_bytes():
+    f = L.fp8_scaled_gemm_workspace_bytes
+    FWD, DGRAD, WGRAD = 0, 1, 2
+    # 2048 x 768 output (96 tiles of 128 x 128), contraction 3072 (48 stages): 2 slices
+    assert f(FWD, 2048, 768, 3072) == 2 * 2048 * 768 * 4
+    assert f(DGRAD, 2048, 3072, 768) == 2 * 2048 * 768 * 4      # dX[M x K], contraction N
+    assert f(WGRAD, 3072, 2304, 768) == 2 * 2304 * 768 * 4      # dW[N x K] (108 tiles), contraction M
+    assert f(FWD, 2048, 768, 2304) == 0           # 36 stages: two slices would be under 24 stages
+    # 128 x 8192 output (64 tiles), contraction 8192: 4 slices
+    assert f(FWD, 128, 8192, 8192) == 4 * 128 * 8192 * 4
+    # one tile, contraction of 240 stages: 10 slices of 24 stages
+    assert f(FWD, 100, 100, 240 * 64) == 10 * 100 * 100 * 4
+    assert f(FWD, 8192, 8192, 8192) == 0          # fills the chip
+    assert f(FWD, 2048, 2304, 768) == 0           # 288 tiles
+    assert f(FWD, 128, 8192, 100) == 0            # contraction not whole 64-byte stages
+    assert f(FWD, 128, 128, 192) == 0             # too short to split
+    assert f(FWD, 0, 128, 4096) == 0
+    assert f(5, 128, 128, 4096) == status("FP8_ERR_OP")
+    assert f(FWD, -1, 128, 4096) == status("FP8_ERR_SIZE")
+
+
+def test_gemm_ws_argument_checks():
+    f = L.fp8_scaled_gemm_ws
+    split = (0, 0, A16, 0, A32, A48, 0, A32, 2048, 768, 3072, A16)      # needs 12 MiB of workspace
+    need = 2 * 2048 * 768 * 4
+    assert f(*split, None, need, None) == status("FP8_ERR_NULL")
+    assert f(*split, MIS, need, None) == status("FP8_ERR_ALIGN")
+    assert f(*split, A48, need - 1, None) == status("FP8_ERR_SIZE")
+    assert f(*split, A48, -1, None) == status("FP8_ERR_SIZE")
+    assert f(9, 0, A16, 0, A32, A48, 0, A32, 64, 64, 64, A16, A48, need, None) == status("FP8_ERR_OP")
+    assert f(0, 0, A16, 2, A32, A48, 0, A32, 64, 64, 64, A16, A48, need, None) == status("FP8_ERR_FORMAT")
+    # an empty output needs nothing
+    assert f(0, 0, None, 0, None, None, 0, None, 0, 768, 3072, None, None, 0, None) == 0
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
+def test_gemm_ws_without_a_device_reports_no_device():
+    f = L.fp8_scaled_gemm_ws
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 2048, 768, 3072, A16, A48, 2 * 2048 * 768 * 4, None) \
+        == status("FP8_ERR_DEVICE")
+    # a product that is not split needs no workspace
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 8192, 8192, 8192, A16, None, 0, None) == status("FP8_ERR_DEVICE")

@@ -298,3 +298,74 @@ def test_two_launch_split_of_the_output(fl, which, R, C, Kc, split, math):
     check_gemm(got[rows, cols], ref, bound, f"split {which} {R}x{C} ({split}) {math}", rel=rel)
     # the epilogue amax covers both launches
     assert int(am.view(torch.int32).item()) & 0xFFFFFFFF == int((got.view(np.uint32) & 0x7FFFFFFF).max())
+
+
+# Products split along the contraction (fp8_scaled_gemm_ws): outputs of few
+# 128 x 128 tiles, contraction lengths whose last slice is shorter (3200 =
+# 50 stages in two), ragged output sides (multiples of 16 where an operand is
+# read contraction-major), a single tile split ten ways, and per product one
+# shape that is not split (workspace 0).
+SPLIT_SHAPES = {
+    "fwd": [(128, 256, 4096), (100, 300, 3200), (16, 48, 6400), (100, 100, 15360), (2048, 768, 3072),
+            (1024, 2048, 4096), (2048, 2048, 1024)],
+    "dgrad": [(128, 3200, 256), (96, 6400, 80), (2048, 3072, 768), (1024, 4096, 2048), (2048, 1024, 2048)],
+    "wgrad": [(3200, 128, 256), (6400, 96, 80), (3072, 2304, 768), (4096, 1024, 2048), (1024, 2048, 2048)],
+}
+UNSPLIT = {(2048, 2048, 1024), (2048, 1024, 2048), (1024, 2048, 2048)}   # 256 output tiles
+
+
+@pytest.mark.parametrize("which", ["fwd", "dgrad", "wgrad"])
+def test_split_products_against_the_oracle(fl, which):
+    """Within the bound of every (M, N, K) and format pair, both exact MFMAs;
+    bit-identical on a second call (the slices are added in a fixed order);
+    a too small workspace is refused before anything runs."""
+    op = {"fwd": fl.OP_FWD, "dgrad": fl.OP_DGRAD, "wgrad": fl.OP_WGRAD}[which]
+    rng = np.random.default_rng(4242)
+    for si, (M, N, K) in enumerate(SPLIT_SHAPES[which]):
+        nbytes = fl.gemm_workspace_bytes(op, M, N, K)
+        assert (nbytes == 0) == ((M, N, K) in UNSPLIT), (which, M, N, K, nbytes)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+        for fa, fb in PAIRS:
+            a8, b8 = operands(rng, which, M, N, K, fa, fb)
+            ba, bb = int(rng.integers(-12, 20)), int(rng.integers(-12, 20))
+            ref, bound = reference(which, a8, fa, ba, b8, fb, bb)
+            A, B, BA, BB = u8_dev(a8), u8_dev(b8), i32_dev(ba), i32_dev(bb)
+            for mfma in ("f16", "bf16"):
+                os.environ["FP8LIN_EXACT_MFMA"] = mfma
+                try:
+                    say("split product", which, "shape", M, N, K, "fmts", fa, fb, "mfma", mfma, "ws", nbytes)
+                    got = fl.scaled_gemm(op, A, fa, BA, B, fb, BB, workspace=ws)
+                    again = fl.scaled_gemm(op, A, fa, BA, B, fb, BB, workspace=ws)
+                finally:
+                    del os.environ["FP8LIN_EXACT_MFMA"]
+                assert torch.equal(got.view(torch.int32), again.view(torch.int32)), (which, M, N, K)
+                check_gemm(got.cpu().numpy(), ref, bound, f"split {which} {M}x{N}x{K} {fa}{fb} {mfma}")
+        if nbytes > 0:
+            with pytest.raises(fl.Fp8Error) as e:
+                fl.scaled_gemm(op, A, fa, BA, B, fb, BB, workspace=ws[:nbytes - 16])
+            assert e.value.status == -2
+
+
+def test_split_product_native_fp8_and_unsplit_identity(fl):
+    """The native FP8 arithmetic split within its own bound (2^-7 of sum |ab|
+    per 64 products, plus fp32 rounding); an unsplit shape with a workspace
+    is fp8_scaled_gemm itself, bit for bit."""
+    rng = np.random.default_rng(77)
+    M, N, K = 128, 512, 4096
+    a8, b8 = operands(rng, "fwd", M, N, K, E4M3, E4M3)
+    ref, bound = reference("fwd", a8, E4M3, 3, b8, E4M3, 5)
+    A, B, BA, BB = u8_dev(a8), u8_dev(b8), i32_dev(3), i32_dev(5)
+    nbytes = fl.gemm_workspace_bytes(fl.OP_FWD, M, N, K)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    say("split native", M, N, K)
+    got = fl.scaled_gemm(fl.OP_FWD, A, E4M3, BA, B, E4M3, BB, math=fl.MATH_NATIVE_FP8, workspace=ws)
+    # the native arithmetic's bound, plus one fp32 rounding per slice added
+    check_gemm(got.cpu().numpy(), ref, bound, "native split", rel=2.0 ** -7 + (K / 64 + 1 + 16) * 2.0 ** -24)
+    M, N, K = 2048, 2048, 1024        # 256 output tiles of 128 x 128: not split
+    assert fl.gemm_workspace_bytes(fl.OP_FWD, M, N, K) == 0
+    a8, b8 = operands(rng, "fwd", M, N, K, E4M3, E4M3)
+    A, B = u8_dev(a8), u8_dev(b8)
+    plain = fl.scaled_gemm(fl.OP_FWD, A, E4M3, BA, B, E4M3, BB)
+    with_ws = fl.scaled_gemm(fl.OP_FWD, A, E4M3, BA, B, E4M3, BB, workspace=ws)
+    assert torch.equal(plain.view(torch.int32), with_ws.view(torch.int32))

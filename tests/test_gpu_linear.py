@@ -150,3 +150,32 @@ def test_linear_frozen_weight_for_inference(fl):
     lin.unfreeze_weight()
     with torch.no_grad():
         assert not torch.equal(lin(xd), y_ref)
+
+
+def test_linear_small_batch_splits_its_forward_product(fl):
+    """32 tokens through a 4096 -> 1024 layer: the forward output has 8 tiles,
+    so its product runs split along the contraction (fp8_scaled_gemm_ws);
+    every product against the oracle."""
+    from fp8_precision_linear_amd import linear
+    x, w, g = tensors((32, 4096), 1024, 2)
+    assert fl.gemm_workspace_bytes(fl.OP_FWD, 32, 1024, 4096) > 0
+    lin = linear.FP8Linear(4096, 1024, device="cuda")
+    with torch.no_grad():
+        lin.weight.copy_(w)
+    xd = x.cuda().requires_grad_()
+    say("fp8 linear, 32 tokens, split forward product")
+    y = lin(xd)
+    y.backward(g.cuda())
+    torch.cuda.synchronize()
+    xw, ww, gw = synth.bf16_words(x), w.numpy().view(np.uint32), g.numpy().view(np.uint32)
+    _, bx, x8 = oracle.quantize(xw, E4M3)
+    _, bw, w8 = oracle.quantize(ww, E4M3)
+    _, bdy, dy8 = oracle.quantize(gw, E5M2)
+    ref, bound = oracle.gemm_fwd(x8, E4M3, bx, w8, E4M3, bw)
+    check_gemm(y.detach().cpu().numpy(), ref, bound, "small-batch linear fwd (split)")
+    ref, bound = oracle.gemm_wgrad(dy8, E5M2, bdy, x8, E4M3, bx)
+    check_gemm(lin.weight.grad.cpu().numpy(), ref, bound, "small-batch linear wgrad")
+    ref, bound = oracle.gemm_dgrad(dy8, E5M2, bdy, w8, E4M3, bw)
+    # dx in x's dtype (bf16): within the bound plus half a bf16 ulp of the result
+    dx = xd.grad.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(dx - ref) <= 1e-5 * bound + np.abs(ref) * 2.0 ** -8), "small-batch linear dgrad"
