@@ -202,8 +202,10 @@ int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t f
  * fp8_scaled_gemm_ws: fp8_scaled_gemm with a workspace.
  *   ws        device, 16-byte aligned, at least
  *             fp8_scaled_gemm_workspace_bytes(op, M, N, K) bytes (the
- *             caller's; the call overwrites it and keeps no pointer).  May be
- *             NULL when that is 0.
+ *             caller's; the call overwrites it and keeps no pointer), not
+ *             overlapping the operands or the output.  May be NULL when that
+ *             is 0.  Calls in flight at the same time need separate
+ *             workspaces.
  *   ws_bytes  its size.
  * Returns FP8_ERR_NULL / FP8_ERR_ALIGN / FP8_ERR_SIZE for a missing,
  * misaligned or too small workspace the product needs, otherwise as

@@ -47,6 +47,9 @@ static int checks(void) {
   bad += expect("gemm E3M4", fp8_scaled_gemm_fwd((uint8_t*)p, FP8_E3M4, (int32_t*)p, (uint8_t*)p, FP8_E4M3, (int32_t*)p, 8, 8, 8, (float*)p, NULL), FP8_ERR_FORMAT);
   bad += expect("gemm op", fp8_scaled_gemm((fp8_gemm_op_t)5, FP8_GEMM_EXACT, (uint8_t*)p, FP8_E4M3, (int32_t*)p, (uint8_t*)p, FP8_E4M3, (int32_t*)p, 8, 8, 8, (float*)p, NULL), FP8_ERR_OP);
   bad += expect("swiglu size", fp8_swiglu_fwd((float*)p, -2, 4, (uint16_t*)p, NULL, NULL), FP8_ERR_SIZE);
+  bad += expect("workspace op", (int)fp8_scaled_gemm_workspace_bytes((fp8_gemm_op_t)7, 8, 8, 64), FP8_ERR_OP);
+  if (fp8_scaled_gemm_workspace_bytes(FP8_GEMM_FWD, 128, 8192, 8192) != 4LL * 128 * 8192 * 4) bad++;
+  bad += expect("ws too small", fp8_scaled_gemm_ws(FP8_GEMM_FWD, FP8_GEMM_EXACT, (uint8_t*)p, FP8_E4M3, (int32_t*)p, (uint8_t*)p, FP8_E4M3, (int32_t*)p, 128, 8192, 8192, (float*)p, p, 16, NULL), FP8_ERR_SIZE);
   bad += expect("quantize margin", fp8_quantize(p, FP8_IN_BF16, 8, FP8_E4M3, -FP8_MAX_MARGIN - 1, (uint8_t*)p, (float*)p, (int32_t*)p, NULL), FP8_ERR_MARGIN);
   if (strlen(fp8_status_string(FP8_ERR_ALIGN)) == 0) bad++;
   return bad;

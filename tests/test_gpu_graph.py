@@ -62,3 +62,50 @@ def test_quantize_and_product_replayed_from_a_graph(fl, n_rows):
         got = outputs()
         for i, (a, b) in enumerate(zip(ref, got)):
             assert torch.equal(a, b), (n_rows, r, i)
+
+
+def test_split_product_replayed_from_a_graph(fl):
+    """A product split along the contraction (its two kernels: slices, then
+    the ordered sum) captured as a graph: every replay, with new operands
+    written in place and eager calls between, equals the eager call bit for bit."""
+    M, N, K = 128, 1024, 4096
+    nbytes = fl.gemm_workspace_bytes(fl.OP_FWD, M, N, K)
+    assert nbytes > 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    x = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    w = (torch.randn(N, K, device="cuda", generator=torch.Generator(device="cuda").manual_seed(3)) * 0.02).to(torch.bfloat16)
+    x8 = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    w8 = torch.empty(N, K, dtype=torch.uint8, device="cuda")
+    bx, bw = (torch.empty(1, dtype=torch.int32, device="cuda") for _ in range(2))
+    ax, aw = (torch.empty(1, dtype=torch.float32, device="cuda") for _ in range(2))
+    y = torch.empty(M, N, dtype=torch.float32, device="cuda")
+
+    def step():
+        fl.quantize(x, fl.E4M3, 0, out=x8, bias=bx, amax=ax)
+        fl.quantize(w, fl.E4M3, 0, out=w8, bias=bw, amax=aw)
+        fl.scaled_gemm(fl.OP_FWD, x8, fl.E4M3, bx, w8, fl.E4M3, bw, out=y, workspace=ws)
+
+    def fill(seed):
+        g = torch.Generator(device="cuda").manual_seed(100 + seed)
+        x.copy_((torch.randn(M, K, device="cuda", generator=g) * (1 + seed)).to(torch.bfloat16))
+
+    fill(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    for r in range(4):
+        say("graph replay, split product", "replay", r)
+        fill(r + 1)
+        step()
+        torch.cuda.synchronize()
+        ref = y.clone()
+        y.fill_(7)
+        ws.fill_(7)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ref.view(torch.int32), y.view(torch.int32)), r
