@@ -28,6 +28,13 @@ struct SplitPlan {
 constexpr int kSplitMinStages = 24;
 constexpr int kSplitSlots = 256;    // workgroups the chip runs at once (one per CU)
 
+// FP8LIN_SPLIT_SLOTS overrides kSplitSlots (tuning).
+inline int64_t split_slots() {
+  const char* v = std::getenv("FP8LIN_SPLIT_SLOTS");
+  const int64_t s = v ? std::atoll(v) : kSplitSlots;
+  return s < 1 ? 1 : s;
+}
+
 // The split for an m x n output with contraction k: as many slices as the
 // chip has room for beside the output's 128x128 tiles, each at least
 // kSplitMinStages stages; none when the tiles already fill the chip, or the
@@ -37,7 +44,7 @@ inline SplitPlan plan_split(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0 || k % kPipeBK != 0) return SplitPlan{1, 0};
   const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
   const int64_t nk = k / kPipeBK;
-  int64_t s = kSplitSlots / tiles;
+  int64_t s = split_slots() / tiles;
   s = s < nk / kSplitMinStages ? s : nk / kSplitMinStages;
   if (s < 2) return SplitPlan{1, 0};
   const int64_t per = (nk + s - 1) / s;  // stages per slice; the last may be shorter

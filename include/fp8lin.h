@@ -30,7 +30,10 @@
  *    FP8LIN_GEMM_TILE=128|256 forces the products' tile, FP8LIN_EXACT_MFMA=
  *    f16|bf16 the 16-bit MFMA of the exact arithmetic, FP8LIN_AMAX_HINT /
  *    FP8LIN_CAST_HINT=cached ordinary instead of streaming loads, and
- *    FP8LIN_CAST_AMAX_UNITS=n the units per lane of fp8_scale_cast_amax.
+ *    FP8LIN_CAST_AMAX_UNITS=n the units per lane of fp8_scale_cast_amax,
+ *    FP8LIN_QUANT_SMALL=n the largest tensor (elements) fp8_quantize does in
+ *    one workgroup, and FP8LIN_SPLIT_SLOTS=n the workgroup slots the split of
+ *    fp8_scaled_gemm_ws plans for (256; it also changes the workspace size).
  */
 #ifndef FP8LIN_H
 #define FP8LIN_H
