@@ -261,6 +261,19 @@ def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=No
     return out
 
 
+def scaled_gemm_auto(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=None):
+    """scaled_gemm with, when the product is split along the contraction (an
+    output of too few tiles to fill the GPU), its workspace taken from
+    torch's caching allocator (gemm_workspace_bytes decides)."""
+    if op == OP_FWD:                  # X8[M, K], W8[N, K]
+        (M, K), N = a8.shape, b8.shape[0]
+    else:                             # dY8[M, N] with W8[N, K] (dgrad) or X8[M, K] (wgrad)
+        (M, N), K = a8.shape, b8.shape[1]
+    nbytes = gemm_workspace_bytes(op, M, N, K)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=a8.device) if nbytes > 0 else None
+    return scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=math, out=out, stream=stream, workspace=ws)
+
+
 def swiglu_fwd(h, out=None, amax=None, stream=None):
     """a = silu(g) * u as a bf16 tensor [rows, f], h = [g | u] float32 [rows, 2f]
     (fp8_swiglu_fwd).  amax: optional float32[1] device tensor that receives

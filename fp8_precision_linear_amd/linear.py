@@ -31,8 +31,8 @@ quantises the weight once; later calls reuse its codes and bias.
 """
 import torch
 
-from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, compute_bias, gemm_workspace_bytes,
-               quantize, scale_cast, scaled_gemm)
+from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, compute_bias, quantize,
+               scale_cast, scaled_gemm_auto)
 from .mlp import BiasLog
 
 ROLES = ("x", "w", "dy")
@@ -86,13 +86,6 @@ def _flat(t):
     return t.contiguous().reshape(-1, t.shape[-1])
 
 
-def _product(op, a8, fa, ba, b8, fb, bb, math, M, N, K):
-    """One product; an output of too few tiles to fill the GPU runs split
-    along the contraction in a workspace from torch's caching allocator."""
-    nbytes = gemm_workspace_bytes(op, M, N, K)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=a8.device) if nbytes > 0 else None
-    return scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=math, workspace=ws)
-
 
 class FP8LinearFunction(torch.autograd.Function):
     """y = x . w^T with FP8-AMAX products; gradients for x and w."""
@@ -104,8 +97,7 @@ class FP8LinearFunction(torch.autograd.Function):
         x2 = _flat(x)
         x8, bx = state.quantise("x", x2)
         w8, bw = state.quantise("w", w.contiguous())
-        M, K = x8.shape
-        y = _product(OP_FWD, x8, E4M3, bx, w8, E4M3, bw, state.math, M, w8.shape[0], K)
+        y = scaled_gemm_auto(OP_FWD, x8, E4M3, bx, w8, E4M3, bw, math=state.math)
         ctx.saved = (x8, bx, w8, bw)
         ctx.state = state
         ctx.x_shape = x.shape
@@ -116,9 +108,8 @@ class FP8LinearFunction(torch.autograd.Function):
         x8, bx, w8, bw = ctx.saved
         state = ctx.state
         dy8, bdy = state.quantise("dy", _flat(dy))
-        (M, N), K = dy8.shape, w8.shape[1]
-        dx = _product(OP_DGRAD, dy8, E5M2, bdy, w8, E4M3, bw, state.math, M, N, K)
-        dw = _product(OP_WGRAD, dy8, E5M2, bdy, x8, E4M3, bx, state.math, M, N, K)
+        dx = scaled_gemm_auto(OP_DGRAD, dy8, E5M2, bdy, w8, E4M3, bw, math=state.math)
+        dw = scaled_gemm_auto(OP_WGRAD, dy8, E5M2, bdy, x8, E4M3, bx, math=state.math)
         ctx.saved = None
         return dx.reshape(ctx.x_shape), dw, None
 

@@ -24,8 +24,9 @@ Backward (dy [T, d]):
 
 The fused gate-up weight is one tensor with one scale, and so is its gradient
 [dG | dU].  Every step runs in libfp8lin's kernels on the current stream with
-no host synchronisation; this module only allocates outputs and orders the
-calls.  Gradients come back in fp32 (autograd converts dx to x's dtype).
+no host synchronisation; this module only allocates outputs (and the
+workspace of a product split along the contraction, for small batches) and
+orders the calls.  Gradients come back in fp32 (autograd converts dx to x's dtype).
 """
 from contextlib import contextmanager
 from dataclasses import dataclass, field
@@ -33,7 +34,7 @@ from dataclasses import dataclass, field
 import torch
 
 from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, compute_bias, quantize,
-               scale_cast, scaled_gemm, swiglu_bwd, swiglu_fwd)
+               scale_cast, scaled_gemm_auto, swiglu_bwd, swiglu_fwd)
 
 # The quantised tensors of one forward + backward, in log order.
 TENSORS = ("x", "w1", "a", "w2", "dy", "dh")
@@ -112,7 +113,7 @@ def mlp_forward(x, w1, w2, cfg=None):
     with _span(cfg, "quant", "w1"):
         w1_8, bw1, _ = quantize(w1, E4M3, m["w1"])
     with _span(cfg, "gemm", "fwd h"):
-        h = scaled_gemm(OP_FWD, x8, E4M3, bx, w1_8, E4M3, bw1, math=cfg.math)
+        h = scaled_gemm_auto(OP_FWD, x8, E4M3, bx, w1_8, E4M3, bw1, math=cfg.math)
     with _span(cfg, "swiglu", "fwd"):
         a = swiglu_fwd(h, amax=a_amax)
     with _span(cfg, "quant", "a"):
@@ -121,7 +122,7 @@ def mlp_forward(x, w1, w2, cfg=None):
     with _span(cfg, "quant", "w2"):
         w2_8, bw2, _ = quantize(w2, E4M3, m["w2"])
     with _span(cfg, "gemm", "fwd y"):
-        y = scaled_gemm(OP_FWD, a8, E4M3, ba, w2_8, E4M3, bw2, math=cfg.math)
+        y = scaled_gemm_auto(OP_FWD, a8, E4M3, ba, w2_8, E4M3, bw2, math=cfg.math)
     if cfg.log is not None:
         for n, b in (("x", bx), ("w1", bw1), ("a", ba), ("w2", bw2)):
             cfg.log.record(n, b)
@@ -138,18 +139,18 @@ def mlp_backward(saved, dy, cfg=None):
     with _span(cfg, "quant", "dy"):
         dy8, bdy, _ = quantize(dy, E5M2, m["dy"])
     with _span(cfg, "gemm", "dgrad da"):
-        da = scaled_gemm(OP_DGRAD, dy8, E5M2, bdy, saved["w2_8"], E4M3, saved["bw2"], math=cfg.math)
+        da = scaled_gemm_auto(OP_DGRAD, dy8, E5M2, bdy, saved["w2_8"], E4M3, saved["bw2"], math=cfg.math)
     with _span(cfg, "gemm", "wgrad dw2"):
-        dw2 = scaled_gemm(OP_WGRAD, dy8, E5M2, bdy, saved["a8"], E4M3, saved["ba"], math=cfg.math)
+        dw2 = scaled_gemm_auto(OP_WGRAD, dy8, E5M2, bdy, saved["a8"], E4M3, saved["ba"], math=cfg.math)
     with _span(cfg, "swiglu", "bwd"):
         dh = swiglu_bwd(saved["h"], da, amax=dh_amax)
     with _span(cfg, "quant", "dh"):
         bdh = compute_bias(dh_amax, E5M2, m["dh"])
         dh8 = scale_cast(dh, bdh, E5M2)
     with _span(cfg, "gemm", "dgrad dx"):
-        dx = scaled_gemm(OP_DGRAD, dh8, E5M2, bdh, saved["w1_8"], E4M3, saved["bw1"], math=cfg.math)
+        dx = scaled_gemm_auto(OP_DGRAD, dh8, E5M2, bdh, saved["w1_8"], E4M3, saved["bw1"], math=cfg.math)
     with _span(cfg, "gemm", "wgrad dw1"):
-        dw1 = scaled_gemm(OP_WGRAD, dh8, E5M2, bdh, saved["x8"], E4M3, saved["bx"], math=cfg.math)
+        dw1 = scaled_gemm_auto(OP_WGRAD, dh8, E5M2, bdh, saved["x8"], E4M3, saved["bx"], math=cfg.math)
     if cfg.log is not None:
         cfg.log.record("dy", bdy)
         cfg.log.record("dh", bdh)

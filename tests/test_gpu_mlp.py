@@ -238,6 +238,18 @@ def test_mlp_llama7b_shapes_sampled(fl):
     stagewise(fl, t, sample=4096)
 
 
+def test_mlp_small_batch_split_products(fl):
+    """The Llama-2-7B MLP with 32 tokens: the down projection, its data
+    gradient and the input's data gradient have outputs of 32 x 4096 or
+    32 x 11008 (a few tiles), so they run split along the contraction
+    (fp8_scaled_gemm_ws); every stage against the oracle, products in full."""
+    T, d, f = 32, 4096, 11008
+    assert fl.gemm_workspace_bytes(fl.OP_FWD, T, d, f) > 0
+    assert fl.gemm_workspace_bytes(fl.OP_DGRAD, T, d, f) > 0
+    assert fl.gemm_workspace_bytes(fl.OP_DGRAD, T, 2 * f, d) > 0
+    stagewise(fl, small_mlp(T, d, f, 5), sample=None)
+
+
 def reference_fp64(t):
     x = t["X"].double().requires_grad_()
     w1 = t["W1"].double().requires_grad_()
