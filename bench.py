@@ -47,7 +47,7 @@ def parse():
                     help="chained MLP: tokens of the CPU oracle's sample")
     ap.add_argument("--math", choices=["exact", "native-fp8"], default="exact",
                     help="product arithmetic: exact (fp16 MFMA on exactly widened FP8) or the native FP8 MFMA")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="rows of each product in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="rows of each product in the CPU sample")
     ap.add_argument("--cpu-cols", type=int, default=8192, help="columns of each product in the CPU sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
