@@ -301,13 +301,13 @@ def test_two_launch_split_of_the_output(fl, which, R, C, Kc, split, math):
 
 
 # Products split along the contraction (fp8_scaled_gemm_ws): outputs of few
-# 128 x 128 tiles, contraction lengths whose last slice is shorter (3200 =
-# 50 stages in two), ragged output sides (multiples of 16 where an operand is
+# 128 x 128 tiles, contraction lengths split evenly (3200 = 50 stages in two)
+# and unevenly (3136 = 49 stages: 25 + 24, the shortest slice allowed), ragged output sides (multiples of 16 where an operand is
 # read contraction-major), a single tile split ten ways, and per product one
 # shape that is not split (workspace 0).
 SPLIT_SHAPES = {
-    "fwd": [(128, 256, 4096), (100, 300, 3200), (16, 48, 6400), (100, 100, 15360), (2048, 768, 3072),
-            (1024, 2048, 4096), (2048, 2048, 1024)],
+    "fwd": [(128, 256, 4096), (100, 300, 3200), (128, 256, 3136), (16, 48, 6400), (100, 100, 15360),
+            (2048, 768, 3072), (1024, 2048, 4096), (2048, 2048, 1024)],
     "dgrad": [(128, 3200, 256), (96, 6400, 80), (2048, 3072, 768), (1024, 4096, 2048), (2048, 1024, 2048)],
     "wgrad": [(3200, 128, 256), (6400, 96, 80), (3072, 2304, 768), (4096, 1024, 2048), (1024, 2048, 2048)],
 }
