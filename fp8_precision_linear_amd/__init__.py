@@ -29,6 +29,7 @@ E4M3, E5M2, E3M4 = 0, 1, 2
 BF16, FP32 = 0, 1
 FMT_MAX = {E4M3: 448.0, E5M2: 57344.0, E3M4: 30.0}
 MAX_MARGIN = 64
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024   # FP8_NOALLOC_SCRATCH_BYTES
 
 STATUS = {0: "FP8_OK", -1: "FP8_ERR_NULL", -2: "FP8_ERR_SIZE", -3: "FP8_ERR_FORMAT",
           -4: "FP8_ERR_DTYPE", -5: "FP8_ERR_ALIGN", -6: "FP8_ERR_MARGIN",
@@ -51,6 +52,7 @@ SIGNATURES = {
     "fp8_scaled_gemm_amax": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_workspace_bytes": (_i64, [_ci, _i64, _i64, _i64]),
     "fp8_scaled_gemm_ws": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp]),
+    "fp8_scaled_gemm_noalloc": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_fwd": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_dgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_wgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
@@ -258,6 +260,22 @@ def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=No
                lib.fp8_scaled_gemm_amax(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8),
                                         int(fb), _ptr(bb), M, N, K, _ptr(out), _ptr(amax),
                                         _stream(stream)))
+    return out
+
+
+def scaled_gemm_noalloc(op, a8, fa, ba, b8, fb, bb, out, math=MATH_EXACT, stream=None):
+    """scaled_gemm with its split workspace in the library's static scratch
+    (fp8_scaled_gemm_noalloc): nothing is allocated, so the output is the
+    caller's.  Calls on one GPU must not overlap in time (they share the
+    scratch)."""
+    _need_cuda(a8, b8, ba, bb, out)
+    if op == OP_FWD:                  # X8[M, K], W8[N, K]
+        (M, K), N = a8.shape, b8.shape[0]
+    else:                             # dY8[M, N] with W8[N, K] (dgrad) or X8[M, K] (wgrad)
+        (M, N), K = a8.shape, b8.shape[1]
+    _check("fp8_scaled_gemm_noalloc",
+           lib.fp8_scaled_gemm_noalloc(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8), int(fb),
+                                       _ptr(bb), M, N, K, _ptr(out), _stream(stream)))
     return out
 
 

@@ -1,6 +1,7 @@
 // C ABI of libfp8lin: argument checks on the host, then kernel launches on the
 // caller's stream.  No allocation, no host synchronisation, no state beyond a
-// per-device "is this gfx950" flag.
+// per-device "is this gfx950" flag and the per-device address of the static
+// scratch that fp8_scaled_gemm_noalloc uses.
 #include <atomic>
 #include <cstring>
 
@@ -11,6 +12,14 @@ namespace {
 constexpr int kMaxDevices = 64;
 // 0 = not checked yet, 1 = gfx950, 2 = something else.
 std::atomic<int> g_arch_ok[kMaxDevices];
+
+// The split workspace of fp8_scaled_gemm_noalloc, for callers that cannot
+// allocate: one copy per device, held until the process ends.  Host code never
+// passes `scratch` itself (on the host it names a stand-in, not device memory):
+// it passes the device address hipGetSymbolAddress returns for the current
+// device, looked up on the first call on that device and kept in g_scratch.
+static __device__ __align__(256) __attribute__((used)) uint8_t scratch[FP8_NOALLOC_SCRATCH_BYTES];
+std::atomic<void*> g_scratch[kMaxDevices];
 
 bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 // amax and bias words: their natural 4-byte alignment (atomics need it)
@@ -37,6 +46,21 @@ int device_ok() {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8_OK : FP8_ERR_HIP; }
+
+// The current device's copy of `scratch` (device_ok() has already checked the
+// device index).  Several threads may look it up at once: each gets the same
+// address.
+int scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8_ERR_DEVICE;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FP8_ERR_HIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return FP8_OK;
+}
 
 // The operands are a_rows x a_cols and b_rows x b_cols, each of those one of
 // M, N, K: the products are formed only after the range check.
@@ -154,10 +178,14 @@ bool out_shape(fp8_gemm_op_t op, int64_t M, int64_t N, int64_t K, int64_t& rows,
   }
 }
 
-// with_ws: the fp8_scaled_gemm_ws form (ws / ws_bytes checked here).
+// Where a split product's workspace comes from: none (never split), the
+// caller's (fp8_scaled_gemm_ws: ws / ws_bytes checked here) or the library's
+// static scratch (fp8_scaled_gemm_noalloc).
+enum WsMode { kNoWorkspace, kCallerWorkspace, kStaticScratch };
+
 int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, const int32_t* ba,
                 const uint8_t* b, fp8_format_t fb, const int32_t* bb, int64_t M, int64_t N,
-                int64_t K, float* out, float* out_amax, bool with_ws, void* ws, int64_t ws_bytes,
+                int64_t K, float* out, float* out_amax, WsMode ws_mode, void* ws, int64_t ws_bytes,
                 hipStream_t st) {
   if (math != FP8_GEMM_EXACT && math != FP8_GEMM_NATIVE_FP8) return FP8_ERR_OP;
   fp8lin::GemmProblem p{};
@@ -189,17 +217,24 @@ int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, c
       return FP8_ERR_OP;
   }
   bool split = false;
-  if (with_ws && !empty) {
+  if (ws_mode != kNoWorkspace && !empty) {
     const int64_t need = fp8lin::gemm_split_workspace_bytes(p.m, p.n, p.k);
     if (need > 0) {
-      if (!ws) return FP8_ERR_NULL;
-      if (misaligned(ws)) return FP8_ERR_ALIGN;
-      if (ws_bytes < need) return FP8_ERR_SIZE;
+      if (ws_mode == kStaticScratch) {
+        if (need > (int64_t)FP8_NOALLOC_SCRATCH_BYTES) return FP8_ERR_SIZE;
+      } else {
+        if (!ws) return FP8_ERR_NULL;
+        if (misaligned(ws)) return FP8_ERR_ALIGN;
+        if (ws_bytes < need) return FP8_ERR_SIZE;
+      }
       split = true;
     }
   }
   if (empty && !out_amax) return FP8_OK;
   if (int s = device_ok()) return s;
+  if (split && ws_mode == kStaticScratch) {
+    if (int s = scratch_of_current_device(&ws)) return s;
+  }
   if (out_amax) {
     p.amax = reinterpret_cast<uint32_t*>(out_amax);
     if (int s = hip_status(fp8lin::launch_clear_u32(p.amax, st))) return s;
@@ -227,8 +262,8 @@ extern "C" {
 int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
                     const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
                     int64_t M, int64_t N, int64_t K, float* out, void* stream) {
-  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, nullptr, false, nullptr, 0,
-                     (hipStream_t)stream);
+  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, nullptr, kNoWorkspace, nullptr,
+                     0, (hipStream_t)stream);
 }
 
 int64_t fp8_scaled_gemm_workspace_bytes(fp8_gemm_op_t op, int64_t M, int64_t N, int64_t K) {
@@ -243,8 +278,16 @@ int fp8_scaled_gemm_ws(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_
                        int64_t M, int64_t N, int64_t K, float* out, void* ws, int64_t ws_bytes,
                        void* stream) {
   if (ws_bytes < 0) return FP8_ERR_SIZE;
-  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, nullptr, true, ws, ws_bytes,
-                     (hipStream_t)stream);
+  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, nullptr, kCallerWorkspace, ws,
+                     ws_bytes, (hipStream_t)stream);
+}
+
+int fp8_scaled_gemm_noalloc(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
+                            const int32_t* ba, const uint8_t* b, fp8_format_t fb,
+                            const int32_t* bb, int64_t M, int64_t N, int64_t K, float* out,
+                            void* stream) {
+  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, nullptr, kStaticScratch,
+                     nullptr, 0, (hipStream_t)stream);
 }
 
 int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
@@ -253,8 +296,8 @@ int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_forma
                          void* stream) {
   if (!out_amax) return FP8_ERR_NULL;
   if (misaligned_word(out_amax)) return FP8_ERR_ALIGN;
-  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, out_amax, false, nullptr, 0,
-                     (hipStream_t)stream);
+  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, out_amax, kNoWorkspace, nullptr,
+                     0, (hipStream_t)stream);
 }
 
 int fp8_scaled_gemm_fwd(const uint8_t* x8, fp8_format_t fx, const int32_t* bx,

@@ -17,7 +17,8 @@
  * Conventions for every entry point:
  *  - Device pointers are device memory of the current HIP device (for example
  *    torch.empty(..., device="cuda").data_ptr()).  The caller allocates every
- *    buffer; the library never allocates, frees or keeps a pointer.
+ *    buffer; the library never allocates, frees or keeps a pointer (its one
+ *    piece of device memory is the static scratch of fp8_scaled_gemm_noalloc).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    on it and the call returns without waiting; nothing is copied to the host.
  *  - Matrices are row-major and dense (leading dimension = column count).
@@ -25,7 +26,8 @@
  *    returns a negative status synchronously and leaves every output untouched.
  *    A launch failure returns FP8_ERR_HIP; a fault during execution surfaces at
  *    the caller's next synchronisation.
- *  - Calls are thread-safe.  Calls that write the same output must not overlap.
+ *  - Calls are thread-safe.  Calls that write the same output must not overlap
+ *    (nor, on one GPU, two fp8_scaled_gemm_noalloc calls).
  *  - Tuning only (read at each call, never needed for correct results):
  *    FP8LIN_GEMM_TILE=128|256 forces the products' tile, FP8LIN_EXACT_MFMA=
  *    f16|bf16 the 16-bit MFMA of the exact arithmetic, FP8LIN_AMAX_HINT /
@@ -221,6 +223,31 @@ int fp8_scaled_gemm_ws(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_
                        const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
                        int64_t M, int64_t N, int64_t K, float* out, void* ws, int64_t ws_bytes,
                        void* stream);
+
+/*
+ * fp8_scaled_gemm_noalloc: fp8_scaled_gemm_ws for callers that cannot
+ * allocate (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The split workspace is the library's own static device
+ * array of FP8_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, created with the code
+ * object and held until the process ends; the call allocates and frees
+ * nothing.  Every split plan with the default FP8LIN_SPLIT_SLOTS fits it
+ * (at most 256 / tiles slices of an output of tiles 128 x 128 tiles).
+ * Arguments, results and bits are those of fp8_scaled_gemm_ws with a large
+ * enough workspace; a product whose split would need more scratch than the
+ * maximum returns FP8_ERR_SIZE before anything runs.  The first call on a
+ * device looks up that device's copy of the array (FP8_ERR_HIP if that
+ * fails).
+ * Every call on one GPU shares its one array and leaves its contents behind
+ * (nothing in it needs clearing: a split product writes every workspace
+ * element it reads).  Calls that overlap in time on one GPU -- from two
+ * streams, or two host threads -- race on it and corrupt each other's
+ * results; callers must order them (one stream, or events).
+ */
+#define FP8_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int fp8_scaled_gemm_noalloc(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
+                            const int32_t* ba, const uint8_t* b, fp8_format_t fb,
+                            const int32_t* bb, int64_t M, int64_t N, int64_t K, float* out,
+                            void* stream);
 
 /* fp8_scaled_gemm that also returns the per-tensor amax of its output (the
  * "Proposed method" bullet-1 statistic of the tensor the product produces),

@@ -31,7 +31,7 @@ def status(code):
 
 def test_every_declared_function_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
         assert n in fl.SIGNATURES, n
@@ -278,3 +278,34 @@ def test_gemm_ws_without_a_device_reports_no_device():
         == status("FP8_ERR_DEVICE")
     # a product that is not split needs no workspace
     assert f(0, 0, A16, 0, A32, A48, 0, A32, 8192, 8192, 8192, A16, None, 0, None) == status("FP8_ERR_DEVICE")
+
+
+def test_gemm_noalloc_argument_checks(monkeypatch):
+    """fp8_scaled_gemm_noalloc: the product checks of fp8_scaled_gemm, and a
+    split that would need more than the static scratch is refused on the host
+    before any device call (the default plans never do: at most 256 / tiles
+    slices of an output of that many 128 x 128 tiles, 16 MiB)."""
+    f = L.fp8_scaled_gemm_noalloc
+    assert f(9, 0, A16, 0, A32, A48, 0, A32, 64, 64, 64, A16, None) == status("FP8_ERR_OP")
+    assert f(0, 5, A16, 0, A32, A48, 0, A32, 64, 64, 64, A16, None) == status("FP8_ERR_OP")
+    assert f(0, 0, A16, 2, A32, A48, 0, A32, 64, 64, 64, A16, None) == status("FP8_ERR_FORMAT")
+    assert f(0, 0, A16, 0, None, A48, 0, A32, 64, 64, 64, A16, None) == status("FP8_ERR_NULL")
+    assert f(0, 0, MIS, 0, A32, A48, 0, A32, 64, 64, 64, A16, None) == status("FP8_ERR_ALIGN")
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, -1, 64, 64, A16, None) == status("FP8_ERR_SIZE")
+    assert f(0, 0, None, 0, None, None, 0, None, 0, 768, 3072, None, None) == 0
+    # the largest default plan fits exactly: 64 slices of a 4-tile output
+    ws = L.fp8_scaled_gemm_workspace_bytes
+    assert ws(0, 256, 256, 64 * 24 * 64) == 64 * 256 * 256 * 4 == fl.NOALLOC_SCRATCH_BYTES
+    assert max(ws(0, m, n, 64 * 24 * 256) for m in (16, 128, 256, 1000, 2048) for n in (16, 128, 512, 2048)) \
+        <= fl.NOALLOC_SCRATCH_BYTES
+    # more planned slots: a 4-tile output split 256 ways needs 64 MiB
+    monkeypatch.setenv("FP8LIN_SPLIT_SLOTS", "4096")
+    assert ws(0, 256, 256, 256 * 24 * 64) == 256 * 256 * 256 * 4
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 256, 256, 256 * 24 * 64, A16, None) == status("FP8_ERR_SIZE")
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
+def test_gemm_noalloc_without_a_device_reports_no_device():
+    f = L.fp8_scaled_gemm_noalloc
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 2048, 768, 3072, A16, None) == status("FP8_ERR_DEVICE")
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 8192, 8192, 8192, A16, None) == status("FP8_ERR_DEVICE")
