@@ -48,17 +48,35 @@ SIGNATURES = {
     "fp8_scale_cast": (_ci, [_vp, _ci, _i64, _vp, _ci, _vp, _vp]),
     "fp8_scale_cast_amax": (_ci, [_vp, _ci, _i64, _vp, _ci, _vp, _vp, _vp]),
     "fp8_quantize": (_ci, [_vp, _ci, _i64, _ci, _i32, _vp, _vp, _vp, _vp]),
+    "fp8_quantize_multi": (_ci, [_vp, _i32, _vp]),
     "fp8_scaled_gemm": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_amax": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_workspace_bytes": (_i64, [_ci, _i64, _i64, _i64]),
     "fp8_scaled_gemm_ws": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp]),
     "fp8_scaled_gemm_noalloc": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
+    "fp8_scaled_gemm_group_workspace_bytes": (_i64, [_ci, _vp, _i32]),
+    "fp8_scaled_gemm_group": (_ci, [_ci, _vp, _i32, _vp, _i64, _vp]),
     "fp8_scaled_gemm_fwd": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_dgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_wgrad": (_ci, [_vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_swiglu_fwd": (_ci, [_vp, _i64, _i64, _vp, _vp, _vp]),
     "fp8_swiglu_bwd": (_ci, [_vp, _vp, _i64, _i64, _vp, _vp, _vp]),
 }
+
+
+class QuantDesc(ctypes.Structure):
+    """fp8_quant_desc_t (include/fp8lin.h): one tensor of fp8_quantize_multi."""
+    _fields_ = [("x", ctypes.c_void_p), ("n", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("fmt", ctypes.c_int32), ("margin", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("y", ctypes.c_void_p), ("amax", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
+
+
+class GemmDesc(ctypes.Structure):
+    """fp8_gemm_desc_t (include/fp8lin.h): one product of fp8_scaled_gemm_group."""
+    _fields_ = [("op", ctypes.c_int32), ("fa", ctypes.c_int32), ("fb", ctypes.c_int32),
+                ("pad", ctypes.c_int32), ("a", ctypes.c_void_p), ("ba", ctypes.c_void_p),
+                ("b", ctypes.c_void_p), ("bb", ctypes.c_void_p), ("M", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("out", ctypes.c_void_p)]
 
 
 def _load():
@@ -104,24 +122,86 @@ def _dtype_code(t):
     raise TypeError(f"inputs are bfloat16 or float32 tensors, got {t.dtype}")
 
 
-def _need_cuda(*ts):
-    for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError("tensors must be contiguous CUDA (HIP) tensors")
+def _need_kind(t, name, dtype, numel=None, shape=None):
+    """A tensor of `dtype` and, when given, that element count or shape."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _need_place(t, name, device):
+    """A contiguous device tensor on `device`."""
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous CUDA (HIP) tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the operands on {device}")
+
+
+def _need(t, name, dtype, device, numel=None, shape=None):
+    """Check a tensor the library reads or writes before any call (its kind,
+    then its place).  A wrong one would otherwise make a kernel write past its
+    buffer or to a host address."""
+    _need_kind(t, name, dtype, numel, shape)
+    _need_place(t, name, device)
+
+
+def _empty(shape, dtype, device, stream):
+    """A new device tensor for a call enqueued on `stream`: allocated on that
+    stream, so that torch's caching allocator does not hand its block to
+    work on another stream while the call may still use it."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _scalar(t, name, dtype, device):
+    _need(t, name, dtype, device, numel=1)
+
+
+def _codes_kind(t, name):
+    """FP8 codes: a 2-D uint8 tensor."""
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D uint8 tensor of FP8 codes")
+    _need_kind(t, name, torch.uint8)
+
+
+def _input(x):
+    """A bf16 or fp32 input tensor: its dtype code (TypeError otherwise)."""
+    if not isinstance(x, torch.Tensor):
+        raise ValueError(f"x must be a tensor, got {type(x).__name__}")
+    return _dtype_code(x)
+
+
+def _places(dev, *named):
+    for t, name in named:
+        if t is not None:
+            _need_place(t, name, dev)
 
 
 def amax(x, out=None, stream=None):
     """float32[1] device tensor holding max|x| (fp8_amax)."""
-    _need_cuda(x)
-    out = torch.empty(1, dtype=torch.float32, device=x.device) if out is None else out
-    _check("fp8_amax", lib.fp8_amax(_ptr(x), _dtype_code(x), x.numel(), _ptr(out), _stream(stream)))
+    dt = _input(x)
+    if out is not None:
+        _need_kind(out, "out", torch.float32, numel=1)
+    _places(x.device, (x, "x"), (out, "out"))
+    out = _empty(1, torch.float32, x.device, stream) if out is None else out
+    _check("fp8_amax", lib.fp8_amax(_ptr(x), dt, x.numel(), _ptr(out), _stream(stream)))
     return out
 
 
 def compute_bias(amax_t, fmt, margin=0, out=None, stream=None):
     """int32[1] device tensor: floor(log2(fmt_max / amax)) - margin (fp8_compute_bias)."""
-    _need_cuda(amax_t)
-    out = torch.empty(1, dtype=torch.int32, device=amax_t.device) if out is None else out
+    _need_kind(amax_t, "amax", torch.float32, numel=1)
+    if out is not None:
+        _need_kind(out, "out", torch.int32, numel=1)
+    _places(amax_t.device, (amax_t, "amax"), (out, "out"))
+    out = _empty(1, torch.int32, amax_t.device, stream) if out is None else out
     _check("fp8_compute_bias",
            lib.fp8_compute_bias(_ptr(amax_t), int(fmt), int(margin), _ptr(out), _stream(stream)))
     return out
@@ -131,15 +211,20 @@ def scale_cast(x, bias, fmt, out=None, stream=None, amax=None):
     """uint8 device tensor of FP8 codes of x * 2^bias, same shape as x (fp8_scale_cast).
     amax: optional float32[1] device tensor that receives max |x|, folded in the
     same pass (fp8_scale_cast_amax; for delayed scaling)."""
-    _need_cuda(x, bias)
-    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    dt = _input(x)
+    _need_kind(bias, "bias", torch.int32, numel=1)
+    if out is not None:
+        _need_kind(out, "out", torch.uint8, numel=x.numel())
+    if amax is not None:
+        _need_kind(amax, "amax", torch.float32, numel=1)
+    _places(x.device, (x, "x"), (bias, "bias"), (out, "out"), (amax, "amax"))
+    out = _empty(x.shape, torch.uint8, x.device, stream) if out is None else out
     if amax is None:
-        _check("fp8_scale_cast", lib.fp8_scale_cast(_ptr(x), _dtype_code(x), x.numel(), _ptr(bias),
+        _check("fp8_scale_cast", lib.fp8_scale_cast(_ptr(x), dt, x.numel(), _ptr(bias),
                                                     int(fmt), _ptr(out), _stream(stream)))
     else:
-        _need_cuda(amax)
         _check("fp8_scale_cast_amax",
-               lib.fp8_scale_cast_amax(_ptr(x), _dtype_code(x), x.numel(), _ptr(bias), int(fmt),
+               lib.fp8_scale_cast_amax(_ptr(x), dt, x.numel(), _ptr(bias), int(fmt),
                                        _ptr(out), _ptr(amax), _stream(stream)))
     return out
 
@@ -148,14 +233,56 @@ def quantize(x, fmt, margin=0, out=None, bias=None, amax=None, stream=None):
     """(codes, bias, amax) of a tensor in one call (fp8_quantize): the results of
     amax -> compute_bias -> scale_cast, in one launch for small tensors and three
     for large ones.  out / bias / amax: optional preallocated device tensors."""
-    _need_cuda(x)
-    out = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
-    bias = torch.empty(1, dtype=torch.int32, device=x.device) if bias is None else bias
-    amax = torch.empty(1, dtype=torch.float32, device=x.device) if amax is None else amax
-    _need_cuda(out, bias, amax)
-    _check("fp8_quantize", lib.fp8_quantize(_ptr(x), _dtype_code(x), x.numel(), int(fmt), int(margin),
+    dt = _input(x)
+    if out is not None:
+        _need_kind(out, "out", torch.uint8, numel=x.numel())
+    if bias is not None:
+        _need_kind(bias, "bias", torch.int32, numel=1)
+    if amax is not None:
+        _need_kind(amax, "amax", torch.float32, numel=1)
+    _places(x.device, (x, "x"), (out, "out"), (bias, "bias"), (amax, "amax"))
+    out = _empty(x.shape, torch.uint8, x.device, stream) if out is None else out
+    bias = _empty(1, torch.int32, x.device, stream) if bias is None else bias
+    amax = _empty(1, torch.float32, x.device, stream) if amax is None else amax
+    _check("fp8_quantize", lib.fp8_quantize(_ptr(x), dt, x.numel(), int(fmt), int(margin),
                                             _ptr(out), _ptr(amax), _ptr(bias), _stream(stream)))
     return out, bias, amax
+
+
+def quantize_multi(xs, fmts, margins=0, outs=None, stream=None):
+    """fp8_quantize of every tensor in xs in one call (fp8_quantize_multi: three
+    launches per 32 tensors).  fmts, margins: one per tensor, or one for all.
+    outs: optional list of (codes, bias, amax) device tensors to write.
+    Returns the list of (codes, bias, amax), each bit-identical to quantize()
+    of that tensor alone."""
+    xs = list(xs)
+    k = len(xs)
+    fmts = list(fmts) if isinstance(fmts, (list, tuple)) else [fmts] * k
+    margins = list(margins) if isinstance(margins, (list, tuple)) else [margins] * k
+    if len(fmts) != k or len(margins) != k or (outs is not None and len(outs) != k):
+        raise ValueError("one format, margin and output triple per tensor")
+    res, descs = [], (QuantDesc * max(k, 1))()
+    dev = xs[0].device if k else None
+    for i, x in enumerate(xs):
+        dt = _input(x)
+        if outs is not None:
+            out, bias, amax = outs[i]
+            _need_kind(out, f"outs[{i}][0]", torch.uint8, numel=x.numel())
+            _need_kind(bias, f"outs[{i}][1]", torch.int32, numel=1)
+            _need_kind(amax, f"outs[{i}][2]", torch.float32, numel=1)
+            _places(dev, (x, f"xs[{i}]"), (out, f"outs[{i}][0]"), (bias, f"outs[{i}][1]"),
+                    (amax, f"outs[{i}][2]"))
+        else:
+            _places(dev, (x, f"xs[{i}]"))
+            out = _empty(x.shape, torch.uint8, dev, stream)
+            bias = _empty(1, torch.int32, dev, stream)
+            amax = _empty(1, torch.float32, dev, stream)
+        descs[i] = QuantDesc(x.data_ptr(), x.numel(), dt, int(fmts[i]), int(margins[i]), 0,
+                             out.data_ptr(), amax.data_ptr(), bias.data_ptr())
+        res.append((out, bias, amax))
+    _check("fp8_quantize_multi", lib.fp8_quantize_multi(ctypes.cast(descs, ctypes.c_void_p), k,
+                                                        _stream(stream)))
+    return res
 
 
 def quantize_chain(x, fmt, margin=0, stream=None):
@@ -165,14 +292,40 @@ def quantize_chain(x, fmt, margin=0, stream=None):
     return scale_cast(x, b, fmt, stream=stream), b, a
 
 
+def _gemm_args(op, a8, ba, b8, bb, out, stream):
+    """(M, N, K, out) of a product after checking its operands: 2-D uint8
+    codes on one device with matching contraction sizes, int32[1] biases, and
+    a float32 output of the product's shape (allocated on `stream` if None)."""
+    _codes_kind(a8, "a8")
+    _codes_kind(b8, "b8")
+    _need_kind(ba, "bias_a", torch.int32, numel=1)
+    _need_kind(bb, "bias_b", torch.int32, numel=1)
+    dev = a8.device
+    if op == OP_FWD:                  # X8[M, K], W8[N, K] -> Y[M, N]
+        (M, K), (N, K2) = a8.shape, b8.shape
+        shape, ok = (M, N), K == K2
+    elif op == OP_DGRAD:              # dY8[M, N], W8[N, K] -> dX[M, K]
+        (M, N), (N2, K) = a8.shape, b8.shape
+        shape, ok = (M, K), N == N2
+    elif op == OP_WGRAD:              # dY8[M, N], X8[M, K] -> dW[N, K]
+        (M, N), (M2, K) = a8.shape, b8.shape
+        shape, ok = (N, K), M == M2
+    else:
+        raise ValueError(f"unknown op {op}")
+    if not ok:
+        raise ValueError("contraction sizes differ")
+    if out is not None:
+        _need_kind(out, "out", torch.float32, shape=shape)
+    for t, name in ((a8, "a8"), (b8, "b8"), (ba, "bias_a"), (bb, "bias_b"), (out, "out")):
+        if t is not None:
+            _need_place(t, name, dev)
+    out = _empty(shape, torch.float32, dev, stream) if out is None else out
+    return M, N, K, out
+
+
 def scaled_gemm_fwd(x8, fx, bx, w8, fw, bw, out=None, stream=None):
     """Y[M, N] = 2^-(bx+bw) * X8[M, K] @ W8[N, K]^T in float32 (fp8_scaled_gemm_fwd)."""
-    _need_cuda(x8, w8, bx, bw)
-    M, K = x8.shape
-    N, K2 = w8.shape
-    if K != K2:
-        raise ValueError("contraction sizes differ")
-    out = torch.empty((M, N), dtype=torch.float32, device=x8.device) if out is None else out
+    M, N, K, out = _gemm_args(OP_FWD, x8, bx, w8, bw, out, stream)
     _check("fp8_scaled_gemm_fwd",
            lib.fp8_scaled_gemm_fwd(_ptr(x8), int(fx), _ptr(bx), _ptr(w8), int(fw), _ptr(bw),
                                    M, N, K, _ptr(out), _stream(stream)))
@@ -181,12 +334,7 @@ def scaled_gemm_fwd(x8, fx, bx, w8, fw, bw, out=None, stream=None):
 
 def scaled_gemm_dgrad(dy8, fdy, bdy, w8, fw, bw, out=None, stream=None):
     """dX[M, K] = 2^-(bdy+bw) * dY8[M, N] @ W8[N, K] in float32 (fp8_scaled_gemm_dgrad)."""
-    _need_cuda(dy8, w8, bdy, bw)
-    M, N = dy8.shape
-    N2, K = w8.shape
-    if N != N2:
-        raise ValueError("contraction sizes differ")
-    out = torch.empty((M, K), dtype=torch.float32, device=dy8.device) if out is None else out
+    M, N, K, out = _gemm_args(OP_DGRAD, dy8, bdy, w8, bw, out, stream)
     _check("fp8_scaled_gemm_dgrad",
            lib.fp8_scaled_gemm_dgrad(_ptr(dy8), int(fdy), _ptr(bdy), _ptr(w8), int(fw), _ptr(bw),
                                      M, N, K, _ptr(out), _stream(stream)))
@@ -195,12 +343,7 @@ def scaled_gemm_dgrad(dy8, fdy, bdy, w8, fw, bw, out=None, stream=None):
 
 def scaled_gemm_wgrad(dy8, fdy, bdy, x8, fx, bx, out=None, stream=None):
     """dW[N, K] = 2^-(bdy+bx) * dY8[M, N]^T @ X8[M, K] in float32 (fp8_scaled_gemm_wgrad)."""
-    _need_cuda(dy8, x8, bdy, bx)
-    M, N = dy8.shape
-    M2, K = x8.shape
-    if M != M2:
-        raise ValueError("contraction sizes differ")
-    out = torch.empty((N, K), dtype=torch.float32, device=dy8.device) if out is None else out
+    M, N, K, out = _gemm_args(OP_WGRAD, dy8, bdy, x8, bx, out, stream)
     _check("fp8_scaled_gemm_wgrad",
            lib.fp8_scaled_gemm_wgrad(_ptr(dy8), int(fdy), _ptr(bdy), _ptr(x8), int(fx), _ptr(bx),
                                      M, N, K, _ptr(out), _stream(stream)))
@@ -226,25 +369,12 @@ def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=No
     workspace: optional device tensor of at least gemm_workspace_bytes(op, M, N, K)
     bytes; with it an output of few tiles is computed split along the
     contraction (fp8_scaled_gemm_ws).  Not combined with amax."""
-    _need_cuda(a8, b8, ba, bb)
-    if op == OP_FWD:
-        (M, K), (N, K2) = a8.shape, b8.shape
-        shape, ok = (M, N), K == K2
-    elif op == OP_DGRAD:
-        (M, N), (N2, K) = a8.shape, b8.shape
-        shape, ok = (M, K), N == N2
-    elif op == OP_WGRAD:
-        (M, N), (M2, K) = a8.shape, b8.shape
-        shape, ok = (N, K), M == M2
-    else:
-        raise ValueError(f"unknown op {op}")
-    if not ok:
-        raise ValueError("contraction sizes differ")
-    out = torch.empty(shape, dtype=torch.float32, device=a8.device) if out is None else out
+    M, N, K, out = _gemm_args(op, a8, ba, b8, bb, out, stream)
     if workspace is not None:
         if amax is not None:
             raise ValueError("a workspace and an output amax are not combined")
-        _need_cuda(workspace)
+        if not workspace.is_cuda or not workspace.is_contiguous() or workspace.device != a8.device:
+            raise ValueError("workspace must be a contiguous CUDA (HIP) tensor on the operands' device")
         nbytes = workspace.numel() * workspace.element_size()
         _check("fp8_scaled_gemm_ws",
                lib.fp8_scaled_gemm_ws(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8), int(fb),
@@ -255,7 +385,7 @@ def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=No
                lib.fp8_scaled_gemm(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8), int(fb),
                                    _ptr(bb), M, N, K, _ptr(out), _stream(stream)))
     else:
-        _need_cuda(amax)
+        _scalar(amax, "amax", torch.float32, a8.device)
         _check("fp8_scaled_gemm_amax",
                lib.fp8_scaled_gemm_amax(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8),
                                         int(fb), _ptr(bb), M, N, K, _ptr(out), _ptr(amax),
@@ -268,11 +398,9 @@ def scaled_gemm_noalloc(op, a8, fa, ba, b8, fb, bb, out, math=MATH_EXACT, stream
     (fp8_scaled_gemm_noalloc): nothing is allocated, so the output is the
     caller's.  Calls on one GPU must not overlap in time (they share the
     scratch)."""
-    _need_cuda(a8, b8, ba, bb, out)
-    if op == OP_FWD:                  # X8[M, K], W8[N, K]
-        (M, K), N = a8.shape, b8.shape[0]
-    else:                             # dY8[M, N] with W8[N, K] (dgrad) or X8[M, K] (wgrad)
-        (M, N), K = a8.shape, b8.shape[1]
+    if out is None:
+        raise ValueError("scaled_gemm_noalloc writes the caller's output: out is required")
+    M, N, K, out = _gemm_args(op, a8, ba, b8, bb, out, stream)
     _check("fp8_scaled_gemm_noalloc",
            lib.fp8_scaled_gemm_noalloc(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8), int(fb),
                                        _ptr(bb), M, N, K, _ptr(out), _stream(stream)))
@@ -282,28 +410,66 @@ def scaled_gemm_noalloc(op, a8, fa, ba, b8, fb, bb, out, math=MATH_EXACT, stream
 def scaled_gemm_auto(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=None):
     """scaled_gemm with, when the product is split along the contraction (an
     output of too few tiles to fill the GPU), its workspace taken from
-    torch's caching allocator (gemm_workspace_bytes decides)."""
-    if op == OP_FWD:                  # X8[M, K], W8[N, K]
-        (M, K), N = a8.shape, b8.shape[0]
-    else:                             # dY8[M, N] with W8[N, K] (dgrad) or X8[M, K] (wgrad)
-        (M, N), K = a8.shape, b8.shape[1]
+    torch's caching allocator (gemm_workspace_bytes decides), on the stream
+    the product runs on."""
+    M, N, K, out = _gemm_args(op, a8, ba, b8, bb, out, stream)
     nbytes = gemm_workspace_bytes(op, M, N, K)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=a8.device) if nbytes > 0 else None
+    ws = _empty(nbytes, torch.uint8, a8.device, stream) if nbytes > 0 else None
     return scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=math, out=out, stream=stream, workspace=ws)
+
+
+class GemmGroup:
+    """Several products run together (fp8_scaled_gemm_group), prepared once:
+    products = [(op, a8, fa, ba, b8, fb, bb), ...] with each output given or
+    allocated here.  The descriptors and the workspace are made here, so a
+    step can call run() with no host work beyond one ctypes call (the
+    tensors' contents may change between calls, not their storage)."""
+
+    def __init__(self, products, outs=None, math=MATH_EXACT, stream=None):
+        self.math = math
+        self.outs, self._keep = [], []
+        k = len(products)
+        self.descs = (GemmDesc * max(k, 1))()
+        for i, (op, a8, fa, ba, b8, fb, bb) in enumerate(products):
+            M, N, K, out = _gemm_args(op, a8, ba, b8, bb, None if outs is None else outs[i], stream)
+            self.descs[i] = GemmDesc(int(op), int(fa), int(fb), 0, a8.data_ptr(), ba.data_ptr(), b8.data_ptr(),
+                                     bb.data_ptr(), M, N, K, out.data_ptr())
+            self.outs.append(out)
+            self._keep.append((a8, ba, b8, bb))
+        self.count = k
+        self.ptr = ctypes.cast(self.descs, ctypes.c_void_p)
+        nbytes = lib.fp8_scaled_gemm_group_workspace_bytes(int(math), self.ptr, k)
+        if nbytes < 0:
+            raise Fp8Error("fp8_scaled_gemm_group_workspace_bytes", nbytes)
+        dev = products[0][1].device if k else None
+        self.ws = _empty(nbytes, torch.uint8, dev, stream) if nbytes > 0 else None
+        self.ws_bytes = nbytes
+
+    def run(self, stream=None):
+        _check("fp8_scaled_gemm_group",
+               lib.fp8_scaled_gemm_group(int(self.math), self.ptr, self.count, _ptr(self.ws), self.ws_bytes,
+                                         _stream(stream)))
+        return self.outs
+
+
+def scaled_gemm_group(products, outs=None, math=MATH_EXACT, stream=None):
+    """Run several products together once (see GemmGroup); returns their outputs."""
+    return GemmGroup(products, outs=outs, math=math, stream=stream).run(stream)
 
 
 def swiglu_fwd(h, out=None, amax=None, stream=None):
     """a = silu(g) * u as a bf16 tensor [rows, f], h = [g | u] float32 [rows, 2f]
     (fp8_swiglu_fwd).  amax: optional float32[1] device tensor that receives
     max |a|."""
-    _need_cuda(h)
-    if h.dtype != torch.float32 or h.dim() != 2 or h.shape[1] % 2:
+    if not isinstance(h, torch.Tensor) or h.dtype != torch.float32 or h.dim() != 2 or h.shape[1] % 2:
         raise ValueError("h must be a float32 [rows, 2f] tensor")
     rows, f = h.shape[0], h.shape[1] // 2
-    out = torch.empty((rows, f), dtype=torch.bfloat16, device=h.device) if out is None else out
-    _need_cuda(out, amax)
-    if out.dtype != torch.bfloat16 or tuple(out.shape) != (rows, f):
-        raise ValueError("out must be a bfloat16 [rows, f] tensor")
+    if out is not None:
+        _need_kind(out, "out", torch.bfloat16, shape=(rows, f))
+    if amax is not None:
+        _need_kind(amax, "amax", torch.float32, numel=1)
+    _places(h.device, (h, "h"), (out, "out"), (amax, "amax"))
+    out = _empty((rows, f), torch.bfloat16, h.device, stream) if out is None else out
     _check("fp8_swiglu_fwd", lib.fp8_swiglu_fwd(_ptr(h), rows, f, _ptr(out), _ptr(amax), _stream(stream)))
     return out
 
@@ -312,16 +478,16 @@ def swiglu_bwd(h, da, out=None, amax=None, stream=None):
     """dh = [da * u * silu'(g) | da * silu(g)] as a bf16 tensor [rows, 2f]
     (fp8_swiglu_bwd); da float32 [rows, f].  amax: optional float32[1] device
     tensor that receives max |dh|."""
-    _need_cuda(h, da)
-    if h.dtype != torch.float32 or h.dim() != 2 or h.shape[1] % 2:
+    if not isinstance(h, torch.Tensor) or h.dtype != torch.float32 or h.dim() != 2 or h.shape[1] % 2:
         raise ValueError("h must be a float32 [rows, 2f] tensor")
     rows, f = h.shape[0], h.shape[1] // 2
-    if da.dtype != torch.float32 or tuple(da.shape) != (rows, f):
-        raise ValueError("da must be a float32 [rows, f] tensor")
-    out = torch.empty((rows, 2 * f), dtype=torch.bfloat16, device=h.device) if out is None else out
-    _need_cuda(out, amax)
-    if out.dtype != torch.bfloat16 or tuple(out.shape) != (rows, 2 * f):
-        raise ValueError("out must be a bfloat16 [rows, 2f] tensor")
+    _need_kind(da, "da", torch.float32, shape=(rows, f))
+    if out is not None:
+        _need_kind(out, "out", torch.bfloat16, shape=(rows, 2 * f))
+    if amax is not None:
+        _need_kind(amax, "amax", torch.float32, numel=1)
+    _places(h.device, (h, "h"), (da, "da"), (out, "out"), (amax, "amax"))
+    out = _empty((rows, 2 * f), torch.bfloat16, h.device, stream) if out is None else out
     _check("fp8_swiglu_bwd", lib.fp8_swiglu_bwd(_ptr(h), _ptr(da), rows, f, _ptr(out), _ptr(amax),
                                                 _stream(stream)))
     return out

@@ -80,6 +80,19 @@ int gemm_checks(const uint8_t* a, int fa, const int32_t* ba, const uint8_t* b, i
   return FP8_OK;
 }
 
+// fp8_quantize's argument checks (no device call).
+int quantize_checks(const void* x, int dtype, int64_t n, int fmt, int32_t margin, const uint8_t* y,
+                    const float* amax, const int32_t* bias) {
+  if (n < 0) return FP8_ERR_SIZE;
+  if (bad_dtype(dtype)) return FP8_ERR_DTYPE;
+  if (bad_format(fmt)) return FP8_ERR_FORMAT;
+  if (margin > FP8_MAX_MARGIN || margin < -FP8_MAX_MARGIN) return FP8_ERR_MARGIN;
+  if (!amax || !bias || (n > 0 && (!x || !y))) return FP8_ERR_NULL;
+  if (misaligned_word(amax) || misaligned_word(bias)) return FP8_ERR_ALIGN;
+  if (n > 0 && (misaligned(x) || misaligned(y))) return FP8_ERR_ALIGN;
+  return FP8_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -133,16 +146,32 @@ int fp8_scale_cast(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* b
 
 int fp8_quantize(const void* x, fp8_dtype_t dtype, int64_t n, fp8_format_t fmt, int32_t margin,
                  uint8_t* y, float* amax, int32_t* bias, void* stream) {
-  if (n < 0) return FP8_ERR_SIZE;
-  if (bad_dtype(dtype)) return FP8_ERR_DTYPE;
-  if (bad_format(fmt)) return FP8_ERR_FORMAT;
-  if (margin > FP8_MAX_MARGIN || margin < -FP8_MAX_MARGIN) return FP8_ERR_MARGIN;
-  if (!amax || !bias || (n > 0 && (!x || !y))) return FP8_ERR_NULL;
-  if (misaligned_word(amax) || misaligned_word(bias)) return FP8_ERR_ALIGN;
-  if (n > 0 && (misaligned(x) || misaligned(y))) return FP8_ERR_ALIGN;
+  if (int s = quantize_checks(x, dtype, n, fmt, margin, y, amax, bias)) return s;
   if (int s = device_ok()) return s;
   return hip_status(fp8lin::launch_quantize(x, dtype, n, fmt, margin, y, amax, bias,
                                             (hipStream_t)stream));
+}
+
+int fp8_quantize_multi(const fp8_quant_desc_t* descs, int32_t count, void* stream) {
+  if (count < 0) return FP8_ERR_SIZE;
+  if (count == 0) return FP8_OK;
+  if (!descs) return FP8_ERR_NULL;
+  for (int32_t i = 0; i < count; ++i) {
+    const fp8_quant_desc_t& d = descs[i];
+    if (int st = quantize_checks(d.x, d.dtype, d.n, d.fmt, d.margin, d.y, d.amax, d.bias)) return st;
+  }
+  if (int st = device_ok()) return st;
+  constexpr int kChunk = 256;  // descriptors converted per host batch
+  fp8lin::QuantDesc q[kChunk];
+  for (int32_t first = 0; first < count; first += kChunk) {
+    const int m = count - first < kChunk ? count - first : kChunk;
+    for (int i = 0; i < m; ++i) {
+      const fp8_quant_desc_t& d = descs[first + i];
+      q[i] = fp8lin::QuantDesc{d.x, d.n, d.dtype, d.fmt, d.margin, d.y, d.amax, d.bias};
+    }
+    if (int st = hip_status(fp8lin::launch_quantize_multi(q, m, (hipStream_t)stream))) return st;
+  }
+  return FP8_OK;
 }
 
 int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* bias,
@@ -183,13 +212,13 @@ bool out_shape(fp8_gemm_op_t op, int64_t M, int64_t N, int64_t K, int64_t& rows,
 // static scratch (fp8_scaled_gemm_noalloc).
 enum WsMode { kNoWorkspace, kCallerWorkspace, kStaticScratch };
 
-int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, const int32_t* ba,
-                const uint8_t* b, fp8_format_t fb, const int32_t* bb, int64_t M, int64_t N,
-                int64_t K, float* out, float* out_amax, WsMode ws_mode, void* ws, int64_t ws_bytes,
-                hipStream_t st) {
+// The checks of one product and its problem in kernel terms (rows, columns and
+// contraction of the output; each operand's layout); empty: no output.
+int make_problem(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, const int32_t* ba,
+                 const uint8_t* b, fp8_format_t fb, const int32_t* bb, int64_t M, int64_t N, int64_t K,
+                 float* out, fp8lin::GemmProblem& p, bool& empty) {
   if (math != FP8_GEMM_EXACT && math != FP8_GEMM_NATIVE_FP8) return FP8_ERR_OP;
-  fp8lin::GemmProblem p{};
-  bool empty = false;
+  empty = false;
   switch (op) {
     case FP8_GEMM_FWD:
       // Y[M x N]: X8 and W8 both contraction (K) contiguous.
@@ -216,6 +245,16 @@ int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, c
     default:
       return FP8_ERR_OP;
   }
+  return FP8_OK;
+}
+
+int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, const int32_t* ba,
+                const uint8_t* b, fp8_format_t fb, const int32_t* bb, int64_t M, int64_t N,
+                int64_t K, float* out, float* out_amax, WsMode ws_mode, void* ws, int64_t ws_bytes,
+                hipStream_t st) {
+  fp8lin::GemmProblem p{};
+  bool empty = false;
+  if (int s = make_problem(op, math, a, fa, ba, b, fb, bb, M, N, K, out, p, empty)) return s;
   bool split = false;
   if (ws_mode != kNoWorkspace && !empty) {
     const int64_t need = fp8lin::gemm_split_workspace_bytes(p.m, p.n, p.k);
@@ -255,9 +294,69 @@ int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, c
   }
 }
 
+// The problems of a group call (checked) and their plan; count products at
+// most kGroupMaxProducts.  Returns the workspace bytes (>= 0) or a status.
+int64_t group_problems(int math, const fp8_gemm_desc_t* d, int32_t count, fp8lin::GemmProblem* ps,
+                       fp8lin::GroupSlot* plan, int* live) {
+  if (count < 0 || count > fp8lin::kGroupMaxProducts) return FP8_ERR_SIZE;
+  if (count > 0 && !d) return FP8_ERR_NULL;
+  *live = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    bool empty = false;
+    fp8lin::GemmProblem p{};
+    if (int s = make_problem((fp8_gemm_op_t)d[i].op, math, d[i].a, (fp8_format_t)d[i].fa, d[i].ba, d[i].b,
+                             (fp8_format_t)d[i].fb, d[i].bb, d[i].M, d[i].N, d[i].K, d[i].out, p, empty))
+      return s;
+    if (!empty) ps[(*live)++] = p;
+  }
+  return fp8lin::gemm_group_plan(ps, *live, plan);
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t fp8_scaled_gemm_group_workspace_bytes(int math, const fp8_gemm_desc_t* descs, int32_t count) {
+  fp8lin::GemmProblem ps[fp8lin::kGroupMaxProducts];
+  fp8lin::GroupSlot plan[fp8lin::kGroupMaxProducts];
+  int live = 0;
+  return group_problems(math, descs, count, ps, plan, &live);
+}
+
+int fp8_scaled_gemm_group(int math, const fp8_gemm_desc_t* descs, int32_t count, void* ws,
+                          int64_t ws_bytes, void* stream) {
+  fp8lin::GemmProblem ps[fp8lin::kGroupMaxProducts];
+  fp8lin::GroupSlot plan[fp8lin::kGroupMaxProducts];
+  int live = 0;
+  const int64_t need = group_problems(math, descs, count, ps, plan, &live);
+  if (need < 0) return (int)need;
+  if (ws_bytes < 0) return FP8_ERR_SIZE;
+  if (need > 0) {
+    if (!ws) return FP8_ERR_NULL;
+    if (misaligned(ws)) return FP8_ERR_ALIGN;
+    if (ws_bytes < need) return FP8_ERR_SIZE;
+  }
+  if (live == 0) return FP8_OK;
+  if (int s = device_ok()) return s;
+  hipStream_t st = (hipStream_t)stream;
+  int idx[3][fp8lin::kGroupMaxProducts];
+  int n[3] = {0, 0, 0};
+  for (int i = 0; i < live; ++i) {
+    const fp8lin::GemmProblem& p = ps[i];
+    const int layout = p.a_kmajor && p.b_kmajor ? 0 : (p.a_kmajor ? 1 : 2);
+    if (plan[i].grouped) {
+      idx[layout][n[layout]++] = i;
+      continue;
+    }
+    hipError_t e = layout == 0 ? fp8lin::launch_gemm_fwd(p, st)
+                   : layout == 1 ? fp8lin::launch_gemm_dgrad(p, st) : fp8lin::launch_gemm_wgrad(p, st);
+    if (e != hipSuccess) return FP8_ERR_HIP;
+  }
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  if (int s = hip_status(fp8lin::launch_gemm_fwd_group(ps, plan, idx[0], n[0], w, st))) return s;
+  if (int s = hip_status(fp8lin::launch_gemm_dgrad_group(ps, plan, idx[1], n[1], w, st))) return s;
+  return hip_status(fp8lin::launch_gemm_wgrad_group(ps, plan, idx[2], n[2], w, st));
+}
 
 int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
                     const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,

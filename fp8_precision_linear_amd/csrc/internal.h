@@ -23,6 +23,19 @@ hipError_t launch_clear_u32(uint32_t* p, hipStream_t stream);
 hipError_t launch_quantize(const void* x, int dtype, int64_t n, int fmt, int32_t margin, uint8_t* y,
                            float* amax, int32_t* bias, hipStream_t stream);
 
+// The quantisation of several tensors (fp8_quantize_multi): three launches per
+// 32 tensors, every tensor's results those of launch_quantize on it alone.
+struct QuantDesc {
+  const void* x;
+  int64_t n;
+  int dtype, fmt;
+  int32_t margin;
+  uint8_t* y;
+  float* amax;
+  int32_t* bias;
+};
+hipError_t launch_quantize_multi(const QuantDesc* d, int count, hipStream_t stream);
+
 // SwiGLU between the products of a chained MLP (swiglu.hip).  amax: optional,
 // cleared then folded with max |output| (fp32 magnitude bits).
 hipError_t launch_swiglu_fwd(const float* h, int64_t rows, int64_t f, uint16_t* a, uint32_t* amax,
@@ -73,5 +86,24 @@ hipError_t launch_gemm_dgrad_ws(const GemmProblem& p, float* ws, hipStream_t str
 hipError_t launch_gemm_wgrad_ws(const GemmProblem& p, float* ws, hipStream_t stream);
 // Workspace bytes the split of an m x n output with contraction k needs (0: not split).
 int64_t gemm_split_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+// Several products run together (fp8_scaled_gemm_group, gemm_group.h).
+constexpr int kGroupMaxProducts = 256;  // products per call
+struct GroupSlot {
+  int grouped;        // 1: in a grouped launch; 0: launched on its own
+  int splits;         // contraction slices (1: not split)
+  int kslice;         // contraction bytes per slice
+  int64_t ws_offset;  // splits > 1: the slices' bytes in the workspace start here
+};
+// The plan of count products (ps: every output contiguous, ldc == n); returns
+// the workspace bytes it needs.
+int64_t gemm_group_plan(const GemmProblem* ps, int count, GroupSlot* plan);
+// The grouped products ps[idx[0..n)] of one operand layout each.
+hipError_t launch_gemm_fwd_group(const GemmProblem* ps, const GroupSlot* plan, const int* idx, int n,
+                                 uint8_t* ws, hipStream_t stream);
+hipError_t launch_gemm_dgrad_group(const GemmProblem* ps, const GroupSlot* plan, const int* idx, int n,
+                                   uint8_t* ws, hipStream_t stream);
+hipError_t launch_gemm_wgrad_group(const GemmProblem* ps, const GroupSlot* plan, const int* idx, int n,
+                                   uint8_t* ws, hipStream_t stream);
 
 }  // namespace fp8lin

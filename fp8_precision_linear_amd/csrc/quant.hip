@@ -131,14 +131,15 @@ __device__ __forceinline__ u16x2 vmax_bf16(u16x2 acc, uint4 v) {
   return acc;
 }
 
+// The lane's largest bf16 magnitude over the tensor's 8-element vectors that
+// block blk of nblk covers (grid-stride), plus block 0's share of the tail.
 template <bool NT>
-__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __restrict__ x,
-                                                             int64_t nvec,
-                                                             const uint16_t* __restrict__ tail,
-                                                             int ntail, uint32_t* out) {
+__device__ __forceinline__ uint32_t amax_bf16_body(const uint4* __restrict__ x, int64_t nvec,
+                                                   const uint16_t* __restrict__ tail, int ntail,
+                                                   int64_t blk, int64_t nblk) {
   u16x2 acc = {0, 0};
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t stride = nblk * kThreads;
+  int64_t i = blk * kThreads + threadIdx.x;
   for (; i + (kAmaxUnroll - 1) * stride < nvec; i += kAmaxUnroll * stride) {
     uint4 v[kAmaxUnroll];
 #pragma unroll
@@ -148,8 +149,16 @@ __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __rest
   }
   for (; i < nvec; i += stride) acc = vmax_bf16(acc, load16<NT>(&x[i]));
   uint32_t m = max((uint32_t)acc.x, (uint32_t)acc.y);
-  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7FFFu));
-  block_max_to(m << 16, out);  // bf16 magnitude widened to fp32 bits
+  if (blk == 0 && (int)threadIdx.x < ntail) m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7FFFu));
+  return m << 16;  // bf16 magnitude widened to fp32 bits
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __restrict__ x,
+                                                             int64_t nvec,
+                                                             const uint16_t* __restrict__ tail,
+                                                             int ntail, uint32_t* out) {
+  block_max_to(amax_bf16_body<NT>(x, nvec, tail, ntail, blockIdx.x, gridDim.x), out);
 }
 
 __device__ __forceinline__ uint32_t vmax_f32(uint32_t acc, uint4 v) {
@@ -159,13 +168,12 @@ __device__ __forceinline__ uint32_t vmax_f32(uint32_t acc, uint4 v) {
 }
 
 template <bool NT>
-__global__ __launch_bounds__(kThreads) void amax_f32_kernel(const uint4* __restrict__ x,
-                                                            int64_t nvec,
-                                                            const uint32_t* __restrict__ tail,
-                                                            int ntail, uint32_t* out) {
+__device__ __forceinline__ uint32_t amax_f32_body(const uint4* __restrict__ x, int64_t nvec,
+                                                  const uint32_t* __restrict__ tail, int ntail,
+                                                  int64_t blk, int64_t nblk) {
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t stride = nblk * kThreads;
+  int64_t i = blk * kThreads + threadIdx.x;
   for (; i + (kAmaxUnroll - 1) * stride < nvec; i += kAmaxUnroll * stride) {
     uint4 v[kAmaxUnroll];
 #pragma unroll
@@ -174,8 +182,16 @@ __global__ __launch_bounds__(kThreads) void amax_f32_kernel(const uint4* __restr
     for (int u = 0; u < kAmaxUnroll; ++u) m = vmax_f32(m, v[u]);
   }
   for (; i < nvec; i += stride) m = vmax_f32(m, load16<NT>(&x[i]));
-  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = max(m, tail[threadIdx.x] & 0x7FFFFFFFu);
-  block_max_to(m, out);
+  if (blk == 0 && (int)threadIdx.x < ntail) m = max(m, tail[threadIdx.x] & 0x7FFFFFFFu);
+  return m;
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void amax_f32_kernel(const uint4* __restrict__ x,
+                                                            int64_t nvec,
+                                                            const uint32_t* __restrict__ tail,
+                                                            int ntail, uint32_t* out) {
+  block_max_to(amax_f32_body<NT>(x, nvec, tail, ntail, blockIdx.x, gridDim.x), out);
 }
 
 // ---------------------------------------------------------------- bias
@@ -223,8 +239,8 @@ __device__ __forceinline__ int32_t load_bias(const BiasArg& a) {
 }
 
 template <int FMT>
-__device__ __forceinline__ void store_derived_bias(const BiasArg& a) {
-  if (a.amax && blockIdx.x == 0 && threadIdx.x == 0) *a.bias_out = load_bias<FMT>(a);
+__device__ __forceinline__ void store_derived_bias(const BiasArg& a, int64_t blk) {
+  if (a.amax && blk == 0 && threadIdx.x == 0) *a.bias_out = load_bias<FMT>(a);
 }
 
 // ---------------------------------------------------------------- cast
@@ -411,9 +427,10 @@ __device__ __forceinline__ uint4 cast_unit_sw(uint4 lo, uint4 hi, int32_t b) {
 // With AMAX the lane's largest input magnitude (bf16 bits) is returned too.
 template <int FMT, bool NT, bool AMAX>
 __device__ __forceinline__ uint32_t cast_bf16_body(const uint4* __restrict__ x, int64_t nunit,
-                                                   const BiasArg& bias, uint4* __restrict__ y) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+                                                   const BiasArg& bias, uint4* __restrict__ y,
+                                                   int64_t blk, int64_t nblk) {
+  const int64_t stride = nblk * kThreads;
+  int64_t i = blk * kThreads + threadIdx.x;
   if (i >= nunit) return 0u;
   u16x2 acc = {0, 0};
   uint4 lo = load16<NT>(&x[2 * i]), hi = load16<NT>(&x[2 * i + 1]);
@@ -444,6 +461,25 @@ __device__ __forceinline__ uint32_t cast_bf16_body(const uint4* __restrict__ x, 
   return max((uint32_t)acc.x, (uint32_t)acc.y);
 }
 
+// Block blk of nblk casting a bf16 tensor: its units, the derived bias (block
+// 0), block 0's share of the tail; returns the lane's largest input magnitude
+// (fp32 bits) when AMAX.
+template <int FMT, bool NT, bool AMAX>
+__device__ __forceinline__ uint32_t cast_bf16_whole(const uint4* __restrict__ x, int64_t nunit,
+                                                    const BiasArg& bias, uint4* __restrict__ y,
+                                                    const uint16_t* __restrict__ tail_x,
+                                                    uint8_t* __restrict__ tail_y, int ntail,
+                                                    int64_t blk, int64_t nblk) {
+  uint32_t m = cast_bf16_body<FMT, NT, AMAX>(x, nunit, bias, y, blk, nblk);
+  store_derived_bias<FMT>(bias, blk);
+  if (blk == 0 && (int)threadIdx.x < ntail) {
+    const uint32_t w = tail_x[threadIdx.x];
+    tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>(w << 16, load_bias<FMT>(bias));
+    m = max(m, w & 0x7FFFu);
+  }
+  return m << 16;
+}
+
 // AMAX: also fold max |x| (fp32 bits) into *amax, once per block.
 template <int FMT, bool NT, bool AMAX>
 __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const uint4* __restrict__ x,
@@ -452,14 +488,9 @@ __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const uint4* __rest
                                                              const uint16_t* __restrict__ tail_x,
                                                              uint8_t* __restrict__ tail_y,
                                                              int ntail, uint32_t* amax) {
-  uint32_t m = cast_bf16_body<FMT, NT, AMAX>(x, nunit, bias, y);
-  store_derived_bias<FMT>(bias);
-  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) {
-    const uint32_t w = tail_x[threadIdx.x];
-    tail_y[threadIdx.x] = (uint8_t)fp8_code<FMT>(w << 16, load_bias<FMT>(bias));
-    m = max(m, w & 0x7FFFu);
-  }
-  if constexpr (AMAX) block_max_fold(m << 16, amax);
+  const uint32_t m = cast_bf16_whole<FMT, NT, AMAX>(x, nunit, bias, y, tail_x, tail_y, ntail,
+                                                    blockIdx.x, gridDim.x);
+  if constexpr (AMAX) block_max_fold(m, amax);
 }
 
 // fp32 input: a wave takes chunks of kF32Chunk consecutive elements; load k
@@ -486,22 +517,21 @@ __device__ __forceinline__ uint32_t cast4_f32(uint4 v, bool hw, int32_t b, uint3
 }
 
 template <int FMT, bool NT, bool AMAX>
-__global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restrict__ x,
-                                                            int64_t nchunk, BiasArg bias,
-                                                            uint32_t* __restrict__ y,
-                                                            const uint32_t* __restrict__ tail_x,
-                                                            uint8_t* __restrict__ tail_y,
-                                                            int ntail, uint32_t* amax) {
-  store_derived_bias<FMT>(bias);
+__device__ __forceinline__ uint32_t cast_f32_whole(const uint4* __restrict__ x, int64_t nchunk,
+                                                   const BiasArg& bias, uint32_t* __restrict__ y,
+                                                   const uint32_t* __restrict__ tail_x,
+                                                   uint8_t* __restrict__ tail_y, int ntail,
+                                                   int64_t blk, int64_t nblk) {
+  store_derived_bias<FMT>(bias, blk);
   const int32_t b = load_bias<FMT>(bias);
   const bool hw = kHwConvert<FMT> && b >= kHwBiasMin && b <= kHwBiasMax;
   uint32_t bound = 0;
   if constexpr (kHwConvert<FMT>) bound = hw_bound_f32<FMT>(b);
   const float scale = __builtin_ldexpf(1.0f, hw ? -b : 0);
   const int lane = threadIdx.x & 63;
-  const int64_t wstride = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t wstride = nblk * (kThreads / 64);
   uint32_t m = 0;
-  for (int64_t w = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); w < nchunk; w += wstride) {
+  for (int64_t w = blk * (kThreads / 64) + (threadIdx.x >> 6); w < nchunk; w += wstride) {
     const int64_t q = w * (kF32Chunk / 4);  // the chunk's first 16-byte group
     uint4 v[kF32Loads];
 #pragma unroll
@@ -512,11 +542,23 @@ __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restr
       if constexpr (AMAX) m = vmax_f32(m, v[k]);
     }
   }
-  if (blockIdx.x == 0)
+  if (blk == 0)
     for (int i = threadIdx.x; i < ntail; i += kThreads) {
       tail_y[i] = (uint8_t)fp8_code<FMT>(tail_x[i], b);
       m = max(m, tail_x[i] & 0x7FFFFFFFu);
     }
+  return m;
+}
+
+template <int FMT, bool NT, bool AMAX>
+__global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restrict__ x,
+                                                            int64_t nchunk, BiasArg bias,
+                                                            uint32_t* __restrict__ y,
+                                                            const uint32_t* __restrict__ tail_x,
+                                                            uint8_t* __restrict__ tail_y,
+                                                            int ntail, uint32_t* amax) {
+  const uint32_t m = cast_f32_whole<FMT, NT, AMAX>(x, nchunk, bias, y, tail_x, tail_y, ntail,
+                                                   blockIdx.x, gridDim.x);
   if constexpr (AMAX) block_max_fold(m, amax);
 }
 
@@ -603,6 +645,97 @@ __global__ __launch_bounds__(kSmallThreads) void quantize_small_f32_kernel(
   const float scale = __builtin_ldexpf(1.0f, hw ? -b : 0);
   for (int64_t i = t; i < nvec; i += kSmallThreads) y[i] = cast4_f32<FMT>(x[i], hw, b, bound, scale);
   if (t < ntail) tail_y[t] = (uint8_t)fp8_code<FMT>(tail_x[t], b);
+}
+
+// ---------------------------------------------------------------- several tensors in three launches
+// The quantisation of up to kMultiMax tensors in three launches in all: one
+// clears every amax word, one reduces every tensor's amax (each tensor has its
+// own run of blocks, sized as the single-tensor amax would size its grid),
+// one casts every tensor (each block derives its tensor's bias from the amax
+// word, block 0 of each tensor stores it).  Every tensor's amax, bias and
+// codes are those of fp8_quantize on it alone, bit for bit: the amax is an
+// order-independent integer max, and each cast block does what the
+// single-tensor cast does for its part of the tensor.
+constexpr int kMultiMax = 32;
+
+struct MultiTensor {
+  const void* x;
+  uint8_t* y;
+  uint32_t* amax;
+  int32_t* bias;
+  int64_t n;
+  int32_t dtype, fmt, margin;
+  int32_t amax_first, amax_blocks;  // this tensor's blocks in the amax launch
+  int32_t cast_first, cast_blocks;  // and in the cast launch
+};
+
+struct MultiArgs {
+  int32_t count;
+  MultiTensor t[kMultiMax];
+};
+
+// The entry of the block's tensor: the last whose first block is at most
+// blockIdx.x (entries are in launch order).  Read through the kernel-argument
+// pointer so that the wave-uniform index stays a scalar load.
+__device__ __forceinline__ const __attribute__((address_space(4))) MultiTensor* multi_entry(bool cast) {
+  const auto* a = (const __attribute__((address_space(4))) MultiArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  const int b = (int)blockIdx.x;
+  int i = 0;
+  while (i + 1 < a->count && (cast ? a->t[i + 1].cast_first : a->t[i + 1].amax_first) <= b) ++i;
+  return &a->t[i];
+}
+
+__global__ void multi_clear_kernel(MultiArgs a) {
+  const auto* ka = (const __attribute__((address_space(4))) MultiArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  if ((int)threadIdx.x < ka->count) *ka->t[threadIdx.x].amax = 0u;
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void multi_amax_kernel(MultiArgs a) {
+  const auto* e = multi_entry(false);
+  const int64_t blk = (int64_t)blockIdx.x - e->amax_first, nblk = e->amax_blocks;
+  const int64_t n = e->n;
+  uint32_t m;
+  if (e->dtype == FP8_IN_BF16) {
+    const int64_t nvec = n / 8;
+    const uint16_t* tail = static_cast<const uint16_t*>(e->x) + nvec * 8;
+    m = amax_bf16_body<NT>(static_cast<const uint4*>(e->x), nvec, tail, (int)(n - nvec * 8), blk, nblk);
+  } else {
+    const int64_t nvec = n / 4;
+    const uint32_t* tail = static_cast<const uint32_t*>(e->x) + nvec * 4;
+    m = amax_f32_body<NT>(static_cast<const uint4*>(e->x), nvec, tail, (int)(n - nvec * 4), blk, nblk);
+  }
+  block_max_to(m, e->amax);
+}
+
+template <int FMT, bool NT>
+__device__ __forceinline__ void multi_cast_one(const __attribute__((address_space(4))) MultiTensor* e,
+                                               int64_t blk, int64_t nblk) {
+  const BiasArg bias{nullptr, e->amax, e->bias, e->margin};
+  const int64_t n = e->n;
+  if (e->dtype == FP8_IN_BF16) {
+    const int64_t nunit = n / 16;
+    cast_bf16_whole<FMT, NT, false>(static_cast<const uint4*>(e->x), nunit, bias, reinterpret_cast<uint4*>(e->y),
+                                    static_cast<const uint16_t*>(e->x) + nunit * 16, e->y + nunit * 16,
+                                    (int)(n - nunit * 16), blk, nblk);
+  } else {
+    const int64_t nchunk = n / kF32Chunk;
+    cast_f32_whole<FMT, NT, false>(static_cast<const uint4*>(e->x), nchunk, bias,
+                                   reinterpret_cast<uint32_t*>(e->y),
+                                   static_cast<const uint32_t*>(e->x) + nchunk * kF32Chunk,
+                                   e->y + nchunk * kF32Chunk, (int)(n - nchunk * kF32Chunk), blk, nblk);
+  }
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void multi_cast_kernel(MultiArgs a) {
+  const auto* e = multi_entry(true);
+  const int64_t blk = (int64_t)blockIdx.x - e->cast_first, nblk = e->cast_blocks;
+  switch (e->fmt) {
+    case FP8_E4M3: multi_cast_one<FP8_E4M3, NT>(e, blk, nblk); break;
+    case FP8_E5M2: multi_cast_one<FP8_E5M2, NT>(e, blk, nblk); break;
+    default: multi_cast_one<FP8_E3M4, NT>(e, blk, nblk); break;
+  }
 }
 
 }  // namespace
@@ -775,6 +908,47 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t n, int fmt, int32_t
   }
   if (hipError_t e = launch_amax(x, dtype, n, amax, stream)) return e;
   return launch_cast_from(x, dtype, n, BiasArg{nullptr, a, bias, margin}, fmt, y, nullptr, stream);
+}
+
+hipError_t launch_quantize_multi(const QuantDesc* d, int count, hipStream_t stream) {
+  const bool nt_amax = streams("FP8LIN_AMAX_HINT"), nt_cast = streams("FP8LIN_CAST_HINT");
+  for (int first = 0; first < count; first += kMultiMax) {
+    MultiArgs a{};
+    a.count = count - first < kMultiMax ? count - first : kMultiMax;
+    int64_t amax_total = 0, cast_total = 0;
+    for (int i = 0; i < a.count; ++i) {
+      const QuantDesc& q = d[first + i];
+      MultiTensor& t = a.t[i];
+      t.x = q.x;
+      t.y = q.y;
+      t.amax = reinterpret_cast<uint32_t*>(q.amax);
+      t.bias = q.bias;
+      t.n = q.n;
+      t.dtype = q.dtype;
+      t.fmt = q.fmt;
+      t.margin = q.margin;
+      // the grids the single-tensor amax and cast would launch
+      const bool bf = q.dtype == FP8_IN_BF16;
+      t.amax_blocks = stream_blocks(bf ? q.n / 8 : q.n / 4, kAmaxUnroll, kAmaxMaxBlocks);
+      if (bf) {
+        t.cast_blocks = stream_blocks(q.n / 16, kCastUnitsPerLane, kCastMaxBlocks);
+      } else {
+        const int64_t want = (q.n / kF32Chunk + (kThreads / 64) - 1) / (kThreads / 64);
+        t.cast_blocks = (int)(want < 1 ? 1 : (want > kCastMaxBlocks ? kCastMaxBlocks : want));
+      }
+      t.amax_first = (int32_t)amax_total;
+      t.cast_first = (int32_t)cast_total;
+      amax_total += t.amax_blocks;
+      cast_total += t.cast_blocks;
+    }
+    hipLaunchKernelGGL(multi_clear_kernel, dim3(1), dim3(64), 0, stream, a);
+    if (nt_amax) hipLaunchKernelGGL(multi_amax_kernel<true>, dim3((uint32_t)amax_total), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(multi_amax_kernel<false>, dim3((uint32_t)amax_total), dim3(kThreads), 0, stream, a);
+    if (nt_cast) hipLaunchKernelGGL(multi_cast_kernel<true>, dim3((uint32_t)cast_total), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(multi_cast_kernel<false>, dim3((uint32_t)cast_total), dim3(kThreads), 0, stream, a);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace fp8lin

@@ -154,6 +154,38 @@ int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32
                         fp8_format_t fmt, uint8_t* y, float* x_amax, void* stream);
 
 /*
+ * fp8_quantize_multi: fp8_quantize of several tensors in one call -- the
+ * per-tensor amax, bias and cast of "Proposed method", bullets 1-4, for each
+ * tensor on its own -- in three launches per 32 tensors (one clears every amax,
+ * one reduces every tensor's amax, one casts every tensor deriving its bias
+ * from its amax), so that a step that quantises many small tensors (a layer's
+ * activations, weights and gradients) pays three kernel dispatches instead of
+ * up to three per tensor.
+ *   descs  host array of count descriptors (read during the call only):
+ *          x, n, dtype, fmt, margin, y, amax, bias exactly as fp8_quantize's
+ *          arguments for that tensor.  The outputs of different tensors must
+ *          not overlap one another or any input.
+ *   count  >= 0 (0: nothing is launched).
+ * Each tensor's amax, bias and codes are bit-identical to fp8_quantize on it
+ * alone.  Every descriptor is checked before anything is launched; the first
+ * bad one's status is returned (as fp8_quantize would return it), and nothing
+ * runs.  FP8_ERR_NULL for descs == NULL with count > 0, FP8_ERR_SIZE for
+ * count < 0.
+ */
+typedef struct {
+  const void* x;   /* device input, 16-byte aligned */
+  int64_t n;       /* elements, >= 0 */
+  int32_t dtype;   /* fp8_dtype_t */
+  int32_t fmt;     /* fp8_format_t */
+  int32_t margin;  /* |margin| <= FP8_MAX_MARGIN */
+  int32_t pad;     /* unused */
+  uint8_t* y;      /* device, n codes, 16-byte aligned */
+  float* amax;     /* device, one float, 4-byte aligned */
+  int32_t* bias;   /* device, one int32, 4-byte aligned */
+} fp8_quant_desc_t;
+int fp8_quantize_multi(const fp8_quant_desc_t* descs, int32_t count, void* stream);
+
+/*
  * The three FP8 x FP8 products with fp32 accumulation, unscaled after the
  * matmul ("Proposed method", bullets 3 and 5).  Each output is overwritten
  * (no accumulation into it).  Operands may be E4M3 or E5M2 in any pairing
@@ -248,6 +280,56 @@ int fp8_scaled_gemm_noalloc(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_fo
                             const int32_t* ba, const uint8_t* b, fp8_format_t fb,
                             const int32_t* bb, int64_t M, int64_t N, int64_t K, float* out,
                             void* stream);
+
+/*
+ * Several products in one call ("Proposed method", bullets 3 and 5: a layer's
+ * forward, data-gradient and weight-gradient products), for steps made of
+ * many small products, where a launch per product leaves most of the chip
+ * idle and pays a dispatch each.  The products of one operand layout and
+ * format pair run in one launch (128 x 128 output tiles of all of them);
+ * products with long contractions are split into slices of about the
+ * shortest contraction among them (raw sums in the workspace, then one
+ * launch adds every split product's slices in slice order and unscales), so
+ * the launch's blocks do similar work.  Products of more than 1024 tiles of
+ * 128 x 128, or that the pipelined kernels do not take (a contraction that is
+ * not a multiple of 64, misaligned rows), run as single products.
+ *   descs  host array of count product descriptors (read during the call
+ *          only): op and the operands, biases, sizes and output exactly as
+ *          fp8_scaled_gemm's arguments.  Outputs must not overlap each other,
+ *          any operand or the workspace.
+ *   count  0 .. 256.
+ *   math   FP8_GEMM_EXACT or FP8_GEMM_NATIVE_FP8, for every product.
+ * Every product's output is within the bound of fp8_scaled_gemm's (the same
+ * arithmetic; a split one sums in another order), and the same inputs give
+ * the same bits on every call.
+ *
+ * fp8_scaled_gemm_group_workspace_bytes: the workspace bytes the call needs
+ * (0: no product is split), a pure function of the descriptors' ops, formats,
+ * sizes and alignments, or a negative status (the first bad descriptor's, as
+ * fp8_scaled_gemm would return it; FP8_ERR_SIZE for count outside 0 .. 256).
+ *
+ * fp8_scaled_gemm_group: every argument is checked before anything runs (the
+ * first bad descriptor's status; FP8_ERR_NULL / FP8_ERR_ALIGN / FP8_ERR_SIZE
+ * for a missing, misaligned or too small workspace the products need).  ws:
+ * device, 16-byte aligned, at least the bytes above, the caller's (the call
+ * overwrites it and keeps no pointer); calls in flight at the same time need
+ * separate workspaces.
+ */
+typedef struct {
+  int32_t op;          /* fp8_gemm_op_t */
+  int32_t fa;          /* fp8_format_t of a */
+  int32_t fb;          /* fp8_format_t of b */
+  int32_t pad;         /* unused */
+  const uint8_t* a;    /* device codes, as fp8_scaled_gemm's a */
+  const int32_t* ba;   /* device, one int32 */
+  const uint8_t* b;    /* device codes, as fp8_scaled_gemm's b */
+  const int32_t* bb;   /* device, one int32 */
+  int64_t M, N, K;     /* as fp8_scaled_gemm's */
+  float* out;          /* device fp32 output */
+} fp8_gemm_desc_t;
+int64_t fp8_scaled_gemm_group_workspace_bytes(int math, const fp8_gemm_desc_t* descs, int32_t count);
+int fp8_scaled_gemm_group(int math, const fp8_gemm_desc_t* descs, int32_t count, void* ws,
+                          int64_t ws_bytes, void* stream);
 
 /* fp8_scaled_gemm that also returns the per-tensor amax of its output (the
  * "Proposed method" bullet-1 statistic of the tensor the product produces),

@@ -42,13 +42,41 @@ def u8_dev(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
 
 
+# |x| at or above which round-to-nearest-even to fp32 gives an infinity
+FP32_OVERFLOW = 2.0 ** 128 - 2.0 ** 103
+# half the fp32 spacing below 2^-126 (the smallest subnormal is 2^-149)
+HALF_SUBNORMAL = 2.0 ** -150
+
+
 def check_gemm(got, ref, bound, what, rel=1e-5):
-    """|got - ref| <= rel * bound elementwise (bound = sum |a||b| * 2^-(ba+bb));
-    reports the worst element and the worst err/bound ratio."""
+    """The products' tolerance, elementwise, against the oracle's fp64 result
+    ref and bound = 2^-(ba+bb) * sum |a||b|:
+      * where ref is NaN (a NaN code among the output's terms, inf * 0,
+        inf - inf) the output must be NaN; where ref is +-inf, that infinity;
+      * otherwise |got - ref| <= rel * bound + 2^-150: the second term is half
+        the fp32 spacing below 2^-126, what the output's own rounding can cost
+        where the exact result lies in fp32's subnormal range or below;
+      * an infinity of ref's sign is also accepted where |ref| + rel * bound
+        reaches fp32's overflow threshold (results beyond fp32's range).
+    Returns the worst err / bound over the finite, in-range outputs."""
     got = np.asarray(got, dtype=np.float64)
-    err = np.abs(got - ref)
-    ok = err <= rel * bound
-    ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+    ref = np.asarray(ref, dtype=np.float64)
+    bound = np.asarray(bound, dtype=np.float64)
+    nan_ref, inf_ref = np.isnan(ref), np.isinf(ref)
+    fin = ~(nan_ref | inf_ref)
+    reffin = np.where(fin, ref, 0.0)
+    bndfin = np.where(fin, bound, 0.0)
+    with np.errstate(invalid="ignore", over="ignore"):
+        err = np.abs(got - reffin)
+        ok_fin = fin & (err <= rel * bndfin + HALF_SUBNORMAL)
+        overflow = fin & np.isinf(got) & (np.sign(got) == np.sign(reffin)) & \
+            (np.abs(reffin) + rel * bndfin >= FP32_OVERFLOW)
+        ok = np.where(nan_ref, np.isnan(got),
+                      np.where(inf_ref, got == ref, ok_fin | overflow))
+        inrange = fin & np.isfinite(got)
+        excess = np.maximum(err - HALF_SUBNORMAL, 0.0)   # beyond the output's own rounding
+        ratio = np.where(inrange & (bndfin > 0), excess / np.where(bndfin > 0, bndfin, 1.0),
+                         np.where(inrange & (excess > 0), np.inf, 0.0))
     worst = float(ratio.max()) if ratio.size else 0.0
     if not ok.all():
         idx = np.argwhere(~ok)

@@ -31,7 +31,7 @@ def status(code):
 
 def test_every_declared_function_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
         assert n in fl.SIGNATURES, n
@@ -129,6 +129,60 @@ def test_python_wrappers_reject_cpu_tensors():
     x = torch.zeros(16, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fl.amax(x)
+
+
+def _raises(fn, text):
+    with pytest.raises(ValueError) as e:
+        fn()
+    assert text in str(e.value), str(e.value)
+
+
+def test_python_wrappers_check_outputs_before_calling():
+    """Every output, bias and code tensor is checked for dtype and size (then
+    for being a contiguous device tensor) before the library is called: a
+    wrong one would make a kernel write past its buffer or to a host address."""
+    x = torch.zeros(16, dtype=torch.bfloat16)
+    i32, f32, u8 = torch.int32, torch.float32, torch.uint8
+    one = lambda dt: torch.zeros(1, dtype=dt)
+    _raises(lambda: fl.amax(x, out=torch.zeros(1, dtype=torch.bfloat16)), "out must be torch.float32")
+    _raises(lambda: fl.amax(x, out=torch.zeros(2, dtype=f32)), "out must hold 1 elements")
+    _raises(lambda: fl.compute_bias(one(i32), 0), "amax must be torch.float32")
+    _raises(lambda: fl.compute_bias(one(f32), 0, out=one(f32)), "out must be torch.int32")
+    _raises(lambda: fl.scale_cast(x, one(f32), 0), "bias must be torch.int32")
+    _raises(lambda: fl.scale_cast(x, torch.zeros(2, dtype=i32), 0), "bias must hold 1 elements")
+    _raises(lambda: fl.scale_cast(x, one(i32), 0, out=torch.zeros(15, dtype=u8)), "out must hold 16 elements")
+    _raises(lambda: fl.scale_cast(x, one(i32), 0, out=torch.zeros(16, dtype=torch.int8)), "out must be torch.uint8")
+    _raises(lambda: fl.scale_cast(x, one(i32), 0, amax=one(i32)), "amax must be torch.float32")
+    _raises(lambda: fl.quantize(x, 0, out=torch.zeros(8, dtype=u8)), "out must hold 16 elements")
+    _raises(lambda: fl.quantize(x, 0, bias=one(f32)), "bias must be torch.int32")
+    _raises(lambda: fl.quantize(x, 0, amax=torch.zeros(4, dtype=f32)), "amax must hold 1 elements")
+    with pytest.raises(TypeError):
+        fl.quantize(torch.zeros(16, dtype=torch.float16), 0)
+    a8, b8 = torch.zeros(4, 8, dtype=u8), torch.zeros(6, 8, dtype=u8)
+    bi = one(i32)
+    _raises(lambda: fl.scaled_gemm(fl.OP_FWD, a8, 0, bi, b8, 0, bi, out=torch.zeros(4, 6, dtype=torch.bfloat16)),
+            "out must be torch.float32")
+    _raises(lambda: fl.scaled_gemm(fl.OP_FWD, a8, 0, bi, b8, 0, bi, out=torch.zeros(6, 4)), "out must have shape (4, 6)")
+    _raises(lambda: fl.scaled_gemm_dgrad(torch.zeros(4, 6, dtype=u8), 1, bi, b8, 0, bi, out=torch.zeros(4, 6)),
+            "out must have shape (4, 8)")
+    _raises(lambda: fl.scaled_gemm_wgrad(torch.zeros(4, 6, dtype=u8), 1, bi, a8, 0, bi, out=torch.zeros(8, 6)),
+            "out must have shape (6, 8)")
+    _raises(lambda: fl.scaled_gemm_fwd(a8.to(torch.int8), 0, bi, b8, 0, bi), "a8 must be torch.uint8")
+    _raises(lambda: fl.scaled_gemm_fwd(a8, 0, one(f32), b8, 0, bi), "bias_a must be torch.int32")
+    _raises(lambda: fl.scaled_gemm_fwd(a8, 0, bi, b8, 0, torch.zeros(2, dtype=i32)), "bias_b must hold 1 elements")
+    _raises(lambda: fl.scaled_gemm_fwd(a8.reshape(-1), 0, bi, b8, 0, bi), "2-D uint8")
+    _raises(lambda: fl.scaled_gemm_fwd(a8, 0, bi, torch.zeros(6, 7, dtype=u8), 0, bi), "contraction sizes differ")
+    _raises(lambda: fl.scaled_gemm_noalloc(fl.OP_FWD, a8, 0, bi, b8, 0, bi, None), "out is required")
+    _raises(lambda: fl.scaled_gemm_noalloc(fl.OP_FWD, a8, 0, bi, b8, 0, bi, torch.zeros(4, 6, dtype=torch.float64)),
+            "out must be torch.float32")
+    # right kinds on the host: refused for not being device tensors
+    _raises(lambda: fl.scaled_gemm(fl.OP_FWD, a8, 0, bi, b8, 0, bi, out=torch.zeros(4, 6)), "CUDA (HIP) tensor")
+    h = torch.zeros(3, 8)
+    _raises(lambda: fl.swiglu_fwd(h, out=torch.zeros(3, 4)), "out must be torch.bfloat16")
+    _raises(lambda: fl.swiglu_fwd(h, amax=torch.zeros(1, dtype=torch.bfloat16)), "amax must be torch.float32")
+    _raises(lambda: fl.swiglu_bwd(h, torch.zeros(3, 5)), "da must have shape (3, 4)")
+    _raises(lambda: fl.swiglu_bwd(h, torch.zeros(3, 4), out=torch.zeros(3, 4, dtype=torch.bfloat16)),
+            "out must have shape (3, 8)")
 
 
 def test_generic_gemm_rejects_unknown_op_and_math():
@@ -309,3 +363,94 @@ def test_gemm_noalloc_without_a_device_reports_no_device():
     f = L.fp8_scaled_gemm_noalloc
     assert f(0, 0, A16, 0, A32, A48, 0, A32, 2048, 768, 3072, A16, None) == status("FP8_ERR_DEVICE")
     assert f(0, 0, A16, 0, A32, A48, 0, A32, 8192, 8192, 8192, A16, None) == status("FP8_ERR_DEVICE")
+
+
+def _qdesc(x=A16, n=10, dtype=0, fmt=0, margin=0, y=A48, amax=A32, bias=A32):
+    return fl.QuantDesc(x.value if isinstance(x, P) else x, n, dtype, fmt, margin, 0,
+                        y.value if isinstance(y, P) else y, amax.value if isinstance(amax, P) else amax,
+                        bias.value if isinstance(bias, P) else bias)
+
+
+def test_quantize_multi_argument_checks():
+    f = L.fp8_quantize_multi
+    ok = _qdesc()
+    arr = lambda *ds: (fl.QuantDesc * len(ds))(*ds)
+    assert f(None, -1, None) == status("FP8_ERR_SIZE")
+    assert f(None, 0, None) == 0
+    assert f(None, 2, None) == status("FP8_ERR_NULL")
+    # the first bad descriptor's fp8_quantize status, nothing launched
+    assert f(arr(ok, _qdesc(n=-1)), 2, None) == status("FP8_ERR_SIZE")
+    assert f(arr(ok, _qdesc(dtype=4)), 2, None) == status("FP8_ERR_DTYPE")
+    assert f(arr(ok, _qdesc(fmt=3)), 2, None) == status("FP8_ERR_FORMAT")
+    assert f(arr(ok, _qdesc(margin=65)), 2, None) == status("FP8_ERR_MARGIN")
+    assert f(arr(ok, _qdesc(x=None)), 2, None) == status("FP8_ERR_NULL")
+    assert f(arr(ok, _qdesc(amax=None)), 2, None) == status("FP8_ERR_NULL")
+    assert f(arr(ok, _qdesc(x=MIS)), 2, None) == status("FP8_ERR_ALIGN")
+    assert f(arr(ok, _qdesc(bias=P(34))), 2, None) == status("FP8_ERR_ALIGN")
+    assert f(arr(_qdesc(fmt=9), _qdesc(n=-3)), 2, None) == status("FP8_ERR_FORMAT")
+    # an empty tensor needs no input or output pointers (its amax and bias are written)
+    assert f(arr(ok, _qdesc(x=None, y=None, n=0), _qdesc(x=None, n=0, amax=None)), 3, None) == status("FP8_ERR_NULL")
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
+def test_quantize_multi_without_a_device_reports_no_device():
+    arr = (fl.QuantDesc * 2)(_qdesc(), _qdesc(n=0, x=None, y=None))
+    assert L.fp8_quantize_multi(arr, 2, None) == status("FP8_ERR_DEVICE")
+
+
+def _gdesc(op=0, fa=0, fb=0, a=A16, ba=A32, b=A48, bb=A32, M=64, N=64, K=64, out=A16):
+    v = lambda p: p.value if isinstance(p, P) else p
+    return fl.GemmDesc(op, fa, fb, 0, v(a), v(ba), v(b), v(bb), M, N, K, v(out))
+
+
+def test_gemm_group_argument_checks():
+    f, wsb = L.fp8_scaled_gemm_group, L.fp8_scaled_gemm_group_workspace_bytes
+    arr = lambda *ds: (fl.GemmDesc * len(ds))(*ds)
+    ok = _gdesc()
+    assert wsb(0, None, 0) == 0 and f(0, None, 0, None, 0, None) == 0
+    assert wsb(0, None, -1) == status("FP8_ERR_SIZE") and wsb(0, arr(ok), 257) == status("FP8_ERR_SIZE")
+    assert wsb(0, None, 1) == status("FP8_ERR_NULL")
+    assert wsb(2, arr(ok), 1) == status("FP8_ERR_OP")
+    assert wsb(0, arr(ok, _gdesc(op=3)), 2) == status("FP8_ERR_OP")
+    assert wsb(0, arr(ok, _gdesc(fa=2)), 2) == status("FP8_ERR_FORMAT")
+    assert wsb(0, arr(ok, _gdesc(out=None)), 2) == status("FP8_ERR_NULL")
+    assert wsb(0, arr(ok, _gdesc(ba=None)), 2) == status("FP8_ERR_NULL")
+    assert wsb(0, arr(ok, _gdesc(a=MIS)), 2) == status("FP8_ERR_ALIGN")
+    assert wsb(0, arr(ok, _gdesc(bb=P(34))), 2) == status("FP8_ERR_ALIGN")
+    assert wsb(0, arr(ok, _gdesc(M=-1)), 2) == status("FP8_ERR_SIZE")
+    # the same status from the call itself, before anything runs
+    assert f(0, arr(ok, _gdesc(fa=2)), 2, None, 0, None) == status("FP8_ERR_FORMAT")
+    # empty products need nothing
+    assert f(0, arr(_gdesc(M=0, a=None, out=None), _gdesc(op=2, N=0, a=None, b=None, out=None)), 2,
+             None, 0, None) == 0
+
+
+def test_gemm_group_workspace_plan():
+    """The GPT-111M layer's nine products at 2048 tokens: per operand layout
+    the contractions are cut to about the shortest in the layout: forward
+    (768, 768, 3072) -> the down product in four slices; data gradient
+    (2304, 3072, 768) -> three and four slices; weight gradient (2048 x 3) ->
+    none.  A product of more than 1024 tiles and one whose contraction is
+    not a whole number of 64-byte stages run alone (no workspace)."""
+    wsb = L.fp8_scaled_gemm_group_workspace_bytes
+    T = 2048
+    lin = [("qkv", 768, 2304), ("up", 768, 3072), ("down", 3072, 768)]
+    fwd = [_gdesc(0, M=T, N=n, K=k) for _, k, n in lin]
+    dgrad = [_gdesc(1, 1, 0, M=T, N=n, K=k) for _, k, n in lin]
+    wgrad = [_gdesc(2, 1, 0, M=T, N=n, K=k) for _, k, n in lin]
+    arr = lambda ds: (fl.GemmDesc * len(ds))(*ds)
+    r = lambda b: (b + 255) // 256 * 256
+    assert wsb(0, arr(fwd), 3) == r(4 * T * 768 * 4)
+    assert wsb(0, arr(dgrad), 3) == r(3 * T * 768 * 4) + r(4 * T * 768 * 4)
+    assert wsb(0, arr(wgrad), 3) == 0
+    assert wsb(0, arr(fwd + dgrad + wgrad), 9) == r(4 * T * 768 * 4) + r(3 * T * 768 * 4) + r(4 * T * 768 * 4)
+    # alone: 8192 x 8192 (4096 tiles); K = 100
+    assert wsb(0, arr([_gdesc(0, M=8192, N=8192, K=64), _gdesc(0, M=128, N=128, K=64 * 40)]), 2) == 0
+    assert wsb(0, arr([_gdesc(0, M=128, N=128, K=100), _gdesc(0, M=128, N=128, K=64 * 40)]), 2) == 0
+    assert wsb(0, arr([_gdesc(0, M=128, N=128, K=64 * 8), _gdesc(0, M=128, N=128, K=64 * 40)]), 2) == r(5 * 128 * 128 * 4)
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
+def test_gemm_group_without_a_device_reports_no_device():
+    arr = (fl.GemmDesc * 1)(_gdesc())
+    assert L.fp8_scaled_gemm_group(0, arr, 1, None, 0, None) == status("FP8_ERR_DEVICE")

@@ -66,3 +66,40 @@ def test_traffic_record_from_counter_csvs(tmp_path):
     json.dump(rec, open(out, "w"))
     assert bench.traffic_record(rec["workload"], path=out) is None
 
+
+
+def test_parity_of_the_step_against_the_oracle_sample(orc):
+    """bench.parity on workload 1 (full outputs): outputs equal to the
+    oracle's pass; a code, a bias or a product output outside the tolerance
+    is reported.  The 'GPU' side here is the oracle's own results on the host."""
+    import numpy as np
+    import torch
+
+    import synth
+    w = synth.WORKLOADS[1]
+    host = {t.name: synth.workload_tensor(w, t.name) for t in w.tensors}
+    res = {}
+    line = bench.cpu_baseline(w, host, 1 << 31, 1 << 31, results=res)
+    assert line["gemm_extrapolated"] is False
+    q, outs = {}, {}
+    for t in w.tensors:
+        if t.name in res["quant"]:
+            a, b, c = res["quant"][t.name]
+            amax = torch.tensor([a], dtype=torch.int64).to(torch.int32).view(torch.float32)
+            q[t.name] = (torch.from_numpy(np.array(c).reshape(t.shape)), torch.tensor([b], dtype=torch.int32),
+                         amax, t.fmt)
+    for key, (ref, bound) in res["gemm"].items():
+        outs[key] = torch.from_numpy(ref.astype(np.float32))
+    p = bench.parity(None, w, q, outs, res)
+    assert p["quantisation_bit_exact"] and p["gemm_within_tolerance"], p
+    assert p["gemm_outputs_checked"] == 128 * 256 and p["gemm_worst_err_over_sum_ab"] < 1e-6
+    # one output off by twice the tolerance
+    key = next(iter(outs))
+    ref, bound = res["gemm"][key]
+    outs[key][3, 5] = float(ref[3, 5] + 2e-5 * bound[3, 5])
+    assert bench.parity(None, w, q, outs, res)["gemm_within_tolerance"] is False
+    outs[key][3, 5] = float(ref[3, 5])
+    # one code changed
+    name = next(iter(q))
+    q[name][0].view(-1)[7] ^= 1
+    assert bench.parity(None, w, q, outs, res)["quantisation_bit_exact"] is False

@@ -65,3 +65,37 @@ def test_threads_on_separate_streams(fl):
         for r in range(reps):
             for a, b in zip(results[t][r], ref[t]):
                 assert torch.equal(a, b), (t, r)
+
+
+def test_side_stream_without_a_stream_context(fl):
+    """A call given another stream than torch's current one, outside any
+    stream context: its outputs and a split product's workspace are allocated
+    on that stream, so memory the current stream allocates and fills right
+    after the call cannot be the blocks the call is still writing.  Results
+    equal the same calls on the current stream."""
+    import oracle
+    from gpu_util import check_gemm
+
+    x = synth.draw_bf16(810, (128, 8192), "normal", 1.0).cuda()
+    w = synth.draw_bf16(811, (1024, 8192), "normal", 0.02).cuda()
+    x8, bx, _ = fl.quantize(x, fl.E4M3, 0)
+    w8, bw, _ = fl.quantize(w, fl.E4M3, 0)
+    assert fl.gemm_workspace_bytes(fl.OP_FWD, 128, 1024, 8192) > 0      # split: a workspace
+    want = fl.scaled_gemm_auto(fl.OP_FWD, x8, fl.E4M3, bx, w8, fl.E4M3, bw)
+    q_want = fl.quantize(x, fl.E4M3, 0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for rep in range(4):
+        say("side stream", rep)
+        y = fl.scaled_gemm_auto(fl.OP_FWD, x8, fl.E4M3, bx, w8, fl.E4M3, bw, stream=side)
+        codes, bias, amax = fl.quantize(x, fl.E4M3, 0, stream=side)
+        # the current stream allocates and overwrites fresh memory meanwhile
+        junk = [torch.full((1 << 22,), float(rep), device="cuda") for _ in range(8)]
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), want.view(torch.int32)), rep
+        assert torch.equal(codes, q_want[0]) and torch.equal(bias, q_want[1]), rep
+        del junk, y, codes, bias, amax
+    ref, bound = oracle.gemm_fwd(x8.cpu().numpy(), 0, int(bx.item()), w8.cpu().numpy(), 0, int(bw.item()))
+    check_gemm(want.cpu().numpy(), ref, bound, "side-stream product")

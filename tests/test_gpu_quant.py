@@ -421,3 +421,60 @@ def test_quantize_in_one_call(fl, dtype, monkeypatch):
                     assert np.array_equal(got, c_ref), what
                     assert np.array_equal(got, cc.cpu().numpy()), what
                     assert int(words_of(ca)[0]) == a_ref and int(cb.item()) == b_ref, what
+
+
+def test_quantize_multi(fl):
+    """fp8_quantize_multi: 41 tensors in one call (two launch groups of up to
+    32), mixed sizes (empty, ragged tails, above and below one block's
+    reach, up to 1M elements), bf16 and fp32, all three formats, margins,
+    tiny and huge scales, planted NaN / inf: every amax, bias and code
+    bit-identical to the oracle and to fp8_quantize of that tensor alone."""
+    sizes = [0, 1, 7, 15, 16, 17, 255, 1023, 4099, 16389, 65536, 131073, 300001, 1_000_003]
+    scales = [(1.0, None), (1e-37, None), (3e4, "inf"), (0.02, "nan")]
+    fmts = [(E4M3, 0), (E5M2, 1), (E3M4, -2), (E4M3, 64), (E5M2, -3)]
+    cases = []
+    for i in range(41):
+        dtype = "bf16" if i % 3 else "fp32"
+        n = sizes[(i * 5) % len(sizes)]
+        scale, special = scales[i % len(scales)]
+        fmt, margin = fmts[i % len(fmts)]
+        words = _quantize_inputs(dtype, n, scale, special, 900 + i)
+        x = (bf16_dev if dtype == "bf16" else f32_dev)(words)
+        cases.append((dtype, n, scale, special, fmt, margin, words, x))
+    say("quantize_multi", len(cases), "tensors")
+    got = fl.quantize_multi([c[7] for c in cases], [c[4] for c in cases], [c[5] for c in cases])
+    torch.cuda.synchronize()
+    for (dtype, n, scale, special, fmt, margin, words, x), (codes, bias, amax) in zip(cases, got):
+        what = (dtype, n, scale, special, fmt, margin)
+        a_ref, b_ref, c_ref = oracle.quantize(words, fmt, margin)
+        assert int(words_of(amax)[0]) == a_ref, what
+        assert int(bias.item()) == b_ref, what
+        assert np.array_equal(codes.cpu().numpy(), c_ref), what
+        one = fl.quantize(x, fmt, margin)
+        assert torch.equal(one[0], codes) and torch.equal(one[1], bias), what
+        assert torch.equal(one[2].view(torch.int32), amax.view(torch.int32)), what
+    # into preallocated outputs, a second time over the same buffers
+    outs = [(torch.full((c[1],), 0xAB, dtype=torch.uint8, device="cuda"),
+             torch.full((1,), 77, dtype=torch.int32, device="cuda"),
+             torch.full((1,), 5.0, dtype=torch.float32, device="cuda")) for c in cases]
+    for _ in range(2):
+        fl.quantize_multi([c[7] for c in cases], [c[4] for c in cases], [c[5] for c in cases], outs=outs)
+    torch.cuda.synchronize()
+    for (codes, bias, amax), (c2, b2, a2) in zip(got, outs):
+        assert torch.equal(codes, c2) and torch.equal(bias, b2)
+        assert torch.equal(amax.view(torch.int32), a2.view(torch.int32))
+
+
+def test_quantize_multi_of_a_workload_step(fl):
+    """The nine tensors quantised in the GPT-111M layer's step (X, W, dY of
+    three linears) in one call, against the oracle."""
+    w = synth.WORKLOADS[2]
+    names = [t.name for t in w.tensors if t.timed]
+    xs = [synth.workload_tensor(w, n).cuda() for n in names]
+    say("quantize_multi workload 2", names)
+    got = fl.quantize_multi(xs, [w.tensor(n).fmt for n in names], [w.tensor(n).margin for n in names])
+    for n, x, (codes, bias, amax) in zip(names, xs, got):
+        a_ref, b_ref, c_ref = oracle.quantize(synth.bf16_words(synth.workload_tensor(w, n)),
+                                              w.tensor(n).fmt, w.tensor(n).margin)
+        assert int(words_of(amax)[0]) == a_ref and int(bias.item()) == b_ref, n
+        assert np.array_equal(codes.cpu().numpy().reshape(-1), np.asarray(c_ref).reshape(-1)), n

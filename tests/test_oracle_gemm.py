@@ -176,3 +176,37 @@ def test_sampled_outputs_equal_full_outputs(orc, which):
     out, bd = at(a8, E5M2, 7, b8, E4M3, -2, rows, cols)
     assert np.array_equal(out, full[rows, cols])
     assert np.array_equal(bd, fbd[rows, cols])
+
+
+# (X8 row in E5M2, W8 row in E4M3) -> the expected output and its bound under
+# the IEEE reading of special codes: a NaN term, inf * 0 or inf - inf gives
+# NaN; otherwise an infinite term gives that infinity (E5M2 0x7C = +inf,
+# 0xFC = -inf, 0x3C = 1; E4M3 0x38 = 1, 0xB8 = -1, 0x7F = NaN)
+SPECIAL_CASES = [
+    ([0x7C, 0x3C], [0x38, 0x38], np.inf, np.inf),
+    ([0xFC, 0x3C], [0x38, 0x38], -np.inf, np.inf),
+    ([0x7C, 0x3C], [0xB8, 0x38], -np.inf, np.inf),
+    ([0x7C, 0xFC], [0x38, 0x38], np.nan, np.inf),      # inf - inf; the magnitudes still add
+    ([0x7C, 0x3C], [0x00, 0x38], np.nan, np.nan),      # inf * 0
+    ([0x7F, 0x3C], [0x38, 0x38], np.nan, np.nan),      # an E5M2 NaN code
+    ([0x3C, 0x3C], [0x7F, 0x38], np.nan, np.nan),      # an E4M3 NaN code
+    ([0x3C, 0x3C], [0xFF, 0x00], np.nan, np.nan),      # -NaN
+]
+
+
+@pytest.mark.parametrize("x,w,want,want_bound", SPECIAL_CASES)
+def test_special_codes_follow_ieee_arithmetic(orc, x, w, want, want_bound):
+    x8 = np.array([x], dtype=np.uint8)
+    w8 = np.array([w], dtype=np.uint8)
+    for bias in (0, 5, -7):
+        y, bound = orc.gemm_fwd(x8, E5M2, bias, w8, E4M3, 0)
+        for got, exp in ((y[0, 0], want), (bound[0, 0], want_bound)):
+            if np.isnan(exp):
+                assert np.isnan(got)
+            else:
+                assert got == exp
+        # the same terms through the two gradient layouts
+        dx, _ = orc.gemm_dgrad(x8, E5M2, bias, w8.T.copy(), E4M3, 0)
+        dw, _ = orc.gemm_wgrad(x8.T.copy(), E5M2, bias, w8.T.copy(), E4M3, 0)
+        for got in (dx[0, 0], dw[0, 0]):
+            assert (np.isnan(got) and np.isnan(want)) or got == want
