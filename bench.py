@@ -61,10 +61,21 @@ def parse():
                     help="products never split along the contraction (no workspace)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the step captured as a HIP graph and replayed")
-    ap.add_argument("--quant", choices=["one-call", "three-calls"], default="one-call",
-                    help="how the timed steps quantise each activation: fp8_quantize, or "
-                         "fp8_amax -> fp8_compute_bias -> fp8_scale_cast (the steps with per-kernel "
-                         "events always make the three calls, to time each kernel)")
+    ap.add_argument("--quant", choices=["multi", "one-call", "three-calls"], default="multi",
+                    help="how the timed steps quantise the in-step tensors: all in one fp8_quantize_multi "
+                         "call, fp8_quantize per tensor, or fp8_amax -> fp8_compute_bias -> fp8_scale_cast "
+                         "per tensor (the steps with per-kernel events always make the three calls, to "
+                         "time each kernel)")
+    ap.add_argument("--gemm", choices=["grouped", "single"], default="grouped",
+                    help="how the timed steps run the products: one fp8_scaled_gemm_group call, or "
+                         "fp8_scaled_gemm (fp8_scaled_gemm_ws when split) per product (the steps with "
+                         "per-kernel events always run them one by one)")
+    ap.add_argument("--per-config", default="1,2,3,4,6",
+                    help="other workloads measured in the same run (shorter: no graph, epilogue, "
+                         "delayed or one-call extras; parity on an oracle sample)")
+    ap.add_argument("--no-per-config", action="store_true")
+    ap.add_argument("--no-native", action="store_true",
+                    help="skip the same step on the native FP8 MFMA arithmetic")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy twice (HBM counter calibration)")
     ap.add_argument("--record-traffic", metavar="DIR",
@@ -319,7 +330,7 @@ def one_call_quant(fl, w, plan, q, x, reps=9):
             "three_calls_us": round(chain_sum, 2), "one_call_us": round(one_sum, 2), "per_tensor": per}
 
 
-def cold_quant(fl, w, plan, q, x, reps):
+def cold_quant(fl, w, plan, q, x, reps, e3m4=True):
     """amax (with its clear) and cast of every in-step quantised tensor, each
     timed alone after flushing the Infinity Cache (outside the timing); median
     over `reps`, HIP events on the launch stream.  Two flushes:
@@ -374,7 +385,7 @@ def cold_quant(fl, w, plan, q, x, reps):
         for k, t in (("amax_ms", ta), ("cast_ms", tc), ("dirty_amax_ms", tad), ("dirty_cast_ms", tcd)):
             tot[k] = tot.get(k, 0.0) + t
         tot["elems"] += elems
-        if fmt == fl.E4M3:
+        if fmt == fl.E4M3 and e3m4:
             b3 = fl.compute_bias(amax, fl.E3M4, w.tensor(n).margin)
             c3 = torch.empty_like(codes)
             t3 = timed(lambda: fl.scale_cast(x[n], b3, fl.E3M4, out=c3))
@@ -472,17 +483,22 @@ def record_traffic(d, out=None):
     print(json.dumps(rec), flush=True)
 
 
-def cpu_baseline(w, host, rows, cols):
+def cpu_baseline(w, host, rows, cols, results=None):
     """The oracle, as it stands, beside the GPU: amax + bias + cast of every
     quantised-in-step tensor at full size (the oracle's scalar loops, one
     thread), and a rows x cols block of every product (OpenMP over rows),
-    extrapolated to the full product by its sampled fraction of the flops."""
+    extrapolated to the full product by its sampled fraction of the flops.
+    results (a dict, optional) receives what the oracle computed, for
+    parity(): "quant" name -> (amax bits, bias, codes), "gemm" (linear,
+    pass) -> (output block, bound block)."""
     import numpy as np
     import oracle
     import synth
 
     plan = plan_of(w)
     codes, biases = {}, {}
+    if results is not None:
+        results.update(quant={}, gemm={})
     # static operands: quantised offline (untimed), like the GPU leg; only the
     # sampled rows are cast, with the bias of the whole tensor
     t_quant = t_gemm = 0.0
@@ -498,6 +514,8 @@ def cpu_baseline(w, host, rows, cols):
             b = oracle.compute_bias(a, t.fmt, t.margin)
             c = oracle.scale_cast(words, b, t.fmt)
             t_quant += time.perf_counter() - t0
+            if results is not None:
+                results["quant"][t.name] = (a, b, c)
             # the products below need every row their sample touches
             codes[t.name] = c
             biases[t.name] = b
@@ -528,10 +546,12 @@ def cpu_baseline(w, host, rows, cols):
             b8 = oracle.scale_cast(np.ascontiguousarray(wb[:, :c]), biases[bn], tb.fmt)
             fn = oracle.gemm_wgrad
         t0 = time.perf_counter()
-        fn(a8, ta.fmt, biases[an], b8, tb.fmt, biases[bn])
+        ref, bound = fn(a8, ta.fmt, biases[an], b8, tb.fmt, biases[bn])
         t_gemm += time.perf_counter() - t0
         contraction = {"fwd": l.K, "dgrad": l.N, "wgrad": l.M}[which]
         flops_sample += 2 * r * c * contraction
+        if results is not None:
+            results["gemm"][(l.name, which)] = (ref, bound)
     step_flops = w.flops()
     # extrapolate each part by its own sampled fraction
     t_step = t_quant * (step_quant_elems / max(sampled_quant_elems, 1)) + t_gemm * (step_flops / flops_sample)
@@ -605,14 +625,16 @@ def cpu_baseline_mlp(m, host, tokens):
             "host_affinity": len(os.sched_getaffinity(0))}
 
 
-def bench_mlp(args, m):
+def measure_mlp(args, m, light=False):
     """The chained FP8 MLP: x [T, d] bf16, fp32 master weights w1 [2F, d] and
     w2 [d, F], upstream gradient g [T, d] (the synthetic loss L = sum(y * g)).
     One step = FP8MLPFunction forward + backward through autograd; every
     product, quantisation and SwiGLU runs in libfp8lin (dx is computed and
     handed to autograd, which drops it: x is a leaf that needs no gradient).
     Weights are re-quantised every step, as training does.  No optimizer step
-    in the timed region (the weight update is not part of the layer)."""
+    in the timed region (the weight update is not part of the layer).
+    Returns the bench line; light: only the step and per-kernel figures (no
+    graph replay, bias history or CPU baseline)."""
     import torch
 
     import fp8_precision_linear_amd as fl
@@ -650,6 +672,24 @@ def bench_mlp(args, m):
         step()
     torch.cuda.synchronize()
     events, cfg.events = cfg.events, None
+    if light:
+        gc.enable()
+        by = {}
+        for kind, name, e0, e1 in events:
+            by[(kind, name)] = by.get((kind, name), 0.0) + e0.elapsed_time(e1) / args.steps
+        gemm_ms = sum(v for (k, _), v in by.items() if k == "gemm")
+        gemm_tflops = m.flops() / (gemm_ms * 1e-3) / 1e12
+        out = {"workload": m.name, "step_ms": round(ms_per_step, 4),
+               "step_tflops": round(m.flops() / (ms_per_step * 1e-3) / 1e12, 2),
+               "gemm_tflops": round(gemm_tflops, 2),
+               "gemm_frac_of_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+               "gemm_frac_of_mfma_used_peak": round(gemm_tflops / mfma_used_peak(args.math), 4),
+               "step_breakdown_ms": {k: round(sum(v for (kk, _), v in by.items() if kk == k), 4)
+                                     for k in ("gemm", "quant", "swiglu")},
+               "parity": "every stage against the oracle in tests/test_gpu_mlp.py (not repeated here)"}
+        del x, w1, w2, g, host
+        torch.cuda.empty_cache()
+        return out
     # the same step captured once into a HIP graph and replayed K times (no
     # host-side launch or autograd work per step); fresh leaf weights, so that
     # their gradient nodes are made on the warm-up stream, not the default one
@@ -739,9 +779,10 @@ def bench_mlp(args, m):
                    "input_sha256": {n: synth.sha256(host[n]) for n in m.ORDER},
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "kernel": "the six products (gemm_pp_kernel)",
-                     "achieved": round(gemm_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / peak, 4),
-                     "frac_of_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "mfma_used_peak": peak,
+                     "frac_of_mfma_used_peak": round(gemm_tflops / peak, 4),
                      "traffic": None,
                      "per_product_us": {n: round(by[("gemm", n)] * 1e3, 1) for n in gemm_flops}},
         "swiglu": {n: {"us": round(by[("swiglu", n)] * 1e3, 1),
@@ -763,73 +804,133 @@ def bench_mlp(args, m):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_mlp(m, host, args.cpu_tokens)
         line["cpu_baseline"]["vs_gpu"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
-    print(json.dumps(line), flush=True)
+    return line
 
 
-def main():
-    args = parse()
-    if args.record_traffic:
-        record_traffic(args.record_traffic)
-        return
-    if args.gpus != 1:
-        print(json.dumps({"error": "the library runs on one GPU (no multi-GPU path); --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
+def parity(fl, w, q, outs, results):
+    """The GPU step's outputs against what cpu_baseline's oracle computed on
+    the same inputs: codes, amax and bias of every in-step quantisation bit
+    for bit, and the sampled output block of every product within
+    1e-5 * 2^-(ba+bb) * sum |a||b| elementwise.  Reports the worst
+    err / (2^-(ba+bb) * sum |a||b|) over the checked outputs."""
+    import numpy as np
     import torch
 
-    import fp8_precision_linear_amd as fl
-    import synth
+    quant_ok, checked = True, 0
+    for n, (a_bits, b, codes) in results["quant"].items():
+        g_codes, g_bias, g_amax, _ = q[n]
+        quant_ok &= (int(g_amax.view(torch.int32).item()) & 0xFFFFFFFF) == a_bits
+        quant_ok &= int(g_bias.item()) == b
+        quant_ok &= bool(np.array_equal(g_codes.cpu().numpy().reshape(-1), np.asarray(codes).reshape(-1)))
+    worst, within = 0.0, True
+    for key, (ref, bound) in results["gemm"].items():
+        r, c = ref.shape
+        got = outs[key][:r, :c].cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)
+        within &= bool(np.all(err <= 1e-5 * bound))
+        ratio = np.where(bound > 0, err / np.where(bound > 0, bound, 1.0), np.where(err > 0, np.inf, 0.0))
+        worst = max(worst, float(ratio.max()) if ratio.size else 0.0)
+        checked += ref.size
+    return {"quantisation_bit_exact": bool(quant_ok),
+            "quantised_tensors": sorted(results["quant"]),
+            "gemm_within_tolerance": within, "gemm_worst_err_over_sum_ab": worst,
+            "gemm_tolerance": 1e-5, "gemm_outputs_checked": checked,
+            "method": "the last timed step's outputs against the oracle's (cpu_baseline's sample): "
+                      "codes, amax and bias bit for bit; the product blocks elementwise"}
 
-    if args.workload in synth.CHAINED_MLPS:
-        bench_mlp(args, synth.CHAINED_MLPS[args.workload])
-        return
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    w = synth.WORKLOADS[args.workload]
-    plan = plan_of(w)
 
-    host = {t.name: synth.workload_tensor(w, t.name) for t in w.tensors}
-    x = {n: v.to(dev) for n, v in host.items()}
-    q = {}   # name -> (codes, bias, amax, fmt)
-    for t in w.tensors:
-        codes = torch.empty(t.shape, dtype=torch.uint8, device=dev)
-        bias = torch.empty(1, dtype=torch.int32, device=dev)
-        amax = torch.empty(1, dtype=torch.float32, device=dev)
-        q[t.name] = (codes, bias, amax, t.fmt)
-        if not t.timed:   # static weights: quantised once, outside the timed step
-            fl.amax(x[t.name], out=amax)
-            fl.compute_bias(amax, t.fmt, t.margin, out=bias)
-            fl.scale_cast(x[t.name], bias, t.fmt, out=codes)
-    outs = {}
-    for item in plan:
-        if item[0] == "gemm":
-            _, l, which = item
-            outs[(l.name, which)] = torch.empty(gemm_operands(l, which)[2], dtype=torch.float32, device=dev)
-    math = fl.MATH_EXACT if args.math == "exact" else fl.MATH_NATIVE_FP8
-    op_of = {"fwd": fl.OP_FWD, "dgrad": fl.OP_DGRAD, "wgrad": fl.OP_WGRAD}
-    # products whose outputs have too few tiles to fill the chip run split
-    # along the contraction in a workspace allocated here, once (the library
-    # allocates nothing); None where a product is not split
-    ws_of, ws = {}, None
-    if not args.no_split:
-        for item in plan:
+class Bench:
+    """One workload set up on the GPU: its synthetic inputs (host and device),
+    static weights quantised once, the step's output and workspace buffers,
+    and the step itself (one pass of every in-step quantisation and every
+    product, on torch's current stream)."""
+
+    def __init__(self, fl, w, args):
+        import torch
+        import synth
+
+        self.fl, self.w, self.args = fl, w, args
+        dev = torch.device("cuda:0")
+        self.plan = plan_of(w)
+        self.host = {t.name: synth.workload_tensor(w, t.name) for t in w.tensors}
+        self.x = {n: v.to(dev) for n, v in self.host.items()}
+        self.q = {}   # name -> (codes, bias, amax, fmt)
+        for t in w.tensors:
+            codes = torch.empty(t.shape, dtype=torch.uint8, device=dev)
+            bias = torch.empty(1, dtype=torch.int32, device=dev)
+            amax = torch.empty(1, dtype=torch.float32, device=dev)
+            self.q[t.name] = (codes, bias, amax, t.fmt)
+            if not t.timed:   # static weights: quantised once, outside the timed step
+                fl.amax(self.x[t.name], out=amax)
+                fl.compute_bias(amax, t.fmt, t.margin, out=bias)
+                fl.scale_cast(self.x[t.name], bias, t.fmt, out=codes)
+        self.outs = {}
+        for item in self.plan:
             if item[0] == "gemm":
                 _, l, which = item
-                ws_of[(l.name, which)] = fl.gemm_workspace_bytes(op_of[which], l.M, l.N, l.K)
-        need = max(ws_of.values(), default=0)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
-    split_products = [f"{k[0]}:{k[1]}" for k, v in ws_of.items() if v > 0]
+                self.outs[(l.name, which)] = torch.empty(gemm_operands(l, which)[2], dtype=torch.float32,
+                                                         device=dev)
+        self.math = fl.MATH_EXACT if args.math == "exact" else fl.MATH_NATIVE_FP8
+        self.op_of = {"fwd": fl.OP_FWD, "dgrad": fl.OP_DGRAD, "wgrad": fl.OP_WGRAD}
+        # products whose outputs have too few tiles to fill the chip run split
+        # along the contraction in a workspace allocated here, once (the
+        # library allocates nothing)
+        self.ws_of, self.ws = {}, None
+        if not args.no_split:
+            for item in self.plan:
+                if item[0] == "gemm":
+                    _, l, which = item
+                    self.ws_of[(l.name, which)] = fl.gemm_workspace_bytes(self.op_of[which], l.M, l.N, l.K)
+            need = max(self.ws_of.values(), default=0)
+            self.ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+        self.split_products = [f"{k[0]}:{k[1]}" for k, v in self.ws_of.items() if v > 0]
+        # the step's in-step quantisations as one call, and its products as one
+        # grouped call, prepared once (descriptors and workspace)
+        self.quant_names = [i[1] for i in self.plan if i[0] == "quant"]
+        self.group = None
+        if args.gemm == "grouped":
+            prods, outs = [], []
+            for item in self.plan:
+                if item[0] == "gemm":
+                    _, l, which = item
+                    an, bn, _ = gemm_operands(l, which)
+                    a8, ba, _, fa = self.q[an]
+                    b8, bb, _, fb = self.q[bn]
+                    prods.append((self.op_of[which], a8, fa, ba, b8, fb, bb))
+                    outs.append(self.outs[(l.name, which)])
+            self.group_math = self.math
+            self.group = fl.GemmGroup(prods, outs=outs, math=self.math)
 
-    def step(ev=None):
-        for item in plan:
+    def step(self, ev=None):
+        import torch
+        fl, w, q, x = self.fl, self.w, self.q, self.x
+        if ev is None and self.args.quant == "multi" and self.quant_names:
+            names = self.quant_names
+            fl.quantize_multi([x[n] for n in names], [q[n][3] for n in names], [w.tensor(n).margin for n in names],
+                              outs=[q[n][:3] for n in names])
+        if ev is None and self.group is not None:
+            if self.args.quant != "multi":
+                for n in self.quant_names:
+                    codes, bias, amax, fmt = q[n]
+                    if self.args.quant == "one-call":
+                        fl.quantize(x[n], fmt, w.tensor(n).margin, out=codes, bias=bias, amax=amax)
+                    else:
+                        fl.amax(x[n], out=amax)
+                        fl.compute_bias(amax, fmt, w.tensor(n).margin, out=bias)
+                        fl.scale_cast(x[n], bias, fmt, out=codes)
+            if self.group_math != self.math:   # the arithmetic was switched after set-up
+                self.group.math = self.math
+                self.group_math = self.math
+            self.group.run()
+            return
+        for item in self.plan:
             if item[0] == "quant":
                 n = item[1]
                 codes, bias, amax, fmt = q[n]
                 t = w.tensor(n)
-                if ev is None and args.quant == "one-call":
+                if ev is None and self.args.quant == "multi":
+                    continue                  # quantised above, all in one call
+                if ev is None and self.args.quant == "one-call":
                     fl.quantize(x[n], fmt, t.margin, out=codes, bias=bias, amax=amax)
                     continue
                 if ev is not None:
@@ -855,93 +956,181 @@ def main():
                 if ev is not None:
                     ev.append(("gemm_start", (l.name, which), torch.cuda.Event(enable_timing=True)))
                     ev[-1][2].record()
-                fl.scaled_gemm(op_of[which], a8, fa, ba, b8, fb, bb, math=math, out=outs[(l.name, which)],
-                               workspace=ws if ws_of.get((l.name, which), 0) > 0 else None)
+                fl.scaled_gemm(self.op_of[which], a8, fa, ba, b8, fb, bb, math=self.math,
+                               out=self.outs[(l.name, which)],
+                               workspace=self.ws if self.ws_of.get((l.name, which), 0) > 0 else None)
                 if ev is not None:
                     ev.append(("gemm_end", (l.name, which), torch.cuda.Event(enable_timing=True)))
                     ev[-1][2].record()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def measure(self, steps, warmup):
+        """K timed steps (wall clock, synchronised on both sides, no events and
+        no Python garbage collection inside), then K more steps with HIP
+        events around every launch (on the launch stream) for per-kernel
+        durations.  Returns the step and per-kernel figures."""
+        import statistics
 
-    # timed region: K steps, wall clock, synchronised on both sides; no
-    # per-kernel events and no Python garbage collection inside it
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        gc.collect()
+        gc.disable()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+        ev, step_ev = [], []
+        for _ in range(steps):
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            self.step(ev)
+            s1.record()
+            step_ev.append((s0, s1))
+        torch.cuda.synchronize()
+        gc.enable()
+        r = {"ms_per_step": ms_per_step,
+             "step_median_ms": statistics.median(a.elapsed_time(b) for a, b in step_ev),
+             "gemm_ms": 0.0, "amax_ms": 0.0, "bias_ms": 0.0, "cast_ms": 0.0,
+             "cast_by": {}, "amax_by": {}, "steps": steps}
+        last = {}
+        for kind, key, e in ev:
+            if kind == "quant_start":
+                last["q"] = e
+            elif kind == "amax_end":
+                t = last["q"].elapsed_time(e)
+                r["amax_ms"] += t
+                r["amax_by"][key] = r["amax_by"].get(key, 0.0) + t
+                last["a"] = e
+            elif kind == "bias_end":
+                r["bias_ms"] += last["a"].elapsed_time(e)
+                last["b"] = e
+            elif kind == "cast_end":
+                t = last["b"].elapsed_time(e)
+                r["cast_ms"] += t
+                r["cast_by"][key] = r["cast_by"].get(key, 0.0) + t
+            elif kind == "gemm_start":
+                last["g"] = e
+            elif kind == "gemm_end":
+                r["gemm_ms"] += last["g"].elapsed_time(e)
+        K = steps
+        w = self.w
+        r["step_flops"] = w.flops()
+        r["gemm_launches"] = sum(1 for i in self.plan if i[0] == "gemm")
+        r["quant_elems"] = sum(self.x[i[1]].numel() for i in self.plan if i[0] == "quant")
+        r["step_tflops"] = r["step_flops"] / (ms_per_step * 1e-3) / 1e12
+        r["gemm_tflops"] = r["step_flops"] * K / (r["gemm_ms"] * 1e-3) / 1e12
+        r["cast_gbs"] = 3.0 * r["quant_elems"] * K / (r["cast_ms"] * 1e-3) / 1e9 if r["cast_ms"] > 0 else None
+        r["amax_gbs"] = 2.0 * r["quant_elems"] * K / (r["amax_ms"] * 1e-3) / 1e9 if r["amax_ms"] > 0 else None
+        return r
+
+
+# the peak of the MFMA each arithmetic runs its contraction on: the exact
+# arithmetic the 16-bit MFMA (FP8 widened exactly), the native one the FP8 MFMA
+def mfma_used_peak(math):
+    return PEAK_F16_TFLOPS if math == "exact" else PEAK_FP8_TFLOPS
+
+
+def per_config_line(fl, wl, args):
+    """A shorter measurement of another workload in the same run: its step
+    (wall clock), GEMM TFLOP/s (events) as a fraction of the dense FP8 peak
+    and of the peak of the MFMA the arithmetic uses, amax / cast GB/s in the
+    step and cold, and parity of the last timed step against the oracle
+    (every output of workloads of at most 200 GFLOP a step, else a 64 x 1024
+    block of every product)."""
+    import torch
+    import synth
+
+    if wl in synth.CHAINED_MLPS:
+        return measure_mlp(args, synth.CHAINED_MLPS[wl], light=True)
+    w = synth.WORKLOADS[wl]
+    b = Bench(fl, w, args)
+    r = b.measure(args.steps, args.warmup)
+    cold = None if args.no_cold else cold_quant(fl, w, b.plan, b.q, b.x, 3, e3m4=False)
+    res = {}
+    full = w.flops() <= 2e11
+    cpu = cpu_baseline(w, b.host, 1 << 31 if full else 64, 1 << 31 if full else 1024, results=res)
+    out = {
+        "workload": w.name,
+        "step_ms": round(r["ms_per_step"], 4),
+        "step_ms_events_median": round(r["step_median_ms"], 4),
+        "step_tflops": round(r["step_tflops"], 2),
+        "gemm_tflops": round(r["gemm_tflops"], 2),
+        "gemm_frac_of_fp8_peak": round(r["gemm_tflops"] / PEAK_FP8_TFLOPS, 4),
+        "gemm_frac_of_mfma_used_peak": round(r["gemm_tflops"] / mfma_used_peak(args.math), 4),
+        "gemm_avg_launch_us": round(r["gemm_ms"] * 1e3 / (r["steps"] * r["gemm_launches"]), 2),
+        "cast_gbs_in_step": round(r["cast_gbs"], 1) if r["cast_gbs"] else None,
+        "amax_gbs_in_step": round(r["amax_gbs"], 1) if r["amax_gbs"] else None,
+        "cold_cast_gbs": cold["cast_gbs"] if cold else None,
+        "cold_amax_gbs": cold["amax_gbs"] if cold else None,
+        "split_along_contraction": b.split_products,
+        "parity": parity(fl, w, b.q, b.outs, res),
+        "oracle_tflops": round(cpu["value"], 4),
+    }
+    if not args.no_native and args.math == "exact":
+        b.math = fl.MATH_NATIVE_FP8
+        rn = b.measure(args.steps, args.warmup)
+        out["native_fp8"] = {"step_tflops": round(rn["step_tflops"], 2),
+                             "gemm_tflops": round(rn["gemm_tflops"], 2),
+                             "gemm_frac_of_fp8_peak": round(rn["gemm_tflops"] / PEAK_FP8_TFLOPS, 4),
+                             "parity": parity(fl, w, b.q, b.outs, res)}
+    del b
     gc.collect()
-    gc.disable()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    torch.cuda.empty_cache()
+    return out
 
-    # per-kernel durations: K more steps with HIP events around every launch
-    # (and around each step, for the per-step median)
-    ev, step_ev = [], []
-    for _ in range(args.steps):
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s0.record()
-        step(ev)
-        s1.record()
-        step_ev.append((s0, s1))
-    torch.cuda.synchronize()
-    gc.enable()
-    import statistics
-    step_median_ms = statistics.median(a.elapsed_time(b) for a, b in step_ev)
 
-    graph_info = None if args.no_graph else graph_replay(step, q, outs, args.steps)
+def main():
+    args = parse()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
+    if args.gpus != 1:
+        print(json.dumps({"error": "the library runs on one GPU (no multi-GPU path); --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import torch
+
+    import fp8_precision_linear_amd as fl
+    import synth
+
+    if args.workload in synth.CHAINED_MLPS:
+        print(json.dumps(measure_mlp(args, synth.CHAINED_MLPS[args.workload])), flush=True)
+        return
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload]
+    b = Bench(fl, w, args)
+    plan, q, x, outs, host = b.plan, b.q, b.x, b.outs, b.host
+    r = b.measure(args.steps, args.warmup)
+    K = args.steps
+    gemm_ms, amax_ms, bias_ms, cast_ms = r["gemm_ms"], r["amax_ms"], r["bias_ms"], r["cast_ms"]
+    step_flops, gemm_tflops, quant_elems = r["step_flops"], r["gemm_tflops"], r["quant_elems"]
+    cast_gbs, amax_gbs = r["cast_gbs"], r["amax_gbs"]
+
+    graph_info = None if args.no_graph else graph_replay(b.step, q, outs, args.steps)
     cold = None if args.no_cold else cold_quant(fl, w, plan, q, x, args.cold_reps)
-    epi = None if args.no_epilogue_amax else epilogue_amax(fl, w, plan, q, outs, math, op_of)
+    epi = None if args.no_epilogue_amax else epilogue_amax(fl, w, plan, q, outs, b.math, b.op_of)
     delayed = None if args.no_delayed else delayed_quant(fl, w, plan, q, x)
     one_call = None if args.no_delayed else one_call_quant(fl, w, plan, q, x)
 
-    # per-kernel durations from the events (same stream as the launches)
-    gemm_ms = amax_ms = bias_ms = cast_ms = 0.0
-    cast_by, amax_by = {}, {}
-    last = {}
-    for kind, key, e in ev:
-        if kind == "quant_start":
-            last["q"] = e
-        elif kind == "amax_end":
-            t = last["q"].elapsed_time(e)
-            amax_ms += t
-            amax_by[key] = amax_by.get(key, 0.0) + t
-            last["a"] = e
-        elif kind == "bias_end":
-            bias_ms += last["a"].elapsed_time(e)
-            last["b"] = e
-        elif kind == "cast_end":
-            t = last["b"].elapsed_time(e)
-            cast_ms += t
-            cast_by[key] = cast_by.get(key, 0.0) + t
-        elif kind == "gemm_start":
-            last["g"] = e
-        elif kind == "gemm_end":
-            gemm_ms += last["g"].elapsed_time(e)
-    K = args.steps
-    step_flops = w.flops()
-    gemm_launches = sum(1 for i in plan if i[0] == "gemm")
-    quant_elems = sum(int(torch.tensor(w.tensor(i[1]).shape).prod()) for i in plan if i[0] == "quant")
-    gemm_tflops = step_flops * K / (gemm_ms * 1e-3) / 1e12
-    cast_gbs = 3.0 * quant_elems * K / (cast_ms * 1e-3) / 1e9 if cast_ms > 0 else None
-    amax_gbs = 2.0 * quant_elems * K / (amax_ms * 1e-3) / 1e9 if amax_ms > 0 else None
-
     rec = traffic_record(w.name)
     traffic = rec["bytes_per_launch"] if rec else None
-    # the exact arithmetic runs its contraction on the fp16 MFMA: that is its peak
-    peak = PEAK_F16_TFLOPS if args.math == "exact" else PEAK_FP8_TFLOPS
+    n_quant = len([i for i in plan if i[0] == "quant"])
 
     line = {
         "metric": "FP8-AMAX scaled GEMM TFLOP/s incl. amax+cast; cast GB/s vs HBM peak",
-        "value": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "value": round(r["step_tflops"], 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "ms_per_step_events_median": round(step_median_ms, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "ms_per_step_events_median": round(r["step_median_ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -955,36 +1144,44 @@ def main():
             "accumulate": "f32",
             "input_sha256": {t.name: synth.sha256(host[t.name]) for t in w.tensors},
             "math": args.math,
-            "split_along_contraction": split_products,
-            "quantisation": ("fp8_quantize per activation (one call: one workgroup up to 256 KiB, "
-                             "else clear, amax and a cast deriving the bias)" if args.quant == "one-call"
-                             else "fp8_amax -> fp8_compute_bias -> fp8_scale_cast per activation"),
+            "split_along_contraction": b.split_products,
+            "quantisation": {"multi": "fp8_quantize_multi: every in-step tensor in one call (clear, amax "
+                                      "and cast launches for all of them)",
+                             "one-call": "fp8_quantize per tensor (one workgroup up to 256 KiB, else clear, "
+                                         "amax and a cast deriving the bias)",
+                             "three-calls": "fp8_amax -> fp8_compute_bias -> fp8_scale_cast per tensor"}[args.quant],
+            "product_calls": ("fp8_scaled_gemm_group: every product in one call (a launch per operand layout "
+                         "and format pair; products of more than 1024 tiles alone)" if args.gemm == "grouped"
+                         else "fp8_scaled_gemm per product (fp8_scaled_gemm_ws when split)"),
+            "products_grouped_ws_bytes": b.group.ws_bytes if b.group is not None else None,
             "parallelism": "single-gpu",
         },
+        # the GEMM's bound is the dense FP8 MFMA peak (its operands are FP8);
+        # the exact arithmetic issues the 16-bit MFMA, whose peak is half of it
         "roofline": {
             "bound": "mfma",
             "kernel": ("gemm_pp_kernel (256x256 tiles, ping-pong waves), exact math: FP8 codes "
                        "widened to fp16, 32x32x16 fp16 MFMA" if args.math == "exact" else
                        "gemm_pp_kernel (256x256 tiles, ping-pong waves), native 32x32x64 FP8 MFMA"),
             "achieved": round(gemm_tflops, 2),
-            "peak": peak,
+            "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / peak, 4),
-            "frac_of_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
             "traffic": traffic,
-            "avg_launch_us": round(gemm_ms * 1e3 / (K * gemm_launches), 2),
-            "flops_per_launch_avg": step_flops / gemm_launches,
+            "mfma_used_peak": mfma_used_peak(args.math),
+            "frac_of_mfma_used_peak": round(gemm_tflops / mfma_used_peak(args.math), 4),
+            "avg_launch_us": round(gemm_ms * 1e3 / (K * r["gemm_launches"]), 2),
+            "flops_per_launch_avg": step_flops / r["gemm_launches"],
         },
         "cast": {
             "bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
             "achieved": round(cast_gbs, 1) if cast_gbs else None,
             "frac": round(cast_gbs / PEAK_HBM_GBS, 4) if cast_gbs else None,
             "bytes_per_element": 3,
-            "avg_launch_us": round(cast_ms * 1e3 / max(K * len([i for i in plan if i[0] == 'quant']), 1), 2),
-            "per_tensor": {n: {"elements": int(torch.tensor(w.tensor(n).shape).prod()),
-                               "us": round(t * 1e3 / K, 2),
-                               "gbs": round(3.0 * int(torch.tensor(w.tensor(n).shape).prod()) / (t * 1e-3 / K) / 1e9, 1)}
-                           for n, t in cast_by.items()},
+            "avg_launch_us": round(cast_ms * 1e3 / max(K * n_quant, 1), 2),
+            "per_tensor": {n: {"elements": x[n].numel(), "us": round(t * 1e3 / K, 2),
+                               "gbs": round(3.0 * x[n].numel() / (t * 1e-3 / K) / 1e9, 1)}
+                           for n, t in r["cast_by"].items()},
         },
         "amax": {
             "bound": "hbm", "unit": "GB/s", "peak": PEAK_HBM_GBS,
@@ -992,8 +1189,8 @@ def main():
             "frac": round(amax_gbs / PEAK_HBM_GBS, 4) if amax_gbs else None,
             "bytes_per_element": 2,
             "per_tensor": {n: {"us": round(t * 1e3 / K, 2),
-                               "gbs": round(2.0 * int(torch.tensor(w.tensor(n).shape).prod()) / (t * 1e-3 / K) / 1e9, 1)}
-                           for n, t in amax_by.items()},
+                               "gbs": round(2.0 * x[n].numel() / (t * 1e-3 / K) / 1e9, 1)}
+                           for n, t in r["amax_by"].items()},
         },
         # the whole in-step quantisation: amax reads x, the cast reads it again
         # and writes the codes (5 bytes per bf16 element), clear and bias
@@ -1015,12 +1212,36 @@ def main():
         "step_breakdown_ms": {"gemm": round(gemm_ms / K, 4), "amax": round(amax_ms / K, 4),
                               "bias": round(bias_ms / K, 4), "cast": round(cast_ms / K, 4)},
     }
+    res = None
     if not args.no_cpu_baseline:
         # small workloads (at most 200 GFLOP a step): the products' full outputs
         full = w.flops() <= 2e11
+        res = {}
         line["cpu_baseline"] = cpu_baseline(w, host, 1 << 31 if full else args.cpu_rows,
-                                            1 << 31 if full else args.cpu_cols)
+                                            1 << 31 if full else args.cpu_cols, results=res)
         line["cpu_baseline"]["vs_gpu"] = round(line["value"] / line["cpu_baseline"]["value"], 1)
+        line["parity"] = parity(fl, w, q, outs, res)
+    if not args.no_native and args.math == "exact":
+        # the same step with the products on the native FP8 MFMA (an opt-in
+        # arithmetic whose error depends on the data), checked against the
+        # same oracle sample
+        b.math = fl.MATH_NATIVE_FP8
+        rn = b.measure(args.steps, args.warmup)
+        line["native_fp8"] = {
+            "value": round(rn["step_tflops"], 2), "ms_per_step": round(rn["ms_per_step"], 4),
+            "gemm_tflops": round(rn["gemm_tflops"], 2),
+            "gemm_frac_of_fp8_peak": round(rn["gemm_tflops"] / PEAK_FP8_TFLOPS, 4),
+            "parity": parity(fl, w, q, outs, res) if res is not None else None,
+            "note": "fp8_scaled_gemm(FP8_GEMM_NATIVE_FP8): each 64-product instruction keeps 13 bits "
+                    "below its largest product, so its error depends on the data; the library's "
+                    "default products are exact (16-bit MFMA on exactly widened codes)"}
+        b.math = fl.MATH_EXACT
+    if not args.no_per_config:
+        del b, plan, q, x, outs, host
+        gc.collect()
+        torch.cuda.empty_cache()
+        others = [int(v) for v in args.per_config.split(",") if v and int(v) != args.workload]
+        line["per_config"] = {str(wl): per_config_line(fl, wl, args) for wl in others}
     print(json.dumps(line), flush=True)
 
 
