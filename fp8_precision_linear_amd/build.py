@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8lin.so")
-SOURCES = ["quant.hip", "gemm_fwd.hip", "gemm_dgrad.hip", "gemm_wgrad.hip", "swiglu.hip", "capi.hip"]
+SOURCES = ["quant.hip", "gemm_fwd.hip", "gemm_dgrad.hip", "gemm_wgrad.hip", "gemm_group.hip", "swiglu.hip",
+           "capi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -341,11 +341,14 @@ int fp8_scaled_gemm_group(int math, const fp8_gemm_desc_t* descs, int32_t count,
   hipStream_t st = (hipStream_t)stream;
   int idx[3][fp8lin::kGroupMaxProducts];
   int n[3] = {0, 0, 0};
+  int step[fp8lin::kGroupMaxProducts];
+  int nstep = 0;
   for (int i = 0; i < live; ++i) {
     const fp8lin::GemmProblem& p = ps[i];
     const int layout = p.a_kmajor && p.b_kmajor ? 0 : (p.a_kmajor ? 1 : 2);
     if (plan[i].grouped) {
-      idx[layout][n[layout]++] = i;
+      if (fp8lin::gemm_step_variant(p) >= 0) step[nstep++] = i;
+      else idx[layout][n[layout]++] = i;
       continue;
     }
     hipError_t e = layout == 0 ? fp8lin::launch_gemm_fwd(p, st)
@@ -353,6 +356,7 @@ int fp8_scaled_gemm_group(int math, const fp8_gemm_desc_t* descs, int32_t count,
     if (e != hipSuccess) return FP8_ERR_HIP;
   }
   uint8_t* w = static_cast<uint8_t*>(ws);
+  if (int s = hip_status(fp8lin::launch_gemm_step_group(ps, plan, step, nstep, w, st))) return s;
   if (int s = hip_status(fp8lin::launch_gemm_fwd_group(ps, plan, idx[0], n[0], w, st))) return s;
   if (int s = hip_status(fp8lin::launch_gemm_dgrad_group(ps, plan, idx[1], n[1], w, st))) return s;
   return hip_status(fp8lin::launch_gemm_wgrad_group(ps, plan, idx[2], n[2], w, st));

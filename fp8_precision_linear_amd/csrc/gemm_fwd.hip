@@ -18,11 +18,16 @@ int64_t gemm_split_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   return gemm_detail::split_workspace_bytes(m, n, k);
 }
 
-// Which products run grouped and how they are split: each grouped launch
-// holds one layout and format pair (a bucket); within a bucket every
-// product's contraction is cut into slices of about the bucket's shortest
-// contraction (at least kGroupMinSliceStages stages, at most 16 slices), so
-// its blocks do similar work.
+// Which products run grouped and how they are split.  The training-step
+// products (forward E4M3 x E4M3, data and weight gradients E5M2 x E4M3) share
+// one launch; any other product is launched with those of its layout and
+// format pair.  A launch's blocks are handed out in order as workgroup slots
+// free up (kGroupSlots of them: two 128 x 128 workgroups per CU), and its
+// launcher orders products longest first, so the work balances without
+// splitting as long as no single block holds more than the average work per
+// slot: a product is cut along the contraction only into slices of at least
+// that average (and at least kGroupMinSliceStages stages, at most 16 slices)
+// -- which happens when a launch has too few tiles to fill the slots.
 int64_t gemm_group_plan(const GemmProblem* ps, int count, GroupSlot* plan) {
   using namespace gemm_detail;
   auto eligible = [](const GemmProblem& p) {
@@ -34,17 +39,19 @@ int64_t gemm_group_plan(const GemmProblem* ps, int count, GroupSlot* plan) {
     if (!p.a_kmajor && !p.b_kmajor) return pipe_ok<false, false>(p);
     return false;
   };
+  // launch groups: the training-step products (key 16), else one per layout
+  // and format pair
   auto bucket = [](const GemmProblem& p) {
+    if (gemm_step_variant(p) >= 0) return 16;
     return (p.a_kmajor ? 1 : 0) + (p.b_kmajor ? 2 : 0) + 4 * (p.fmt_a == FP8_E5M2 ? 1 : 0) +
            8 * (p.fmt_b == FP8_E5M2 ? 1 : 0);
   };
-  int shortest[16];
-  for (int b = 0; b < 16; ++b) shortest[b] = 0x7FFFFFFF;
+  int64_t work[17] = {0};  // tile-stages of each launch group
   for (int i = 0; i < count; ++i) {
-    plan[i] = GroupSlot{eligible(ps[i]) ? 1 : 0, 1, 0, 0};
-    if (plan[i].grouped && ps[i].k > 0) {
-      const int b = bucket(ps[i]);
-      shortest[b] = std::min(shortest[b], ps[i].k / kPipeBK);
+    plan[i] = GroupSlot{eligible(ps[i]) ? 1 : 0, 1, ps[i].k, 0};
+    if (plan[i].grouped) {
+      const GemmProblem& p = ps[i];
+      work[bucket(p)] += (int64_t)((p.m + 127) / 128) * ((p.n + 127) / 128) * (p.k / kPipeBK);
     }
   }
   int64_t bytes = 0;
@@ -52,10 +59,10 @@ int64_t gemm_group_plan(const GemmProblem* ps, int count, GroupSlot* plan) {
     if (!plan[i].grouped) continue;
     const GemmProblem& p = ps[i];
     const int nk = p.k / kPipeBK;
-    plan[i].kslice = p.k;
     if (nk == 0) continue;
-    const int len = std::max(kGroupMinSliceStages, shortest[bucket(p)]);
-    int s = std::min(16, std::max(1, nk / len));
+    const int64_t avg = (work[bucket(p)] + kGroupSlots - 1) / kGroupSlots;
+    const int len = (int)std::max<int64_t>(kGroupMinSliceStages, avg);
+    int s = std::min(16, (nk + len - 1) / len);
     const int per = (nk + s - 1) / s;
     s = (nk + per - 1) / per;
     plan[i].splits = s;

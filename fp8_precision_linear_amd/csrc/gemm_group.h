@@ -20,11 +20,27 @@ namespace gemm_detail {
 constexpr int kGroupMax = 14;            // products per launch (kernel-argument table)
 constexpr int kGroupMaxTiles = 1024;     // larger products fill the chip alone
 constexpr int kGroupMinSliceStages = 8;  // shortest contraction slice of a split
+constexpr int kGroupSlots = 512;         // 128 x 128 workgroups the chip runs at once (2 per CU)
+
+// The order of a launch's products: longest blocks (most contraction stages
+// per slice) first, so that the blocks handed out last are short ones.
+inline void order_longest_first(const GroupSlot* plan, int* idx, int n) {
+  for (int a = 1; a < n; ++a) {  // stable insertion sort by descending kslice
+    const int v = idx[a];
+    int b = a;
+    while (b > 0 && plan[idx[b - 1]].kslice < plan[v].kslice) {
+      idx[b] = idx[b - 1];
+      --b;
+    }
+    idx[b] = v;
+  }
+}
 
 struct GroupEntry {
   GemmProblem p;
   int tiles_m, tiles_n, splits, kslice, first;
-  float* ws;  // splits > 1: slice s of the raw sums at ws + s * m * n
+  int variant;  // in the training-step kernel: which of its three products
+  float* ws;    // splits > 1: slice s of the raw sums at ws + s * m * n
 };
 
 struct GroupArgs {
@@ -43,13 +59,12 @@ __device__ __forceinline__ const __attribute__((address_space(4))) Entry* group_
   return &a->e[i];
 }
 
+// One block's (product, tile, slice) of a grouped launch: e is its entry, sa
+// and sb the block's LDS rings.
 template <bool AK, bool BK, int FA, int FB, int MATH>
-__global__ __launch_bounds__(256) void gemm_group_kernel(GroupArgs args) {
+__device__ __forceinline__ void group_block(const __attribute__((address_space(4))) GroupEntry* e,
+                                            uint8_t* sa, uint8_t* sb) {
   constexpr int R = 128;
-  __shared__ __attribute__((aligned(1024))) uint8_t sa[kPipeStages * R * kPipeBK];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb[kPipeStages * R * kPipeBK];
-
-  const auto* e = group_entry<GroupArgs, GroupEntry>();
   GemmProblem q;
   __builtin_memcpy(&q, (const GemmProblem*)&e->p, sizeof(GemmProblem));
   const int tiles_m = e->tiles_m, tiles_n = e->tiles_n, splits = e->splits, kslice = e->kslice;
@@ -75,6 +90,13 @@ __global__ __launch_bounds__(256) void gemm_group_kernel(GroupArgs args) {
   const int row0 = m0 + (wave >> 1) * (R / 2), col0 = n0 + (wave & 1) * (R / 2);
   if (splits == 1) store_block_as<false>(q, acc, row0, col0, lane);
   else store_raw_block(e->ws + (int64_t)s * q.m * q.n, q.m, q.n, acc, row0, col0, lane);
+}
+
+template <bool AK, bool BK, int FA, int FB, int MATH>
+__global__ __launch_bounds__(256) void gemm_group_kernel(GroupArgs args) {
+  __shared__ __attribute__((aligned(1024))) uint8_t sa[kPipeStages * 128 * kPipeBK];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb[kPipeStages * 128 * kPipeBK];
+  group_block<AK, BK, FA, FB, MATH>(group_entry<GroupArgs, GroupEntry>(), sa, sb);
 }
 
 // The ordered sum of the split products' slices: out[i] = 2^-(ba+bb) *
@@ -132,8 +154,11 @@ __global__ __launch_bounds__(kReduceThreads) void group_reduce_kernel(ReduceArgs
 // One launch (or a few, kGroupMax products at a time) of the products ps[idx[j]]
 // (all of layout AK, BK and formats FA, FB), then the reduction of the split ones.
 template <bool AK, bool BK, int FA, int FB, int MATH>
-hipError_t launch_group_bucket(const GemmProblem* ps, const GroupSlot* plan, const int* idx, int n,
+hipError_t launch_group_bucket(const GemmProblem* ps, const GroupSlot* plan, const int* idx_in, int n,
                                uint8_t* ws, hipStream_t stream) {
+  int idx[kGroupMaxProducts];
+  for (int j = 0; j < n; ++j) idx[j] = idx_in[j];
+  order_longest_first(plan, idx, n);
   for (int lo = 0; lo < n; lo += kGroupMax) {
     const int cnt = n - lo < kGroupMax ? n - lo : kGroupMax;
     GroupArgs g{};

@@ -105,5 +105,11 @@ hipError_t launch_gemm_dgrad_group(const GemmProblem* ps, const GroupSlot* plan,
                                    uint8_t* ws, hipStream_t stream);
 hipError_t launch_gemm_wgrad_group(const GemmProblem* ps, const GroupSlot* plan, const int* idx, int n,
                                    uint8_t* ws, hipStream_t stream);
+// The training-step products (forward E4M3 x E4M3, data and weight gradients
+// E5M2 x E4M3, each on the MFMA its single launch would use) in one launch
+// (gemm_group.hip); gemm_step_variant is -1 for any other product.
+int gemm_step_variant(const GemmProblem& p);
+hipError_t launch_gemm_step_group(const GemmProblem* ps, const GroupSlot* plan, const int* idx, int n,
+                                  uint8_t* ws, hipStream_t stream);
 
 }  // namespace fp8lin

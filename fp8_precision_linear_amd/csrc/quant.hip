@@ -153,12 +153,50 @@ __device__ __forceinline__ uint32_t amax_bf16_body(const uint4* __restrict__ x, 
   return m << 16;  // bf16 magnitude widened to fp32 bits
 }
 
+// The same with the loads software-pipelined: the next batch of kAmaxUnroll
+// loads is issued before the current batch is reduced, so a lane keeps up to
+// twice as many loads in flight and none of its waits leaves the memory
+// pipeline empty.
 template <bool NT>
+__device__ __forceinline__ uint32_t amax_bf16_body_pipe(const uint4* __restrict__ x, int64_t nvec,
+                                                        const uint16_t* __restrict__ tail, int ntail,
+                                                        int64_t blk, int64_t nblk) {
+  u16x2 acc = {0, 0};
+  const int64_t stride = nblk * kThreads;
+  int64_t i = blk * kThreads + threadIdx.x;
+  if (i + (kAmaxUnroll - 1) * stride < nvec) {
+    uint4 cur[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) cur[u] = load16<NT>(&x[i + u * stride]);
+    for (;;) {
+      const int64_t nx = i + kAmaxUnroll * stride;
+      const bool more = nx + (kAmaxUnroll - 1) * stride < nvec;
+      uint4 nxt[kAmaxUnroll];
+      if (more) {
+#pragma unroll
+        for (int u = 0; u < kAmaxUnroll; ++u) nxt[u] = load16<NT>(&x[nx + u * stride]);
+      }
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; ++u) acc = vmax_bf16(acc, cur[u]);
+      i = nx;
+      if (!more) break;
+#pragma unroll
+      for (int u = 0; u < kAmaxUnroll; ++u) cur[u] = nxt[u];
+    }
+  }
+  for (; i < nvec; i += stride) acc = vmax_bf16(acc, load16<NT>(&x[i]));
+  uint32_t m = max((uint32_t)acc.x, (uint32_t)acc.y);
+  if (blk == 0 && (int)threadIdx.x < ntail) m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7FFFu));
+  return m << 16;
+}
+
+template <bool NT, bool PIPE>
 __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __restrict__ x,
                                                              int64_t nvec,
                                                              const uint16_t* __restrict__ tail,
                                                              int ntail, uint32_t* out) {
-  block_max_to(amax_bf16_body<NT>(x, nvec, tail, ntail, blockIdx.x, gridDim.x), out);
+  if constexpr (PIPE) block_max_to(amax_bf16_body_pipe<NT>(x, nvec, tail, ntail, blockIdx.x, gridDim.x), out);
+  else block_max_to(amax_bf16_body<NT>(x, nvec, tail, ntail, blockIdx.x, gridDim.x), out);
 }
 
 __device__ __forceinline__ uint32_t vmax_f32(uint32_t acc, uint4 v) {
@@ -761,6 +799,18 @@ static int cast_amax_units() {
   return u < 1 ? 1 : (u > 64 ? 64 : u);
 }
 
+// Tuning: FP8LIN_AMAX_PIPE=1 the software-pipelined bf16 amax loop,
+// FP8LIN_AMAX_BLOCKS=n its largest grid.
+static bool amax_pipelined() {
+  const char* v = std::getenv("FP8LIN_AMAX_PIPE");
+  return v && std::atoi(v) != 0;
+}
+static int amax_max_blocks() {
+  const char* v = std::getenv("FP8LIN_AMAX_BLOCKS");
+  const int b = v ? std::atoi(v) : kAmaxMaxBlocks;
+  return b < 1 ? 1 : (b > 65536 ? 65536 : b);
+}
+
 hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t stream) {
   uint32_t* out = reinterpret_cast<uint32_t*>(amax);
   hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, out);
@@ -770,10 +820,15 @@ hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStre
       const int64_t nvec = n / 8;
       const int ntail = (int)(n - nvec * 8);
       const uint16_t* tail = static_cast<const uint16_t*>(x) + nvec * 8;
-      const dim3 grid(stream_blocks(nvec, kAmaxUnroll, kAmaxMaxBlocks));
+      const dim3 grid(stream_blocks(nvec, kAmaxUnroll, amax_max_blocks()));
       const uint4* xv = static_cast<const uint4*>(x);
-      if (nt) hipLaunchKernelGGL(amax_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
-      else hipLaunchKernelGGL(amax_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
+      if (amax_pipelined()) {
+        if (nt) hipLaunchKernelGGL((amax_bf16_kernel<true, true>), grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
+        else hipLaunchKernelGGL((amax_bf16_kernel<false, true>), grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
+      } else {
+        if (nt) hipLaunchKernelGGL((amax_bf16_kernel<true, false>), grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
+        else hipLaunchKernelGGL((amax_bf16_kernel<false, false>), grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
+      }
     } else {
       const int64_t nvec = n / 4;
       const int ntail = (int)(n - nvec * 4);

@@ -426,12 +426,14 @@ def test_gemm_group_argument_checks():
 
 
 def test_gemm_group_workspace_plan():
-    """The GPT-111M layer's nine products at 2048 tokens: per operand layout
-    the contractions are cut to about the shortest in the layout: forward
-    (768, 768, 3072) -> the down product in four slices; data gradient
-    (2304, 3072, 768) -> three and four slices; weight gradient (2048 x 3) ->
-    none.  A product of more than 1024 tiles and one whose contraction is
-    not a whole number of 64-byte stages run alone (no workspace)."""
+    """A launch splits a product along the contraction only into slices of at
+    least its average work per workgroup slot (512 of them; tile-stages /
+    512, at least 8 stages), the blocks balancing by longest-first order
+    otherwise.  The GPT-111M layer's nine products at 2048 tokens (38016
+    tile-stages, 75 per slot) are one training-step launch without a split;
+    each pass alone (12672 tile-stages, 25 per slot) splits its 32- to
+    48-stage products in two.  A product of more than 1024 tiles, or whose
+    contraction is not a whole number of 64-byte stages, runs alone."""
     wsb = L.fp8_scaled_gemm_group_workspace_bytes
     T = 2048
     lin = [("qkv", 768, 2304), ("up", 768, 3072), ("down", 3072, 768)]
@@ -440,14 +442,19 @@ def test_gemm_group_workspace_plan():
     wgrad = [_gdesc(2, 1, 0, M=T, N=n, K=k) for _, k, n in lin]
     arr = lambda ds: (fl.GemmDesc * len(ds))(*ds)
     r = lambda b: (b + 255) // 256 * 256
-    assert wsb(0, arr(fwd), 3) == r(4 * T * 768 * 4)
-    assert wsb(0, arr(dgrad), 3) == r(3 * T * 768 * 4) + r(4 * T * 768 * 4)
-    assert wsb(0, arr(wgrad), 3) == 0
-    assert wsb(0, arr(fwd + dgrad + wgrad), 9) == r(4 * T * 768 * 4) + r(3 * T * 768 * 4) + r(4 * T * 768 * 4)
-    # alone: 8192 x 8192 (4096 tiles); K = 100
-    assert wsb(0, arr([_gdesc(0, M=8192, N=8192, K=64), _gdesc(0, M=128, N=128, K=64 * 40)]), 2) == 0
-    assert wsb(0, arr([_gdesc(0, M=128, N=128, K=100), _gdesc(0, M=128, N=128, K=64 * 40)]), 2) == 0
-    assert wsb(0, arr([_gdesc(0, M=128, N=128, K=64 * 8), _gdesc(0, M=128, N=128, K=64 * 40)]), 2) == r(5 * 128 * 128 * 4)
+    assert wsb(0, arr(fwd + dgrad + wgrad), 9) == 0
+    assert wsb(0, arr(fwd), 3) == r(2 * T * 768 * 4)                       # down (48 stages)
+    assert wsb(0, arr(dgrad), 3) == 2 * r(2 * T * 768 * 4)                 # qkv (36), up (48)
+    assert wsb(0, arr(wgrad), 3) == r(2 * 2304 * 768 * 4) + r(2 * 3072 * 768 * 4) + r(2 * 768 * 3072 * 4)
+    # one 128 x 128 tile of 40 stages: 5 slices of 8; with an 8-stage one beside it, the same
+    one = _gdesc(0, M=128, N=128, K=64 * 40)
+    assert wsb(0, arr([one]), 1) == r(5 * 128 * 128 * 4)
+    assert wsb(0, arr([_gdesc(0, M=128, N=128, K=64 * 8), one]), 2) == r(5 * 128 * 128 * 4)
+    # run alone, no workspace: 8192 x 8192 (4096 tiles), K = 100
+    assert wsb(0, arr([_gdesc(0, M=8192, N=8192, K=64 * 40)]), 1) == 0
+    assert wsb(0, arr([_gdesc(0, M=128, N=128, K=100)]), 1) == 0
+    # 128 tokens through a 70B QKV projection (80 tiles of 128 stages): 7 slices
+    assert wsb(0, arr([_gdesc(0, M=128, N=10240, K=8192)]), 1) == r(7 * 128 * 10240 * 4)
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
