@@ -900,14 +900,16 @@ class Bench:
                     outs.append(self.outs[(l.name, which)])
             self.group_math = self.math
             self.group = fl.GemmGroup(prods, outs=outs, math=self.math)
+        names = self.quant_names
+        self.qmulti = fl.QuantizeMulti([self.x[n] for n in names], [self.q[n][3] for n in names],
+                                       [w.tensor(n).margin for n in names],
+                                       outs=[self.q[n][:3] for n in names]) if names else None
 
     def step(self, ev=None):
         import torch
         fl, w, q, x = self.fl, self.w, self.q, self.x
-        if ev is None and self.args.quant == "multi" and self.quant_names:
-            names = self.quant_names
-            fl.quantize_multi([x[n] for n in names], [q[n][3] for n in names], [w.tensor(n).margin for n in names],
-                              outs=[q[n][:3] for n in names])
+        if ev is None and self.args.quant == "multi" and self.qmulti is not None:
+            self.qmulti.run()
         if ev is None and self.group is not None:
             if self.args.quant != "multi":
                 for n in self.quant_names:

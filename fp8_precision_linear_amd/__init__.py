@@ -249,40 +249,54 @@ def quantize(x, fmt, margin=0, out=None, bias=None, amax=None, stream=None):
     return out, bias, amax
 
 
+class QuantizeMulti:
+    """fp8_quantize_multi prepared once for fixed tensors: xs and their
+    formats and margins; outs (list of (codes, bias, amax)) given or
+    allocated here.  run() is then one library call (the tensors' contents
+    may change between calls, not their storage)."""
+
+    def __init__(self, xs, fmts, margins=0, outs=None, stream=None):
+        xs = list(xs)
+        k = len(xs)
+        fmts = list(fmts) if isinstance(fmts, (list, tuple)) else [fmts] * k
+        margins = list(margins) if isinstance(margins, (list, tuple)) else [margins] * k
+        if len(fmts) != k or len(margins) != k or (outs is not None and len(outs) != k):
+            raise ValueError("one format, margin and output triple per tensor")
+        self.descs = (QuantDesc * max(k, 1))()
+        self.outs, self._keep = [], xs
+        dev = xs[0].device if k else None
+        for i, x in enumerate(xs):
+            dt = _input(x)
+            if outs is not None:
+                out, bias, amax = outs[i]
+                _need_kind(out, f"outs[{i}][0]", torch.uint8, numel=x.numel())
+                _need_kind(bias, f"outs[{i}][1]", torch.int32, numel=1)
+                _need_kind(amax, f"outs[{i}][2]", torch.float32, numel=1)
+                _places(dev, (x, f"xs[{i}]"), (out, f"outs[{i}][0]"), (bias, f"outs[{i}][1]"),
+                        (amax, f"outs[{i}][2]"))
+            else:
+                _places(dev, (x, f"xs[{i}]"))
+                out = _empty(x.shape, torch.uint8, dev, stream)
+                bias = _empty(1, torch.int32, dev, stream)
+                amax = _empty(1, torch.float32, dev, stream)
+            self.descs[i] = QuantDesc(x.data_ptr(), x.numel(), dt, int(fmts[i]), int(margins[i]), 0,
+                                      out.data_ptr(), amax.data_ptr(), bias.data_ptr())
+            self.outs.append((out, bias, amax))
+        self.count = k
+        self.ptr = ctypes.cast(self.descs, ctypes.c_void_p)
+
+    def run(self, stream=None):
+        _check("fp8_quantize_multi", lib.fp8_quantize_multi(self.ptr, self.count, _stream(stream)))
+        return self.outs
+
+
 def quantize_multi(xs, fmts, margins=0, outs=None, stream=None):
-    """fp8_quantize of every tensor in xs in one call (fp8_quantize_multi: three
-    launches per 32 tensors).  fmts, margins: one per tensor, or one for all.
-    outs: optional list of (codes, bias, amax) device tensors to write.
-    Returns the list of (codes, bias, amax), each bit-identical to quantize()
-    of that tensor alone."""
-    xs = list(xs)
-    k = len(xs)
-    fmts = list(fmts) if isinstance(fmts, (list, tuple)) else [fmts] * k
-    margins = list(margins) if isinstance(margins, (list, tuple)) else [margins] * k
-    if len(fmts) != k or len(margins) != k or (outs is not None and len(outs) != k):
-        raise ValueError("one format, margin and output triple per tensor")
-    res, descs = [], (QuantDesc * max(k, 1))()
-    dev = xs[0].device if k else None
-    for i, x in enumerate(xs):
-        dt = _input(x)
-        if outs is not None:
-            out, bias, amax = outs[i]
-            _need_kind(out, f"outs[{i}][0]", torch.uint8, numel=x.numel())
-            _need_kind(bias, f"outs[{i}][1]", torch.int32, numel=1)
-            _need_kind(amax, f"outs[{i}][2]", torch.float32, numel=1)
-            _places(dev, (x, f"xs[{i}]"), (out, f"outs[{i}][0]"), (bias, f"outs[{i}][1]"),
-                    (amax, f"outs[{i}][2]"))
-        else:
-            _places(dev, (x, f"xs[{i}]"))
-            out = _empty(x.shape, torch.uint8, dev, stream)
-            bias = _empty(1, torch.int32, dev, stream)
-            amax = _empty(1, torch.float32, dev, stream)
-        descs[i] = QuantDesc(x.data_ptr(), x.numel(), dt, int(fmts[i]), int(margins[i]), 0,
-                             out.data_ptr(), amax.data_ptr(), bias.data_ptr())
-        res.append((out, bias, amax))
-    _check("fp8_quantize_multi", lib.fp8_quantize_multi(ctypes.cast(descs, ctypes.c_void_p), k,
-                                                        _stream(stream)))
-    return res
+    """fp8_quantize of every tensor in xs in one call (fp8_quantize_multi: one
+    launch per 32 tensors of at most 256 KiB, three per 32 others).  fmts,
+    margins: one per tensor, or one for all.  outs: optional list of (codes,
+    bias, amax) device tensors to write.  Returns the list of (codes, bias,
+    amax), each bit-identical to quantize() of that tensor alone."""
+    return QuantizeMulti(xs, fmts, margins, outs=outs, stream=stream).run(stream)
 
 
 def quantize_chain(x, fmt, margin=0, stream=None):

@@ -153,50 +153,12 @@ __device__ __forceinline__ uint32_t amax_bf16_body(const uint4* __restrict__ x, 
   return m << 16;  // bf16 magnitude widened to fp32 bits
 }
 
-// The same with the loads software-pipelined: the next batch of kAmaxUnroll
-// loads is issued before the current batch is reduced, so a lane keeps up to
-// twice as many loads in flight and none of its waits leaves the memory
-// pipeline empty.
 template <bool NT>
-__device__ __forceinline__ uint32_t amax_bf16_body_pipe(const uint4* __restrict__ x, int64_t nvec,
-                                                        const uint16_t* __restrict__ tail, int ntail,
-                                                        int64_t blk, int64_t nblk) {
-  u16x2 acc = {0, 0};
-  const int64_t stride = nblk * kThreads;
-  int64_t i = blk * kThreads + threadIdx.x;
-  if (i + (kAmaxUnroll - 1) * stride < nvec) {
-    uint4 cur[kAmaxUnroll];
-#pragma unroll
-    for (int u = 0; u < kAmaxUnroll; ++u) cur[u] = load16<NT>(&x[i + u * stride]);
-    for (;;) {
-      const int64_t nx = i + kAmaxUnroll * stride;
-      const bool more = nx + (kAmaxUnroll - 1) * stride < nvec;
-      uint4 nxt[kAmaxUnroll];
-      if (more) {
-#pragma unroll
-        for (int u = 0; u < kAmaxUnroll; ++u) nxt[u] = load16<NT>(&x[nx + u * stride]);
-      }
-#pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) acc = vmax_bf16(acc, cur[u]);
-      i = nx;
-      if (!more) break;
-#pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) cur[u] = nxt[u];
-    }
-  }
-  for (; i < nvec; i += stride) acc = vmax_bf16(acc, load16<NT>(&x[i]));
-  uint32_t m = max((uint32_t)acc.x, (uint32_t)acc.y);
-  if (blk == 0 && (int)threadIdx.x < ntail) m = max(m, (uint32_t)(tail[threadIdx.x] & 0x7FFFu));
-  return m << 16;
-}
-
-template <bool NT, bool PIPE>
 __global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint4* __restrict__ x,
                                                              int64_t nvec,
                                                              const uint16_t* __restrict__ tail,
                                                              int ntail, uint32_t* out) {
-  if constexpr (PIPE) block_max_to(amax_bf16_body_pipe<NT>(x, nvec, tail, ntail, blockIdx.x, gridDim.x), out);
-  else block_max_to(amax_bf16_body<NT>(x, nvec, tail, ntail, blockIdx.x, gridDim.x), out);
+  block_max_to(amax_bf16_body<NT>(x, nvec, tail, ntail, blockIdx.x, gridDim.x), out);
 }
 
 __device__ __forceinline__ uint32_t vmax_f32(uint32_t acc, uint4 v) {
@@ -629,7 +591,7 @@ __device__ __forceinline__ uint32_t small_block_max(uint32_t v) {
 // bf16: x holds nunit 16-element units (2 x 16 bytes each), then ntail < 16
 // elements at tail_x.
 template <int FMT>
-__global__ __launch_bounds__(kSmallThreads) void quantize_small_bf16_kernel(
+__device__ __forceinline__ void quantize_small_bf16(
     const uint4* __restrict__ x, int64_t nunit, const uint16_t* __restrict__ tail_x,
     uint8_t* __restrict__ tail_y, int ntail, uint4* __restrict__ y, int32_t margin,
     uint32_t* __restrict__ amax, int32_t* __restrict__ bias) {
@@ -660,10 +622,18 @@ __global__ __launch_bounds__(kSmallThreads) void quantize_small_bf16_kernel(
   if (t < ntail) tail_y[t] = (uint8_t)fp8_code<FMT>((uint32_t)tail_x[t] << 16, b);
 }
 
+template <int FMT>
+__global__ __launch_bounds__(kSmallThreads) void quantize_small_bf16_kernel(
+    const uint4* __restrict__ x, int64_t nunit, const uint16_t* __restrict__ tail_x,
+    uint8_t* __restrict__ tail_y, int ntail, uint4* __restrict__ y, int32_t margin,
+    uint32_t* __restrict__ amax, int32_t* __restrict__ bias) {
+  quantize_small_bf16<FMT>(x, nunit, tail_x, tail_y, ntail, y, margin, amax, bias);
+}
+
 // fp32: x holds nvec groups of 4 elements (16 bytes -> one 4-byte word of
 // codes), then ntail < 4 elements at tail_x.
 template <int FMT>
-__global__ __launch_bounds__(kSmallThreads) void quantize_small_f32_kernel(
+__device__ __forceinline__ void quantize_small_f32(
     const uint4* __restrict__ x, int64_t nvec, const uint32_t* __restrict__ tail_x,
     uint8_t* __restrict__ tail_y, int ntail, uint32_t* __restrict__ y, int32_t margin,
     uint32_t* __restrict__ amax, int32_t* __restrict__ bias) {
@@ -685,8 +655,18 @@ __global__ __launch_bounds__(kSmallThreads) void quantize_small_f32_kernel(
   if (t < ntail) tail_y[t] = (uint8_t)fp8_code<FMT>(tail_x[t], b);
 }
 
-// ---------------------------------------------------------------- several tensors in three launches
-// The quantisation of up to kMultiMax tensors in three launches in all: one
+template <int FMT>
+__global__ __launch_bounds__(kSmallThreads) void quantize_small_f32_kernel(
+    const uint4* __restrict__ x, int64_t nvec, const uint32_t* __restrict__ tail_x,
+    uint8_t* __restrict__ tail_y, int ntail, uint32_t* __restrict__ y, int32_t margin,
+    uint32_t* __restrict__ amax, int32_t* __restrict__ bias) {
+  quantize_small_f32<FMT>(x, nvec, tail_x, tail_y, ntail, y, margin, amax, bias);
+}
+
+// ---------------------------------------------------------------- several tensors in few launches
+// Small tensors (at most the one-workgroup quantisation's size) are quantised
+// by one workgroup each, kMultiMax of them per launch.  The others: up to
+// kMultiMax tensors in three launches in all: one
 // clears every amax word, one reduces every tensor's amax (each tensor has its
 // own run of blocks, sized as the single-tensor amax would size its grid),
 // one casts every tensor (each block derives its tensor's bias from the amax
@@ -765,6 +745,35 @@ __device__ __forceinline__ void multi_cast_one(const __attribute__((address_spac
   }
 }
 
+// Small tensors (at most the one-workgroup quantisation's size): workgroup b
+// quantises tensor b whole, as fp8_quantize's one-workgroup path does.
+template <int FMT>
+__device__ __forceinline__ void multi_small_one(const __attribute__((address_space(4))) MultiTensor* e) {
+  const int64_t n = e->n;
+  if (e->dtype == FP8_IN_BF16) {
+    const int64_t nunit = n / 16;
+    quantize_small_bf16<FMT>(static_cast<const uint4*>(e->x), nunit,
+                             static_cast<const uint16_t*>(e->x) + nunit * 16, e->y + nunit * 16,
+                             (int)(n - nunit * 16), reinterpret_cast<uint4*>(e->y), e->margin, e->amax,
+                             e->bias);
+  } else {
+    const int64_t nvec = n / 4;
+    quantize_small_f32<FMT>(static_cast<const uint4*>(e->x), nvec, static_cast<const uint32_t*>(e->x) + nvec * 4,
+                            e->y + nvec * 4, (int)(n - nvec * 4), reinterpret_cast<uint32_t*>(e->y), e->margin,
+                            e->amax, e->bias);
+  }
+}
+
+__global__ __launch_bounds__(kSmallThreads) void multi_small_kernel(MultiArgs a) {
+  const auto* ka = (const __attribute__((address_space(4))) MultiArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  const auto* e = &ka->t[blockIdx.x];
+  switch (e->fmt) {
+    case FP8_E4M3: multi_small_one<FP8_E4M3>(e); break;
+    case FP8_E5M2: multi_small_one<FP8_E5M2>(e); break;
+    default: multi_small_one<FP8_E3M4>(e); break;
+  }
+}
+
 template <bool NT>
 __global__ __launch_bounds__(kThreads) void multi_cast_kernel(MultiArgs a) {
   const auto* e = multi_entry(true);
@@ -799,18 +808,6 @@ static int cast_amax_units() {
   return u < 1 ? 1 : (u > 64 ? 64 : u);
 }
 
-// Tuning: FP8LIN_AMAX_PIPE=1 the software-pipelined bf16 amax loop,
-// FP8LIN_AMAX_BLOCKS=n its largest grid.
-static bool amax_pipelined() {
-  const char* v = std::getenv("FP8LIN_AMAX_PIPE");
-  return v && std::atoi(v) != 0;
-}
-static int amax_max_blocks() {
-  const char* v = std::getenv("FP8LIN_AMAX_BLOCKS");
-  const int b = v ? std::atoi(v) : kAmaxMaxBlocks;
-  return b < 1 ? 1 : (b > 65536 ? 65536 : b);
-}
-
 hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t stream) {
   uint32_t* out = reinterpret_cast<uint32_t*>(amax);
   hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, out);
@@ -820,15 +817,10 @@ hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStre
       const int64_t nvec = n / 8;
       const int ntail = (int)(n - nvec * 8);
       const uint16_t* tail = static_cast<const uint16_t*>(x) + nvec * 8;
-      const dim3 grid(stream_blocks(nvec, kAmaxUnroll, amax_max_blocks()));
+      const dim3 grid(stream_blocks(nvec, kAmaxUnroll, kAmaxMaxBlocks));
       const uint4* xv = static_cast<const uint4*>(x);
-      if (amax_pipelined()) {
-        if (nt) hipLaunchKernelGGL((amax_bf16_kernel<true, true>), grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
-        else hipLaunchKernelGGL((amax_bf16_kernel<false, true>), grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
-      } else {
-        if (nt) hipLaunchKernelGGL((amax_bf16_kernel<true, false>), grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
-        else hipLaunchKernelGGL((amax_bf16_kernel<false, false>), grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
-      }
+      if (nt) hipLaunchKernelGGL(amax_bf16_kernel<true>, grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
+      else hipLaunchKernelGGL(amax_bf16_kernel<false>, grid, dim3(kThreads), 0, stream, xv, nvec, tail, ntail, out);
     } else {
       const int64_t nvec = n / 4;
       const int ntail = (int)(n - nvec * 4);
@@ -965,23 +957,49 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t n, int fmt, int32_t
   return launch_cast_from(x, dtype, n, BiasArg{nullptr, a, bias, margin}, fmt, y, nullptr, stream);
 }
 
+static MultiTensor multi_entry_of(const QuantDesc& q) {
+  MultiTensor t{};
+  t.x = q.x;
+  t.y = q.y;
+  t.amax = reinterpret_cast<uint32_t*>(q.amax);
+  t.bias = q.bias;
+  t.n = q.n;
+  t.dtype = q.dtype;
+  t.fmt = q.fmt;
+  t.margin = q.margin;
+  return t;
+}
+
 hipError_t launch_quantize_multi(const QuantDesc* d, int count, hipStream_t stream) {
-  const bool nt_amax = streams("FP8LIN_AMAX_HINT"), nt_cast = streams("FP8LIN_CAST_HINT");
-  for (int first = 0; first < count; first += kMultiMax) {
+  // small tensors: one workgroup each, all in one launch (per kMultiMax)
+  {
     MultiArgs a{};
-    a.count = count - first < kMultiMax ? count - first : kMultiMax;
+    for (int i = 0; i < count; ++i) {
+      const QuantDesc& q = d[i];
+      if (!(q.n == 0 || q.n <= small_quant_max(q.dtype))) continue;
+      a.t[a.count++] = multi_entry_of(q);
+      if (a.count == kMultiMax || i == count - 1) {
+        hipLaunchKernelGGL(multi_small_kernel, dim3(a.count), dim3(kSmallThreads), 0, stream, a);
+        a.count = 0;
+      }
+    }
+    if (a.count > 0) hipLaunchKernelGGL(multi_small_kernel, dim3(a.count), dim3(kSmallThreads), 0, stream, a);
+    if (hipError_t e = hipGetLastError()) return e;
+  }
+  // the rest: clear, amax and cast launches for kMultiMax tensors at a time
+  const bool nt_amax = streams("FP8LIN_AMAX_HINT"), nt_cast = streams("FP8LIN_CAST_HINT");
+  int next = 0;
+  while (true) {
+    MultiArgs a{};
+    while (next < count && a.count < kMultiMax) {
+      const QuantDesc& q = d[next++];
+      if (!(q.n == 0 || q.n <= small_quant_max(q.dtype))) a.t[a.count++] = multi_entry_of(q);
+    }
+    if (a.count == 0) break;
     int64_t amax_total = 0, cast_total = 0;
     for (int i = 0; i < a.count; ++i) {
-      const QuantDesc& q = d[first + i];
       MultiTensor& t = a.t[i];
-      t.x = q.x;
-      t.y = q.y;
-      t.amax = reinterpret_cast<uint32_t*>(q.amax);
-      t.bias = q.bias;
-      t.n = q.n;
-      t.dtype = q.dtype;
-      t.fmt = q.fmt;
-      t.margin = q.margin;
+      const QuantDesc q{t.x, t.n, t.dtype, t.fmt, t.margin, t.y, reinterpret_cast<float*>(t.amax), t.bias};
       // the grids the single-tensor amax and cast would launch
       const bool bf = q.dtype == FP8_IN_BF16;
       t.amax_blocks = stream_blocks(bf ? q.n / 8 : q.n / 4, kAmaxUnroll, kAmaxMaxBlocks);

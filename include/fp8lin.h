@@ -156,11 +156,12 @@ int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32
 /*
  * fp8_quantize_multi: fp8_quantize of several tensors in one call -- the
  * per-tensor amax, bias and cast of "Proposed method", bullets 1-4, for each
- * tensor on its own -- in three launches per 32 tensors (one clears every amax,
- * one reduces every tensor's amax, one casts every tensor deriving its bias
- * from its amax), so that a step that quantises many small tensors (a layer's
- * activations, weights and gradients) pays three kernel dispatches instead of
- * up to three per tensor.
+ * tensor on its own -- so that a step that quantises many tensors (a layer's
+ * activations, weights and gradients) pays a few kernel dispatches instead of
+ * up to three per tensor: tensors of at most 256 KiB are quantised by one
+ * workgroup each, 32 tensors per launch; the others take three launches per
+ * 32 tensors (one clears every amax, one reduces every tensor's amax, one
+ * casts every tensor deriving its bias from its amax).
  *   descs  host array of count descriptors (read during the call only):
  *          x, n, dtype, fmt, margin, y, amax, bias exactly as fp8_quantize's
  *          arguments for that tensor.  The outputs of different tensors must
