@@ -1152,8 +1152,9 @@ def main():
                              "one-call": "fp8_quantize per tensor (one workgroup up to 256 KiB, else clear, "
                                          "amax and a cast deriving the bias)",
                              "three-calls": "fp8_amax -> fp8_compute_bias -> fp8_scale_cast per tensor"}[args.quant],
-            "product_calls": ("fp8_scaled_gemm_group: every product in one call (a launch per operand layout "
-                         "and format pair; products of more than 1024 tiles alone)" if args.gemm == "grouped"
+            "product_calls": ("fp8_scaled_gemm_group: every product in one call (the training-step products in "
+                              "one launch, other format pairs a launch per layout; products of more than 1024 "
+                              "tiles alone)" if args.gemm == "grouped"
                          else "fp8_scaled_gemm per product (fp8_scaled_gemm_ws when split)"),
             "products_grouped_ws_bytes": b.group.ws_bytes if b.group is not None else None,
             "parallelism": "single-gpu",
