@@ -905,65 +905,84 @@ class Bench:
                                        [w.tensor(n).margin for n in names],
                                        outs=[self.q[n][:3] for n in names]) if names else None
 
-    def step(self, ev=None):
+    def event_calls(self):
+        """The step as direct library calls (every argument prepared here, so
+        that the HIP events around each call bracket only its launch): for
+        each in-step tensor fp8_amax, fp8_compute_bias, fp8_scale_cast; for
+        each product fp8_scaled_gemm (fp8_scaled_gemm_ws when split)."""
+        import ctypes
+
         import torch
         fl, w, q, x = self.fl, self.w, self.q, self.x
-        if ev is None and self.args.quant == "multi" and self.qmulti is not None:
-            self.qmulti.run()
-        if ev is None and self.group is not None:
-            if self.args.quant != "multi":
-                for n in self.quant_names:
-                    codes, bias, amax, fmt = q[n]
-                    if self.args.quant == "one-call":
-                        fl.quantize(x[n], fmt, w.tensor(n).margin, out=codes, bias=bias, amax=amax)
-                    else:
-                        fl.amax(x[n], out=amax)
-                        fl.compute_bias(amax, fmt, w.tensor(n).margin, out=bias)
-                        fl.scale_cast(x[n], bias, fmt, out=codes)
+        P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        calls = []
+        for item in self.plan:
+            if item[0] == "quant":
+                n = item[1]
+                codes, bias, amax, fmt = q[n]
+                dt = fl.BF16 if x[n].dtype == torch.bfloat16 else fl.FP32
+                calls.append(("amax", n, fl.lib.fp8_amax, (P(x[n]), dt, x[n].numel(), P(amax), st)))
+                calls.append(("bias", n, fl.lib.fp8_compute_bias, (P(amax), fmt, w.tensor(n).margin, P(bias), st)))
+                calls.append(("cast", n, fl.lib.fp8_scale_cast,
+                              (P(x[n]), dt, x[n].numel(), P(bias), fmt, P(codes), st)))
+            else:
+                _, l, which = item
+                an, bn, _ = gemm_operands(l, which)
+                a8, ba, _, fa = q[an]
+                b8, bb, _, fb = q[bn]
+                args = (self.op_of[which], self.math, P(a8), fa, P(ba), P(b8), fb, P(bb), l.M, l.N, l.K,
+                        P(self.outs[(l.name, which)]))
+                if self.ws_of.get((l.name, which), 0) > 0:
+                    calls.append(("gemm", (l.name, which), fl.lib.fp8_scaled_gemm_ws,
+                                  args + (P(self.ws), self.ws.numel(), st)))
+                else:
+                    calls.append(("gemm", (l.name, which), fl.lib.fp8_scaled_gemm, args + (st,)))
+        return calls
+
+    def step_events(self, ev, calls):
+        import torch
+        for kind, key, fn, args in calls:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            status = fn(*args)
+            e1.record()
+            if status != 0:
+                raise RuntimeError(f"{fn.__name__}: status {status}")
+            ev.append((kind, key, e0, e1))
+
+    def step(self):
+        """One timed step: the in-step quantisations (one fp8_quantize_multi
+        call, or per tensor), then the products (one fp8_scaled_gemm_group
+        call, or per product), all on torch's current stream."""
+        fl, w, q, x = self.fl, self.w, self.q, self.x
+        if self.args.quant == "multi":
+            if self.qmulti is not None:
+                self.qmulti.run()
+        else:
+            for n in self.quant_names:
+                codes, bias, amax, fmt = q[n]
+                if self.args.quant == "one-call":
+                    fl.quantize(x[n], fmt, w.tensor(n).margin, out=codes, bias=bias, amax=amax)
+                else:
+                    fl.amax(x[n], out=amax)
+                    fl.compute_bias(amax, fmt, w.tensor(n).margin, out=bias)
+                    fl.scale_cast(x[n], bias, fmt, out=codes)
+        if self.group is not None:
             if self.group_math != self.math:   # the arithmetic was switched after set-up
                 self.group.math = self.math
                 self.group_math = self.math
             self.group.run()
             return
         for item in self.plan:
-            if item[0] == "quant":
-                n = item[1]
-                codes, bias, amax, fmt = q[n]
-                t = w.tensor(n)
-                if ev is None and self.args.quant == "multi":
-                    continue                  # quantised above, all in one call
-                if ev is None and self.args.quant == "one-call":
-                    fl.quantize(x[n], fmt, t.margin, out=codes, bias=bias, amax=amax)
-                    continue
-                if ev is not None:
-                    ev.append(("quant_start", n, torch.cuda.Event(enable_timing=True)))
-                    ev[-1][2].record()
-                fl.amax(x[n], out=amax)
-                if ev is not None:
-                    ev.append(("amax_end", n, torch.cuda.Event(enable_timing=True)))
-                    ev[-1][2].record()
-                fl.compute_bias(amax, fmt, t.margin, out=bias)
-                if ev is not None:
-                    ev.append(("bias_end", n, torch.cuda.Event(enable_timing=True)))
-                    ev[-1][2].record()
-                fl.scale_cast(x[n], bias, fmt, out=codes)
-                if ev is not None:
-                    ev.append(("cast_end", n, torch.cuda.Event(enable_timing=True)))
-                    ev[-1][2].record()
-            else:
-                _, l, which = item
-                an, bn, _ = gemm_operands(l, which)
-                a8, ba, _, fa = q[an]
-                b8, bb, _, fb = q[bn]
-                if ev is not None:
-                    ev.append(("gemm_start", (l.name, which), torch.cuda.Event(enable_timing=True)))
-                    ev[-1][2].record()
-                fl.scaled_gemm(self.op_of[which], a8, fa, ba, b8, fb, bb, math=self.math,
-                               out=self.outs[(l.name, which)],
-                               workspace=self.ws if self.ws_of.get((l.name, which), 0) > 0 else None)
-                if ev is not None:
-                    ev.append(("gemm_end", (l.name, which), torch.cuda.Event(enable_timing=True)))
-                    ev[-1][2].record()
+            if item[0] != "gemm":
+                continue
+            _, l, which = item
+            an, bn, _ = gemm_operands(l, which)
+            a8, ba, _, fa = q[an]
+            b8, bb, _, fb = q[bn]
+            fl.scaled_gemm(self.op_of[which], a8, fa, ba, b8, fb, bb, math=self.math, out=self.outs[(l.name, which)],
+                           workspace=self.ws if self.ws_of.get((l.name, which), 0) > 0 else None)
 
     def measure(self, steps, warmup):
         """K timed steps (wall clock, synchronised on both sides, no events and
@@ -985,38 +1004,39 @@ class Bench:
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
         ev, step_ev = [], []
+        calls = self.event_calls()
+        # Where the host takes longer to enqueue a step's calls than the GPU
+        # to run them (small workloads), a spin kernel leads each event-timed
+        # step for the difference, so that the step's launches and events are
+        # queued before the GPU reaches them and each event pair brackets its
+        # kernel alone rather than the gaps between launches; where the GPU is
+        # the slower one (the queue runs ahead by itself) there is no spin.
+        warm = []
+        t0 = time.perf_counter()
+        self.step_events(warm, calls)
+        host_us = (time.perf_counter() - t0) * 1e6
+        torch.cuda.synchronize()
+        spin_us = max(0.0, 1.5 * host_us - ms_per_step * 1e3)
+        spin_cycles = int(spin_us * 2500)  # >= spin_us at clocks up to 2.5 GHz
         for _ in range(steps):
+            if spin_cycles:
+                torch.cuda._sleep(spin_cycles)
             s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s0.record()
-            self.step(ev)
+            self.step_events(ev, calls)
             s1.record()
             step_ev.append((s0, s1))
         torch.cuda.synchronize()
         gc.enable()
-        r = {"ms_per_step": ms_per_step,
+        r = {"ms_per_step": ms_per_step, "event_step_spin_us": round(spin_us, 1),
              "step_median_ms": statistics.median(a.elapsed_time(b) for a, b in step_ev),
              "gemm_ms": 0.0, "amax_ms": 0.0, "bias_ms": 0.0, "cast_ms": 0.0,
              "cast_by": {}, "amax_by": {}, "steps": steps}
-        last = {}
-        for kind, key, e in ev:
-            if kind == "quant_start":
-                last["q"] = e
-            elif kind == "amax_end":
-                t = last["q"].elapsed_time(e)
-                r["amax_ms"] += t
-                r["amax_by"][key] = r["amax_by"].get(key, 0.0) + t
-                last["a"] = e
-            elif kind == "bias_end":
-                r["bias_ms"] += last["a"].elapsed_time(e)
-                last["b"] = e
-            elif kind == "cast_end":
-                t = last["b"].elapsed_time(e)
-                r["cast_ms"] += t
-                r["cast_by"][key] = r["cast_by"].get(key, 0.0) + t
-            elif kind == "gemm_start":
-                last["g"] = e
-            elif kind == "gemm_end":
-                r["gemm_ms"] += last["g"].elapsed_time(e)
+        for kind, key, e0, e1 in ev:
+            t = e0.elapsed_time(e1)
+            r[kind + "_ms"] += t
+            if kind in ("amax", "cast"):
+                r[kind + "_by"][key] = r[kind + "_by"].get(key, 0.0) + t
         K = steps
         w = self.w
         r["step_flops"] = w.flops()
