@@ -96,24 +96,6 @@ __device__ __forceinline__ void block_max_to(uint32_t v, uint32_t* out) {
   }
 }
 
-// The same, for grids of many blocks: the atomic is skipped when the stored
-// value is already at least as large, so that few of the blocks touch the one
-// address (atomics on it cost more than the loads: reading the value when the
-// block starts instead, which lets more blocks through, was slower).
-__device__ __forceinline__ void block_max_fold(uint32_t v, uint32_t* out) {
-  __shared__ uint32_t part[kWaves];
-  v = wave_max_u32(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) part[wave] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t m = part[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w) m = max(m, part[w]);
-    if (m > __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(out, m);
-  }
-}
-
 __global__ void amax_clear_kernel(uint32_t* out) { *out = 0u; }
 
 // bf16: each 16-byte vector holds 8 values; the running max is kept as two
@@ -425,12 +407,12 @@ __device__ __forceinline__ uint4 cast_unit_sw(uint4 lo, uint4 hi, int32_t b) {
 // choice between the hardware conversion (bias in [kHwBiasMin, kHwBiasMax],
 // E4M3 and E5M2) and fp8_code is a wave-uniform branch per unit after them.
 // With AMAX the lane's largest input magnitude (bf16 bits) is returned too.
-template <int FMT, bool NT, bool AMAX>
+template <int FMT, bool NT, bool AMAX, int TPB = kThreads>
 __device__ __forceinline__ uint32_t cast_bf16_body(const uint4* __restrict__ x, int64_t nunit,
                                                    const BiasArg& bias, uint4* __restrict__ y,
                                                    int64_t blk, int64_t nblk) {
-  const int64_t stride = nblk * kThreads;
-  int64_t i = blk * kThreads + threadIdx.x;
+  const int64_t stride = nblk * TPB;
+  int64_t i = blk * TPB + threadIdx.x;
   if (i >= nunit) return 0u;
   u16x2 acc = {0, 0};
   uint4 lo = load16<NT>(&x[2 * i]), hi = load16<NT>(&x[2 * i + 1]);
@@ -464,13 +446,13 @@ __device__ __forceinline__ uint32_t cast_bf16_body(const uint4* __restrict__ x, 
 // Block blk of nblk casting a bf16 tensor: its units, the derived bias (block
 // 0), block 0's share of the tail; returns the lane's largest input magnitude
 // (fp32 bits) when AMAX.
-template <int FMT, bool NT, bool AMAX>
+template <int FMT, bool NT, bool AMAX, int TPB = kThreads>
 __device__ __forceinline__ uint32_t cast_bf16_whole(const uint4* __restrict__ x, int64_t nunit,
                                                     const BiasArg& bias, uint4* __restrict__ y,
                                                     const uint16_t* __restrict__ tail_x,
                                                     uint8_t* __restrict__ tail_y, int ntail,
                                                     int64_t blk, int64_t nblk) {
-  uint32_t m = cast_bf16_body<FMT, NT, AMAX>(x, nunit, bias, y, blk, nblk);
+  uint32_t m = cast_bf16_body<FMT, NT, AMAX, TPB>(x, nunit, bias, y, blk, nblk);
   store_derived_bias<FMT>(bias, blk);
   if (blk == 0 && (int)threadIdx.x < ntail) {
     const uint32_t w = tail_x[threadIdx.x];
@@ -480,17 +462,14 @@ __device__ __forceinline__ uint32_t cast_bf16_whole(const uint4* __restrict__ x,
   return m << 16;
 }
 
-// AMAX: also fold max |x| (fp32 bits) into *amax, once per block.
-template <int FMT, bool NT, bool AMAX>
+template <int FMT, bool NT>
 __global__ __launch_bounds__(kThreads) void cast_bf16_kernel(const uint4* __restrict__ x,
                                                              int64_t nunit, BiasArg bias,
                                                              uint4* __restrict__ y,
                                                              const uint16_t* __restrict__ tail_x,
                                                              uint8_t* __restrict__ tail_y,
-                                                             int ntail, uint32_t* amax) {
-  const uint32_t m = cast_bf16_whole<FMT, NT, AMAX>(x, nunit, bias, y, tail_x, tail_y, ntail,
-                                                    blockIdx.x, gridDim.x);
-  if constexpr (AMAX) block_max_fold(m, amax);
+                                                             int ntail) {
+  cast_bf16_whole<FMT, NT, false>(x, nunit, bias, y, tail_x, tail_y, ntail, blockIdx.x, gridDim.x);
 }
 
 // fp32 input: a wave takes chunks of kF32Chunk consecutive elements; load k
@@ -516,7 +495,7 @@ __device__ __forceinline__ uint32_t cast4_f32(uint4 v, bool hw, int32_t b, uint3
   return pack4_f32<FMT>(v, b);
 }
 
-template <int FMT, bool NT, bool AMAX>
+template <int FMT, bool NT, bool AMAX, int TPB = kThreads>
 __device__ __forceinline__ uint32_t cast_f32_whole(const uint4* __restrict__ x, int64_t nchunk,
                                                    const BiasArg& bias, uint32_t* __restrict__ y,
                                                    const uint32_t* __restrict__ tail_x,
@@ -529,9 +508,9 @@ __device__ __forceinline__ uint32_t cast_f32_whole(const uint4* __restrict__ x, 
   if constexpr (kHwConvert<FMT>) bound = hw_bound_f32<FMT>(b);
   const float scale = __builtin_ldexpf(1.0f, hw ? -b : 0);
   const int lane = threadIdx.x & 63;
-  const int64_t wstride = nblk * (kThreads / 64);
+  const int64_t wstride = nblk * (TPB / 64);
   uint32_t m = 0;
-  for (int64_t w = blk * (kThreads / 64) + (threadIdx.x >> 6); w < nchunk; w += wstride) {
+  for (int64_t w = blk * (TPB / 64) + (threadIdx.x >> 6); w < nchunk; w += wstride) {
     const int64_t q = w * (kF32Chunk / 4);  // the chunk's first 16-byte group
     uint4 v[kF32Loads];
 #pragma unroll
@@ -543,29 +522,185 @@ __device__ __forceinline__ uint32_t cast_f32_whole(const uint4* __restrict__ x, 
     }
   }
   if (blk == 0)
-    for (int i = threadIdx.x; i < ntail; i += kThreads) {
+    for (int i = threadIdx.x; i < ntail; i += TPB) {
       tail_y[i] = (uint8_t)fp8_code<FMT>(tail_x[i], b);
       m = max(m, tail_x[i] & 0x7FFFFFFFu);
     }
   return m;
 }
 
-template <int FMT, bool NT, bool AMAX>
+template <int FMT, bool NT>
 __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restrict__ x,
                                                             int64_t nchunk, BiasArg bias,
                                                             uint32_t* __restrict__ y,
                                                             const uint32_t* __restrict__ tail_x,
                                                             uint8_t* __restrict__ tail_y,
-                                                            int ntail, uint32_t* amax) {
-  const uint32_t m = cast_f32_whole<FMT, NT, AMAX>(x, nchunk, bias, y, tail_x, tail_y, ntail,
-                                                   blockIdx.x, gridDim.x);
-  if constexpr (AMAX) block_max_fold(m, amax);
+                                                            int ntail) {
+  cast_f32_whole<FMT, NT, false>(x, nchunk, bias, y, tail_x, tail_y, ntail, blockIdx.x, gridDim.x);
 }
 
-// Grid size: `per_lane` units of work per lane, between 1 and `cap` blocks.
-int stream_blocks(int64_t units, int64_t per_lane, int64_t cap) {
-  const int64_t want = (units + per_lane * kThreads - 1) / (per_lane * kThreads);
+// ---------------------------------------------------------------- cast + amax
+// The cast that also returns max |x| takes two launches and no atomics:
+//  * the main cast covers all of the input but a last stretch; each of its
+//    blocks stores its largest input magnitude as one word in the bytes of y
+//    that the stretch's codes will occupy -- bf16: the plain cast's launch
+//    shape (256-lane blocks, one 16-element unit per lane) and 16-bit words
+//    (a bf16 magnitude); fp32: 1024-lane blocks, one 1024-element chunk per
+//    wave, 32-bit words.  The stretch is the fewest whole units / chunks
+//    whose codes hold every word;
+//  * one 1024-lane block then loads the words and, only once every lane holds
+//    its share of them, casts the stretch and the tail over them and stores
+//    the maximum at *amax.
+// No block waits at its end for an atomic on one shared word (atomics per
+// block measured 40 us against the plain cast's 31.5 on 128 MiB), and the
+// result is max |x| over every element, the same integer maximum as
+// fp8_amax's.
+constexpr int kLastThreads = 1024;
+constexpr int kPartMaxBlocksBf16 = 32768;  // 64 KiB of 16-bit words at most
+constexpr int kPartThreadsF32 = 1024;
+constexpr int kPartMaxBlocksF32 = 8192;    // 32 KiB of 32-bit words at most
+constexpr int64_t kPartSmallUnits = 8192;  // bf16: up to 131072 elements in the last block alone
+constexpr int64_t kPartSmallChunks = 64;   // fp32: up to 65536 (+ 1023) elements likewise
+
+// Block-wide max of v (TPB lanes); lane 0 passes it to store(m).
+template <int TPB, typename Store>
+__device__ __forceinline__ void block_max_then(uint32_t v, Store&& store) {
+  __shared__ uint32_t part[TPB / 64];
+  v = wave_max_u32(v);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = part[0];
+#pragma unroll
+    for (int w = 1; w < TPB / 64; ++w) m = max(m, part[w]);
+    store(m);
+  }
+}
+
+// The largest of the nwords words (W bits each, W = 16 or 32) the main cast
+// left at `words`, read as 32-bit loads, all in flight at once (at most
+// kMax words).  Every load is complete -- its value reduced into the lane's
+// register -- before the block's barrier, so that no store after it can
+// overtake a load of the same address.
+template <int W, int kMax>
+__device__ __forceinline__ uint32_t words_max(const uint32_t* words, int nwords) {
+  constexpr int kPerWord = 32 / W;
+  constexpr int kPerLane = kMax / kPerWord / kLastThreads;
+  const int nloads = (nwords + kPerWord - 1) / kPerWord;
+  uint32_t m = 0;
+  {
+    uint32_t v[kPerLane];
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) {
+      v[k] = 0u;
+      if (k * kLastThreads < nloads)  // (uniform) lanes past the last load re-read it, count 0
+        v[k] = words[min((int)threadIdx.x + k * kLastThreads, nloads - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) {
+      const int i = (int)threadIdx.x + k * kLastThreads;
+      if constexpr (W == 16) {  // the high half of the last load may lie past the last word
+        const uint32_t lo = i < nloads ? (v[k] & 0xFFFFu) : 0u;
+        const uint32_t hi = 2 * i + 1 < nwords ? (v[k] >> 16) : 0u;
+        m = max(m, max(lo, hi) << 16);  // bf16 magnitude widened to fp32 bits
+      } else {
+        m = max(m, i < nloads ? v[k] : 0u);
+      }
+    }
+  }
+  asm volatile("" : "+v"(m));  // m (hence every load) complete before the barrier
+  __syncthreads();
+  return m;
+}
+
+template <int FMT, bool NT>
+__global__ __launch_bounds__(kThreads) void cast_part_bf16_kernel(const uint4* __restrict__ x,
+                                                                  int64_t nunit, BiasArg bias,
+                                                                  uint4* __restrict__ y,
+                                                                  uint16_t* words) {
+  const uint32_t m = cast_bf16_body<FMT, NT, true>(x, nunit, bias, y, blockIdx.x, gridDim.x);
+  block_max_then<kThreads>(m, [&](uint32_t b) { words[blockIdx.x] = (uint16_t)b; });
+}
+
+// x, y: the stretch's first unit; nunit (<= kPartSmallUnits): its units.
+// The stretch's input is loaded first, all of it at once (at most
+// kLastUnits units per lane), so that its latency overlaps the words'.
+constexpr int kLastUnits = (int)(kPartSmallUnits / kLastThreads);
+static_assert(kPartMaxBlocksBf16 / 8 <= kPartSmallUnits, "the stretch fits the last block");
+
+template <int FMT, bool NT>
+__global__ __launch_bounds__(kLastThreads) void cast_last_bf16_kernel(
+    const uint4* __restrict__ x, int nunit, BiasArg bias, uint4* __restrict__ y,
+    const uint32_t* words, int nwords, const uint16_t* __restrict__ tail_x,
+    uint8_t* __restrict__ tail_y, int ntail, uint32_t* amax) {
+  const int t = (int)threadIdx.x;
+  uint4 lo[kLastUnits], hi[kLastUnits];
+#pragma unroll
+  for (int u = 0; u < kLastUnits; ++u) {
+    if (u * kLastThreads < nunit) {  // (uniform) lanes past the last unit re-read it, unused
+      const int i = min(t + u * kLastThreads, nunit - 1);
+      lo[u] = load16<NT>(&x[2 * i]);
+      hi[u] = load16<NT>(&x[2 * i + 1]);
+    }
+  }
+  const uint32_t tw = t < ntail ? tail_x[t] : 0u;
+  uint32_t m = words_max<16, kPartMaxBlocksBf16>(words, nwords);  // then the barrier
+  const int32_t b = load_bias<FMT>(bias);
+  const bool hw = kHwConvert<FMT> && b >= kHwBiasMin && b <= kHwBiasMax;
+  uint32_t bound2 = 0;
+  if constexpr (kHwConvert<FMT>) bound2 = hw_bound2<FMT>(b);
+  const float scale = __builtin_ldexpf(1.0f, hw ? -b : 0);
+  u16x2 acc = {0, 0};
+#pragma unroll
+  for (int u = 0; u < kLastUnits; ++u) {
+    const int i = t + u * kLastThreads;
+    if (i < nunit) {
+      uint4 o;
+      if constexpr (kHwConvert<FMT>)
+        o = hw ? cast_unit_hw<FMT>(lo[u], hi[u], b, bound2, scale) : cast_unit_sw<FMT>(lo[u], hi[u], b);
+      else
+        o = cast_unit_sw<FMT>(lo[u], hi[u], b);
+      y[i] = o;
+      acc = vmax_bf16(vmax_bf16(acc, lo[u]), hi[u]);
+    }
+  }
+  if (t < ntail) {
+    tail_y[t] = (uint8_t)fp8_code<FMT>(tw << 16, b);
+    acc.x = max(acc.x, (unsigned short)(tw & 0x7FFFu));
+  }
+  m = max(m, (uint32_t)max(acc.x, acc.y) << 16);
+  block_max_then<kLastThreads>(m, [&](uint32_t v) { *amax = v; });
+}
+
+template <int FMT, bool NT>
+__global__ __launch_bounds__(kPartThreadsF32) void cast_part_f32_kernel(const uint4* __restrict__ x,
+                                                                        int64_t nchunk, BiasArg bias,
+                                                                        uint32_t* __restrict__ y,
+                                                                        uint32_t* words) {
+  const uint32_t m = cast_f32_whole<FMT, NT, true, kPartThreadsF32>(x, nchunk, bias, y, nullptr,
+                                                                     nullptr, 0, blockIdx.x, gridDim.x);
+  block_max_then<kPartThreadsF32>(m, [&](uint32_t b) { words[blockIdx.x] = b; });
+}
+
+template <int FMT, bool NT>
+__global__ __launch_bounds__(kLastThreads) void cast_last_f32_kernel(
+    const uint4* __restrict__ x, int64_t nchunk, BiasArg bias, uint32_t* __restrict__ y,
+    const uint32_t* words, int nwords, const uint32_t* __restrict__ rest_x,
+    uint8_t* __restrict__ rest_y, int nrest, uint32_t* amax) {
+  uint32_t m = words_max<32, kPartMaxBlocksF32>(words, nwords);
+  m = max(m, cast_f32_whole<FMT, NT, true, kLastThreads>(x, nchunk, bias, y, rest_x, rest_y, nrest, 0, 1));
+  block_max_then<kLastThreads>(m, [&](uint32_t b) { *amax = b; });
+}
+
+// Grid size: `per_lane` units of work per lane of `lanes`-unit blocks, between
+// 1 and `cap` blocks.
+int stream_blocks_of(int64_t units, int64_t per_lane, int64_t cap, int64_t lanes) {
+  const int64_t want = (units + per_lane * lanes - 1) / (per_lane * lanes);
   return (int)(want < 1 ? 1 : (want > cap ? cap : want));
+}
+
+int stream_blocks(int64_t units, int64_t per_lane, int64_t cap) {
+  return stream_blocks_of(units, per_lane, cap, kThreads);
 }
 
 // ---------------------------------------------------------------- quantisation in one workgroup
@@ -794,20 +929,6 @@ static bool streams(const char* var) {
   return !(h && std::strcmp(h, "cached") == 0);
 }
 
-// Units of work per lane of the cast that also folds its input's amax: each
-// block ends with (at most) one atomic on the single amax word, so this
-// variant runs fewer, longer-lived blocks than the plain cast (the body loops,
-// loading the next unit during the current one).  Measured on MI355X, bias +
-// cast-with-amax against amax -> bias -> cast, 128 / 448 MiB bf16: 80 / 150 us
-// with 1 unit per lane, 57 / 142 with 16, against 65 / 187; 16 to 32 were
-// within noise of each other.  FP8LIN_CAST_AMAX_UNITS overrides it (tuning).
-constexpr int kCastAmaxUnitsPerLane = 16;
-static int cast_amax_units() {
-  const char* v = std::getenv("FP8LIN_CAST_AMAX_UNITS");
-  const int u = v ? std::atoi(v) : kCastAmaxUnitsPerLane;
-  return u < 1 ? 1 : (u > 64 ? 64 : u);
-}
-
 hipError_t launch_amax(const void* x, int dtype, int64_t n, float* amax, hipStream_t stream) {
   uint32_t* out = reinterpret_cast<uint32_t*>(amax);
   hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, out);
@@ -867,9 +988,69 @@ void with_cast_variant(int fmt, bool nt, bool amax, Fn&& fn) {
 
 static hipError_t launch_cast_from(const void* x, int dtype, int64_t n, const BiasArg& bias, int fmt,
                                    uint8_t* y, uint32_t* amax, hipStream_t stream) {
-  if (amax) hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, amax);
-  if (n <= 0) return hipGetLastError();
   const bool nt = streams("FP8LIN_CAST_HINT");
+  if (amax && n <= 0) {
+    hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, amax);
+    return hipGetLastError();
+  }
+  if (amax) {
+    // the cast with its input's amax: two launches, see cast_part_*_kernel
+    if (dtype == FP8_IN_BF16) {
+      const int64_t nunit = n / 16;
+      const int ntail = (int)(n - nunit * 16);
+      const uint16_t* tail_x = static_cast<const uint16_t*>(x) + nunit * 16;
+      uint8_t* tail_y = y + nunit * 16;
+      const uint4* xv = static_cast<const uint4*>(x);
+      uint4* yv = reinterpret_cast<uint4*>(y);
+      int64_t first = 0;  // the last block's stretch starts at this unit
+      int nwords = 0;
+      if (nunit > kPartSmallUnits) {
+        const int64_t nb0 = stream_blocks(nunit, kCastUnitsPerLane, kPartMaxBlocksBf16);
+        first = nunit - (nb0 + 7) / 8;  // 16 code bytes hold eight 16-bit words
+        nwords = stream_blocks(first, kCastUnitsPerLane, kPartMaxBlocksBf16);  // <= nb0
+      }
+      uint4* stretch = yv + first;
+      with_cast_variant(fmt, nt, false, [&](auto f, auto t, auto) {
+        constexpr int F = decltype(f)::value;
+        constexpr bool T = decltype(t)::value;
+        if (nwords > 0)
+          hipLaunchKernelGGL((cast_part_bf16_kernel<F, T>), dim3(nwords), dim3(kThreads), 0, stream,
+                             xv, first, bias, yv, reinterpret_cast<uint16_t*>(stretch));
+        hipLaunchKernelGGL((cast_last_bf16_kernel<F, T>), dim3(1), dim3(kLastThreads), 0, stream,
+                           xv + 2 * first, (int)(nunit - first), bias, stretch,
+                           reinterpret_cast<const uint32_t*>(stretch), nwords, tail_x, tail_y, ntail,
+                           amax);
+      });
+    } else {
+      const int64_t nchunk = n / kF32Chunk;
+      const int nrest = (int)(n - nchunk * kF32Chunk);
+      const uint32_t* rest_x = static_cast<const uint32_t*>(x) + nchunk * kF32Chunk;
+      uint8_t* rest_y = y + nchunk * kF32Chunk;
+      const uint4* xv = static_cast<const uint4*>(x);
+      uint32_t* yw = reinterpret_cast<uint32_t*>(y);
+      constexpr int64_t kChunksPerBlock = kPartThreadsF32 / 64;  // one per wave
+      int64_t first = 0;  // in chunks
+      int nwords = 0;
+      if (nchunk > kPartSmallChunks) {
+        const int64_t nb0 = stream_blocks_of(nchunk, 1, kPartMaxBlocksF32, kChunksPerBlock);
+        first = nchunk - (nb0 + kF32Chunk / 4 - 1) / (kF32Chunk / 4);  // a chunk's codes hold 256 words
+        nwords = stream_blocks_of(first, 1, kPartMaxBlocksF32, kChunksPerBlock);  // <= nb0
+      }
+      uint32_t* stretch = yw + first * (kF32Chunk / 4);
+      with_cast_variant(fmt, nt, false, [&](auto f, auto t, auto) {
+        constexpr int F = decltype(f)::value;
+        constexpr bool T = decltype(t)::value;
+        if (nwords > 0)
+          hipLaunchKernelGGL((cast_part_f32_kernel<F, T>), dim3(nwords), dim3(kPartThreadsF32), 0,
+                             stream, xv, first, bias, yw, stretch);
+        hipLaunchKernelGGL((cast_last_f32_kernel<F, T>), dim3(1), dim3(kLastThreads), 0, stream,
+                           xv + first * (kF32Chunk / 4), nchunk - first, bias, stretch, stretch, nwords,
+                           rest_x, rest_y, nrest, amax);
+      });
+    }
+    return hipGetLastError();
+  }
+  if (n <= 0) return hipGetLastError();
   if (dtype == FP8_IN_BF16) {
     // 16-element units, one per lane; the last n % 16 elements by block 0
     const int64_t nunit = n / 16;
@@ -878,11 +1059,10 @@ static hipError_t launch_cast_from(const void* x, int dtype, int64_t n, const Bi
     uint4* yv = reinterpret_cast<uint4*>(y);
     const uint16_t* tail_x = static_cast<const uint16_t*>(x) + nunit * 16;
     const uint4* xv = static_cast<const uint4*>(x);
-    const dim3 grid(stream_blocks(nunit, amax ? cast_amax_units() : kCastUnitsPerLane, kCastMaxBlocks));
-    with_cast_variant(fmt, nt, amax != nullptr, [&](auto f, auto t, auto a) {
-      hipLaunchKernelGGL((cast_bf16_kernel<decltype(f)::value, decltype(t)::value, decltype(a)::value>),
-                         grid, dim3(kThreads), 0, stream, xv, nunit, bias, yv, tail_x, tail_y, ntail,
-                         amax);
+    const dim3 grid(stream_blocks(nunit, kCastUnitsPerLane, kCastMaxBlocks));
+    with_cast_variant(fmt, nt, false, [&](auto f, auto t, auto) {
+      hipLaunchKernelGGL((cast_bf16_kernel<decltype(f)::value, decltype(t)::value>),
+                         grid, dim3(kThreads), 0, stream, xv, nunit, bias, yv, tail_x, tail_y, ntail);
     });
   } else {
     const int64_t nchunk = n / kF32Chunk;
@@ -891,15 +1071,13 @@ static hipError_t launch_cast_from(const void* x, int dtype, int64_t n, const Bi
     uint8_t* rest_y = y + nchunk * kF32Chunk;
     uint32_t* yw = reinterpret_cast<uint32_t*>(y);
     const uint4* xv = static_cast<const uint4*>(x);
-    // one chunk per wave (cast_amax_units() with the amax), four waves per
-    // block, at least one block (the rest)
-    const int64_t per_block = (int64_t)(kThreads / 64) * (amax ? cast_amax_units() : 1);
+    // one chunk per wave, four waves per block, at least one block (the rest)
+    const int64_t per_block = kThreads / 64;
     const int64_t want = (nchunk + per_block - 1) / per_block;
     const dim3 grid((uint32_t)(want < 1 ? 1 : (want > kCastMaxBlocks ? kCastMaxBlocks : want)));
-    with_cast_variant(fmt, nt, amax != nullptr, [&](auto f, auto t, auto a) {
-      hipLaunchKernelGGL((cast_f32_kernel<decltype(f)::value, decltype(t)::value, decltype(a)::value>),
-                         grid, dim3(kThreads), 0, stream, xv, nchunk, bias, yw, rest_x, rest_y, nrest,
-                         amax);
+    with_cast_variant(fmt, nt, false, [&](auto f, auto t, auto) {
+      hipLaunchKernelGGL((cast_f32_kernel<decltype(f)::value, decltype(t)::value>),
+                         grid, dim3(kThreads), 0, stream, xv, nchunk, bias, yw, rest_x, rest_y, nrest);
     });
   }
   return hipGetLastError();

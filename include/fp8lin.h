@@ -31,8 +31,7 @@
  *  - Tuning only (read at each call, never needed for correct results):
  *    FP8LIN_GEMM_TILE=128|256 forces the products' tile, FP8LIN_EXACT_MFMA=
  *    f16|bf16 the 16-bit MFMA of the exact arithmetic, FP8LIN_AMAX_HINT /
- *    FP8LIN_CAST_HINT=cached ordinary instead of streaming loads, and
- *    FP8LIN_CAST_AMAX_UNITS=n the units per lane of fp8_scale_cast_amax,
+ *    FP8LIN_CAST_HINT=cached ordinary instead of streaming loads,
  *    FP8LIN_QUANT_SMALL=n the largest tensor (elements) fp8_quantize does in
  *    one workgroup, and FP8LIN_SPLIT_SLOTS=n the workgroup slots the split of
  *    fp8_scaled_gemm_ws plans for (256; it also changes the workspace size).
@@ -146,9 +145,12 @@ int fp8_quantize(const void* x, fp8_dtype_t dtype, int64_t n, fp8_format_t fmt, 
  * input once (3 bytes per bf16 element instead of amax + cast's 5).
  *   x_amax  device, one float, 4-byte aligned, written: bit-identical to
  *           fp8_amax over x (0 for n == 0).
- * The codes are those of fp8_scale_cast.  Launches a one-lane clear of
- * x_amax, then the cast.  Returns FP8_ERR_NULL / FP8_ERR_ALIGN for a null or
- * misaligned x_amax, otherwise as fp8_scale_cast.
+ * The codes are those of fp8_scale_cast.  Two launches and no atomics: the
+ * cast of all but a last stretch of x, each workgroup leaving its largest
+ * magnitude as a word in the code bytes of that stretch, then one workgroup
+ * that reduces those words and casts the stretch over them (one launch of one
+ * workgroup alone for inputs up to 256 KiB).  Returns FP8_ERR_NULL /
+ * FP8_ERR_ALIGN for a null or misaligned x_amax, otherwise as fp8_scale_cast.
  */
 int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32_t* bias,
                         fp8_format_t fmt, uint8_t* y, float* x_amax, void* stream);

@@ -164,7 +164,13 @@ def test_workload_tensors_bit_exact(fl, wl):
         got = codes.cpu().numpy().reshape(-1)
         ref = oracle.scale_cast(words.reshape(-1), b_ref, t.fmt)
         assert np.array_equal(got, ref), f"{t.name}: {np.count_nonzero(got != ref)} codes differ"
-        del codes, x
+        # the cast that folds its own input's amax, with the bias just derived
+        say("workload", wl, t.name, "fused cast + amax")
+        am = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+        fused = fl.scale_cast(x.cuda(), bias, t.fmt, amax=am).cpu().numpy().reshape(-1)
+        assert int(words_of(am)[0]) == a_ref, t.name
+        assert np.array_equal(fused, ref), f"{t.name}: {np.count_nonzero(fused != ref)} fused codes differ"
+        del codes, x, fused
 
 
 @pytest.mark.parametrize("wl", [1, 3, 5])
@@ -305,6 +311,56 @@ def test_cast_with_fused_amax(fl, dtype):
     assert fl.lib.fp8_scale_cast_amax(None, 0, 0, None, 0, None, am.data_ptr(), None) == 0
     torch.cuda.synchronize()
     assert am.item() == 0.0
+
+
+def _fused_seams(dtype, n):
+    """Element indices at the seams of fp8_scale_cast_amax's two launches for
+    an n-element input: the first element, the main cast's last, the last
+    workgroup's stretch's first and last, and the tail's last.  The main cast
+    runs one bf16 unit (16 elements) per lane of 256-lane workgroups, or one
+    fp32 chunk (1024 elements) per wave of 16-wave workgroups, and each of its
+    workgroups leaves one word (16 / 32 bits) in the codes of the stretch: the
+    fewest whole units / chunks that hold them all.  Inputs up to 8192 units /
+    64 chunks go to the last workgroup alone."""
+    size, small, per_block, words_per, cap = ((16, 8192, 256, 8, 32768) if dtype == "bf16"
+                                              else (1024, 64, 16, 256, 8192))
+    units = n // size
+    if units <= small:
+        first = 0
+    else:
+        nb0 = min(cap, -(-units // per_block))
+        first = units - -(-nb0 // words_per)
+    idx = {0, max(first * size - 1, 0), first * size, units * size - 1, n - 1}
+    return sorted(i for i in idx if 0 <= i < n)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_cast_with_fused_amax_at_its_seams(fl, dtype):
+    """fp8_scale_cast_amax casts all but a last stretch of its input in one
+    launch, each workgroup leaving its largest magnitude as a word in the code
+    bytes of that stretch, then one workgroup reduces the words and casts the
+    stretch over them.  Sizes on both sides of the one-workgroup limit, the
+    largest magnitude or a NaN planted at each seam: codes and amax bit-exact."""
+    rng = np.random.default_rng(29)
+    sizes = (131072, 131072 + 3, 8193 * 16 + 3, 5_000_003) if dtype == "bf16" else \
+        (65536 + 1023, 65 * 1024 + 7, 3_000_017)
+    for n in sizes:
+        v = (rng.standard_normal(n) * 3).astype(np.float32)
+        if dtype == "bf16":
+            base = synth.bf16_words(synth.to_bf16(v)).copy()
+            big, nan, dev = np.uint16(0xC700), np.uint16(0x7FC0), bf16_dev   # -32768, NaN
+        else:
+            base = v.view(np.uint32).copy()
+            big, nan, dev = np.uint32(0xC7000000), np.uint32(0x7FC00000), f32_dev
+        for i in _fused_seams(dtype, n):
+            for plant, val in (("largest", big), ("NaN", nan)):
+                w = base.copy()
+                w[i] = val
+                say("cast+amax seams", dtype, n, plant, "at", i)
+                am = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+                got = fl.scale_cast(dev(w), i32_dev(-8), E4M3, amax=am).cpu().numpy()
+                assert int(words_of(am)[0]) == oracle.amax_bits(w), (n, plant, i)
+                assert np.array_equal(got, oracle.scale_cast(w, -8, E4M3)), (n, plant, i)
 
 
 def test_delayed_scaling_with_the_fused_cast(fl):
