@@ -182,9 +182,9 @@ def epilogue_amax(fl, w, plan, q, outs, math, op_of, reps=9):
 
 
 def delayed_quant(fl, w, plan, q, x, reps=9):
-    """Delayed scaling on the step's in-step tensors: the cast with the amax of
-    its own input folded in (fp8_scale_cast_amax) after a bias from the amax a
-    previous call returned, against the current-step chain amax -> bias ->
+    """Delayed scaling on the step's in-step tensors: one fp8_quantize_delayed
+    call (the bias from the amax a previous call left, the cast, and its own
+    input's amax folded in), against the current-step chain amax -> bias ->
     cast; each timed alone with HIP events, interleaved, median of `reps`.
     A 200 us spin kernel leads each timing, so that the host's argument
     checks and launches are done before the start event fires: the events
@@ -216,8 +216,7 @@ def delayed_quant(fl, w, plan, q, x, reps=9):
         for _ in range(reps):
             chain.append(once(lambda: (fl.amax(x[n], out=amax), fl.compute_bias(amax, fmt, margin, out=bias),
                                        fl.scale_cast(x[n], bias, fmt, out=codes))))
-            fused.append(once(lambda: (fl.compute_bias(prev, fmt, margin, out=bias),
-                                       fl.scale_cast(x[n], bias, fmt, out=codes, amax=prev))))
+            fused.append(once(lambda: fl.quantize_delayed(x[n], fmt, prev, margin, out=codes, bias=bias)))
         tc, tf = statistics.median(chain), statistics.median(fused)
         k = x[n].numel()
         per[n] = {"chain_us": round(tc * 1e3, 1), "fused_us": round(tf * 1e3, 1),
@@ -226,8 +225,8 @@ def delayed_quant(fl, w, plan, q, x, reps=9):
     if not per:
         return None
     gbs = 3.0 * elems / (t_fused * 1e-3) / 1e9
-    return {"method": f"bias from the previous call's amax + cast with its input's amax folded in "
-                      f"(3 B per element) vs amax -> bias -> cast (5 B); each alone, warm, HIP "
+    return {"method": f"fp8_quantize_delayed: bias from the previous call's amax, cast, its input's "
+                      f"amax folded in (3 B per element) vs amax -> bias -> cast (5 B); each alone, warm, HIP "
                       f"events after a spin that covers the host's launches, median of {reps}",
             "chain_us": round(t_chain * 1e3, 1), "fused_us": round(t_fused * 1e3, 1),
             "fused_gbs": round(gbs, 1), "fused_frac": round(gbs / PEAK_HBM_GBS, 4),

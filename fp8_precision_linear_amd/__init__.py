@@ -49,6 +49,7 @@ SIGNATURES = {
     "fp8_scale_cast_amax": (_ci, [_vp, _ci, _i64, _vp, _ci, _vp, _vp, _vp]),
     "fp8_quantize": (_ci, [_vp, _ci, _i64, _ci, _i32, _vp, _vp, _vp, _vp]),
     "fp8_quantize_multi": (_ci, [_vp, _i32, _vp]),
+    "fp8_quantize_delayed": (_ci, [_vp, _ci, _i64, _ci, _i32, _vp, _vp, _vp, _vp]),
     "fp8_scaled_gemm": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_amax": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "fp8_scaled_gemm_workspace_bytes": (_i64, [_ci, _i64, _i64, _i64]),
@@ -247,6 +248,26 @@ def quantize(x, fmt, margin=0, out=None, bias=None, amax=None, stream=None):
     _check("fp8_quantize", lib.fp8_quantize(_ptr(x), dt, x.numel(), int(fmt), int(margin),
                                             _ptr(out), _ptr(amax), _ptr(bias), _stream(stream)))
     return out, bias, amax
+
+
+def quantize_delayed(x, fmt, amax, margin=0, out=None, bias=None, stream=None):
+    """Delayed scaling in one call (fp8_quantize_delayed): the bias from the
+    amax the previous step left in `amax` (float32[1] device tensor), the codes
+    at that bias, then max |x| of this input into `amax` for the next step.
+    Returns (codes, bias); out / bias: optional preallocated device tensors."""
+    dt = _input(x)
+    _need_kind(amax, "amax", torch.float32, numel=1)
+    if out is not None:
+        _need_kind(out, "out", torch.uint8, numel=x.numel())
+    if bias is not None:
+        _need_kind(bias, "bias", torch.int32, numel=1)
+    _places(x.device, (x, "x"), (amax, "amax"), (out, "out"), (bias, "bias"))
+    out = _empty(x.shape, torch.uint8, x.device, stream) if out is None else out
+    bias = _empty(1, torch.int32, x.device, stream) if bias is None else bias
+    _check("fp8_quantize_delayed",
+           lib.fp8_quantize_delayed(_ptr(x), dt, x.numel(), int(fmt), int(margin), _ptr(out),
+                                    _ptr(amax), _ptr(bias), _stream(stream)))
+    return out, bias
 
 
 class QuantizeMulti:

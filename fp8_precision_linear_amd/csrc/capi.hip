@@ -190,6 +190,14 @@ int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32
                                         reinterpret_cast<uint32_t*>(x_amax), (hipStream_t)stream));
 }
 
+int fp8_quantize_delayed(const void* x, fp8_dtype_t dtype, int64_t n, fp8_format_t fmt,
+                         int32_t margin, uint8_t* y, float* amax, int32_t* bias, void* stream) {
+  if (int s = quantize_checks(x, dtype, n, fmt, margin, y, amax, bias)) return s;
+  if (int s = device_ok()) return s;
+  return hip_status(fp8lin::launch_quantize_delayed(x, dtype, n, fmt, margin, y, amax, bias,
+                                                    (hipStream_t)stream));
+}
+
 }  // extern "C"
 
 namespace {

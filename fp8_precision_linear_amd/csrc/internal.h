@@ -23,6 +23,12 @@ hipError_t launch_clear_u32(uint32_t* p, hipStream_t stream);
 hipError_t launch_quantize(const void* x, int dtype, int64_t n, int fmt, int32_t margin, uint8_t* y,
                            float* amax, int32_t* bias, hipStream_t stream);
 
+// Delayed scaling in one call (fp8_quantize_delayed): the bias from the amax
+// word (the previous step's), the cast, then max |x| of this input into the
+// same word; two launches (one for small tensors).
+hipError_t launch_quantize_delayed(const void* x, int dtype, int64_t n, int fmt, int32_t margin,
+                                   uint8_t* y, float* amax, int32_t* bias, hipStream_t stream);
+
 // The quantisation of several tensors (fp8_quantize_multi): one launch per 32
 // small tensors (one workgroup each), three launches per 32 others; every
 // tensor's results those of launch_quantize on it alone.

@@ -204,6 +204,13 @@ __global__ void bias_kernel(const uint32_t* __restrict__ amax, int fmt, int32_t 
   *bias = bias_from_amax_bits(*amax, fmt, margin);
 }
 
+// Delayed scaling of an empty tensor: the bias from the previous amax, then
+// the amax of nothing (0).
+__global__ void delayed_empty_kernel(uint32_t* amax, int fmt, int32_t margin, int32_t* bias) {
+  *bias = bias_from_amax_bits(*amax, fmt, margin);
+  *amax = 0u;
+}
+
 // Where a cast takes its bias from: the int32 at `bias`, or -- the whole
 // quantisation in one call -- the amax word the amax kernel just wrote, turned
 // into the bias in every block exactly as bias_kernel does; lane 0 of block 0
@@ -554,7 +561,10 @@ __global__ __launch_bounds__(kThreads) void cast_f32_kernel(const uint4* __restr
 // No block waits at its end for an atomic on one shared word (atomics per
 // block measured 40 us against the plain cast's 31.5 on 128 MiB), and the
 // result is max |x| over every element, the same integer maximum as
-// fp8_amax's.
+// fp8_amax's.  With delayed scaling in one call the bias comes from the amax
+// word itself (the previous step's): every block of both launches derives it
+// from that word, and only the last block overwrites the word, at its very
+// end, after a barrier that every lane reaches with the bias derived.
 constexpr int kLastThreads = 1024;
 constexpr int kPartMaxBlocksBf16 = 32768;  // 64 KiB of 16-bit words at most
 constexpr int kPartThreadsF32 = 1024;
@@ -619,6 +629,7 @@ __global__ __launch_bounds__(kThreads) void cast_part_bf16_kernel(const uint4* _
                                                                   uint4* __restrict__ y,
                                                                   uint16_t* words) {
   const uint32_t m = cast_bf16_body<FMT, NT, true>(x, nunit, bias, y, blockIdx.x, gridDim.x);
+  store_derived_bias<FMT>(bias, blockIdx.x);
   block_max_then<kThreads>(m, [&](uint32_t b) { words[blockIdx.x] = (uint16_t)b; });
 }
 
@@ -646,6 +657,7 @@ __global__ __launch_bounds__(kLastThreads) void cast_last_bf16_kernel(
   const uint32_t tw = t < ntail ? tail_x[t] : 0u;
   uint32_t m = words_max<16, kPartMaxBlocksBf16>(words, nwords);  // then the barrier
   const int32_t b = load_bias<FMT>(bias);
+  store_derived_bias<FMT>(bias, 0);
   const bool hw = kHwConvert<FMT> && b >= kHwBiasMin && b <= kHwBiasMax;
   uint32_t bound2 = 0;
   if constexpr (kHwConvert<FMT>) bound2 = hw_bound2<FMT>(b);
@@ -669,6 +681,7 @@ __global__ __launch_bounds__(kLastThreads) void cast_last_bf16_kernel(
     acc.x = max(acc.x, (unsigned short)(tw & 0x7FFFu));
   }
   m = max(m, (uint32_t)max(acc.x, acc.y) << 16);
+  __builtin_amdgcn_s_waitcnt(0);  // every load of this wave (the amax word's too) has returned
   block_max_then<kLastThreads>(m, [&](uint32_t v) { *amax = v; });
 }
 
@@ -689,6 +702,7 @@ __global__ __launch_bounds__(kLastThreads) void cast_last_f32_kernel(
     uint8_t* __restrict__ rest_y, int nrest, uint32_t* amax) {
   uint32_t m = words_max<32, kPartMaxBlocksF32>(words, nwords);
   m = max(m, cast_f32_whole<FMT, NT, true, kLastThreads>(x, nchunk, bias, y, rest_x, rest_y, nrest, 0, 1));
+  __builtin_amdgcn_s_waitcnt(0);  // every load of this wave (the amax word's too) has returned
   block_max_then<kLastThreads>(m, [&](uint32_t b) { *amax = b; });
 }
 
@@ -990,7 +1004,11 @@ static hipError_t launch_cast_from(const void* x, int dtype, int64_t n, const Bi
                                    uint8_t* y, uint32_t* amax, hipStream_t stream) {
   const bool nt = streams("FP8LIN_CAST_HINT");
   if (amax && n <= 0) {
-    hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, amax);
+    if (bias.amax)
+      hipLaunchKernelGGL(delayed_empty_kernel, dim3(1), dim3(1), 0, stream, amax, fmt, bias.margin,
+                         bias.bias_out);
+    else
+      hipLaunchKernelGGL(amax_clear_kernel, dim3(1), dim3(1), 0, stream, amax);
     return hipGetLastError();
   }
   if (amax) {
@@ -1081,6 +1099,12 @@ static hipError_t launch_cast_from(const void* x, int dtype, int64_t n, const Bi
     });
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_delayed(const void* x, int dtype, int64_t n, int fmt, int32_t margin,
+                                   uint8_t* y, float* amax, int32_t* bias, hipStream_t stream) {
+  uint32_t* a = reinterpret_cast<uint32_t*>(amax);
+  return launch_cast_from(x, dtype, n, BiasArg{nullptr, a, bias, margin}, fmt, y, a, stream);
 }
 
 hipError_t launch_cast(const void* x, int dtype, int64_t n, const int32_t* bias, int fmt,

@@ -156,6 +156,24 @@ int fp8_scale_cast_amax(const void* x, fp8_dtype_t dtype, int64_t n, const int32
                         fp8_format_t fmt, uint8_t* y, float* x_amax, void* stream);
 
 /*
+ * Delayed scaling of one tensor in one call ("Proposed method", bullets 1-2,
+ * with the scale taken from the previous step's amax): bias =
+ * fp8_compute_bias(amax, fmt, margin) from the amax the previous step left in
+ * *amax, the cast at that bias (codes as fp8_scale_cast), and then max |x| of
+ * this input into *amax for the next step -- fp8_compute_bias followed by
+ * fp8_scale_cast_amax, bit for bit, without the bias's own launch.
+ *   amax  device, one float, 4-byte aligned: read (the previous step's amax;
+ *         0 gives bias 0), then overwritten with max |x| (as fp8_amax).
+ *   bias  device, one int32, 4-byte aligned, written with the bias used.
+ *   x, y, margin as for fp8_quantize.
+ * Two launches, as fp8_scale_cast_amax (one for inputs up to 256 KiB); every
+ * workgroup derives the bias from *amax, which only the last one overwrites,
+ * at its end.  n == 0 writes the bias and amax = 0.  Errors as fp8_quantize.
+ */
+int fp8_quantize_delayed(const void* x, fp8_dtype_t dtype, int64_t n, fp8_format_t fmt,
+                         int32_t margin, uint8_t* y, float* amax, int32_t* bias, void* stream);
+
+/*
  * fp8_quantize_multi: fp8_quantize of several tensors in one call -- the
  * per-tensor amax, bias and cast of "Proposed method", bullets 1-4, for each
  * tensor on its own -- so that a step that quantises many tensors (a layer's

@@ -31,7 +31,7 @@ def status(code):
 
 def test_every_declared_function_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(L, n), n
         assert n in fl.SIGNATURES, n
@@ -263,6 +263,29 @@ def test_scale_cast_amax_without_a_device_reports_no_device():
     assert L.fp8_scale_cast_amax(None, 0, 0, None, 0, None, A16, None) == status("FP8_ERR_DEVICE")
     assert L.fp8_scale_cast_amax(A16, 0, 5, A32, 2, A48, A16, None) == status("FP8_ERR_DEVICE")
 
+
+
+def test_quantize_delayed_argument_checks():
+    f = L.fp8_quantize_delayed
+    assert f(A16, 0, -1, 0, 0, A48, A32, A32, None) == status("FP8_ERR_SIZE")
+    assert f(A16, 2, 10, 0, 0, A48, A32, A32, None) == status("FP8_ERR_DTYPE")
+    assert f(A16, 0, 10, 3, 0, A48, A32, A32, None) == status("FP8_ERR_FORMAT")
+    assert f(A16, 0, 10, 0, 65, A48, A32, A32, None) == status("FP8_ERR_MARGIN")
+    assert f(None, 0, 10, 0, 0, A48, A32, A32, None) == status("FP8_ERR_NULL")
+    assert f(A16, 0, 10, 0, 0, None, A32, A32, None) == status("FP8_ERR_NULL")
+    assert f(A16, 0, 10, 0, 0, A48, None, A32, None) == status("FP8_ERR_NULL")
+    assert f(A16, 0, 10, 0, 0, A48, A32, None, None) == status("FP8_ERR_NULL")
+    assert f(MIS, 0, 10, 0, 0, A48, A32, A32, None) == status("FP8_ERR_ALIGN")
+    assert f(A16, 0, 10, 0, 0, MIS, A32, A32, None) == status("FP8_ERR_ALIGN")
+    assert f(A16, 0, 10, 0, 0, A48, P(18), A32, None) == status("FP8_ERR_ALIGN")
+    assert f(A16, 0, 10, 0, 0, A48, A32, P(18), None) == status("FP8_ERR_ALIGN")
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
+def test_quantize_delayed_without_a_device_reports_no_device():
+    # n == 0 still writes the bias and clears the amax
+    assert L.fp8_quantize_delayed(None, 0, 0, 0, 0, None, A16, A32, None) == status("FP8_ERR_DEVICE")
+    assert L.fp8_quantize_delayed(A16, 0, 5, 0, 0, A48, A16, A32, None) == status("FP8_ERR_DEVICE")
 
 
 def test_quantize_argument_checks():

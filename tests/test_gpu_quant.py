@@ -387,6 +387,61 @@ def test_delayed_scaling_with_the_fused_cast(fl):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_quantize_delayed(fl, dtype):
+    """fp8_quantize_delayed: the bias from the amax word the previous step left
+    (zero, normal, subnormal, inf and NaN amaxes at three margins), the codes
+    at that bias, and this input's amax written over the word; every result
+    bit-exact against the oracle, on sizes on both sides of the one-workgroup
+    limit, at the two launches' seams, every format; n == 0 too."""
+    rng = np.random.default_rng(31)
+    prev_words = [0x0, 0x3F800000, 0x43E00000, 0x00000100, 0x7F800000, 0x7FC00000, 0x38000000]
+    sizes = (17, 131072, 8193 * 16 + 3, 1_000_003) if dtype == "bf16" else (17, 65536 + 1023, 65 * 1024 + 7, 1_000_003)
+    for n in sizes:
+        v = (rng.standard_normal(n) * 9).astype(np.float32)
+        if dtype == "bf16":
+            words = synth.bf16_words(synth.to_bf16(v)).copy()
+            x = bf16_dev(words)
+        else:
+            words = v.view(np.uint32).copy()
+            x = f32_dev(words)
+        a_ref = oracle.amax_bits(words)
+        for k, pw in enumerate(prev_words):
+            fmt, margin = ALL_FMTS[k % 3], (-2, 0, 3)[k % 3]
+            say("quantize_delayed", dtype, n, "prev amax", hex(pw), "fmt", fmt, "margin", margin)
+            am = torch.from_numpy(np.array([pw], dtype=np.uint32).view(np.float32)).cuda()
+            codes, bias = fl.quantize_delayed(x, fmt, am, margin)
+            b_ref = oracle.compute_bias(pw, fmt, margin)
+            assert int(bias.item()) == b_ref, (n, hex(pw), fmt, margin)
+            assert np.array_equal(codes.cpu().numpy(), oracle.scale_cast(words, b_ref, fmt)), (n, hex(pw), fmt)
+            assert int(words_of(am)[0]) == a_ref, (n, hex(pw), fmt)
+    # n == 0: the bias from the previous amax, and the amax of nothing
+    am = torch.full((1,), 3.0, dtype=torch.float32, device="cuda")
+    bias = torch.full((1,), 99, dtype=torch.int32, device="cuda")
+    assert fl.lib.fp8_quantize_delayed(None, 0, 0, E5M2, 1, None, am.data_ptr(), bias.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert am.item() == 0.0 and int(bias.item()) == oracle.compute_bias(0x40400000, E5M2, 1)
+
+
+def test_delayed_scaling_in_one_call(fl):
+    """A six-step delayed-scaling schedule through fp8_quantize_delayed alone:
+    step t's bias from step t-1's amax (the word starts at 0: bias 0), the
+    same codes, biases and amaxes as the oracle's schedule."""
+    rng = np.random.default_rng(37)
+    am = torch.zeros(1, dtype=torch.float32, device="cuda")
+    prev_bits = 0
+    for t, sc in enumerate([1.0, 3.0, 0.25, 40.0, 40.0, 1e-3]):
+        v = (rng.standard_normal(300_001) * sc).astype(np.float32)
+        words = synth.bf16_words(synth.to_bf16(v)).copy()
+        say("delayed scaling in one call, step", t)
+        codes, bias = fl.quantize_delayed(bf16_dev(words), E5M2, am, 0)
+        b_ref = oracle.compute_bias(prev_bits, E5M2, 0)
+        assert int(bias.item()) == b_ref, t
+        assert np.array_equal(codes.cpu().numpy(), oracle.scale_cast(words, b_ref, E5M2)), t
+        prev_bits = oracle.amax_bits(words)
+        assert int(words_of(am)[0]) == prev_bits, t
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_degenerate_tensors(fl, dtype):
     """Tensors the method meets at its edges: all +0, all -0, mixed zeros,
     all NaN, all inf, one NaN among zeros, a constant, a single element, only
