@@ -20,9 +20,10 @@ Scaling modes (ScalingState):
     tensor itself, as the method states (one fp8_quantize call, which makes
     them in one launch for small tensors and three for large ones);
   * "delayed": the bias of a tensor comes from the amax its previous step's
-    cast returned, and the cast (fp8_scale_cast_amax) returns this step's
-    amax in the same pass, so each quantisation reads its input once; the
-    first step of each tensor uses "current".  Values beyond the previous
+    quantisation returned, and the cast returns this step's amax in the same
+    pass (one fp8_quantize_delayed call, which overwrites the previous amax
+    with the new one), so each quantisation reads its input once; the first
+    step of each tensor uses "current".  Values beyond the previous
     step's scale saturate: the pages' delayed / infrequent bias update trades
     that for the skipped amax pass.
 Every bias is logged per tensor (BiasLog), without a host synchronisation.
@@ -31,8 +32,8 @@ quantises the weight once; later calls reuse its codes and bias.
 """
 import torch
 
-from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, compute_bias, quantize,
-               scale_cast, scaled_gemm_auto)
+from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, quantize, quantize_delayed,
+               scaled_gemm_auto)
 from .mlp import BiasLog
 
 ROLES = ("x", "w", "dy")
@@ -71,9 +72,8 @@ class ScalingState:
         fmt, margin = FORMATS[role], self.margins[role]
         prev = self.amax.get(role)
         if self.mode == "delayed" and prev is not None:
-            bias = compute_bias(prev, fmt, margin)
-            amax = torch.empty(1, dtype=torch.float32, device=t.device)
-            codes = scale_cast(t, bias, fmt, amax=amax)
+            codes, bias = quantize_delayed(t, fmt, prev, margin)  # prev now holds this step's amax
+            amax = prev
         else:
             codes, bias, amax = quantize(t, fmt, margin)
         self.amax[role] = amax
