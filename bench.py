@@ -470,9 +470,11 @@ def record_traffic(d, out=None):
         "source_sha256": sources_sha(GEMM_SOURCES),
         "commands": [
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/fetch -o run -- "
-            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax --no-delayed --no-graph",
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax --no-graph "
+            "--no-per-config --no-native",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/write -o run -- "
-            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax --no-delayed --no-graph",
+            "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax --no-graph "
+            "--no-per-config --no-native",
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/copy_fetch -o run -- "
             "python3 bench.py --copy-calibration",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/copy_write -o run -- "
@@ -484,6 +486,69 @@ def record_traffic(d, out=None):
     with open(out, "w") as fh:
         json.dump(rec, fh, indent=1)
     print(json.dumps(rec), flush=True)
+    table = hbm_table(rows("fetch"), rows("write"), f_factor, w_factor)
+    with open(os.path.join(os.path.dirname(out), "quant_gemm_llama70b_infer_hbm_bytes.txt"), "w") as fh:
+        fh.write(table)
+    print(table, flush=True)
+
+
+def hbm_table(fetch_rows, write_rows, f_factor, w_factor):
+    """Per-kernel HBM bytes of the library's dispatches in the counter runs:
+    median over the dispatches of one kernel and grid (the products one row
+    per product of the step, by their order in it), scaled by the copy
+    calibration."""
+    import re
+    import statistics
+
+    def per_dispatch(rs, counter):
+        vals = {}
+        for r in rs:
+            if r["Counter_Name"] == counter and "fp8lin" in r["Kernel_Name"]:
+                v = vals.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], int(r["Grid_Size"]), 0.0])
+                v[2] += float(r["Counter_Value"])
+        return vals
+
+    def short(k):
+        m = re.search(r"(\w+)(<[^(]*>)?\(", k.replace("(anonymous namespace)::", ""))
+        return (m.group(1) + (m.group(2) or "")) if m else k
+
+    f, wr = per_dispatch(fetch_rows, "FETCH_SIZE"), per_dispatch(write_rows, "WRITE_SIZE")
+    groups, order, nth_gemm = {}, [], 0
+    products = ("qkv", "o", "gate", "up", "down")
+    for d in sorted(f):
+        name, grid, v = f[d]
+        key = (short(name), grid)
+        if "gemm_pp_kernel" in name or "gemm_quad_kernel" in name:
+            key = (short(name) + " " + products[nth_gemm % 5], grid)
+            nth_gemm += 1
+        if key not in groups:
+            groups[key] = []
+            order.append(key)
+        groups[key].append((v * 1024.0 * f_factor / 1e6, wr.get(d, [0, 0, float("nan")])[2] * 1024.0 * w_factor / 1e6))
+    lines = [
+        "HBM-side bytes per dispatch of the library's kernels (rocprofv3 FETCH_SIZE and WRITE_SIZE,",
+        f"KiB per dispatch, scaled by the plain-copy calibration: x{f_factor:.4f} for FETCH_SIZE,",
+        f"x{w_factor:.4f} for WRITE_SIZE), Llama-2-70B-shaped inference workload (8192 tokens): the",
+        "timed steps (one fp8_quantize_multi + the five products), the separate-calls event pass",
+        "(fp8_amax / fp8_compute_bias / fp8_scale_cast per tensor) and the delayed-scaling timings",
+        "(fp8_quantize_delayed per tensor), and the weights' one-time quantisation at set-up.",
+        "Median over the dispatches of each kernel and grid.",
+        "One MI355X.",
+        "",
+        "Commands (from /tmp, TMPDIR=/tmp), then python3 bench.py --record-traffic <DIR>:",
+        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/fetch -o run -- python3 bench.py --steps 2 "
+        "--warmup 1 --no-cpu-baseline --no-cold --no-epilogue-amax --no-graph --no-per-config --no-native",
+        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/write -o run -- (the same)",
+        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/copy_fetch -o run -- python3 bench.py --copy-calibration",
+        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/copy_write -o run -- python3 bench.py --copy-calibration",
+        "",
+        f"{'kernel':46s} {'grid':>9s} {'dispatches':>10s} {'read MB':>9s} {'written MB':>10s}",
+    ]
+    for key in order:
+        v = groups[key]
+        lines.append(f"{key[0][:46]:46s} {key[1]:9d} {len(v):10d} {statistics.median(a for a, _ in v):9.1f} "
+                     f"{statistics.median(b for _, b in v):10.1f}")
+    return "\n".join(lines) + "\n"
 
 
 def cpu_baseline(w, host, rows, cols, results=None):
