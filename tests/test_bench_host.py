@@ -14,7 +14,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
-FIELDS = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+FIELDS = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
 GEMM = "void fp8lin::gemm_detail::gemm_pp_kernel<true, true, 0, 0, 0>(fp8lin::GemmProblem, int, int)"
 OTHER = "void fp8lin::(anonymous namespace)::amax_bf16_kernel<true>(HIP_vector_type<unsigned int, 4u> const*)"
 COPY = "__amd_rocclr_copyBuffer"
@@ -27,7 +27,8 @@ def write_csv(d, sub, rows):
         w.writeheader()
         for i, (kernel, counter, value) in enumerate(rows):
             w.writerow({"Correlation_Id": i + 1, "Dispatch_Id": i + 1, "Kernel_Name": kernel,
-                        "Counter_Name": counter, "Counter_Value": value})
+                        "Grid_Size": 512 if kernel == GEMM else 256, "Counter_Name": counter,
+                        "Counter_Value": value})
 
 
 def test_more_than_one_gpu_is_refused():
@@ -45,10 +46,11 @@ def test_traffic_record_from_counter_csvs(tmp_path):
     # the copy: FETCH_SIZE reads half the copied bytes, WRITE_SIZE all of them
     write_csv(d, "copy_fetch", [(COPY, "FETCH_SIZE", copy_kib / 2), (COPY, "FETCH_SIZE", 1.0)])
     write_csv(d, "copy_write", [(COPY, "WRITE_SIZE", copy_kib)])
-    # three product dispatches among other kernels (ignored)
+    # three product dispatches after another kernel (ignored by the record);
+    # the two runs are the same program, so their dispatch ids match
     write_csv(d, "fetch", [(OTHER, "FETCH_SIZE", 5e6), (GEMM, "FETCH_SIZE", 1000.0),
                            (GEMM, "FETCH_SIZE", 2000.0), (GEMM, "FETCH_SIZE", 3000.0)])
-    write_csv(d, "write", [(GEMM, "WRITE_SIZE", 400.0), (OTHER, "WRITE_SIZE", 7.0),
+    write_csv(d, "write", [(OTHER, "WRITE_SIZE", 7.0), (GEMM, "WRITE_SIZE", 400.0),
                            (GEMM, "WRITE_SIZE", 800.0)])
     out = str(tmp_path / "traffic.json")
     bench.record_traffic(d, out=out)
@@ -60,6 +62,13 @@ def test_traffic_record_from_counter_csvs(tmp_path):
     assert rec["bytes_per_launch"] == round(2000.0 * kib * 2.0 + 600.0 * kib)
     assert rec["source_sha256"] == bench.sources_sha(bench.GEMM_SOURCES)
     assert bench.traffic_record(rec["workload"], path=out)["bytes_per_launch"] == rec["bytes_per_launch"]
+    # the per-kernel table beside it: the products one row each, in step order
+    table = open(tmp_path / "quant_gemm_llama70b_infer_hbm_bytes.txt").read().splitlines()
+    rows = {" ".join(l.split()[:-4]): l.split()[-4:] for l in table if l.startswith(("amax", "gemm"))}
+    assert rows["amax_bf16_kernel<true>"] == ["256", "1", f"{5e6 * kib * 2.0 / 1e6:.1f}", f"{7.0 * kib / 1e6:.1f}"]
+    assert rows["gemm_pp_kernel<true, true, 0, 0, 0> qkv"][2] == f"{1000.0 * kib * 2.0 / 1e6:.1f}"
+    assert rows["gemm_pp_kernel<true, true, 0, 0, 0> o"][3] == f"{800.0 * kib / 1e6:.1f}"
+    assert rows["gemm_pp_kernel<true, true, 0, 0, 0> gate"][2] == f"{3000.0 * kib * 2.0 / 1e6:.1f}"
     # another workload, or other kernel sources: no record
     assert bench.traffic_record("another-workload", path=out) is None
     rec["source_sha256"] = "0" * 64
