@@ -1,5 +1,5 @@
 """Concurrent calls: several host threads, each on its own HIP stream, run the
-quantisation and the three products at once; every result equals the same
+quantisation (current and delayed scaling) and the three products at once; every result equals the same
 calls run one at a time (the library keeps no state between calls beyond a
 per-device architecture flag, and ctypes releases the GIL during a call)."""
 import threading
@@ -27,7 +27,12 @@ def work(fl, x, w, g, stream):
         y = fl.scaled_gemm(fl.OP_FWD, x8, fl.E4M3, bx, w8, fl.E4M3, bw, stream=stream)
         dx = fl.scaled_gemm(fl.OP_DGRAD, g8, fl.E5M2, bg, w8, fl.E4M3, bw, stream=stream)
         dw = fl.scaled_gemm(fl.OP_WGRAD, g8, fl.E5M2, bg, x8, fl.E4M3, bx, stream=stream)
-    return [x8, bx, ax, w8, bw, aw, g8, bg, ag, y, dx, dw]
+        # delayed scaling: the cast that leaves its block maxima in its own codes
+        prev = ax.clone()
+        xd8, bxd = fl.quantize_delayed(x, fl.E4M3, prev, 0, stream=stream)
+        gam = torch.empty(1, dtype=torch.float32, device=g.device)
+        gd8 = fl.scale_cast(g, bg, fl.E5M2, stream=stream, amax=gam)
+    return [x8, bx, ax, w8, bw, aw, g8, bg, ag, y, dx, dw, xd8, bxd, prev, gd8, gam]
 
 
 def test_threads_on_separate_streams(fl):
