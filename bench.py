@@ -136,7 +136,7 @@ def traffic_record(workload, path=None):
 
 def epilogue_amax(fl, w, plan, q, outs, math, op_of, reps=9):
     """The largest product of the step three ways (interleaved, median of
-    `reps`, HIP events): alone; with the amax of its fp32 output folded in its epilogue
+    `reps`, gpu_us): alone; with the amax of its fp32 output folded in its epilogue
     (fp8_scaled_gemm_amax); and followed by a separate fp8_amax pass over
     that output, which is what quantising the output next would otherwise
     need."""
@@ -152,15 +152,7 @@ def epilogue_amax(fl, w, plan, q, outs, math, op_of, reps=9):
     b8, bb, _, fb = q[bn]
     out = outs[(l.name, which)]
     amax = torch.empty(1, dtype=torch.float32, device="cuda")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def once(fn):
-        torch.cuda.synchronize()
-        e0.record()
-        fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3
+    once = gpu_us
 
     plain = lambda: fl.scaled_gemm(op_of[which], a8, fa, ba, b8, fb, bb, math=math, out=out)
     fused = lambda: fl.scaled_gemm(op_of[which], a8, fa, ba, b8, fb, bb, math=math, out=out, amax=amax)
@@ -192,17 +184,10 @@ def delayed_quant(fl, w, plan, q, x, reps=9):
     import statistics
 
     import torch
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     prev = torch.empty(1, dtype=torch.float32, device="cuda")
 
     def once(fn):
-        torch.cuda.synchronize()
-        torch.cuda._sleep(200 * 2500)  # >= 200 us at clocks up to 2.5 GHz
-        e0.record()
-        fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1)
+        return gpu_us(fn) * 1e-3
 
     per, t_chain, t_fused, elems = {}, 0.0, 0.0, 0
     for item in plan:
@@ -292,22 +277,31 @@ def graph_replay(step, q, outs, steps):
     return {"ms_per_step": round(ms, 4), "replays": steps, "outputs_identical_to_eager": bool(same)}
 
 
+def gpu_us(fn, lead_us=200):
+    """GPU time of the calls fn() makes, in us: HIP events on the launch
+    stream around them, led by a spin kernel of `lead_us` so that the host's
+    argument checks and launches are done before the start event fires (the
+    events then time the GPU's work, not the host's)."""
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(lead_us * 2500))  # >= lead_us at clocks up to 2.5 GHz
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e3
+
+
 def one_call_quant(fl, w, plan, q, x, reps=9):
-    """Each in-step quantisation two ways (interleaved, median of `reps`, HIP
-    events around the calls on the launch stream): fp8_quantize, and the
-    three calls amax -> compute_bias -> scale_cast.  Same outputs bit for bit
-    (checked here on the last repetition)."""
+    """Each in-step quantisation two ways (interleaved, median of `reps`,
+    gpu_us): fp8_quantize, and the three calls amax -> compute_bias ->
+    scale_cast.  Same outputs bit for bit (checked here on the last
+    repetition)."""
     import statistics
 
     import torch
-
-    def once(fn):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        fn()
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) * 1e3
+    once = gpu_us
 
     per, chain_sum, one_sum = {}, 0.0, 0.0
     for item in plan:
@@ -329,7 +323,8 @@ def one_call_quant(fl, w, plan, q, x, reps=9):
         one_sum += om
         per[n] = {"elements": x[n].numel(), "three_calls_us": round(cm, 2), "one_call_us": round(om, 2)}
     return {"method": "fp8_quantize vs fp8_amax -> fp8_compute_bias -> fp8_scale_cast, each tensor alone, "
-                      "HIP events, median of %d; outputs identical" % reps,
+                      "warm, HIP events after a spin that covers the host's launches, median of %d; outputs "
+                      "identical" % reps,
             "three_calls_us": round(chain_sum, 2), "one_call_us": round(one_sum, 2), "per_tensor": per}
 
 
