@@ -162,11 +162,19 @@ struct MNMajorLoader {
   }
 };
 
+// Block bid's output tile.  Workgroup bid runs on XCD bid % 8: when the tile
+// count allows, each XCD takes a contiguous run of the tile order, so the
+// tiles it runs at once share operand panels in its L2.  The order walks
+// groups of G tile-rows column by column.  With G = 4 a 32-tile-row output
+// (8192 rows) gives each XCD one group of 4 rows across every column, and the
+// eight XCDs walk the columns (the weight panels) together: 1.1-1.3% faster
+// on the Llama-2-70B products than G = 8 (two runs each; G = 2 the same as
+// 4, G = 16 half the gain, G = 32 none; the 13B gradients within noise).
 __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int total = tiles_m * tiles_n;
   int t = bid;
   if ((total & 7) == 0) t = (bid & 7) * (total >> 3) + (bid >> 3);
-  constexpr int G = 8;
+  constexpr int G = 4;
   const int width = G * tiles_n;
   const int first_m = (t / width) * G;
   const int gsize = min(tiles_m - first_m, G);
