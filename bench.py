@@ -1154,6 +1154,11 @@ def per_config_line(fl, wl, args):
         "parity": parity(fl, w, b.q, b.outs, res),
         "oracle_tflops": round(cpu["value"], 4),
     }
+    if r["ms_per_step"] < 1.0 and not args.no_graph:
+        # launch-bound: the same step replayed from a HIP graph
+        g = graph_replay(b.step, b.q, b.outs, args.steps)
+        g["tflops"] = round(w.flops() / (g["ms_per_step"] * 1e-3) / 1e12, 2)
+        out["hip_graph"] = g
     if not args.no_native and args.math == "exact":
         b.math = fl.MATH_NATIVE_FP8
         rn = b.measure(args.steps, args.warmup)
