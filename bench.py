@@ -78,6 +78,9 @@ def parse():
                     help="skip the same step on the native FP8 MFMA arithmetic")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device copy twice (HBM counter calibration)")
+    ap.add_argument("--loop-gemm", type=float, metavar="SECONDS",
+                    help="only run the workload's largest product back to back for SECONDS (sustained "
+                         "rate; for reading power and clocks with amd-smi meanwhile)")
     ap.add_argument("--record-traffic", metavar="DIR",
                     help="only write profiles/gemm_traffic.json from rocprofv3 --pmc CSVs under DIR "
                          "(fetch/, write/, copy_fetch/, copy_write/)")
@@ -421,6 +424,39 @@ def copy_calibration():
         y.copy_(x)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 2}), flush=True)
+
+
+def loop_gemm(args):
+    """The workload's largest product, back to back for args.loop_gemm seconds
+    (synchronising every 10 launches), on the workload's own quantised
+    operands: the sustained rate, while amd-smi reads power and clocks."""
+    import torch
+
+    import fp8_precision_linear_amd as fl
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    _, l, which = max((i for i in plan_of(w) if i[0] == "gemm"), key=lambda i: i[1].M * i[1].N * i[1].K)
+    an, bn, _ = gemm_operands(l, which)
+    q = {}
+    for n in (an, bn):
+        t = w.tensor(n)
+        codes, bias, _ = fl.quantize(synth.workload_tensor(w, n).cuda(), t.fmt, t.margin)
+        q[n] = (codes, bias, t.fmt)
+    (a8, ba, fa), (b8, bb, fb) = q[an], q[bn]
+    op = {"fwd": fl.OP_FWD, "dgrad": fl.OP_DGRAD, "wgrad": fl.OP_WGRAD}[which]
+    math = fl.MATH_EXACT if args.math == "exact" else fl.MATH_NATIVE_FP8
+    out = fl.scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=math)
+    torch.cuda.synchronize()
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < args.loop_gemm:
+        for _ in range(10):
+            fl.scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=math, out=out)
+        torch.cuda.synchronize()
+        n += 10
+    dt = time.perf_counter() - t0
+    flops = 2.0 * l.M * l.N * l.K
+    print(json.dumps({"product": f"{l.name}:{which}:{l.M}x{l.N}x{l.K}", "math": args.math, "launches": n,
+                      "seconds": round(dt, 2), "tflops": round(n * flops / dt / 1e12, 1)}), flush=True)
 
 
 def record_traffic(d, out=None):
@@ -1183,6 +1219,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.loop_gemm:
+        loop_gemm(args)
         return
     import torch
 
