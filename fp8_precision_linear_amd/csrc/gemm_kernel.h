@@ -193,8 +193,9 @@ __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, i
 template <int FMT>
 __device__ __forceinline__ uint2 fp8x4_to_f16(uint32_t w) {
   if constexpr (FMT == FP8_E5M2) {
-    return make_uint2(((w & 0xFFu) << 8) | ((w & 0xFF00u) << 16),
-                      ((w >> 8) & 0xFF00u) | (w & 0xFF000000u));
+    // one v_perm_b32 per output dword: bytes (high to low) [c1, 0, c0, 0] and
+    // [c3, 0, c2, 0] of the dword's codes c0..c3 (selector 0x0C reads a zero byte)
+    return make_uint2(__builtin_amdgcn_perm(0u, w, 0x010C000Cu), __builtin_amdgcn_perm(0u, w, 0x030C020Cu));
   } else {
     return make_uint2(
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),

@@ -711,10 +711,11 @@ hipError_t launch_math(const GemmProblem& p, hipStream_t stream) {
 
 // Exact products run on the bf16 MFMA when either operand is E5M2 and on the
 // fp16 MFMA otherwise: both are exact (every FP8 value is a normal bf16; every
-// E4M3 value a normal fp16, every E5M2 value an fp16), and on the MI355X this
-// choice measured fastest (bf16 ~10% ahead with an E5M2 operand, fp16 1-2%
-// ahead for E4M3 x E4M3).  FP8LIN_EXACT_MFMA=f16 or bf16 forces one (tuning
-// and tests).
+// E4M3 value a normal fp16, every E5M2 value an fp16).  Measured on the
+// MI355X: fp16 1-2% ahead for E4M3 x E4M3; with an E5M2 operand the two
+// within 0.2-0.7% of each other (bf16 was ~10% ahead while the fp16 path
+// widened E5M2 with shifts and masks rather than one byte permutation per two
+// codes).  FP8LIN_EXACT_MFMA=f16 or bf16 forces one (tuning and tests).
 inline bool exact_on_bf16(const GemmProblem& p) {
   const char* s = std::getenv("FP8LIN_EXACT_MFMA");
   if (s && std::strcmp(s, "bf16") == 0) return true;
