@@ -1246,6 +1246,12 @@ def main():
     epi = None if args.no_epilogue_amax else epilogue_amax(fl, w, plan, q, outs, b.math, b.op_of)
     delayed = None if args.no_delayed else delayed_quant(fl, w, plan, q, x)
     one_call = None if args.no_delayed else one_call_quant(fl, w, plan, q, x)
+    # the timed step's own quantisation call (one fp8_quantize_multi over every
+    # in-step tensor), alone: median of 9, gpu_us
+    step_call_us = None
+    if b.qmulti is not None:
+        import statistics
+        step_call_us = statistics.median(gpu_us(b.qmulti.run) for _ in range(9))
 
     rec = traffic_record(w.name)
     traffic = rec["bytes_per_launch"] if rec else None
@@ -1332,6 +1338,12 @@ def main():
             "frac": round(5.0 * quant_elems * K / ((amax_ms + bias_ms + cast_ms) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
             if cast_ms > 0 else None,
             "bytes_per_element": 5,
+            "method": "separate calls per tensor (fp8_amax, fp8_compute_bias, fp8_scale_cast) with "
+                      "events; step_call_*: the timed step's one fp8_quantize_multi call alone",
+            "step_call_us": round(step_call_us, 1) if step_call_us else None,
+            "step_call_gbs": round(5.0 * quant_elems / (step_call_us * 1e-6) / 1e9, 1) if step_call_us else None,
+            "step_call_frac": round(5.0 * quant_elems / (step_call_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+            if step_call_us else None,
         },
         "cold": cold,
         "epilogue_amax": epi,
