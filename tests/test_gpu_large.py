@@ -47,6 +47,25 @@ def test_amax_and_cast_past_2_31_elements(fl, dtype):
         words = words_of(x[lo:hi])
         got = codes[lo:hi].cpu().numpy()
         assert np.array_equal(got, oracle.scale_cast(words, b, E4M3)), (dtype, lo)
+    # the cast with its amax folded in (a main cast over 2^31 elements, then
+    # the last block over the stretch) and delayed scaling in one call: the
+    # same codes, bit for bit, and the same amax
+    say("large fused cast + amax", dtype, n)
+    am = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+    fused = fl.scale_cast(x, bias, E4M3, amax=am)
+    assert torch.equal(fused, codes) and int(words_of(am)[0]) == a_bits
+    del fused
+    prev = amax.clone()
+    delayed, db = fl.quantize_delayed(x, E4M3, prev, 0)
+    assert int(db.item()) == b and torch.equal(delayed, codes) and int(words_of(prev)[0]) == a_bits
+    del delayed
+    for pos in (n - 5, (1 << 31) - 100000):   # in the last block's stretch, and in the main cast
+        keep = x[pos].clone()
+        x[pos] = -1000.0
+        am.fill_(7.0)
+        fl.scale_cast(x, bias, E4M3, out=codes, amax=am)
+        assert am.item() == 1000.0, (dtype, pos, am.item())
+        x[pos] = keep
     del x, codes
     free()
 
