@@ -363,6 +363,37 @@ def test_cast_with_fused_amax_at_its_seams(fl, dtype):
                 assert np.array_equal(got, oracle.scale_cast(w, -8, E4M3)), (n, plant, i)
 
 
+def test_cast_with_fused_amax_random_sizes(fl):
+    """fp8_scale_cast_amax and fp8_quantize_delayed over 40 seeded sizes from
+    1 to 6M elements (both input types, every format, biases on both
+    conversion paths, the largest magnitude planted at a random position):
+    codes, amax and bias bit-exact against the oracle."""
+    rng = np.random.default_rng(41)
+    sizes = sorted(set(int(v) for v in np.exp(rng.uniform(0, np.log(6e6), 40))))
+    for k, n in enumerate(sizes):
+        dtype = ("bf16", "fp32")[k % 2]
+        fmt, b = ALL_FMTS[k % 3], (-3, 4, 150)[(k // 3) % 3]
+        v = (rng.standard_normal(n) * 5).astype(np.float32)
+        v[rng.integers(0, n)] = -200.0
+        if dtype == "bf16":
+            words = synth.bf16_words(synth.to_bf16(v)).copy()
+            x = bf16_dev(words)
+        else:
+            words = v.view(np.uint32).copy()
+            x = f32_dev(words)
+        say("cast+amax random size", dtype, n, "fmt", fmt, "bias", b)
+        a_ref = oracle.amax_bits(words)
+        am = torch.full((1,), 7.0, dtype=torch.float32, device="cuda")
+        got = fl.scale_cast(x, i32_dev(b), fmt, amax=am).cpu().numpy()
+        assert int(words_of(am)[0]) == a_ref, (n, dtype)
+        assert np.array_equal(got, oracle.scale_cast(words, b, fmt)), (n, dtype, fmt, b)
+        prev = torch.from_numpy(np.array([0x3F800000 + k], dtype=np.uint32).view(np.float32)).cuda()
+        codes, bias = fl.quantize_delayed(x, fmt, prev, 1)
+        b_ref = oracle.compute_bias(0x3F800000 + k, fmt, 1)
+        assert int(bias.item()) == b_ref and int(words_of(prev)[0]) == a_ref, (n, dtype)
+        assert np.array_equal(codes.cpu().numpy(), oracle.scale_cast(words, b_ref, fmt)), (n, dtype, fmt)
+
+
 def test_delayed_scaling_with_the_fused_cast(fl):
     """Delayed scaling: step t casts with the bias computed from the amax the
     step t-1 cast returned (bias 0 at t = 0), and returns its own amax; every
