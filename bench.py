@@ -830,8 +830,8 @@ def measure_mlp(args, m, light=False):
     # HBM bytes per group: amax reads the input, the cast reads it again and
     # writes one byte per element; SwiGLU fwd reads g, u (fp32) and writes a
     # (bf16), bwd reads g, u, da and writes dg, du
-    quant_bytes = {"x": (2 + 2 + 1) * T * d, "w1": (4 + 4 + 1) * 2 * f * d, "a": (2 + 1) * T * f,
-                   "w2": (4 + 4 + 1) * d * f, "dy": (4 + 4 + 1) * T * d, "dh": (2 + 1) * T * 2 * f}
+    quant_bytes = {"x+w1+w2": (2 + 2 + 1) * T * d + (4 + 4 + 1) * 2 * f * d + (4 + 4 + 1) * d * f,
+                   "a": (2 + 1) * T * f, "dy": (4 + 4 + 1) * T * d, "dh": (2 + 1) * T * 2 * f}
     sw_bytes = {"fwd": (8 + 2) * T * f, "bwd": (12 + 4) * T * f}
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9
 

@@ -10,10 +10,11 @@ findings"); the activation between that model's MLP products, SwiGLU, is not
 spelled out there and is taken as a = silu(g) * u.
 
 Forward (x [T, d], w1 = [W_gate; W_up] [2F, d], w2 = W_down [d, F]):
-    x8  = cast_E4(x),  w1_8 = cast_E4(w1)         amax -> bias -> cast each
+    x8  = cast_E4(x),  w1_8 = cast_E4(w1),  w2_8 = cast_E4(w2)
+                                     amax -> bias -> cast each, the three in one call
     h   = x8 . w1_8^T                [T, 2F] fp32  (gate columns, then up)
     a   = silu(g) * u                [T, F]  bf16, amax folded in the kernel
-    a8  = cast_E4(a),  w2_8 = cast_E4(w2)
+    a8  = cast_E4(a)
     y   = a8 . w2_8^T                [T, d]  fp32
 Backward (dy [T, d]):
     dy8 = cast_E5(dy)
@@ -34,7 +35,7 @@ from dataclasses import dataclass, field
 import torch
 
 from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, compute_bias, quantize,
-               scale_cast, scaled_gemm_auto, swiglu_bwd, swiglu_fwd)
+               quantize_multi, scale_cast, scaled_gemm_auto, swiglu_bwd, swiglu_fwd)
 
 # The quantised tensors of one forward + backward, in log order.
 TENSORS = ("x", "w1", "a", "w2", "dy", "dh")
@@ -108,10 +109,10 @@ def mlp_forward(x, w1, w2, cfg=None):
     _shapes(x, w1, w2)
     m = cfg.margins
     a_amax = torch.empty(1, dtype=torch.float32, device=x.device)
-    with _span(cfg, "quant", "x"):
-        x8, bx, _ = quantize(x, E4M3, m["x"])
-    with _span(cfg, "quant", "w1"):
-        w1_8, bw1, _ = quantize(w1, E4M3, m["w1"])
+    # the three inputs known at the start in one call (three launches for all)
+    with _span(cfg, "quant", "x+w1+w2"):
+        (x8, bx, _), (w1_8, bw1, _), (w2_8, bw2, _) = quantize_multi(
+            [x, w1, w2], E4M3, [m["x"], m["w1"], m["w2"]])
     with _span(cfg, "gemm", "fwd h"):
         h = scaled_gemm_auto(OP_FWD, x8, E4M3, bx, w1_8, E4M3, bw1, math=cfg.math)
     with _span(cfg, "swiglu", "fwd"):
@@ -119,8 +120,6 @@ def mlp_forward(x, w1, w2, cfg=None):
     with _span(cfg, "quant", "a"):
         ba = compute_bias(a_amax, E4M3, m["a"])
         a8 = scale_cast(a, ba, E4M3)
-    with _span(cfg, "quant", "w2"):
-        w2_8, bw2, _ = quantize(w2, E4M3, m["w2"])
     with _span(cfg, "gemm", "fwd y"):
         y = scaled_gemm_auto(OP_FWD, a8, E4M3, ba, w2_8, E4M3, bw2, math=cfg.math)
     if cfg.log is not None:
