@@ -70,6 +70,10 @@ def parse():
                     help="how the timed steps run the products: one fp8_scaled_gemm_group call, or "
                          "fp8_scaled_gemm (fp8_scaled_gemm_ws when split) per product (the steps with "
                          "per-kernel events always run them one by one)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="timed steps: quantise the first product's operands and run that product on "
+                         "torch's stream while a second stream quantises the other tensors (then the "
+                         "remaining products, after an event), with --quant multi --gemm grouped")
     ap.add_argument("--per-config", default="1,2,3,4,6",
                     help="other workloads measured in the same run (shorter: no graph, epilogue, "
                          "delayed or one-call extras; parity on an oracle sample)")
@@ -1003,6 +1007,31 @@ class Bench:
         self.qmulti = fl.QuantizeMulti([self.x[n] for n in names], [self.q[n][3] for n in names],
                                        [w.tensor(n).margin for n in names],
                                        outs=[self.q[n][:3] for n in names]) if names else None
+        # --overlap: the first product's in-step operands, then that product,
+        # on torch's stream; the other quantisations on a second stream
+        # (default priority) meanwhile; the other products after its event
+        self.overlap = None
+        gemms = [i for i in self.plan if i[0] == "gemm"]
+        if args.overlap and self.group is not None and names and gemms:
+            first_ops = [n for n in gemm_operands(gemms[0][1], gemms[0][2])[:2] if n in names]
+            rest = [n for n in names if n not in first_ops]
+            if first_ops and rest and len(gemms) > 1:
+                mk_q = lambda ns: fl.QuantizeMulti([self.x[n] for n in ns], [self.q[n][3] for n in ns],
+                                                   [w.tensor(n).margin for n in ns],
+                                                   outs=[self.q[n][:3] for n in ns])
+
+                def mk_g(items):
+                    prods, outs = [], []
+                    for _, l, which in items:
+                        an, bn, _ = gemm_operands(l, which)
+                        a8, ba, _, fa = self.q[an]
+                        b8, bb, _, fb = self.q[bn]
+                        prods.append((self.op_of[which], a8, fa, ba, b8, fb, bb))
+                        outs.append(self.outs[(l.name, which)])
+                    return fl.GemmGroup(prods, outs=outs, math=self.math)
+                self.overlap = {"q_first": mk_q(first_ops), "q_rest": mk_q(rest), "g_first": mk_g(gemms[:1]),
+                                "g_rest": mk_g(gemms[1:]), "side": torch.cuda.Stream(),
+                                "event": torch.cuda.Event(), "first": first_ops, "rest": rest}
 
     def event_calls(self):
         """The step as direct library calls (every argument prepared here, so
@@ -1055,6 +1084,22 @@ class Bench:
         call, or per tensor), then the products (one fp8_scaled_gemm_group
         call, or per product), all on torch's current stream."""
         fl, w, q, x = self.fl, self.w, self.q, self.x
+        if self.overlap is not None:
+            import torch
+            o, main = self.overlap, torch.cuda.current_stream()
+            for g in (o["g_first"], o["g_rest"]):
+                g.math = self.math
+            # the side stream first waits for everything before (the previous
+            # step's products read the codes it is about to rewrite)
+            o["side"].wait_stream(main)
+            with torch.cuda.stream(o["side"]):
+                o["q_rest"].run()
+                o["event"].record()
+            o["q_first"].run()
+            o["g_first"].run()
+            main.wait_event(o["event"])
+            o["g_rest"].run()
+            return
         if self.args.quant == "multi":
             if self.qmulti is not None:
                 self.qmulti.run()
@@ -1290,6 +1335,8 @@ def main():
                               "tiles alone)" if args.gemm == "grouped"
                          else "fp8_scaled_gemm per product (fp8_scaled_gemm_ws when split)"),
             "products_grouped_ws_bytes": b.group.ws_bytes if b.group is not None else None,
+            "overlapped_quantisation": ({"side_stream": b.overlap["rest"], "before_first_product": b.overlap["first"]}
+                                        if b.overlap is not None else None),
             "parallelism": "single-gpu",
         },
         # the GEMM's bound is the dense FP8 MFMA peak (its operands are FP8);
