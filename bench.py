@@ -300,6 +300,22 @@ def gpu_us(fn, lead_us=200):
     return s.elapsed_time(e) * 1e3
 
 
+def products_call(b, flops, reps=9):
+    """The timed step's products alone, as the step runs them (one
+    fp8_scaled_gemm_group call): median of `reps` gpu_us, and the TFLOP/s
+    that gives; None where the step calls the products one by one."""
+    import statistics
+
+    if b.group is None:
+        return None
+    b.group.math = b.group_math = b.math
+    us = statistics.median(gpu_us(b.group.run) for _ in range(reps))
+    tf = flops / (us * 1e-6) / 1e12
+    return {"us": round(us, 1), "tflops": round(tf, 2), "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "frac_of_mfma_used_peak": round(tf / mfma_used_peak("exact" if b.math == b.fl.MATH_EXACT
+                                                                else "native-fp8"), 4)}
+
+
 def one_call_quant(fl, w, plan, q, x, reps=9):
     """Each in-step quantisation two ways (interleaved, median of `reps`,
     gpu_us): fp8_quantize, and the three calls amax -> compute_bias ->
@@ -577,11 +593,11 @@ def hbm_table(fetch_rows, write_rows, f_factor, w_factor):
         "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d <DIR>/copy_fetch -o run -- python3 bench.py --copy-calibration",
         "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d <DIR>/copy_write -o run -- python3 bench.py --copy-calibration",
         "",
-        f"{'kernel':46s} {'grid':>9s} {'dispatches':>10s} {'read MB':>9s} {'written MB':>10s}",
+        f"{'kernel':52s} {'grid':>9s} {'dispatches':>10s} {'read MB':>9s} {'written MB':>10s}",
     ]
     for key in order:
         v = groups[key]
-        lines.append(f"{key[0][:46]:46s} {key[1]:9d} {len(v):10d} {statistics.median(a for a, _ in v):9.1f} "
+        lines.append(f"{key[0][:52]:52s} {key[1]:9d} {len(v):10d} {statistics.median(a for a, _ in v):9.1f} "
                      f"{statistics.median(b for _, b in v):10.1f}")
     return "\n".join(lines) + "\n"
 
@@ -1232,6 +1248,7 @@ def per_config_line(fl, wl, args):
         "cold_cast_gbs": cold["cast_gbs"] if cold else None,
         "cold_amax_gbs": cold["amax_gbs"] if cold else None,
         "split_along_contraction": b.split_products,
+        "step_products_call": products_call(b, w.flops()),
         "parity": parity(fl, w, b.q, b.outs, res),
         "oracle_tflops": round(cpu["value"], 4),
     }
@@ -1396,6 +1413,7 @@ def main():
         "epilogue_amax": epi,
         "delayed_scaling": delayed,
         "one_call_quantisation": one_call,
+        "step_products_call": products_call(b, step_flops),
         "hip_graph": None if graph_info is None else dict(
             graph_info, tflops=round(step_flops / (graph_info["ms_per_step"] * 1e-3) / 1e12, 2)),
         "step_breakdown_ms": {"gemm": round(gemm_ms / K, 4), "amax": round(amax_ms / K, 4),

@@ -52,6 +52,7 @@ SIGNATURES = {
     "fp8_quantize_delayed": (_ci, [_vp, _ci, _i64, _ci, _i32, _vp, _vp, _vp, _vp]),
     "fp8_scaled_gemm": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_amax": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "fp8_scaled_gemm_accumulate": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
     "fp8_scaled_gemm_workspace_bytes": (_i64, [_ci, _i64, _i64, _i64]),
     "fp8_scaled_gemm_ws": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp]),
     "fp8_scaled_gemm_noalloc": (_ci, [_ci, _ci, _vp, _ci, _vp, _vp, _ci, _vp, _i64, _i64, _i64, _vp, _vp]),
@@ -425,6 +426,19 @@ def scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=MATH_EXACT, out=None, stream=No
                lib.fp8_scaled_gemm_amax(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8),
                                         int(fb), _ptr(bb), M, N, K, _ptr(out), _ptr(amax),
                                         _stream(stream)))
+    return out
+
+
+def scaled_gemm_accumulate(op, a8, fa, ba, b8, fb, bb, out, math=MATH_EXACT, stream=None):
+    """out += the product (fp8_scaled_gemm_accumulate): one fp32 addition per
+    output of what scaled_gemm would store; out is the caller's float32
+    buffer of the product's output shape, read and written in place."""
+    if out is None:
+        raise ValueError("scaled_gemm_accumulate adds into the caller's output: out is required")
+    M, N, K, out = _gemm_args(op, a8, ba, b8, bb, out, stream)
+    _check("fp8_scaled_gemm_accumulate",
+           lib.fp8_scaled_gemm_accumulate(int(op), int(math), _ptr(a8), int(fa), _ptr(ba), _ptr(b8),
+                                          int(fb), _ptr(bb), M, N, K, _ptr(out), _stream(stream)))
     return out
 
 

@@ -233,7 +233,7 @@ int make_problem(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, 
       if (int s = gemm_checks(a, fa, ba, b, fb, bb, M, N, K, out, M, K, N, K)) return s;
       empty = M == 0 || N == 0;
       p = fp8lin::GemmProblem{a, K, true, fa, ba, b, K, true, fb, bb, out, N,
-                              (int)M, (int)N, (int)K, math, nullptr};
+                              (int)M, (int)N, (int)K, math, nullptr, false};
       break;
     case FP8_GEMM_DGRAD:
       // dX[M x K]: rows of dY8 (contraction N contiguous) times W8 read as
@@ -241,14 +241,14 @@ int make_problem(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, 
       if (int s = gemm_checks(a, fa, ba, b, fb, bb, M, K, N, out, M, N, N, K)) return s;
       empty = M == 0 || K == 0;
       p = fp8lin::GemmProblem{a, N, true, fa, ba, b, K, false, fb, bb, out, K,
-                              (int)M, (int)K, (int)N, math, nullptr};
+                              (int)M, (int)K, (int)N, math, nullptr, false};
       break;
     case FP8_GEMM_WGRAD:
       // dW[N x K]: dY8 read as [contraction M][N] times X8 read as [contraction M][K].
       if (int s = gemm_checks(a, fa, ba, b, fb, bb, N, K, M, out, M, N, M, K)) return s;
       empty = N == 0 || K == 0;
       p = fp8lin::GemmProblem{a, N, false, fa, ba, b, K, false, fb, bb, out, K,
-                              (int)N, (int)K, (int)M, math, nullptr};
+                              (int)N, (int)K, (int)M, math, nullptr, false};
       break;
     default:
       return FP8_ERR_OP;
@@ -259,10 +259,11 @@ int make_problem(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, 
 int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, const int32_t* ba,
                 const uint8_t* b, fp8_format_t fb, const int32_t* bb, int64_t M, int64_t N,
                 int64_t K, float* out, float* out_amax, WsMode ws_mode, void* ws, int64_t ws_bytes,
-                hipStream_t st) {
+                hipStream_t st, bool accumulate = false) {
   fp8lin::GemmProblem p{};
   bool empty = false;
   if (int s = make_problem(op, math, a, fa, ba, b, fb, bb, M, N, K, out, p, empty)) return s;
+  p.accumulate = accumulate;
   bool split = false;
   if (ws_mode != kNoWorkspace && !empty) {
     const int64_t need = fp8lin::gemm_split_workspace_bytes(p.m, p.n, p.k);
@@ -409,6 +410,14 @@ int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_forma
   if (misaligned_word(out_amax)) return FP8_ERR_ALIGN;
   return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, out_amax, kNoWorkspace, nullptr,
                      0, (hipStream_t)stream);
+}
+
+int fp8_scaled_gemm_accumulate(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
+                               const int32_t* ba, const uint8_t* b, fp8_format_t fb,
+                               const int32_t* bb, int64_t M, int64_t N, int64_t K, float* out,
+                               void* stream) {
+  return scaled_gemm(op, math, a, fa, ba, b, fb, bb, M, N, K, out, nullptr, kNoWorkspace, nullptr,
+                     0, (hipStream_t)stream, true);
 }
 
 int fp8_scaled_gemm_fwd(const uint8_t* x8, fp8_format_t fx, const int32_t* bx,

@@ -351,6 +351,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles
 
   // 32x32 accumulator layout: register r of lane l holds row
   // 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32 of the MFMA tile.
+  // With p.accumulate the 16 outputs of a tile are read (all issued) before
+  // the unscaled sums are added to them and stored.
   const int unscale = -(*p.bias_a + *p.bias_b);
   uint32_t mx = 0;
 #pragma unroll
@@ -358,11 +360,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmProblem p, int tiles
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = n0 + wn * (BN / 2) + j * 32 + rl;
+      float old[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        old[r] = (p.accumulate && row < p.m && col < p.n) ? p.c[(int64_t)row * p.ldc + col] : 0.0f;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < p.m && col < p.n) {
-          const float v = __builtin_ldexpf(acc[i][j][r], unscale);
+          float v = __builtin_ldexpf(acc[i][j][r], unscale);
+          if (p.accumulate) v = old[r] + v;
           p.c[(int64_t)row * p.ldc + col] = v;
           mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu);
         }

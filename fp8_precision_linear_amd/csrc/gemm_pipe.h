@@ -312,17 +312,32 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[TM][TN]) {
 // Unscale and store a wave's TM x TN block of 32x32 tiles whose top-left
 // output is (row0, col0).  32x32 accumulator layout: register r of lane l
 // holds row 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32.  With
-// AMAX the largest stored magnitude is folded into *p.amax.  The stores are
-// non-temporal: the output is not read back by the product, and a wave of
-// tiles writes about twice an XCD's L2 in outputs (measured: 0.2-1% faster).
-template <bool AMAX, int TM, int TN>
+// AMAX the largest stored magnitude is folded into *p.amax.  With ACC each
+// output is first read and the unscaled sum added to it (one fp32 addition);
+// the reads of a row of tiles are all issued before its stores.  The stores
+// are non-temporal: the output is not read back by the product, and a wave
+// of tiles writes about twice an XCD's L2 in outputs (measured: 0.2-1%
+// faster).
+template <bool AMAX, bool ACC = false, int TM, int TN>
 __device__ __forceinline__ void store_block_as(const GemmProblem& p, const v16f (&acc)[TM][TN],
                                                int row0, int col0, int lane) {
   const int h = lane >> 5, rl = lane & 31;
   const int unscale = -(*p.bias_a + *p.bias_b);
   uint32_t mx = 0;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    float old[TN][16];
+    if constexpr (ACC) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = col0 + j * 32 + rl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          old[j][r] = (row < p.m && col < p.n) ? p.c[(int64_t)row * p.ldc + col] : 0.0f;
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = col0 + j * 32 + rl;
@@ -330,19 +345,27 @@ __device__ __forceinline__ void store_block_as(const GemmProblem& p, const v16f 
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < p.m && col < p.n) {
-          const float v = __builtin_ldexpf(acc[i][j][r], unscale);
+          float v = __builtin_ldexpf(acc[i][j][r], unscale);
+          if constexpr (ACC) v = old[j][r] + v;
           __builtin_nontemporal_store(v, &p.c[(int64_t)row * p.ldc + col]);
           if constexpr (AMAX) mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu);
         }
       }
     }
+  }
   if constexpr (AMAX) amax_fold(mx, p.amax);
 }
 
-template <int TM, int TN>
+// The epilogue of a kernel instantiated with ACC (fp8_scaled_gemm_accumulate,
+// which never asks for the output's amax) or without it (the amax optional).
+// The accumulating epilogue is its own instantiation so that the common one
+// keeps its code and registers (a runtime choice between the two in one
+// kernel cost the 70B QKV product ~2%).
+template <bool ACC, int TM, int TN>
 __device__ __forceinline__ void store_block(const GemmProblem& p, const v16f (&acc)[TM][TN],
                                             int row0, int col0, int lane) {
-  if (p.amax) store_block_as<true>(p, acc, row0, col0, lane);
+  if constexpr (ACC) store_block_as<false, true>(p, acc, row0, col0, lane);
+  else if (p.amax) store_block_as<true>(p, acc, row0, col0, lane);
   else store_block_as<false>(p, acc, row0, col0, lane);
 }
 
@@ -432,7 +455,7 @@ struct PingPongWave {
   }
 };
 
-template <bool AK, bool BK, int FA, int FB, int MATH>
+template <bool AK, bool BK, int FA, int FB, int MATH, bool ACC>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, int tiles_m, int tiles_n) {
   constexpr int R = 256;
   // Ring of four stages per operand: slot s of A at sa + s * 16 KB, of B at
@@ -455,7 +478,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmProblem p, int tiles_m
     PingPongWave<1, AK, BK, FA, FB, MATH> w(p, m0, n0, gw, lane, lds_addr(sa), lds_addr(sb), acc);
     w.run();
   }
-  store_block(p, acc, m0 + g * (R / 2), n0 + gw * (R / 4), lane);
+  store_block<ACC>(p, acc, m0 + g * (R / 2), n0 + gw * (R / 4), lane);
 }
 
 // ---------------------------------------------------------- quad, 128 x 128
@@ -519,7 +542,7 @@ struct QuadWave {
   }
 };
 
-template <bool AK, bool BK, int FA, int FB, int MATH>
+template <bool AK, bool BK, int FA, int FB, int MATH, bool ACC>
 __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmProblem p, int tiles_m, int tiles_n) {
   constexpr int R = 128;
   __shared__ __attribute__((aligned(1024))) uint8_t sa[kPipeStages * R * kPipeBK];
@@ -534,7 +557,7 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmProblem p, int tiles
   zero_acc(acc);
   QuadWave<AK, BK, FA, FB, MATH> w(p, m0, n0, wave, lane, lds_addr(sa), lds_addr(sb), acc);
   w.run();
-  store_block(p, acc, m0 + (wave >> 1) * (R / 2), n0 + (wave & 1) * (R / 2), lane);
+  store_block<ACC>(p, acc, m0 + (wave >> 1) * (R / 2), n0 + (wave & 1) * (R / 2), lane);
 }
 
 // ----------------------------------------------------------------- launch
@@ -545,39 +568,41 @@ inline dim3 tile_grid(const GemmProblem& p, int bm, int bn, int& tiles_m, int& t
   return dim3(tiles_m * tiles_n);
 }
 
-// Instantiate KERNEL<AK, BK, FA, FB, MATH> for the operand formats of p.
-#define FP8LIN_FORMAT_DISPATCH(KERNEL, GRID, BLOCK)                                           \
-  do {                                                                                        \
-    if (p.fmt_a == FP8_E4M3 && p.fmt_b == FP8_E4M3) {                                         \
-      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E4M3, FP8_E4M3, MATH>), GRID, BLOCK, 0, stream,  \
-                         p, tiles_m, tiles_n);                                                \
-    } else if (p.fmt_a == FP8_E5M2 && p.fmt_b == FP8_E4M3) {                                  \
-      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E5M2, FP8_E4M3, MATH>), GRID, BLOCK, 0, stream,  \
-                         p, tiles_m, tiles_n);                                                \
-    } else if (p.fmt_a == FP8_E4M3 && p.fmt_b == FP8_E5M2) {                                  \
-      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E4M3, FP8_E5M2, MATH>), GRID, BLOCK, 0, stream,  \
-                         p, tiles_m, tiles_n);                                                \
-    } else if (p.fmt_a == FP8_E5M2 && p.fmt_b == FP8_E5M2) {                                  \
-      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E5M2, FP8_E5M2, MATH>), GRID, BLOCK, 0, stream,  \
-                         p, tiles_m, tiles_n);                                                \
-    } else {                                                                                  \
-      return hipErrorInvalidValue;                                                            \
-    }                                                                                         \
-    return hipGetLastError();                                                                 \
+// Instantiate KERNEL<AK, BK, FA, FB, MATH, ACC> for the operand formats of p.
+#define FP8LIN_FORMAT_DISPATCH(KERNEL, GRID, BLOCK, ACC)                                           \
+  do {                                                                                             \
+    if (p.fmt_a == FP8_E4M3 && p.fmt_b == FP8_E4M3) {                                              \
+      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E4M3, FP8_E4M3, MATH, ACC>), GRID, BLOCK, 0, stream,  \
+                         p, tiles_m, tiles_n);                                                     \
+    } else if (p.fmt_a == FP8_E5M2 && p.fmt_b == FP8_E4M3) {                                       \
+      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E5M2, FP8_E4M3, MATH, ACC>), GRID, BLOCK, 0, stream,  \
+                         p, tiles_m, tiles_n);                                                     \
+    } else if (p.fmt_a == FP8_E4M3 && p.fmt_b == FP8_E5M2) {                                       \
+      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E4M3, FP8_E5M2, MATH, ACC>), GRID, BLOCK, 0, stream,  \
+                         p, tiles_m, tiles_n);                                                     \
+    } else if (p.fmt_a == FP8_E5M2 && p.fmt_b == FP8_E5M2) {                                       \
+      hipLaunchKernelGGL((KERNEL<AK, BK, FP8_E5M2, FP8_E5M2, MATH, ACC>), GRID, BLOCK, 0, stream,  \
+                         p, tiles_m, tiles_n);                                                     \
+    } else {                                                                                       \
+      return hipErrorInvalidValue;                                                                 \
+    }                                                                                              \
+    return hipGetLastError();                                                                      \
   } while (0)
 
 template <bool AK, bool BK, int MATH>
 hipError_t launch_pp(const GemmProblem& p, hipStream_t stream) {
   int tiles_m, tiles_n;
   const dim3 grid = tile_grid(p, 256, 256, tiles_m, tiles_n), block(512);
-  FP8LIN_FORMAT_DISPATCH(gemm_pp_kernel, grid, block);
+  if (p.accumulate) FP8LIN_FORMAT_DISPATCH(gemm_pp_kernel, grid, block, true);
+  FP8LIN_FORMAT_DISPATCH(gemm_pp_kernel, grid, block, false);
 }
 
 template <bool AK, bool BK, int MATH>
 hipError_t launch_quad(const GemmProblem& p, hipStream_t stream) {
   int tiles_m, tiles_n;
   const dim3 grid = tile_grid(p, 128, 128, tiles_m, tiles_n), block(256);
-  FP8LIN_FORMAT_DISPATCH(gemm_quad_kernel, grid, block);
+  if (p.accumulate) FP8LIN_FORMAT_DISPATCH(gemm_quad_kernel, grid, block, true);
+  FP8LIN_FORMAT_DISPATCH(gemm_quad_kernel, grid, block, false);
 }
 
 template <bool AK, bool BK, int MATH>

@@ -77,6 +77,10 @@ struct GemmProblem {
   // optional: fold max |C[m][n]| (as fp32 magnitude bits) into *amax with
   // atomicMax; nullptr for none
   uint32_t* amax;
+  // C[m][n] += the unscaled product (one fp32 addition per output) instead
+  // of C[m][n] = it; only the single-product kernels (pipelined and general)
+  // take it
+  bool accumulate;
 };
 
 // One launcher per operand layout (gemm_fwd.hip, gemm_dgrad.hip, gemm_wgrad.hip).

@@ -367,6 +367,24 @@ int fp8_scaled_gemm_amax(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_forma
                          const int32_t* bb, int64_t M, int64_t N, int64_t K, float* out,
                          float* out_amax, void* stream);
 
+/* fp8_scaled_gemm that adds its result to the output instead of overwriting
+ * it: out[i][j] = out[i][j] + 2^-(ba+bb) * sum_k a.b, one fp32
+ * round-to-nearest-even addition per output of the sum fp8_scaled_gemm
+ * would have stored.  For a weight gradient summed over micro-batches into
+ * one fp32 buffer (training, "Proposed method" bullet 5; the pages give the
+ * product only as "matmul, then unscale", bullet 3, and accumulating into an
+ * existing buffer is this library's reading of the training loop).
+ *   out  device, read and written, 16-byte aligned, not overlapping the
+ *        operands; calls that overlap in time on one output race.
+ * K == 0 adds zero to every output (-0 becomes +0).  Never split along the
+ * contraction.  Same checks and status codes as fp8_scaled_gemm.  Within
+ * fp8_scaled_gemm's bound plus the addition's own rounding: |out - (old +
+ * exact)| <= 1e-5 * 2^-(ba+bb) * sum|a||b| + 2^-24 * |old + exact|. */
+int fp8_scaled_gemm_accumulate(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
+                               const int32_t* ba, const uint8_t* b, fp8_format_t fb,
+                               const int32_t* bb, int64_t M, int64_t N, int64_t K, float* out,
+                               void* stream);
+
 /*
  * The gated activation between the two products of a chained FP8 MLP: Llama
  * 2's SwiGLU (the review page trains Llama 2 models, "Main findings", without

@@ -170,6 +170,20 @@ def gemm_wgrad(dy8, fdy, bdy, x8, fx, bx):
     return y, bd
 
 
+def gemm_accumulate(op, old, a8, fa, ba, b8, fb, bb):
+    """old + the product, in float64: the reading that accumulating into an
+    existing fp32 buffer (a weight gradient summed over micro-batches, the
+    training of "Proposed method" bullet 5) adds the unscaled product of
+    bullet 3 to what the buffer holds.  op: 0 fwd, 1 dgrad, 2 wgrad (a, b as
+    gemm_fwd / gemm_dgrad / gemm_wgrad take them); old: float32 array of the
+    output's shape.  Returns (old + product, the product's bound)."""
+    y, bd = (gemm_fwd, gemm_dgrad, gemm_wgrad)[op](a8, fa, ba, b8, fb, bb)
+    old = np.asarray(old)
+    if old.dtype != np.float32 or old.shape != y.shape:
+        raise ValueError(f"old must be float32 of the output's shape {y.shape}")
+    return old.astype(np.float64) + y, bd
+
+
 def _at(fn, a, fa, ba, b, fb, bb, M, N, K, rows, cols):
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     cols = np.ascontiguousarray(cols, dtype=np.int64)

@@ -48,7 +48,7 @@ FP32_OVERFLOW = 2.0 ** 128 - 2.0 ** 103
 HALF_SUBNORMAL = 2.0 ** -150
 
 
-def check_gemm(got, ref, bound, what, rel=1e-5):
+def check_gemm(got, ref, bound, what, rel=1e-5, extra=0.0):
     """The products' tolerance, elementwise, against the oracle's fp64 result
     ref and bound = 2^-(ba+bb) * sum |a||b|:
       * where ref is NaN (a NaN code among the output's terms, inf * 0,
@@ -58,7 +58,10 @@ def check_gemm(got, ref, bound, what, rel=1e-5):
         where the exact result lies in fp32's subnormal range or below;
       * an infinity of ref's sign is also accepted where |ref| + rel * bound
         reaches fp32's overflow threshold (results beyond fp32's range).
-    Returns the worst err / bound over the finite, in-range outputs."""
+    extra (scalar or elementwise) widens the finite bar by further rounding
+    the operation is allowed, e.g. the fp32 addition of an accumulating
+    product.  Returns the worst err / bound over the finite, in-range
+    outputs, beyond HALF_SUBNORMAL + extra."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     bound = np.asarray(bound, dtype=np.float64)
@@ -66,15 +69,16 @@ def check_gemm(got, ref, bound, what, rel=1e-5):
     fin = ~(nan_ref | inf_ref)
     reffin = np.where(fin, ref, 0.0)
     bndfin = np.where(fin, bound, 0.0)
+    extra = np.where(fin, np.asarray(extra, dtype=np.float64), 0.0)
     with np.errstate(invalid="ignore", over="ignore"):
         err = np.abs(got - reffin)
-        ok_fin = fin & (err <= rel * bndfin + HALF_SUBNORMAL)
+        ok_fin = fin & (err <= rel * bndfin + HALF_SUBNORMAL + extra)
         overflow = fin & np.isinf(got) & (np.sign(got) == np.sign(reffin)) & \
             (np.abs(reffin) + rel * bndfin >= FP32_OVERFLOW)
         ok = np.where(nan_ref, np.isnan(got),
                       np.where(inf_ref, got == ref, ok_fin | overflow))
         inrange = fin & np.isfinite(got)
-        excess = np.maximum(err - HALF_SUBNORMAL, 0.0)   # beyond the output's own rounding
+        excess = np.maximum(err - HALF_SUBNORMAL - extra, 0.0)   # beyond the output's own rounding
         ratio = np.where(inrange & (bndfin > 0), excess / np.where(bndfin > 0, bndfin, 1.0),
                          np.where(inrange & (excess > 0), np.inf, 0.0))
     worst = float(ratio.max()) if ratio.size else 0.0

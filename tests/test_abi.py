@@ -31,7 +31,7 @@ def status(code):
 
 def test_every_declared_function_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(L, n), n
         assert n in fl.SIGNATURES, n
@@ -215,6 +215,36 @@ def test_gemm_amax_without_a_device_reports_no_device():
     f = L.fp8_scaled_gemm_amax
     assert f(0, 0, A16, 0, A32, A48, 0, A32, 0, 8, 8, A16, A32, None) == status("FP8_ERR_DEVICE")
     assert f(0, 0, A16, 0, A32, A48, 0, A32, 64, 64, 64, A16, A32, None) == status("FP8_ERR_DEVICE")
+
+
+def test_gemm_accumulate_argument_checks():
+    """fp8_scaled_gemm_accumulate checks what fp8_scaled_gemm checks, before
+    any HIP call; an empty output is a no-op."""
+    f = L.fp8_scaled_gemm_accumulate
+    assert f(3, 0, A16, 0, A32, A48, 0, A32, 8, 8, 8, A16, None) == status("FP8_ERR_OP")
+    assert f(0, 2, A16, 0, A32, A48, 0, A32, 8, 8, 8, A16, None) == status("FP8_ERR_OP")
+    for op in (0, 1, 2):
+        assert f(op, 0, A16, 2, A32, A48, 0, A32, 8, 8, 8, A16, None) == status("FP8_ERR_FORMAT")
+        assert f(op, 0, A16, 0, A32, A48, 0, A32, 8, 8, 8, None, None) == status("FP8_ERR_NULL")
+        assert f(op, 0, A16, 0, None, A48, 0, A32, 8, 8, 8, A16, None) == status("FP8_ERR_NULL")
+        assert f(op, 0, A16, 0, A32, A48, 0, A32, 8, 8, 8, MIS, None) == status("FP8_ERR_ALIGN")
+        assert f(op, 0, A16, 0, A32, A48, 0, A32, -1, 8, 8, A16, None) == status("FP8_ERR_SIZE")
+    assert f(0, 0, None, 0, None, None, 0, None, 0, 8, 8, None, None) == 0
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
+def test_gemm_accumulate_without_a_device_reports_no_device():
+    f = L.fp8_scaled_gemm_accumulate
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 64, 64, 64, A16, None) == status("FP8_ERR_DEVICE")
+
+
+def test_gemm_accumulate_wrapper_needs_an_output():
+    a8 = torch.zeros(8, 8, dtype=torch.uint8)
+    b0 = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fl.scaled_gemm_accumulate(fl.OP_FWD, a8, fl.E4M3, b0, a8, fl.E4M3, b0, None)
+    with pytest.raises(ValueError):   # CPU tensors
+        fl.scaled_gemm_accumulate(fl.OP_FWD, a8, fl.E4M3, b0, a8, fl.E4M3, b0, torch.zeros(8, 8))
 
 
 def test_swiglu_argument_checks():

@@ -15,7 +15,7 @@ sys.path.insert(0, ROOT)
 import bench  # noqa: E402
 
 FIELDS = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
-GEMM = "void fp8lin::gemm_detail::gemm_pp_kernel<true, true, 0, 0, 0>(fp8lin::GemmProblem, int, int)"
+GEMM = "void fp8lin::gemm_detail::gemm_pp_kernel<true, true, 0, 0, 0, false>(fp8lin::GemmProblem, int, int)"
 OTHER = "void fp8lin::(anonymous namespace)::amax_bf16_kernel<true>(HIP_vector_type<unsigned int, 4u> const*)"
 COPY = "__amd_rocclr_copyBuffer"
 
@@ -66,9 +66,9 @@ def test_traffic_record_from_counter_csvs(tmp_path):
     table = open(tmp_path / "quant_gemm_llama70b_infer_hbm_bytes.txt").read().splitlines()
     rows = {" ".join(l.split()[:-4]): l.split()[-4:] for l in table if l.startswith(("amax", "gemm"))}
     assert rows["amax_bf16_kernel<true>"] == ["256", "1", f"{5e6 * kib * 2.0 / 1e6:.1f}", f"{7.0 * kib / 1e6:.1f}"]
-    assert rows["gemm_pp_kernel<true, true, 0, 0, 0> qkv"][2] == f"{1000.0 * kib * 2.0 / 1e6:.1f}"
-    assert rows["gemm_pp_kernel<true, true, 0, 0, 0> o"][3] == f"{800.0 * kib / 1e6:.1f}"
-    assert rows["gemm_pp_kernel<true, true, 0, 0, 0> gate"][2] == f"{3000.0 * kib * 2.0 / 1e6:.1f}"
+    assert rows["gemm_pp_kernel<true, true, 0, 0, 0, false> qkv"][2] == f"{1000.0 * kib * 2.0 / 1e6:.1f}"
+    assert rows["gemm_pp_kernel<true, true, 0, 0, 0, false> o"][3] == f"{800.0 * kib / 1e6:.1f}"
+    assert rows["gemm_pp_kernel<true, true, 0, 0, 0, false> gate"][2] == f"{3000.0 * kib * 2.0 / 1e6:.1f}"
     # another workload, or other kernel sources: no record
     assert bench.traffic_record("another-workload", path=out) is None
     rec["source_sha256"] = "0" * 64

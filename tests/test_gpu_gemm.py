@@ -118,6 +118,85 @@ def test_identity_operand_is_exact_including_subnormals(fl, tile, which):
     assert np.array_equal(got.astype(np.float64), want)
 
 
+ACC_SHAPES = [(300, 520, 392), (64, 64, 0), (257, 129, 1000), (33, 700, 130), (512, 512, 128),
+              (260, 300, 17)]
+OP_OF = {"fwd": 0, "dgrad": 1, "wgrad": 2}
+
+
+def old_buffer(rng, shape, scale):
+    """What an accumulation buffer may hold: values of the product's size,
+    exact zeros of both signs, and a few far larger ones."""
+    old = (rng.standard_normal(shape) * scale).astype(np.float32)
+    flat = old.reshape(-1)
+    if flat.size:
+        idx = rng.choice(flat.size, min(flat.size, 40), replace=False)
+        flat[idx[:10]] = 0.0
+        flat[idx[10:20]] = -0.0
+        flat[idx[20:]] *= 1e4
+    return old
+
+
+@pytest.mark.parametrize("which", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("fa,fb", PAIRS)
+def test_accumulate_into_the_output(fl, tile, which, fa, fb):
+    """fp8_scaled_gemm_accumulate: out = old + product, one fp32 addition per
+    output.  Against the oracle's old + exact product (float64):
+    |gpu - ref| <= 1e-5 * bound + 2^-24 * |ref| (the addition's rounding);
+    then a second product added on top of the first result (two
+    micro-batches) against old + product 1 + product 2, within both
+    products' bounds and both additions' roundings.  The kernels, tile sizes
+    and ragged edges are those of the plain products."""
+    rng = np.random.default_rng(zlib.crc32(f"accumulate {which} {fa} {fb}".encode()))
+    op = OP_OF[which]
+    for (M, N, K) in ACC_SHAPES:
+        a8, b8 = operands(rng, which, M, N, K, fa, fb)
+        c8, d8 = operands(rng, which, M, N, K, fa, fb)
+        ba, bb = (int(v) for v in rng.integers(-12, 20, 2))
+        y1, bound1 = reference(which, a8, fa, ba, b8, fb, bb)
+        y2, bound2 = reference(which, c8, fa, ba, d8, fb, bb)
+        scale = float(np.sqrt(np.mean(y1 ** 2))) if y1.size and np.any(y1) else 1.0
+        old = old_buffer(rng, y1.shape, scale)
+        ref1, _ = oracle.gemm_accumulate(op, old, a8, fa, ba, b8, fb, bb)
+        say("gemm accumulate", which, "tile", tile, "fmts", fa, fb, "MNK", M, N, K)
+        out = torch.from_numpy(old.copy()).cuda()
+        BA, BB = i32_dev(ba), i32_dev(bb)
+        fl.scaled_gemm_accumulate(op, u8_dev(a8), fa, BA, u8_dev(b8), fb, BB, out)
+        got1 = out.cpu().numpy()
+        check_gemm(got1, ref1, bound1, f"accumulate {which} {M}x{N}x{K} fmts {fa},{fb} tile {tile}",
+                   extra=2.0 ** -24 * np.abs(ref1))
+        if K == 0:   # old + 0: the buffer itself, -0 turned to +0
+            assert np.array_equal(got1, old + np.float32(0.0))
+            assert not np.any(np.signbit(got1) & (got1 == 0))
+        fl.scaled_gemm_accumulate(op, u8_dev(c8), fa, BA, u8_dev(d8), fb, BB, out)
+        ref2 = ref1 + y2
+        check_gemm(out.cpu().numpy(), ref2, bound1 + bound2, f"accumulate twice {which} {M}x{N}x{K}",
+                   extra=2.0 ** -24 * (np.abs(ref1) + np.abs(ref2)) * (1 + 2.0 ** -20))
+
+
+@pytest.mark.parametrize("tile_size", ["128", "256"])
+def test_accumulate_native_arithmetic(fl, monkeypatch, tile_size):
+    """The same through the native FP8 MFMA, against its window bound plus the
+    addition's rounding (forward and weight gradient, each pipelined tile)."""
+    monkeypatch.setenv("FP8LIN_GEMM_TILE", tile_size)
+    rng = np.random.default_rng(zlib.crc32(f"accumulate native {tile_size}".encode()))
+    for which, (M, N, K) in (("fwd", (300, 520, 392)), ("wgrad", (512, 512, 128))):
+        fa = fb = E4M3
+        a8, b8 = operands(rng, which, M, N, K, fa, fb)
+        ba, bb = 2, -3
+        y, _ = reference(which, a8, fa, ba, b8, fb, bb)
+        old = old_buffer(rng, y.shape, float(np.sqrt(np.mean(y ** 2))))
+        op = OP_OF[which]
+        ref, _ = oracle.gemm_accumulate(op, old, a8, fa, ba, b8, fb, bb)
+        av, bv = operand_values(which, oracle.decode_fp8(a8, fa), oracle.decode_fp8(b8, fb))
+        nb = native_bound(av, bv, -(ba + bb))
+        say("gemm accumulate native", which, "MNK", M, N, K)
+        out = torch.from_numpy(old.copy()).cuda()
+        fl.scaled_gemm_accumulate(op, u8_dev(a8), fa, i32_dev(ba), u8_dev(b8), fb, i32_dev(bb), out,
+                                  math=fl.MATH_NATIVE_FP8)
+        check_gemm(out.cpu().numpy(), ref, nb, f"accumulate native {which} {M}x{N}x{K}", rel=1.0,
+                   extra=2.0 ** -24 * np.abs(ref))
+
+
 def plant_specials(rng, codes, fmt, contraction):
     """Put NaN codes (both signs; and for E5M2 the other NaN codes and both
     infinities) at random places of an operand, about one per three

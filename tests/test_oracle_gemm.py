@@ -210,3 +210,51 @@ def test_special_codes_follow_ieee_arithmetic(orc, x, w, want, want_bound):
         dw, _ = orc.gemm_wgrad(x8.T.copy(), E5M2, bias, w8.T.copy(), E4M3, 0)
         for got in (dx[0, 0], dw[0, 0]):
             assert (np.isnan(got) and np.isnan(want)) or got == want
+
+
+# ------------------------------------------------------------ accumulation
+# oracle.gemm_accumulate: old + product.  Pins: a zero buffer gives the
+# product itself; accumulating the product over the second half of the
+# contraction onto the first half's equals the whole contraction's product
+# (linearity of the sum; a dropped, negated or transposed buffer fails it);
+# all-zero operands leave the buffer as it was.
+
+CONTRACTION_AXES = {0: (1, 1), 1: (1, 0), 2: (0, 0)}   # op -> (axis of a, axis of b)
+
+
+def _halves(x, axis, h):
+    return (np.ascontiguousarray(np.take(x, np.arange(h), axis=axis)),
+            np.ascontiguousarray(np.take(x, np.arange(h, x.shape[axis]), axis=axis)))
+
+
+@pytest.mark.parametrize("op", [0, 1, 2])
+def test_accumulate_is_linear_in_the_contraction(orc, op):
+    rng = np.random.default_rng(50 + op)
+    shapes = {0: ((12, 40), (9, 40)), 1: ((12, 40), (40, 9)), 2: ((40, 12), (40, 9))}[op]
+    fa, fb = (E4M3, E4M3) if op == 0 else (E5M2, E4M3)
+    a = finite_codes(rng, shapes[0], fa)
+    b = finite_codes(rng, shapes[1], fb)
+    ba, bb = 3, -2
+    gemm = (orc.gemm_fwd, orc.gemm_dgrad, orc.gemm_wgrad)[op]
+    full, bound = gemm(a, fa, ba, b, fb, bb)
+    ax_a, ax_b = CONTRACTION_AXES[op]
+    a1, a2 = _halves(a, ax_a, 17)
+    b1, b2 = _halves(b, ax_b, 17)
+    first, _ = gemm(a1, fa, ba, b1, fb, bb)
+    # the first half's product rounded to the fp32 buffer it would sit in
+    old = first.astype(np.float32)
+    acc, bd = orc.gemm_accumulate(op, old, a2, fa, ba, b2, fb, bb)
+    second, _ = gemm(a2, fa, ba, b2, fb, bb)
+    assert np.array_equal(acc, old.astype(np.float64) + second)
+    # against the whole contraction: only the buffer's fp32 rounding differs
+    assert np.all(np.abs(acc - full) <= 2.0 ** -24 * np.abs(first) + 1e-12 * bound)
+    assert not np.allclose(acc, full - 2 * second)             # a negated product would land here
+    zero = np.zeros_like(old)
+    acc0, bd0 = orc.gemm_accumulate(op, zero, a2, fa, ba, b2, fb, bb)
+    assert np.array_equal(acc0, second) and np.array_equal(bd0, bd)
+    # all-zero operands: the buffer comes back unchanged
+    za, zb = np.zeros_like(a2), np.zeros_like(b2)
+    same, _ = orc.gemm_accumulate(op, old, za, fa, ba, zb, fb, bb)
+    assert np.array_equal(same, old.astype(np.float64))
+    with pytest.raises(ValueError):                            # a transposed buffer
+        orc.gemm_accumulate(op, np.ascontiguousarray(old.T), a2, fa, ba, b2, fb, bb)
