@@ -29,11 +29,17 @@ Scaling modes (ScalingState):
 Every bias is logged per tensor (BiasLog), without a host synchronisation.
 For post-training-quantised inference (bullet 5) FP8Linear.freeze_weight()
 quantises the weight once; later calls reuse its codes and bias.
+
+With FP8Linear(..., fuse_wgrad_accumulation=True) the weight gradient of a
+backward pass is added straight into weight.grad by
+fp8_scaled_gemm_accumulate (one fp32 addition per element), so micro-batches
+accumulate without a separate fp32 gradient per pass; the first pass after
+weight.grad was cleared (None) writes it.  The weight must be an fp32 master.
 """
 import torch
 
 from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, quantize, quantize_delayed,
-               scaled_gemm_auto)
+               scaled_gemm_accumulate, scaled_gemm_auto)
 from .mlp import BiasLog
 
 ROLES = ("x", "w", "dy")
@@ -49,6 +55,7 @@ class ScalingState:
         if mode not in ("current", "delayed"):
             raise ValueError(f"mode is 'current' or 'delayed', got {mode!r}")
         self.mode = mode
+        self.fuse_wgrad_accumulation = False
         self.margins = {r: 0 for r in ROLES}
         self.margins.update(margins or {})
         self.math = math
@@ -100,6 +107,7 @@ class FP8LinearFunction(torch.autograd.Function):
         y = scaled_gemm_auto(OP_FWD, x8, E4M3, bx, w8, E4M3, bw, math=state.math)
         ctx.saved = (x8, bx, w8, bw)
         ctx.state = state
+        ctx.weight = w
         ctx.x_shape = x.shape
         return y.reshape(*x.shape[:-1], w.shape[0])
 
@@ -109,8 +117,16 @@ class FP8LinearFunction(torch.autograd.Function):
         state = ctx.state
         dy8, bdy = state.quantise("dy", _flat(dy))
         dx = scaled_gemm_auto(OP_DGRAD, dy8, E5M2, bdy, w8, E4M3, bw, math=state.math)
-        dw = scaled_gemm_auto(OP_WGRAD, dy8, E5M2, bdy, x8, E4M3, bx, math=state.math)
+        w = ctx.weight
+        if state.fuse_wgrad_accumulation and w.grad is not None:
+            # weight.grad += dW in the product's epilogue; autograd gets no
+            # weight gradient to add
+            scaled_gemm_accumulate(OP_WGRAD, dy8, E5M2, bdy, x8, E4M3, bx, w.grad, math=state.math)
+            dw = None
+        else:
+            dw = scaled_gemm_auto(OP_WGRAD, dy8, E5M2, bdy, x8, E4M3, bx, math=state.math)
         ctx.saved = None
+        ctx.weight = None
         return dx.reshape(ctx.x_shape), dw, None
 
 
@@ -120,9 +136,12 @@ class FP8Linear(torch.nn.Module):
     default."""
 
     def __init__(self, in_features, out_features, mode="current", margins=None, math=MATH_EXACT,
-                 log=None, device=None, dtype=torch.float32, std=0.02):
+                 log=None, device=None, dtype=torch.float32, std=0.02, fuse_wgrad_accumulation=False):
         super().__init__()
+        if fuse_wgrad_accumulation and dtype != torch.float32:
+            raise ValueError("fused weight-gradient accumulation needs an fp32 weight")
         self.state = ScalingState(mode, margins, math, log)
+        self.state.fuse_wgrad_accumulation = fuse_wgrad_accumulation
         self.weight = torch.nn.Parameter(torch.randn(out_features, in_features, device=device,
                                                      dtype=dtype) * std)
 

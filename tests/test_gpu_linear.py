@@ -103,6 +103,48 @@ def test_linear_delayed_scaling_uses_the_previous_steps_amax(fl):
             lin.weight.mul_(1.5)
 
 
+def test_linear_fused_weight_gradient_accumulation(fl):
+    """fuse_wgrad_accumulation: three micro-batches' weight gradients summed
+    into weight.grad by fp8_scaled_gemm_accumulate (the first pass, with
+    weight.grad cleared, writes it).  After micro-batch t, weight.grad
+    against the oracle's sum of the t + 1 weight-gradient products (float64,
+    from the oracle's codes): within their bounds plus one fp32 rounding per
+    addition; the same holds for an unfused layer (autograd adding fp32
+    gradients), and dx is the unfused layer's bit for bit."""
+    from fp8_precision_linear_amd import linear
+    fused = linear.FP8Linear(200, 136, device="cuda", fuse_wgrad_accumulation=True)
+    plain = linear.FP8Linear(200, 136, device="cuda")
+    _, w, _ = tensors((210, 200), 136, 40)
+    with torch.no_grad():
+        fused.weight.copy_(w)
+        plain.weight.copy_(w)
+    _, bw, w8 = oracle.quantize(w.numpy().view(np.uint32), E4M3)
+    ref = np.zeros((136, 200))
+    bound = np.zeros((136, 200))
+    rounding = np.zeros((136, 200))
+    for t in range(3):
+        x, _, g = tensors((210, 200), 136, 41 + t, x_scale=1.0 + t, g_scale=1e-4 * (3 - t))
+        _, bx, x8 = oracle.quantize(synth.bf16_words(x).reshape(210, 200), E4M3)
+        _, bdy, dy8 = oracle.quantize(g.numpy().view(np.uint32), E5M2)
+        y_ref, y_bound = oracle.gemm_wgrad(dy8, E5M2, bdy, x8, E4M3, bx)
+        ref, bound = ref + y_ref, bound + y_bound
+        if t:
+            rounding += 2.0 ** -24 * np.abs(ref) * (1 + 2.0 ** -20)
+        say("fp8 linear, fused weight-gradient accumulation, micro-batch", t)
+        grads = {}
+        for name, lin in (("fused", fused), ("plain", plain)):
+            xd = x.cuda().requires_grad_()
+            lin(xd).backward(g.cuda())
+            grads[name] = xd.grad
+        torch.cuda.synchronize()
+        assert torch.equal(grads["fused"], grads["plain"])
+        for name, lin in (("fused", fused), ("plain", plain)):
+            check_gemm(lin.weight.grad.cpu().numpy(), ref, bound, f"{name} accumulated wgrad, micro-batch {t}",
+                       extra=rounding)
+    with pytest.raises(ValueError):
+        linear.FP8Linear(8, 8, device="cuda", dtype=torch.bfloat16, fuse_wgrad_accumulation=True)
+
+
 def test_linear_end_to_end_against_unquantised_fp64(fl):
     from fp8_precision_linear_amd import linear
     x, w, g = tensors((512, 384), 256, 3)
