@@ -54,7 +54,7 @@ def parse():
                     help="skip the cold (cache-flushed) amax and cast measurement")
     ap.add_argument("--cold-reps", type=int, default=5)
     ap.add_argument("--no-epilogue-amax", action="store_true",
-                    help="skip the epilogue-amax measurement on the largest product")
+                    help="skip the epilogue measurements (output amax, accumulation) on the largest product")
     ap.add_argument("--no-delayed", action="store_true",
                     help="skip the delayed-scaling (cast with its amax folded in) measurement")
     ap.add_argument("--no-split", action="store_true",
@@ -178,6 +178,45 @@ def epilogue_amax(fl, w, plan, q, outs, math, op_of, reps=9):
             "gemm_us": round(t_plain, 1), "gemm_with_epilogue_amax_us": round(t_fused, 1),
             "gemm_then_amax_pass_us": round(t_sep, 1),
             "saved_us": round(t_sep - t_fused, 1)}
+
+
+def epilogue_accumulate(fl, w, plan, q, outs, math, op_of, reps=9):
+    """The largest product of the step added into an fp32 buffer (a gradient
+    accumulated over micro-batches) two ways (interleaved, median of `reps`,
+    gpu_us): fp8_scaled_gemm_accumulate (the add in the product's epilogue),
+    and the product into a second buffer followed by an elementwise add
+    (torch's, 12 bytes an element); the plain product beside them.  The
+    buffer's contents do not matter for the timing."""
+    import statistics
+
+    import torch
+    gemms = [i for i in plan if i[0] == "gemm"]
+    if not gemms:
+        return None
+    _, l, which = max(gemms, key=lambda i: i[1].M * i[1].N * i[1].K)
+    an, bn, _ = gemm_operands(l, which)
+    a8, ba, _, fa = q[an]
+    b8, bb, _, fb = q[bn]
+    out = outs[(l.name, which)]
+    tmp = torch.empty_like(out)
+    op = op_of[which]
+    plain = lambda: fl.scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=math, out=out)
+    fused = lambda: fl.scaled_gemm_accumulate(op, a8, fa, ba, b8, fb, bb, out, math=math)
+
+    def separate():
+        fl.scaled_gemm(op, a8, fa, ba, b8, fb, bb, math=math, out=tmp)
+        out.add_(tmp)
+
+    ts = {"plain": [], "fused": [], "separate": []}
+    for _ in range(reps):
+        for k, fn in (("plain", plain), ("fused", fused), ("separate", separate)):
+            ts[k].append(gpu_us(fn))
+    t_plain, t_fused, t_sep = (statistics.median(ts[k]) for k in ("plain", "fused", "separate"))
+    del tmp
+    plain()   # the step's own output again
+    return {"product": f"{l.name}:{which}:{l.M}x{l.N}x{l.K}",
+            "gemm_us": round(t_plain, 1), "gemm_accumulate_us": round(t_fused, 1),
+            "gemm_then_add_pass_us": round(t_sep, 1), "saved_us": round(t_sep - t_fused, 1)}
 
 
 def delayed_quant(fl, w, plan, q, x, reps=9):
@@ -1306,6 +1345,7 @@ def main():
     graph_info = None if args.no_graph else graph_replay(b.step, q, outs, args.steps)
     cold = None if args.no_cold else cold_quant(fl, w, plan, q, x, args.cold_reps)
     epi = None if args.no_epilogue_amax else epilogue_amax(fl, w, plan, q, outs, b.math, b.op_of)
+    acc = None if args.no_epilogue_amax else epilogue_accumulate(fl, w, plan, q, outs, b.math, b.op_of)
     delayed = None if args.no_delayed else delayed_quant(fl, w, plan, q, x)
     one_call = None if args.no_delayed else one_call_quant(fl, w, plan, q, x)
     # the timed step's own quantisation call (one fp8_quantize_multi over every
@@ -1411,6 +1451,7 @@ def main():
         },
         "cold": cold,
         "epilogue_amax": epi,
+        "epilogue_accumulate": acc,
         "delayed_scaling": delayed,
         "one_call_quantisation": one_call,
         "step_products_call": products_call(b, step_flops),

@@ -312,32 +312,17 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[TM][TN]) {
 // Unscale and store a wave's TM x TN block of 32x32 tiles whose top-left
 // output is (row0, col0).  32x32 accumulator layout: register r of lane l
 // holds row 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32.  With
-// AMAX the largest stored magnitude is folded into *p.amax.  With ACC each
-// output is first read and the unscaled sum added to it (one fp32 addition);
-// the reads of a row of tiles are all issued before its stores.  The stores
-// are non-temporal: the output is not read back by the product, and a wave
-// of tiles writes about twice an XCD's L2 in outputs (measured: 0.2-1%
-// faster).
-template <bool AMAX, bool ACC = false, int TM, int TN>
+// AMAX the largest stored magnitude is folded into *p.amax.  The stores are
+// non-temporal: the output is not read back by the product, and a wave of
+// tiles writes about twice an XCD's L2 in outputs (measured: 0.2-1% faster).
+template <bool AMAX, int TM, int TN>
 __device__ __forceinline__ void store_block_as(const GemmProblem& p, const v16f (&acc)[TM][TN],
                                                int row0, int col0, int lane) {
   const int h = lane >> 5, rl = lane & 31;
   const int unscale = -(*p.bias_a + *p.bias_b);
   uint32_t mx = 0;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    float old[TN][16];
-    if constexpr (ACC) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = col0 + j * 32 + rl;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          old[j][r] = (row < p.m && col < p.n) ? p.c[(int64_t)row * p.ldc + col] : 0.0f;
-        }
-      }
-    }
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int col = col0 + j * 32 + rl;
@@ -345,15 +330,55 @@ __device__ __forceinline__ void store_block_as(const GemmProblem& p, const v16f 
       for (int r = 0; r < 16; ++r) {
         const int row = row0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < p.m && col < p.n) {
-          float v = __builtin_ldexpf(acc[i][j][r], unscale);
-          if constexpr (ACC) v = old[j][r] + v;
+          const float v = __builtin_ldexpf(acc[i][j][r], unscale);
           __builtin_nontemporal_store(v, &p.c[(int64_t)row * p.ldc + col]);
           if constexpr (AMAX) mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu);
         }
       }
     }
-  }
   if constexpr (AMAX) amax_fold(mx, p.amax);
+}
+
+// The same block added into the output: out = old + the unscaled sum, one
+// fp32 addition per element.  The old values of tile-row i + 1 are loaded
+// before tile-row i is added and stored (two rows of them in registers), so
+// only the first row's read latency is exposed.  Addresses are one per-lane
+// pointer (row0 + 4h, col0 + lane % 32) plus a row offset that is the same
+// for every lane, which keeps the 64-bit address arithmetic out of the
+// vector registers that hold the old values.
+template <int TM, int TN>
+__device__ __forceinline__ void accumulate_block(const GemmProblem& p, const v16f (&acc)[TM][TN],
+                                                 int row0, int col0, int lane) {
+  const int h = lane >> 5, rl = lane & 31;
+  const int unscale = -(*p.bias_a + *p.bias_b);
+  const int rlane = row0 + 4 * h, clane = col0 + rl;
+  float* const q = p.c + (int64_t)rlane * p.ldc + clane;
+  // element (i, j, r): row rlane + dr, column clane + 32 j, dr = 32 i + 8 (r / 4) + r % 4
+  auto in = [&](int dr, int j) { return rlane + dr < p.m && clane + 32 * j < p.n; };
+  auto at = [&](int dr, int j) { return q + (int64_t)dr * p.ldc + 32 * j; };
+  float old[2][TN][16];
+  auto load_row = [&](int i, float (&o)[TN][16]) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dr = 32 * i + 8 * (r >> 2) + (r & 3);
+        o[j][r] = in(dr, j) ? *at(dr, j) : 0.0f;
+      }
+  };
+  load_row(0, old[0]);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i + 1 < TM) load_row(i + 1, old[(i + 1) & 1]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dr = 32 * i + 8 * (r >> 2) + (r & 3);
+        if (in(dr, j))
+          __builtin_nontemporal_store(old[i & 1][j][r] + __builtin_ldexpf(acc[i][j][r], unscale), at(dr, j));
+      }
+  }
 }
 
 // The epilogue of a kernel instantiated with ACC (fp8_scaled_gemm_accumulate,
@@ -364,7 +389,7 @@ __device__ __forceinline__ void store_block_as(const GemmProblem& p, const v16f 
 template <bool ACC, int TM, int TN>
 __device__ __forceinline__ void store_block(const GemmProblem& p, const v16f (&acc)[TM][TN],
                                             int row0, int col0, int lane) {
-  if constexpr (ACC) store_block_as<false, true>(p, acc, row0, col0, lane);
+  if constexpr (ACC) accumulate_block(p, acc, row0, col0, lane);
   else if (p.amax) store_block_as<true>(p, acc, row0, col0, lane);
   else store_block_as<false>(p, acc, row0, col0, lane);
 }

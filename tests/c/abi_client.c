@@ -5,8 +5,10 @@
  *   abi_client checks        argument checks and status strings (no device)
  *   abi_client run DIR N     quantise a seeded bf16 vector of N elements to
  *                            E4M3, multiply a 64 x 128 product of it with a
- *                            seeded E4M3 weight, and write the amax, bias,
- *                            codes and product to DIR as raw files
+ *                            seeded E4M3 weight, add the product onto a
+ *                            copy of it (fp8_scaled_gemm_accumulate), and
+ *                            write the amax, bias, codes and both outputs to
+ *                            DIR as raw files
  * Exit status 0 on success.
  */
 #include <stdint.h>
@@ -27,6 +29,7 @@ extern hipError_t hipStreamSynchronize(hipStream_t s);
 extern hipError_t hipStreamDestroy(hipStream_t s);
 #define H2D 1
 #define D2H 2
+#define D2D 3
 
 static int expect(const char* what, int got, int want) {
   if (got != want) {
@@ -46,6 +49,7 @@ static int checks(void) {
   bad += expect("cast null", fp8_scale_cast(p, FP8_IN_FP32, 4, NULL, FP8_E5M2, (uint8_t*)p, NULL), FP8_ERR_NULL);
   bad += expect("gemm E3M4", fp8_scaled_gemm_fwd((uint8_t*)p, FP8_E3M4, (int32_t*)p, (uint8_t*)p, FP8_E4M3, (int32_t*)p, 8, 8, 8, (float*)p, NULL), FP8_ERR_FORMAT);
   bad += expect("gemm op", fp8_scaled_gemm((fp8_gemm_op_t)5, FP8_GEMM_EXACT, (uint8_t*)p, FP8_E4M3, (int32_t*)p, (uint8_t*)p, FP8_E4M3, (int32_t*)p, 8, 8, 8, (float*)p, NULL), FP8_ERR_OP);
+  bad += expect("accumulate null", fp8_scaled_gemm_accumulate(FP8_GEMM_WGRAD, FP8_GEMM_EXACT, (uint8_t*)p, FP8_E5M2, (int32_t*)p, (uint8_t*)p, FP8_E4M3, (int32_t*)p, 8, 8, 8, NULL, NULL), FP8_ERR_NULL);
   bad += expect("swiglu size", fp8_swiglu_fwd((float*)p, -2, 4, (uint16_t*)p, NULL, NULL), FP8_ERR_SIZE);
   bad += expect("workspace op", (int)fp8_scaled_gemm_workspace_bytes((fp8_gemm_op_t)7, 8, 8, 64), FP8_ERR_OP);
   if (fp8_scaled_gemm_workspace_bytes(FP8_GEMM_FWD, 128, 8192, 8192) != 4LL * 128 * 8192 * 4) bad++;
@@ -114,6 +118,13 @@ static int run(const char* dir, int64_t n) {
   TRY(fp8_scale_cast(dx, FP8_IN_BF16, n, (const int32_t*)dbias, FP8_E4M3, (uint8_t*)dy, st));
   TRY(fp8_scaled_gemm_fwd((const uint8_t*)dy, FP8_E4M3, (const int32_t*)dbias, (const uint8_t*)dw,
                           FP8_E4M3, (const int32_t*)dbw, M, N, K, (float*)dout, st));
+  /* the product added onto a copy of itself: twice the product */
+  void* dacc;
+  if (hipMalloc(&dacc, (size_t)(M * N) * 4) || hipStreamSynchronize(st) ||
+      hipMemcpy(dacc, dout, (size_t)(M * N) * 4, D2D))
+    return 3;
+  TRY(fp8_scaled_gemm_accumulate(FP8_GEMM_FWD, FP8_GEMM_EXACT, (const uint8_t*)dy, FP8_E4M3, (const int32_t*)dbias,
+                                 (const uint8_t*)dw, FP8_E4M3, (const int32_t*)dbw, M, N, K, (float*)dacc, st));
   /* the same quantisation in one call, into separate buffers */
   void *dy1, *damax1, *dbias1;
   if (hipMalloc(&dy1, (size_t)n) || hipMalloc(&damax1, 4) || hipMalloc(&dbias1, 4)) return 3;
@@ -127,8 +138,10 @@ static int run(const char* dir, int64_t n) {
       hipMemcpy(codes1, dy1, (size_t)n, D2H))
     return 4;
   float* out = malloc((size_t)(M * N) * 4);
+  float* out2 = malloc((size_t)(M * N) * 4);
   if (hipMemcpy(&amax, damax, 4, D2H) || hipMemcpy(&bias, dbias, 4, D2H) ||
-      hipMemcpy(codes, dy, (size_t)n, D2H) || hipMemcpy(out, dout, (size_t)(M * N) * 4, D2H))
+      hipMemcpy(codes, dy, (size_t)n, D2H) || hipMemcpy(out, dout, (size_t)(M * N) * 4, D2H) ||
+      hipMemcpy(out2, dacc, (size_t)(M * N) * 4, D2H))
     return 4;
   if (memcmp(&amax, &amax1, 4) != 0 || bias != bias1 || memcmp(codes, codes1, (size_t)n) != 0) {
     fprintf(stderr, "fp8_quantize differs from amax -> compute_bias -> scale_cast\n");
@@ -137,11 +150,13 @@ static int run(const char* dir, int64_t n) {
   int bad = write_file(dir, "x.bf16", x, (size_t)n * 2) + write_file(dir, "w.e4m3", w, (size_t)(N * K)) +
             write_file(dir, "amax.f32", &amax, 4) + write_file(dir, "bias.i32", &bias, 4) +
             write_file(dir, "codes.u8", codes, (size_t)n) +
-            write_file(dir, "y.f32", out, (size_t)(M * N) * 4);
+            write_file(dir, "y.f32", out, (size_t)(M * N) * 4) +
+            write_file(dir, "y2.f32", out2, (size_t)(M * N) * 4);
   hipFree(dx); hipFree(dy); hipFree(damax); hipFree(dbias); hipFree(dw); hipFree(dbw); hipFree(dout);
+  hipFree(dacc);
   hipFree(dy1); hipFree(damax1); hipFree(dbias1);
   hipStreamDestroy(st);
-  free(x); free(w); free(codes); free(codes1); free(out);
+  free(x); free(w); free(codes); free(codes1); free(out); free(out2);
   return bad ? 5 : 0;
 }
 

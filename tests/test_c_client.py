@@ -1,9 +1,10 @@
 """The C ABI from a plain C program (tests/c/abi_client.c, built with gcc
 against include/fp8lin.h and libfp8lin.so; no Python in the client).  Without
 a GPU it checks the argument errors and status strings; on the GPU it
-quantises a seeded bf16 vector and runs a forward product, and its output
-files are compared with the oracle (amax, bias and codes bit-exact; the
-product within 1e-5 * 2^-(ba+bb) * sum |a||b|)."""
+quantises a seeded bf16 vector and runs a forward product (and adds it onto a
+copy of its output with fp8_scaled_gemm_accumulate), and its output files are
+compared with the oracle (amax, bias and codes bit-exact; the product within
+1e-5 * 2^-(ba+bb) * sum |a||b|)."""
 import os
 import subprocess
 
@@ -48,3 +49,6 @@ def test_c_client_quantise_and_product(client, tmp_path):
     assert np.array_equal(rd("codes.u8", np.uint8), codes)
     ref, bound = oracle.gemm_fwd(codes[:64 * 128].reshape(64, 128), 0, b, w, 0, 3)
     check_gemm(rd("y.f32", np.float32).reshape(64, 48), ref, bound, "C client product")
+    # fp8_scaled_gemm_accumulate of the same product onto a copy of it:
+    # 2 * (gpu product), exact in fp32, so within twice the product's bound of 2 * ref
+    check_gemm(rd("y2.f32", np.float32).reshape(64, 48), 2 * ref, 2 * bound, "C client accumulate")
