@@ -33,7 +33,7 @@ int64_t gemm_group_plan(const GemmProblem* ps, int count, GroupSlot* plan) {
   auto eligible = [](const GemmProblem& p) {
     if (p.m <= 0 || p.n <= 0 || p.ldc != p.n) return false;
     const int64_t tiles = (int64_t)((p.m + 127) / 128) * ((p.n + 127) / 128);
-    if (tiles > kGroupMaxTiles) return false;
+    if (tiles >= kGroupMaxTiles) return false;
     if (p.a_kmajor && p.b_kmajor) return pipe_ok<true, true>(p);
     if (p.a_kmajor && !p.b_kmajor) return pipe_ok<true, false>(p);
     if (!p.a_kmajor && !p.b_kmajor) return pipe_ok<false, false>(p);

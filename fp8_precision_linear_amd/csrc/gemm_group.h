@@ -8,8 +8,9 @@
 // the group's shortest contraction, so the blocks do similar work; a split
 // product's slices store raw sums in the caller's workspace, and one more
 // launch adds them in slice order and unscales (the bits are the same on
-// every call).  Products too large to gain (more than kGroupMaxTiles tiles)
-// or that the pipelined kernels do not take run as single products.
+// every call).  Products too large to gain (kGroupMaxTiles tiles or more:
+// at least a whole wave of the single-product kernel's 256 x 256 tiles) or
+// that the pipelined kernels do not take run as single products.
 #pragma once
 
 #include "gemm_split.h"
@@ -18,7 +19,7 @@ namespace fp8lin {
 namespace gemm_detail {
 
 constexpr int kGroupMax = 14;            // products per launch (kernel-argument table)
-constexpr int kGroupMaxTiles = 1024;     // larger products fill the chip alone
+constexpr int kGroupMaxTiles = 1024;     // products this large fill the chip alone
 constexpr int kGroupMinSliceStages = 8;  // shortest contraction slice of a split
 constexpr int kGroupSlots = 512;         // 128 x 128 workgroups the chip runs at once (2 per CU)
 

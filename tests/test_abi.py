@@ -485,7 +485,7 @@ def test_gemm_group_workspace_plan():
     otherwise.  The GPT-111M layer's nine products at 2048 tokens (38016
     tile-stages, 75 per slot) are one training-step launch without a split;
     each pass alone (12672 tile-stages, 25 per slot) splits its 32- to
-    48-stage products in two.  A product of more than 1024 tiles, or whose
+    48-stage products in two.  A product of 1024 tiles or more, or whose
     contraction is not a whole number of 64-byte stages, runs alone."""
     wsb = L.fp8_scaled_gemm_group_workspace_bytes
     T = 2048
