@@ -40,7 +40,6 @@ import torch
 
 from . import (E4M3, E5M2, MATH_EXACT, OP_DGRAD, OP_FWD, OP_WGRAD, quantize, quantize_delayed,
                scaled_gemm_accumulate, scaled_gemm_auto)
-from .mlp import BiasLog
 
 ROLES = ("x", "w", "dy")
 FORMATS = {"x": E4M3, "w": E4M3, "dy": E5M2}
@@ -49,7 +48,7 @@ FORMATS = {"x": E4M3, "w": E4M3, "dy": E5M2}
 class ScalingState:
     """Per-tensor scaling of one linear layer: margins, the mode ("current" or
     "delayed"), each role's amax from its last quantisation (device
-    float32[1]), and an optional BiasLog."""
+    float32[1]), and an optional bias log (mlp.BiasLog)."""
 
     def __init__(self, mode="current", margins=None, math=MATH_EXACT, log=None):
         if mode not in ("current", "delayed"):
