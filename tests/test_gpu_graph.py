@@ -1,6 +1,7 @@
-"""fp8_quantize (both of its paths) and a product captured as a HIP graph:
-every replay, with the inputs rewritten in place and eager work between the
-replays, gives the eager calls' outputs bit for bit.  The library launches on
+"""fp8_quantize (both of its paths), a product, a split product and an
+accumulating product captured as HIP graphs: every replay, with the inputs
+rewritten in place and eager work between the replays, gives the eager
+calls' outputs bit for bit.  The library launches on
 torch's current stream, so capture records its kernels (no memset nodes: the
 amax word is cleared by a kernel)."""
 import pytest
@@ -109,3 +110,55 @@ def test_split_product_replayed_from_a_graph(fl):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(ref.view(torch.int32), y.view(torch.int32)), r
+
+
+
+def test_accumulating_product_replayed_from_a_graph(fl):
+    """fp8_scaled_gemm_accumulate captured as a graph (a weight gradient summed
+    over micro-batches): each replay adds the product of the operands then in
+    place to the buffer.  A replay from a given buffer equals the eager call
+    from the same buffer bit for bit, and so does a second replay on top of
+    the first."""
+    M, N, K = 1024, 768, 512    # wgrad: dY8 [M x N], X8 [M x K] -> dW [N x K]
+    dy8 = torch.empty(M, N, dtype=torch.uint8, device="cuda")
+    x8 = torch.empty(M, K, dtype=torch.uint8, device="cuda")
+    bdy = torch.tensor([20], dtype=torch.int32, device="cuda")
+    bx = torch.tensor([3], dtype=torch.int32, device="cuda")
+    dw = torch.zeros(N, K, dtype=torch.float32, device="cuda")
+
+    def codes(t, seed, dtype):
+        v = torch.randn(t.shape, device="cuda", generator=torch.Generator(device="cuda").manual_seed(seed))
+        t.copy_((v * 8).to(dtype).view(torch.uint8))
+
+    def step():
+        fl.scaled_gemm_accumulate(fl.OP_WGRAD, dy8, fl.E5M2, bdy, x8, fl.E4M3, bx, dw)
+
+    codes(dy8, 1, torch.float8_e5m2)
+    codes(x8, 2, torch.float8_e4m3fn)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        step()
+    for r in range(4):
+        say("graph replay, accumulating product", "replay", r)
+        codes(x8, 10 + r, torch.float8_e4m3fn)
+        start = dw.clone()
+        step()                          # eager: start + product
+        torch.cuda.synchronize()
+        ref1 = dw.clone()
+        dw.copy_(start)
+        graph.replay()                  # the same from the same buffer
+        torch.cuda.synchronize()
+        assert torch.equal(ref1.view(torch.int32), dw.view(torch.int32)), r
+        graph.replay()                  # a second product on top
+        torch.cuda.synchronize()
+        got2 = dw.clone()
+        dw.copy_(ref1)
+        step()                          # eager from the same buffer
+        torch.cuda.synchronize()
+        assert torch.equal(got2.view(torch.int32), dw.view(torch.int32)), r
+        assert not torch.equal(got2, ref1)
