@@ -219,6 +219,42 @@ def epilogue_accumulate(fl, w, plan, q, outs, math, op_of, reps=9):
             "gemm_then_add_pass_us": round(t_sep, 1), "saved_us": round(t_sep - t_fused, 1)}
 
 
+def small_batch_products(fl, w, plan, q, math, op_of, rows=(1, 2, 8), reps=20):
+    """The step's forward weights with only a few rows of activations (a
+    served model decoding a token or two): each product alone, `reps` calls
+    back to back between events after a spin kernel, for each row count;
+    the rate at which its weight streams from HBM.  The activation rows are
+    the step's own codes (its first rows)."""
+    import torch
+    out = {}
+    for _, l, which in (i for i in plan if i[0] == "gemm" and i[2] == "fwd"):
+        an, bn, _ = gemm_operands(l, which)
+        a8, ba, _, fa = q[an]
+        b8, bb, _, fb = q[bn]
+        line = {}
+        for m in rows:
+            x = a8[:m].contiguous()
+            y = torch.empty(m, l.N, dtype=torch.float32, device="cuda")
+            nb = fl.gemm_workspace_bytes(op_of[which], m, l.N, l.K)
+            ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+            f = lambda: fl.scaled_gemm(op_of[which], x, fa, ba, b8, fb, bb, math=math, out=y,
+                                       workspace=ws if nb else None)
+            f()
+            torch.cuda.synchronize()
+            torch.cuda._sleep(200 * 2500)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                f()
+            e.record()
+            torch.cuda.synchronize()
+            us = s.elapsed_time(e) * 1e3 / reps
+            line[str(m)] = {"us": round(us, 1), "weight_gbs": round(l.N * l.K / (us * 1e-6) / 1e9, 1),
+                            "weight_frac": round(l.N * l.K / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        out[f"{l.name}:{l.N}x{l.K}"] = line
+    return out
+
+
 def delayed_quant(fl, w, plan, q, x, reps=9):
     """Delayed scaling on the step's in-step tensors: one fp8_quantize_delayed
     call (the bias from the amax a previous call left, the cast, and its own
@@ -1372,6 +1408,7 @@ def main():
     cold = None if args.no_cold else cold_quant(fl, w, plan, q, x, args.cold_reps)
     epi = None if args.no_epilogue_amax else epilogue_amax(fl, w, plan, q, outs, b.math, b.op_of)
     acc = None if args.no_epilogue_amax else epilogue_accumulate(fl, w, plan, q, outs, b.math, b.op_of)
+    small = None if args.no_epilogue_amax else small_batch_products(fl, w, plan, q, b.math, b.op_of)
     delayed = None if args.no_delayed else delayed_quant(fl, w, plan, q, x)
     one_call = None if args.no_delayed else one_call_quant(fl, w, plan, q, x)
     # the timed step's own quantisation call (one fp8_quantize_multi over every
@@ -1478,6 +1515,7 @@ def main():
         "cold": cold,
         "epilogue_amax": epi,
         "epilogue_accumulate": acc,
+        "small_batch_products": small,
         "delayed_scaling": delayed,
         "one_call_quantisation": one_call,
         "step_products_call": products_call(b, step_flops),

@@ -585,6 +585,14 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmProblem p, int tiles
   store_block<ACC>(p, acc, m0 + (wave >> 1) * (R / 2), n0 + (wave & 1) * (R / 2), lane);
 }
 
+}  // namespace gemm_detail
+}  // namespace fp8lin
+
+#include "gemm_gemv.h"
+
+namespace fp8lin {
+namespace gemm_detail {
+
 // ----------------------------------------------------------------- launch
 
 inline dim3 tile_grid(const GemmProblem& p, int bm, int bn, int& tiles_m, int& tiles_n) {
@@ -776,6 +784,7 @@ inline bool exact_on_bf16(const GemmProblem& p) {
 template <bool AK, bool BK>
 hipError_t launch_layout(const GemmProblem& p, hipStream_t stream) {
   if (p.m <= 0 || p.n <= 0) return hipSuccess;
+  if (gemv_ok<AK, BK>(p)) return launch_gemv(p, stream);
   if (p.math == kMathNativeFp8) return launch_math<AK, BK, kMathNativeFp8>(p, stream);
   if (exact_on_bf16(p)) return launch_math<AK, BK, kMathExactBf16>(p, stream);
   return launch_math<AK, BK, kMathExact>(p, stream);

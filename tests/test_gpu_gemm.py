@@ -118,6 +118,66 @@ def test_identity_operand_is_exact_including_subnormals(fl, tile, which):
     assert np.array_equal(got.astype(np.float64), want)
 
 
+# Forward products of one or two rows (a token or two through a weight) run
+# in the vector kernel: every W row streamed in 1 KB runs, exact fp32
+# products summed per run, per row and over the wave in a fixed order.  Rows
+# 1 and 2, a single run (K = 16), ragged tails of a run (K = 1040), column
+# counts that leave waves idle (N = 1, 17), the largest contraction it takes
+# (M * K = 64 KiB) and one past it (the tiled kernels then), K = 0.
+GEMV_SHAPES = [(1, 1000, 16), (2, 17, 1040), (1, 4103, 8192), (2, 1, 2048), (1, 256, 65536),
+               (2, 96, 32768), (1, 64, 65552), (2, 40, 0)]
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS)
+def test_one_and_two_row_forward_products(fl, fa, fb):
+    """Against the oracle within 1e-5 * sum|a||b|, through fp8_scaled_gemm,
+    fp8_scaled_gemm_ws (the same kernel, the workspace unused: the same bits),
+    fp8_scaled_gemm_amax (max |out| bit-identical) and
+    fp8_scaled_gemm_accumulate (old + product)."""
+    rng = np.random.default_rng(zlib.crc32(f"gemv {fa} {fb}".encode()))
+    for (M, N, K) in GEMV_SHAPES:
+        a8, b8 = operands(rng, "fwd", M, N, K, fa, fb)
+        ba, bb = (int(v) for v in rng.integers(-12, 20, 2))
+        say("gemm one or two rows", "fmts", fa, fb, "MNK", M, N, K)
+        A, B, BA, BB = u8_dev(a8), u8_dev(b8), i32_dev(ba), i32_dev(bb)
+        got = fl.scaled_gemm(fl.OP_FWD, A, fa, BA, B, fb, BB).cpu().numpy()
+        ref, bound = oracle.gemm_fwd(a8, fa, ba, b8, fb, bb)
+        check_gemm(got, ref, bound, f"rows {M}x{N}x{K} fmts {fa},{fb}")
+        nb = fl.gemm_workspace_bytes(fl.OP_FWD, M, N, K)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        got_ws = fl.scaled_gemm(fl.OP_FWD, A, fa, BA, B, fb, BB, workspace=ws).cpu().numpy()
+        if M * K <= 65536:   # the vector kernel either way: the same bits
+            assert np.array_equal(got_ws.view(np.uint32), got.view(np.uint32))
+        else:
+            check_gemm(got_ws, ref, bound, f"rows {M}x{N}x{K} split")
+        amax = torch.empty(1, dtype=torch.float32, device="cuda")
+        got_a = fl.scaled_gemm(fl.OP_FWD, A, fa, BA, B, fb, BB, amax=amax).cpu().numpy()
+        assert np.array_equal(got_a.view(np.uint32), got.view(np.uint32))
+        want_amax = int(np.max(got.view(np.uint32) & 0x7FFFFFFF)) if got.size else 0
+        assert int(amax.cpu().numpy().view(np.uint32)[0]) == want_amax
+        old = old_buffer(rng, ref.shape, float(np.sqrt(np.mean(ref ** 2))) if ref.size and np.any(ref) else 1.0)
+        acc_ref, _ = oracle.gemm_accumulate(0, old, a8, fa, ba, b8, fb, bb)
+        out = torch.from_numpy(old.copy()).cuda()
+        fl.scaled_gemm_accumulate(fl.OP_FWD, A, fa, BA, B, fb, BB, out)
+        check_gemm(out.cpu().numpy(), acc_ref, bound, f"rows accumulate {M}x{N}x{K}",
+                   extra=2.0 ** -24 * np.abs(acc_ref))
+
+
+def test_one_row_products_with_nan_and_inf_codes(fl):
+    """The vector kernel's IEEE arithmetic on NaN codes and E5M2 infinities,
+    as the tiled kernels' (R19): NaN where a term is NaN, inf * 0 or
+    inf - inf, that infinity where one infinite term has no opposite."""
+    rng = np.random.default_rng(zlib.crc32(b"gemv specials"))
+    for fa, fb in PAIRS:
+        a8, b8 = operands(rng, "fwd", 2, 300, 2048, fa, fb)
+        a8 = plant_specials(rng, a8, fa, 2048)
+        b8 = plant_specials(rng, b8, fb, 2048)
+        say("gemm one or two rows, specials", "fmts", fa, fb)
+        got = fl.scaled_gemm(fl.OP_FWD, u8_dev(a8), fa, i32_dev(2), u8_dev(b8), fb, i32_dev(-1)).cpu().numpy()
+        ref, bound = oracle.gemm_fwd(a8, fa, 2, b8, fb, -1)
+        check_gemm(got, ref, bound, f"rows specials fmts {fa},{fb}")
+
+
 ACC_SHAPES = [(300, 520, 392), (64, 64, 0), (257, 129, 1000), (33, 700, 130), (512, 512, 128),
               (260, 300, 17)]
 OP_OF = {"fwd": 0, "dgrad": 1, "wgrad": 2}
