@@ -589,6 +589,7 @@ __global__ __launch_bounds__(256) void gemm_quad_kernel(GemmProblem p, int tiles
 }  // namespace fp8lin
 
 #include "gemm_gemv.h"
+#include "gemm_rows.h"
 
 namespace fp8lin {
 namespace gemm_detail {
@@ -785,6 +786,8 @@ template <bool AK, bool BK>
 hipError_t launch_layout(const GemmProblem& p, hipStream_t stream) {
   if (p.m <= 0 || p.n <= 0) return hipSuccess;
   if (gemv_ok<AK, BK>(p)) return launch_gemv(p, stream);
+  if (rows_ok<AK, BK>(p))
+    return exact_on_bf16(p) ? launch_rows<kMathExactBf16>(p, stream) : launch_rows<kMathExact>(p, stream);
   if (p.math == kMathNativeFp8) return launch_math<AK, BK, kMathNativeFp8>(p, stream);
   if (exact_on_bf16(p)) return launch_math<AK, BK, kMathExactBf16>(p, stream);
   return launch_math<AK, BK, kMathExact>(p, stream);

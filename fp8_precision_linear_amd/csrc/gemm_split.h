@@ -179,12 +179,14 @@ hipError_t launch_split_math(const GemmProblem& p, const SplitPlan& sp, float* w
 // The product with a workspace: split when the plan says so and the
 // pipelined kernels take the operands (ws holds at least
 // split_workspace_bytes), otherwise exactly launch_layout.  The output must be
-// contiguous (ldc == n).  A forward product of one or two rows takes the
-// vector kernel instead (gemm_gemv.h; the workspace goes unused).
+// contiguous (ldc == n).  A forward product of at most 32 rows takes the
+// small-row kernels instead (gemm_gemv.h, gemm_rows.h; the workspace goes
+// unused).
 template <bool AK, bool BK>
 hipError_t launch_layout_ws(const GemmProblem& p, float* ws, hipStream_t stream) {
   const SplitPlan sp = plan_split(p.m, p.n, p.k);
-  if (sp.splits <= 1 || !pipe_ok<AK, BK>(p) || p.ldc != p.n || p.amax || gemv_ok<AK, BK>(p))
+  if (sp.splits <= 1 || !pipe_ok<AK, BK>(p) || p.ldc != p.n || p.amax || gemv_ok<AK, BK>(p) ||
+      rows_ok<AK, BK>(p))
     return launch_layout<AK, BK>(p, stream);
   if (p.math == kMathNativeFp8) return launch_split_math<AK, BK, kMathNativeFp8>(p, sp, ws, stream);
   if (exact_on_bf16(p)) return launch_split_math<AK, BK, kMathExactBf16>(p, sp, ws, stream);

@@ -163,16 +163,67 @@ def test_one_and_two_row_forward_products(fl, fa, fb):
                    extra=2.0 ** -24 * np.abs(acc_ref))
 
 
+# Forward products of 3 to 32 rows run in the row-streaming MFMA kernel:
+# stages of 256 contraction bytes over 32 weight rows through LDS DMA, eight
+# waves' partial sums added in a fixed order.  Rows 3..32, ragged and small
+# column counts, one stage (K = 256), 43 stages (K = 11008) and a long
+# contraction, K = 0, a contraction the kernel does not take (K % 256 != 0:
+# the tiled kernels).
+ROWS_SHAPES = [(3, 1000, 256), (8, 33, 11008), (17, 4103, 2048), (32, 96, 28672), (31, 1, 512),
+               (5, 40, 0), (8, 300, 320)]
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS)
+@pytest.mark.parametrize("mfma", ["auto", "f16", "bf16"])
+def test_few_row_forward_products(fl, monkeypatch, fa, fb, mfma):
+    """Against the oracle within 1e-5 * sum|a||b|, through fp8_scaled_gemm,
+    fp8_scaled_gemm_ws (the same kernel, the workspace unused: the same bits),
+    fp8_scaled_gemm_amax (max |out| bit-identical) and
+    fp8_scaled_gemm_accumulate (old + product)."""
+    if mfma != "auto":
+        monkeypatch.setenv("FP8LIN_EXACT_MFMA", mfma)
+    else:
+        monkeypatch.delenv("FP8LIN_EXACT_MFMA", raising=False)
+    rng = np.random.default_rng(zlib.crc32(f"rows {fa} {fb} {mfma}".encode()))
+    for (M, N, K) in ROWS_SHAPES:
+        a8, b8 = operands(rng, "fwd", M, N, K, fa, fb)
+        ba, bb = (int(v) for v in rng.integers(-12, 20, 2))
+        say("gemm few rows", "fmts", fa, fb, "mfma", mfma, "MNK", M, N, K)
+        A, B, BA, BB = u8_dev(a8), u8_dev(b8), i32_dev(ba), i32_dev(bb)
+        got = fl.scaled_gemm(fl.OP_FWD, A, fa, BA, B, fb, BB).cpu().numpy()
+        ref, bound = oracle.gemm_fwd(a8, fa, ba, b8, fb, bb)
+        check_gemm(got, ref, bound, f"few rows {M}x{N}x{K} fmts {fa},{fb} {mfma}")
+        nb = fl.gemm_workspace_bytes(fl.OP_FWD, M, N, K)
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+        got_ws = fl.scaled_gemm(fl.OP_FWD, A, fa, BA, B, fb, BB, workspace=ws).cpu().numpy()
+        if K % 256 == 0:   # the row kernel either way: the same bits
+            assert np.array_equal(got_ws.view(np.uint32), got.view(np.uint32))
+        else:
+            check_gemm(got_ws, ref, bound, f"few rows {M}x{N}x{K} split")
+        amax = torch.empty(1, dtype=torch.float32, device="cuda")
+        got_a = fl.scaled_gemm(fl.OP_FWD, A, fa, BA, B, fb, BB, amax=amax).cpu().numpy()
+        assert np.array_equal(got_a.view(np.uint32), got.view(np.uint32))
+        want_amax = int(np.max(got.view(np.uint32) & 0x7FFFFFFF)) if got.size else 0
+        assert int(amax.cpu().numpy().view(np.uint32)[0]) == want_amax
+        old = old_buffer(rng, ref.shape, float(np.sqrt(np.mean(ref ** 2))) if ref.size and np.any(ref) else 1.0)
+        acc_ref, _ = oracle.gemm_accumulate(0, old, a8, fa, ba, b8, fb, bb)
+        out = torch.from_numpy(old.copy()).cuda()
+        fl.scaled_gemm_accumulate(fl.OP_FWD, A, fa, BA, B, fb, BB, out)
+        check_gemm(out.cpu().numpy(), acc_ref, bound, f"few rows accumulate {M}x{N}x{K}",
+                   extra=2.0 ** -24 * np.abs(acc_ref))
+
+
 def test_one_row_products_with_nan_and_inf_codes(fl):
-    """The vector kernel's IEEE arithmetic on NaN codes and E5M2 infinities,
-    as the tiled kernels' (R19): NaN where a term is NaN, inf * 0 or
-    inf - inf, that infinity where one infinite term has no opposite."""
+    """The vector kernel's (2 rows) and the row kernel's (8 rows) IEEE
+    arithmetic on NaN codes and E5M2 infinities, as the tiled kernels' (R19):
+    NaN where a term is NaN, inf * 0 or inf - inf, that infinity where one
+    infinite term has no opposite."""
     rng = np.random.default_rng(zlib.crc32(b"gemv specials"))
-    for fa, fb in PAIRS:
-        a8, b8 = operands(rng, "fwd", 2, 300, 2048, fa, fb)
+    for (fa, fb), M in zip(PAIRS + PAIRS, [2] * 4 + [8] * 4):
+        a8, b8 = operands(rng, "fwd", M, 300, 2048, fa, fb)
         a8 = plant_specials(rng, a8, fa, 2048)
         b8 = plant_specials(rng, b8, fb, 2048)
-        say("gemm one or two rows, specials", "fmts", fa, fb)
+        say("gemm few rows, specials", "rows", M, "fmts", fa, fb)
         got = fl.scaled_gemm(fl.OP_FWD, u8_dev(a8), fa, i32_dev(2), u8_dev(b8), fb, i32_dev(-1)).cpu().numpy()
         ref, bound = oracle.gemm_fwd(a8, fa, 2, b8, fb, -1)
         check_gemm(got, ref, bound, f"rows specials fmts {fa},{fb}")
