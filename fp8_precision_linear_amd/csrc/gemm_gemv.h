@@ -1,11 +1,11 @@
-// The forward product for one or two rows (a token or two through a large
-// weight, as when a served model decodes at batch 1 or 2).  Each weight byte
-// is used M <= 2 times, so the product is the rate at which W streams from
-// HBM; the tiled kernels fill at most 2 of their 128 or 256 tile rows and
-// read W in 64-byte row pieces, which reaches ~3 TB/s.  Here every wave reads
-// whole rows of W in 1 KB runs (16 contiguous bytes per lane, eight runs in
-// flight), which streams at 6-7 TB/s, and forms the dot products on the
-// vector ALU.
+// The forward product for one or two rows whose contraction is a multiple of
+// 16 but not of 256 (where it is, the row kernel of gemm_rows.h takes them:
+// it streams the weight faster).  Each weight byte is used M <= 2 times, so
+// the product is the rate at which W streams from HBM; the tiled kernels fill
+// at most 2 of their 128 or 256 tile rows and read W in 64-byte row pieces,
+// which reaches ~3 TB/s.  Here every wave reads whole rows of W in 1 KB runs
+// (16 contiguous bytes per lane, eight runs in flight), which streams at
+// 5-6 TB/s, and forms the dot products on the vector ALU.
 //
 // "Training and inference of large language models using 8-bit floating
 // point", review page, "Proposed method", bullet 3 (the product of the scaled
@@ -169,7 +169,8 @@ hipError_t launch_gemv_m(const GemmProblem& p, hipStream_t stream) {
 
 // One or two rows only: the FMAs grow with the rows and the vector ALU, not
 // HBM, bounds three or more (28672 x 8192 weights: 38.1, 46.2, 68.7 and
-// 79.9 us for 1 to 4 rows, against ~72 us in the tiled kernels).
+// 79.9 us for 1 to 4 rows, against ~72 us in the tiled kernels and 37 us in
+// the row kernel).
 inline hipError_t launch_gemv(const GemmProblem& p, hipStream_t stream) {
   return p.m == 1 ? launch_gemv_m<1>(p, stream) : launch_gemv_m<2>(p, stream);
 }

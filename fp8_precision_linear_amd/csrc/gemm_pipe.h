@@ -785,9 +785,9 @@ inline bool exact_on_bf16(const GemmProblem& p) {
 template <bool AK, bool BK>
 hipError_t launch_layout(const GemmProblem& p, hipStream_t stream) {
   if (p.m <= 0 || p.n <= 0) return hipSuccess;
-  if (gemv_ok<AK, BK>(p)) return launch_gemv(p, stream);
   if (rows_ok<AK, BK>(p))
     return exact_on_bf16(p) ? launch_rows<kMathExactBf16>(p, stream) : launch_rows<kMathExact>(p, stream);
+  if (gemv_ok<AK, BK>(p)) return launch_gemv(p, stream);
   if (p.math == kMathNativeFp8) return launch_math<AK, BK, kMathNativeFp8>(p, stream);
   if (exact_on_bf16(p)) return launch_math<AK, BK, kMathExactBf16>(p, stream);
   return launch_math<AK, BK, kMathExact>(p, stream);

@@ -179,8 +179,8 @@ hipError_t launch_split_math(const GemmProblem& p, const SplitPlan& sp, float* w
 // The product with a workspace: split when the plan says so and the
 // pipelined kernels take the operands (ws holds at least
 // split_workspace_bytes), otherwise exactly launch_layout.  The output must be
-// contiguous (ldc == n).  A forward product of at most 32 rows takes the
-// small-row kernels instead (gemm_gemv.h, gemm_rows.h; the workspace goes
+// contiguous (ldc == n).  A forward product of at most 64 rows (two at most
+// when K is not a multiple of 256) takes the small-row kernels instead (gemm_gemv.h, gemm_rows.h; the workspace goes
 // unused).
 template <bool AK, bool BK>
 hipError_t launch_layout_ws(const GemmProblem& p, float* ws, hipStream_t stream) {

@@ -240,11 +240,13 @@ typedef enum {
 /* Any of the three products with a chosen arithmetic (FP8_GEMM_EXACT or
  * FP8_GEMM_NATIVE_FP8); the named entry points below are this call with
  * FP8_GEMM_EXACT.  Returns FP8_ERR_OP for an unknown op or math.
- * A forward product of one or two rows (exact arithmetic, K a multiple of 16,
- * M * K <= 65536, 16-byte aligned rows: a token or two through a weight) runs
- * on a kernel that streams the weight's rows and sums the exact fp32
- * products on the vector ALU; its results meet the same bound, with the
- * same bits on every call. */
+ * Forward products of few rows (a small batch of tokens through a weight;
+ * exact arithmetic, 16-byte aligned rows) run on kernels that stream the
+ * weight's rows: 1 to 64 rows with K a multiple of 256 on the exact MFMA
+ * (the weight's rows through LDS in 256-byte runs), one or two rows with K
+ * another multiple of 16 and M * K <= 65536 on the vector ALU (exact fp32
+ * products).  Their results meet the same bound, with the same bits on every
+ * call. */
 int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,
                     const int32_t* ba, const uint8_t* b, fp8_format_t fb, const int32_t* bb,
                     int64_t M, int64_t N, int64_t K, float* out, void* stream);
