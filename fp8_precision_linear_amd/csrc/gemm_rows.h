@@ -12,7 +12,7 @@
 // One workgroup of eight waves per 32 output columns (32 rows of W) and all M
 // rows (RB blocks of 32).  Stage = 256 contraction bytes: a 32 x 256-byte tile
 // of W and RB of X (X's rows past M re-read row M - 1 and are zeroed in the
-// fragments), SL stages in a ring, SL - 1 in flight.  Wave w multiplies bytes
+// fragments), SL stages in a ring (2 to 4), SL - 1 in flight.  Wave w multiplies bytes
 // [32w, 32w + 32) of every stage (two 32x32x16 MFMAs per row block) into its
 // own partial sums; the eight waves' partial sums meet in LDS and are added in
 // wave order, then unscaled once.
@@ -175,14 +175,23 @@ hipError_t launch_rows_acc(const GemmProblem& p, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-// Up to 32 rows: one row block, four stages (64 KB of LDS, two workgroups per
-// CU).  33 to 64 rows: two row blocks in three stages (72 KB, still two
-// workgroups per CU; four stages, 96 KB, leave one and were slower where the
-// grid exceeds the CUs: 28672 x 8192 weights at 64 rows 58.0 against 47.7 us).
+// Up to 32 rows: one row block, three stages (48 KB of LDS, three workgroups
+// per CU; four stages, two workgroups per CU, measured 1-3% slower on the 70B
+// weights and 10% on 10240 x 8192, whose 320 workgroups leave 64 CUs with two;
+// five and six stages slower still).  Two stages (32 KB, five workgroups per
+// CU) where a grid of at least 768 workgroups would not fit the CUs at three
+// and the rows are few (28672 x 8192 weights at 1 and 8 rows: 33.0 / 33.6
+// against 36.3 / 36.0 us; at 32 rows 37.1 against 36.7; with 256 or 320
+// workgroups two stages lose up to 60%).  33 to 64 rows: two row blocks in
+// three stages (72 KB, two workgroups per CU; four stages, 96 KB, leave one
+// and were slower where the grid exceeds the CUs: 28672 x 8192 weights at 64
+// rows 58.0 against 47.7 us).
 template <int MATH>
 hipError_t launch_rows(const GemmProblem& p, hipStream_t stream) {
+  if (p.m <= 8 && p.n >= 768 * 32)
+    return p.accumulate ? launch_rows_acc<MATH, true, 1, 2>(p, stream) : launch_rows_acc<MATH, false, 1, 2>(p, stream);
   if (p.m <= 32)
-    return p.accumulate ? launch_rows_acc<MATH, true, 1, 4>(p, stream) : launch_rows_acc<MATH, false, 1, 4>(p, stream);
+    return p.accumulate ? launch_rows_acc<MATH, true, 1, 3>(p, stream) : launch_rows_acc<MATH, false, 1, 3>(p, stream);
   return p.accumulate ? launch_rows_acc<MATH, true, 2, 3>(p, stream) : launch_rows_acc<MATH, false, 2, 3>(p, stream);
 }
 
