@@ -133,7 +133,7 @@ __global__ __launch_bounds__(kGemvWaves * 64) void gemm_gemv_kernel(GemmProblem 
 // Whether a product takes the vector kernel: the forward layout (both
 // operands contraction-contiguous), exact arithmetic, one or two output rows,
 // a contraction that is a multiple of 16 and whose X rows fit the LDS, 16-byte
-// aligned rows.
+// aligned rows, fewer than 2^26 columns.
 template <bool AK, bool BK>
 bool gemv_ok(const GemmProblem& p) {
   if constexpr (!(AK && BK)) {
@@ -141,6 +141,8 @@ bool gemv_ok(const GemmProblem& p) {
   } else {
     if (p.math == kMathNativeFp8 || p.m < 1 || p.m > kGemvRows || p.n < 1) return false;
     if (p.k % 16 != 0 || (int64_t)p.m * p.k > kGemvLdsBytes) return false;
+    // a dispatch counts its lanes in 32 bits: 1024 per 16 columns
+    if ((int64_t)((p.n + kGemvWaves - 1) / kGemvWaves) * (kGemvWaves * 64) > (int64_t)0xFFFFFFFF) return false;
     auto aligned = [](const void* q, int64_t ld) { return ((uintptr_t)q % 16 == 0) && (ld % 16 == 0); };
     return aligned(p.a, p.lda) && aligned(p.b, p.ldb);
   }

@@ -154,6 +154,8 @@ bool rows_ok(const GemmProblem& p) {
   } else {
     if (p.math == kMathNativeFp8 || p.m < 1 || p.m > kRowsMax || p.n < 1) return false;
     if (p.k % kRowsStage != 0) return false;
+    // a dispatch counts its lanes in 32 bits: 512 per 32 columns
+    if ((int64_t)((p.n + 31) / 32) * (kRowsWaves * 64) > (int64_t)0xFFFFFFFF) return false;
     auto aligned = [](const void* q, int64_t ld) { return ((uintptr_t)q % 16 == 0) && (ld % 16 == 0); };
     return aligned(p.a, p.lda) && aligned(p.b, p.ldb);
   }

@@ -133,3 +133,30 @@ def test_products_past_2_31_operand_bytes(fl, K):
     check_gemm(dw.cpu().numpy()[cols, kc], ref, bound, f"wgrad M={M} K={K}")
     del x8, w8, dy8, y, dx, dw
     free()
+
+
+@pytest.mark.parametrize("M,N", [(2, (1 << 26) - 16), (1, (1 << 26) + 16)])
+def test_few_row_products_at_the_largest_vector_grid(fl, M, N):
+    """A dispatch counts its lanes in 32 bits.  The one-or-two-row vector
+    kernel launches 1024 lanes per 16 columns, so it takes at most 2^26 - 16
+    columns (its largest grid, 2^32 - 1024 lanes) and hands 2^26 + 16 to the
+    tiled kernels (here the general one: K = 16).  Sampled outputs, the last
+    columns among them, against the oracle.  (The row kernel's limit, 2^28
+    columns, would need a weight of 68 GB or more.)"""
+    K = 16
+    say("few-row products at the largest grid", M, N, K)
+    x8 = random_codes((M, K), 21)
+    w8 = random_codes((N, K), 22)
+    b0, b1 = i32_dev(4), i32_dev(-3)
+    y = fl.scaled_gemm(fl.OP_FWD, x8, E4M3, b0, w8, E4M3, b1)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(N)
+    cols = np.concatenate([rng.integers(0, N, 200), N - 1 - np.arange(56)])
+    rows = rng.integers(0, M, cols.size)
+    idx = torch.from_numpy(cols).cuda()
+    wsub = w8[idx].cpu().numpy()             # the sampled weight rows only
+    ref, bound = oracle.gemm_fwd_at(x8.cpu().numpy(), E4M3, 4, wsub, E4M3, -3, rows, np.arange(cols.size))
+    got = y[torch.from_numpy(rows).cuda(), idx].cpu().numpy()
+    check_gemm(got, ref, bound, f"few rows M={M} N={N}")
+    del x8, w8, y
+    free()
