@@ -12,10 +12,10 @@
 // One workgroup of eight waves per 32 output columns (32 rows of W) and all M
 // rows (RB blocks of 32).  Stage = 256 contraction bytes: a 32 x 256-byte tile
 // of W and RB of X (X's rows past M re-read row M - 1 and are zeroed in the
-// fragments), SL stages in a ring (2 to 4), SL - 1 in flight.  Wave w multiplies bytes
-// [32w, 32w + 32) of every stage (two 32x32x16 MFMAs per row block) into its
-// own partial sums; the eight waves' partial sums meet in LDS and are added in
-// wave order, then unscaled once.
+// fragments), SL stages in a ring (2 or 3, chosen by launch_rows), SL - 1 in
+// flight.  Wave w multiplies bytes [32w, 32w + 32) of every stage (two
+// 32x32x16 MFMAs per row block) into its own partial sums; the eight waves'
+// partial sums meet in LDS and are added in wave order, then unscaled once.
 //
 // Stage order: workgroup b starts at stage 5b mod (K / 256) and wraps.  Where
 // W's rows lie a power of two apart (K = 8192), workgroups that walk the
