@@ -28,12 +28,18 @@ int64_t gemm_split_workspace_bytes(int64_t m, int64_t n, int64_t k) {
 // slot: a product is cut along the contraction only into slices of at least
 // that average (and at least kGroupMinSliceStages stages, at most 16 slices)
 // -- which happens when a launch has too few tiles to fill the slots.
+// A forward product of few rows through a weight of 16 MiB or more runs alone
+// in a small-row kernel (gemm_rows.h, gemm_gemv.h), which streams the weight
+// at 5-7 TB/s where a grouped launch's 128 x 128 tiles reach about 3.
 int64_t gemm_group_plan(const GemmProblem* ps, int count, GroupSlot* plan) {
   using namespace gemm_detail;
   auto eligible = [](const GemmProblem& p) {
     if (p.m <= 0 || p.n <= 0 || p.ldc != p.n) return false;
     const int64_t tiles = (int64_t)((p.m + 127) / 128) * ((p.n + 127) / 128);
     if (tiles >= kGroupMaxTiles) return false;
+    if (p.a_kmajor && p.b_kmajor && (int64_t)p.n * p.k >= ((int64_t)1 << 24) &&
+        (rows_ok<true, true>(p) || gemv_ok<true, true>(p)))
+      return false;
     if (p.a_kmajor && p.b_kmajor) return pipe_ok<true, true>(p);
     if (p.a_kmajor && !p.b_kmajor) return pipe_ok<true, false>(p);
     if (!p.a_kmajor && !p.b_kmajor) return pipe_ok<false, false>(p);

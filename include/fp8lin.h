@@ -319,9 +319,11 @@ int fp8_scaled_gemm_noalloc(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_fo
  * shortest contraction among them (raw sums in the workspace, then one
  * launch adds every split product's slices in slice order and unscales), so
  * the launch's blocks do similar work.  Products of 1024 tiles of 128 x 128
- * or more (a whole wave of the single product's 256 x 256 tiles), or that the
- * pipelined kernels do not take (a contraction that is not a multiple of 64,
- * misaligned rows), run as single products.
+ * or more (a whole wave of the single product's 256 x 256 tiles), forward
+ * products of few rows through a weight of 16 MiB or more that the small-row
+ * kernels take (see fp8_scaled_gemm), or products the pipelined kernels do not
+ * take (a contraction that is not a multiple of 64, misaligned rows), run as
+ * single products.
  *   descs  host array of count product descriptors (read during the call
  *          only): op and the operands, biases, sizes and output exactly as
  *          fp8_scaled_gemm's arguments.  Outputs must not overlap each other,

@@ -508,6 +508,10 @@ def test_gemm_group_workspace_plan():
     assert wsb(0, arr([_gdesc(0, M=128, N=128, K=100)]), 1) == 0
     # 128 tokens through a 70B QKV projection (80 tiles of 128 stages): 7 slices
     assert wsb(0, arr([_gdesc(0, M=128, N=10240, K=8192)]), 1) == r(7 * 128 * 10240 * 4)
+    # 64 tokens or fewer through a weight of 16 MiB or more: alone in the row
+    # kernel, no workspace (under 16 MiB: grouped and split)
+    assert wsb(0, arr([_gdesc(0, M=64, N=10240, K=8192)]), 1) == 0
+    assert wsb(0, arr([_gdesc(0, M=64, N=1024, K=8192)]), 1) > 0
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")

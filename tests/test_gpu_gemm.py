@@ -730,6 +730,25 @@ def test_grouped_products(fl, mfma, monkeypatch):
             assert same, (which, a8.shape, b8.shape)
 
 
+def test_grouped_products_of_a_small_batch(fl):
+    """A decode-shaped group (8 tokens through a 16 MiB weight and a 32 MiB
+    one, 2 tokens through one with K not a multiple of 256, and a small
+    weight): the large-weight products run alone in the small-row kernels,
+    bit-identical to fp8_scaled_gemm; the small one stays grouped; every
+    product against the oracle."""
+    rng = np.random.default_rng(zlib.crc32(b"group small batch"))
+    specs = [("fwd", 8, 8192, 2048), ("fwd", 8, 4096, 8192), ("fwd", 2, 65536, 272), ("fwd", 8, 768, 768)]
+    prods, host = _group_case(fl, rng, specs)
+    say("grouped small batch", len(prods))
+    outs = fl.scaled_gemm_group(prods)
+    for (op, A, fa, BA, B, fb, BB), (which, a8, _, ba, b8, _, bb), got in zip(prods, host, outs):
+        ref, bound = reference(which, a8, fa, ba, b8, fb, bb)
+        check_gemm(got.cpu().numpy(), ref, bound, f"grouped small batch {a8.shape} {b8.shape}")
+        single = fl.scaled_gemm(op, A, fa, BA, B, fb, BB)
+        if b8.size >= 1 << 24:   # alone in the small-row kernel: the same call
+            assert torch.equal(single.view(torch.int32), got.view(torch.int32)), b8.shape
+
+
 def test_grouped_products_native_arithmetic(fl):
     """The native FP8 arithmetic through the group, within its own bound
     (tests/mfma_bound.py; one extra fp32 rounding per slice added)."""
