@@ -194,18 +194,22 @@ def test_linear_frozen_weight_for_inference(fl):
         assert not torch.equal(lin(xd), y_ref)
 
 
-def test_linear_small_batch_splits_its_forward_product(fl):
-    """32 tokens through a 4096 -> 1024 layer: the forward output has 8 tiles,
-    so its product runs split along the contraction (fp8_scaled_gemm_ws);
-    every product against the oracle."""
+@pytest.mark.parametrize("tokens", [1, 32, 100])
+def test_linear_small_batch_forward_product(fl, tokens):
+    """A few tokens through a 4096 -> 1024 layer: the forward output has 8
+    tiles of 128 x 128, so the layer hands its product a workspace
+    (fp8_scaled_gemm_ws).  32 tokens: the row kernel takes the product (the
+    workspace goes unused); 100 tokens: it runs split along the
+    contraction; 1 token: the row kernel as a decoding step would run it.
+    Every product against the oracle."""
     from fp8_precision_linear_amd import linear
-    x, w, g = tensors((32, 4096), 1024, 2)
-    assert fl.gemm_workspace_bytes(fl.OP_FWD, 32, 1024, 4096) > 0
+    x, w, g = tensors((tokens, 4096), 1024, 2)
+    assert fl.gemm_workspace_bytes(fl.OP_FWD, tokens, 1024, 4096) > 0
     lin = linear.FP8Linear(4096, 1024, device="cuda")
     with torch.no_grad():
         lin.weight.copy_(w)
     xd = x.cuda().requires_grad_()
-    say("fp8 linear, 32 tokens, split forward product")
+    say("fp8 linear, small batch", tokens, "tokens")
     y = lin(xd)
     y.backward(g.cuda())
     torch.cuda.synchronize()
@@ -214,7 +218,7 @@ def test_linear_small_batch_splits_its_forward_product(fl):
     _, bw, w8 = oracle.quantize(ww, E4M3)
     _, bdy, dy8 = oracle.quantize(gw, E5M2)
     ref, bound = oracle.gemm_fwd(x8, E4M3, bx, w8, E4M3, bw)
-    check_gemm(y.detach().cpu().numpy(), ref, bound, "small-batch linear fwd (split)")
+    check_gemm(y.detach().cpu().numpy(), ref, bound, f"small-batch linear fwd ({tokens} tokens)")
     ref, bound = oracle.gemm_wgrad(dy8, E5M2, bdy, x8, E4M3, bx)
     check_gemm(lin.weight.grad.cpu().numpy(), ref, bound, "small-batch linear wgrad")
     ref, bound = oracle.gemm_dgrad(dy8, E5M2, bdy, w8, E4M3, bw)
