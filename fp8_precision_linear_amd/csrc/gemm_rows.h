@@ -182,15 +182,16 @@ hipError_t launch_rows_acc(const GemmProblem& p, hipStream_t stream) {
 // weights and 10% on 10240 x 8192, whose 320 workgroups leave 64 CUs with two;
 // five and six stages slower still).  Two stages (32 KB, five workgroups per
 // CU) where a grid of at least 768 workgroups would not fit the CUs at three
-// and the rows are few (28672 x 8192 weights at 1 and 8 rows: 33.0 / 33.6
-// against 36.3 / 36.0 us; at 32 rows 37.1 against 36.7; with 256 or 320
-// workgroups two stages lose up to 60%).  33 to 64 rows: two row blocks in
+// and the rows are few (28672 x 8192 weights at 1, 8, 16 rows: 33.0, 33.6,
+// 34.7 against 36.3, 36.0, 36.3 us; 57344 x 8192 at 24 rows 89 against 97;
+// from 28 rows mixed: 32768 x 4096 at 32 rows 21.7 against 20.8; with 256 or
+// 320 workgroups two stages lose up to 60%).  33 to 64 rows: two row blocks in
 // three stages (72 KB, two workgroups per CU; four stages, 96 KB, leave one
 // and were slower where the grid exceeds the CUs: 28672 x 8192 weights at 64
 // rows 58.0 against 47.7 us).
 template <int MATH>
 hipError_t launch_rows(const GemmProblem& p, hipStream_t stream) {
-  if (p.m <= 8 && p.n >= 768 * 32)
+  if (p.m <= 24 && p.n >= 768 * 32)
     return p.accumulate ? launch_rows_acc<MATH, true, 1, 2>(p, stream) : launch_rows_acc<MATH, false, 1, 2>(p, stream);
   if (p.m <= 32)
     return p.accumulate ? launch_rows_acc<MATH, true, 1, 3>(p, stream) : launch_rows_acc<MATH, false, 1, 3>(p, stream);
