@@ -265,8 +265,11 @@ int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, c
   if (int s = make_problem(op, math, a, fa, ba, b, fb, bb, M, N, K, out, p, empty)) return s;
   p.accumulate = accumulate;
   bool split = false;
+  // the static scratch bounds its plan; a caller's workspace is sized by
+  // fp8_scaled_gemm_workspace_bytes (no bound)
+  const int64_t max_bytes = ws_mode == kStaticScratch ? (int64_t)FP8_NOALLOC_SCRATCH_BYTES : INT64_MAX;
   if (ws_mode != kNoWorkspace && !empty) {
-    const int64_t need = fp8lin::gemm_split_workspace_bytes(p.m, p.n, p.k);
+    const int64_t need = fp8lin::gemm_split_workspace_bytes(p.m, p.n, p.k, max_bytes);
     if (need > 0) {
       if (ws_mode == kStaticScratch) {
         if (need > (int64_t)FP8_NOALLOC_SCRATCH_BYTES) return FP8_ERR_SIZE;
@@ -291,9 +294,9 @@ int scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa, c
   if (split) {
     float* w = static_cast<float*>(ws);
     switch (op) {
-      case FP8_GEMM_FWD: return hip_status(fp8lin::launch_gemm_fwd_ws(p, w, st));
-      case FP8_GEMM_DGRAD: return hip_status(fp8lin::launch_gemm_dgrad_ws(p, w, st));
-      default: return hip_status(fp8lin::launch_gemm_wgrad_ws(p, w, st));
+      case FP8_GEMM_FWD: return hip_status(fp8lin::launch_gemm_fwd_ws(p, w, max_bytes, st));
+      case FP8_GEMM_DGRAD: return hip_status(fp8lin::launch_gemm_dgrad_ws(p, w, max_bytes, st));
+      default: return hip_status(fp8lin::launch_gemm_wgrad_ws(p, w, max_bytes, st));
     }
   }
   switch (op) {
@@ -382,7 +385,7 @@ int64_t fp8_scaled_gemm_workspace_bytes(fp8_gemm_op_t op, int64_t M, int64_t N, 
   if (bad_dim(M) || bad_dim(N) || bad_dim(K)) return FP8_ERR_SIZE;
   int64_t rows, cols, depth;
   if (!out_shape(op, M, N, K, rows, cols, depth)) return FP8_ERR_OP;
-  return fp8lin::gemm_split_workspace_bytes(rows, cols, depth);
+  return fp8lin::gemm_split_workspace_bytes(rows, cols, depth, INT64_MAX);
 }
 
 int fp8_scaled_gemm_ws(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t fa,

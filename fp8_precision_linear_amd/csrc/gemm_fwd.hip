@@ -10,12 +10,12 @@ hipError_t launch_gemm_fwd(const GemmProblem& p, hipStream_t stream) {
   return gemm_detail::launch_layout<true, true>(p, stream);
 }
 
-hipError_t launch_gemm_fwd_ws(const GemmProblem& p, float* ws, hipStream_t stream) {
-  return gemm_detail::launch_layout_ws<true, true>(p, ws, stream);
+hipError_t launch_gemm_fwd_ws(const GemmProblem& p, float* ws, int64_t max_bytes, hipStream_t stream) {
+  return gemm_detail::launch_layout_ws<true, true>(p, ws, max_bytes, stream);
 }
 
-int64_t gemm_split_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  return gemm_detail::split_workspace_bytes(m, n, k);
+int64_t gemm_split_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t max_bytes) {
+  return gemm_detail::split_workspace_bytes(m, n, k, max_bytes);
 }
 
 // Which products run grouped and how they are split.  The training-step

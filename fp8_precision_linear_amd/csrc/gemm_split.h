@@ -35,24 +35,43 @@ inline int64_t split_slots() {
   return s < 1 ? 1 : s;
 }
 
-// The split for an m x n output with contraction k: as many slices as the
-// chip has room for beside the output's 128x128 tiles, each at least
-// kSplitMinStages stages; none when the tiles already fill the chip, or the
-// contraction is not a whole number of stages (those products run the
-// general kernel).
-inline SplitPlan plan_split(int64_t m, int64_t n, int64_t k) {
+// The split for an m x n output with contraction k, each slice at least
+// kSplitMinStages stages; none when the contraction is not a whole number of
+// stages (those products run the general kernel).  Two candidates: as many
+// slices as leave one workgroup per CU beside the output's 128x128 tiles, and
+// as many as leave two.  Each is costed in stage times of a workgroup alone
+// on a CU (~0.5 us: 10240 x 8192 at 192 rows, 160 workgroups of 128 stages,
+// 63.5 us): the busiest CU's stages (ceil(W / slots) workgroups of nk / s
+// stages, W = tiles x s), divided by 1.15 where two workgroups share a CU
+// (one's LDS reads and conversions run under the other's MFMAs: 8192 x 28672
+// at 65 rows, 112 stages per CU as four or eight slices, 71.2 against 62.6
+// us), plus the pass that adds the slices ((s + 1) x m x n x 4 bytes at
+// ~5 TB/s).  On 20 outputs of 65-384 rows through 70B weights this takes the
+// faster plan, up to 27% faster than one workgroup per CU alone (10240 x 8192
+// at 192 rows: three slices 49.9 us, unsplit 63.2), and keeps plans the
+// second candidate would slow (8192 x 8192 at 128 rows: four slices 27.2,
+// five 30.6).  The second candidate is taken only if its workspace fits
+// max_bytes; the first needs at most slots x 64 KiB (16 MiB).
+inline SplitPlan plan_split(int64_t m, int64_t n, int64_t k, int64_t max_bytes = INT64_MAX) {
   if (m <= 0 || n <= 0 || k <= 0 || k % kPipeBK != 0) return SplitPlan{1, 0};
   const int64_t tiles = ((m + 127) / 128) * ((n + 127) / 128);
-  const int64_t nk = k / kPipeBK;
-  int64_t s = split_slots() / tiles;
-  s = s < nk / kSplitMinStages ? s : nk / kSplitMinStages;
+  const int64_t nk = k / kPipeBK, smax = nk / kSplitMinStages, slots = split_slots();
+  auto clamp = [&](int64_t v) { return v < smax ? v : smax; };
+  auto cost = [&](int64_t v) {
+    const int64_t per_cu = (tiles * v + slots - 1) / slots;
+    const double reduce = v > 1 ? (double)(v + 1) * (double)m * (double)n * 4.0 / 2.5e6 : 0.0;
+    return (double)per_cu * (double)nk / (double)v / (per_cu > 1 ? 1.15 : 1.0) + reduce;
+  };
+  int64_t s = clamp(slots / tiles);
+  const int64_t s2 = clamp(2 * slots / tiles);
+  if (s2 > s && s2 >= 2 && cost(s2) < cost(s < 1 ? 1 : s) - 1e-9 && s2 * m * n * 4 <= max_bytes) s = s2;
   if (s < 2) return SplitPlan{1, 0};
   const int64_t per = (nk + s - 1) / s;  // stages per slice; the last may be shorter
   return SplitPlan{(int)((nk + per - 1) / per), (int)(per * kPipeBK)};
 }
 
-inline int64_t split_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  const SplitPlan sp = plan_split(m, n, k);
+inline int64_t split_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t max_bytes = INT64_MAX) {
+  const SplitPlan sp = plan_split(m, n, k, max_bytes);
   return sp.splits > 1 ? (int64_t)sp.splits * m * n * 4 : 0;
 }
 
@@ -176,15 +195,16 @@ hipError_t launch_split_math(const GemmProblem& p, const SplitPlan& sp, float* w
   return hipGetLastError();
 }
 
-// The product with a workspace: split when the plan says so and the
-// pipelined kernels take the operands (ws holds at least
-// split_workspace_bytes), otherwise exactly launch_layout.  The output must be
-// contiguous (ldc == n).  A forward product of at most 64 rows (two at most
-// when K is not a multiple of 256) takes the small-row kernels instead (gemm_gemv.h, gemm_rows.h; the workspace goes
-// unused).
+// The product with a workspace: split when the plan (within max_bytes of
+// workspace) says so and the pipelined kernels take the operands (ws holds at
+// least split_workspace_bytes with the same max_bytes), otherwise exactly
+// launch_layout.  The output must be contiguous (ldc == n).  A forward
+// product of at most 64 rows (two at most when K is not a multiple of 256)
+// takes the small-row kernels instead (gemm_gemv.h, gemm_rows.h; the
+// workspace goes unused).
 template <bool AK, bool BK>
-hipError_t launch_layout_ws(const GemmProblem& p, float* ws, hipStream_t stream) {
-  const SplitPlan sp = plan_split(p.m, p.n, p.k);
+hipError_t launch_layout_ws(const GemmProblem& p, float* ws, int64_t max_bytes, hipStream_t stream) {
+  const SplitPlan sp = plan_split(p.m, p.n, p.k, max_bytes);
   if (sp.splits <= 1 || !pipe_ok<AK, BK>(p) || p.ldc != p.n || p.amax || gemv_ok<AK, BK>(p) ||
       rows_ok<AK, BK>(p))
     return launch_layout<AK, BK>(p, stream);

@@ -8,8 +8,8 @@ hipError_t launch_gemm_wgrad(const GemmProblem& p, hipStream_t stream) {
   return gemm_detail::launch_layout<false, false>(p, stream);
 }
 
-hipError_t launch_gemm_wgrad_ws(const GemmProblem& p, float* ws, hipStream_t stream) {
-  return gemm_detail::launch_layout_ws<false, false>(p, ws, stream);
+hipError_t launch_gemm_wgrad_ws(const GemmProblem& p, float* ws, int64_t max_bytes, hipStream_t stream) {
+  return gemm_detail::launch_layout_ws<false, false>(p, ws, max_bytes, stream);
 }
 
 hipError_t launch_gemm_wgrad_group(const GemmProblem* ps, const GroupSlot* plan, const int* idx, int n,

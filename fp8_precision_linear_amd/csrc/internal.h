@@ -89,14 +89,18 @@ hipError_t launch_gemm_dgrad(const GemmProblem& p, hipStream_t stream);  // B co
 hipError_t launch_gemm_wgrad(const GemmProblem& p, hipStream_t stream);  // A, B contraction-strided
 // The same with a workspace (gemm_split.h): an output of too few 128x128 tiles
 // to fill the chip is computed split along the contraction, the slices' raw
-// sums in ws, then added in slice order and unscaled.  ws holds at least
-// gemm_split_workspace_bytes(p.m, p.n, p.k) bytes, 16-byte aligned; the output
-// must be contiguous.  Anything not split runs as launch_gemm_*.
-hipError_t launch_gemm_fwd_ws(const GemmProblem& p, float* ws, hipStream_t stream);
-hipError_t launch_gemm_dgrad_ws(const GemmProblem& p, float* ws, hipStream_t stream);
-hipError_t launch_gemm_wgrad_ws(const GemmProblem& p, float* ws, hipStream_t stream);
-// Workspace bytes the split of an m x n output with contraction k needs (0: not split).
-int64_t gemm_split_workspace_bytes(int64_t m, int64_t n, int64_t k);
+// sums in ws, then added in slice order and unscaled.  The split is planned
+// within max_bytes of workspace; ws holds at least
+// gemm_split_workspace_bytes(p.m, p.n, p.k, max_bytes) bytes, 16-byte
+// aligned; the output must be contiguous.  Anything not split runs as
+// launch_gemm_*.
+hipError_t launch_gemm_fwd_ws(const GemmProblem& p, float* ws, int64_t max_bytes, hipStream_t stream);
+hipError_t launch_gemm_dgrad_ws(const GemmProblem& p, float* ws, int64_t max_bytes, hipStream_t stream);
+hipError_t launch_gemm_wgrad_ws(const GemmProblem& p, float* ws, int64_t max_bytes, hipStream_t stream);
+// Workspace bytes the split of an m x n output with contraction k needs,
+// planned within max_bytes where it can be (0: not split; more than max_bytes
+// only where even the one-workgroup-per-CU split needs more).
+int64_t gemm_split_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t max_bytes);
 
 // Several products run together (fp8_scaled_gemm_group, gemm_group.h).
 constexpr int kGroupMaxProducts = 256;  // products per call

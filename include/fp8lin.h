@@ -256,8 +256,11 @@ int fp8_scaled_gemm(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_t f
  * small batch of tokens; an output with a short side) run faster split along
  * the contraction: each slice's sum goes to a caller-provided workspace, then
  * the slices are added in slice order and unscaled once, so equal inputs give
- * equal bits on every call.  These two entry points are for callers who can
- * provide that workspace; fp8_scaled_gemm never splits.
+ * equal bits on every call.  The number of slices is the cheaper of two:
+ * as many as leave one 128 x 128 workgroup per CU beside the output's tiles,
+ * or as many as leave two (each slice at least 24 stages of 64 contraction
+ * bytes).  These two entry points are for callers who can provide that
+ * workspace; fp8_scaled_gemm never splits.
  *
  * fp8_scaled_gemm_workspace_bytes: the workspace bytes fp8_scaled_gemm_ws
  * needs for this product and shape (0: it is not split and needs none), or
@@ -290,10 +293,12 @@ int fp8_scaled_gemm_ws(fp8_gemm_op_t op, int math, const uint8_t* a, fp8_format_
  * forbid hipMalloc).  The split workspace is the library's own static device
  * array of FP8_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, created with the code
  * object and held until the process ends; the call allocates and frees
- * nothing.  Every split plan with the default FP8LIN_SPLIT_SLOTS fits it
- * (at most 256 / tiles slices of an output of tiles 128 x 128 tiles).
- * Arguments, results and bits are those of fp8_scaled_gemm_ws with a large
- * enough workspace; a product whose split would need more scratch than the
+ * nothing.  Its split takes the plan of fp8_scaled_gemm_ws where that fits
+ * the array, and otherwise the one-workgroup-per-CU split, which with the
+ * default FP8LIN_SPLIT_SLOTS always fits (at most 256 / tiles slices of an
+ * output of tiles 128 x 128 tiles).  Arguments and results are those of
+ * fp8_scaled_gemm_ws (the same bits where the plans agree; else within the
+ * same bound); a product whose split would still need more scratch than the
  * maximum returns FP8_ERR_SIZE before anything runs.  The first call on a
  * device looks up that device's copy of the array (FP8_ERR_HIP if that
  * fails).

@@ -351,8 +351,16 @@ def test_gemm_workspace_bytes():
     assert f(DGRAD, 2048, 3072, 768) == 2 * 2048 * 768 * 4      # dX[M x K], contraction N
     assert f(WGRAD, 3072, 2304, 768) == 2 * 2304 * 768 * 4      # dW[N x K] (108 tiles), contraction M
     assert f(FWD, 2048, 768, 2304) == 0           # 36 stages: two slices would be under 24 stages
-    # 128 x 8192 output (64 tiles), contraction 8192: 4 slices
+    # 128 x 8192 output (64 tiles), contraction 8192: 4 slices (one workgroup
+    # per CU; five, the most of 24 stages, would leave 64 CUs with two)
     assert f(FWD, 128, 8192, 8192) == 4 * 128 * 8192 * 4
+    # 192 x 10240 (160 tiles), contraction 8192: 3 slices, two workgroups on
+    # most CUs (one per CU would leave it unsplit); 65 x 28672 (224 tiles): 2;
+    # 128 x 28672 (224 tiles): none (adding two slices of 14.7 MB costs what
+    # sharing the CUs saves)
+    assert f(FWD, 192, 10240, 8192) == 3 * 192 * 10240 * 4
+    assert f(FWD, 65, 28672, 8192) == 2 * 65 * 28672 * 4
+    assert f(FWD, 128, 28672, 8192) == 0
     # one tile, contraction of 240 stages: 10 slices of 24 stages
     assert f(FWD, 100, 100, 240 * 64) == 10 * 100 * 100 * 4
     assert f(FWD, 8192, 8192, 8192) == 0          # fills the chip
@@ -400,11 +408,13 @@ def test_gemm_noalloc_argument_checks(monkeypatch):
     assert f(0, 0, MIS, 0, A32, A48, 0, A32, 64, 64, 64, A16, None) == status("FP8_ERR_ALIGN")
     assert f(0, 0, A16, 0, A32, A48, 0, A32, -1, 64, 64, A16, None) == status("FP8_ERR_SIZE")
     assert f(0, 0, None, 0, None, None, 0, None, 0, 768, 3072, None, None) == 0
-    # the largest default plan fits exactly: 64 slices of a 4-tile output
+    # the largest plan of one workgroup per CU fits exactly: 64 slices of a 4-tile output
     ws = L.fp8_scaled_gemm_workspace_bytes
     assert ws(0, 256, 256, 64 * 24 * 64) == 64 * 256 * 256 * 4 == fl.NOALLOC_SCRATCH_BYTES
-    assert max(ws(0, m, n, 64 * 24 * 256) for m in (16, 128, 256, 1000, 2048) for n in (16, 128, 512, 2048)) \
-        <= fl.NOALLOC_SCRATCH_BYTES
+    # a caller's workspace may be planned for two workgroups per CU past the
+    # scratch: 192 x 10240 in 3 slices, 23.6 MB (the no-allocation product
+    # then runs it unsplit)
+    assert ws(0, 192, 10240, 8192) == 3 * 192 * 10240 * 4 > fl.NOALLOC_SCRATCH_BYTES
     # more planned slots: a 4-tile output split 256 ways needs 64 MiB
     monkeypatch.setenv("FP8LIN_SPLIT_SLOTS", "4096")
     assert ws(0, 256, 256, 256 * 24 * 64) == 256 * 256 * 256 * 4
@@ -413,9 +423,14 @@ def test_gemm_noalloc_argument_checks(monkeypatch):
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on a real device")
 def test_gemm_noalloc_without_a_device_reports_no_device():
+    """Past the size checks, the call needs a device: products split, unsplit,
+    and split by a plan smaller than a caller's workspace would get (its own
+    fits the static scratch, so no size error)."""
     f = L.fp8_scaled_gemm_noalloc
     assert f(0, 0, A16, 0, A32, A48, 0, A32, 2048, 768, 3072, A16, None) == status("FP8_ERR_DEVICE")
     assert f(0, 0, A16, 0, A32, A48, 0, A32, 8192, 8192, 8192, A16, None) == status("FP8_ERR_DEVICE")
+    assert L.fp8_scaled_gemm_workspace_bytes(0, 192, 10240, 8192) > fl.NOALLOC_SCRATCH_BYTES
+    assert f(0, 0, A16, 0, A32, A48, 0, A32, 192, 10240, 8192, A16, None) == status("FP8_ERR_DEVICE")
 
 
 def _qdesc(x=A16, n=10, dtype=0, fmt=0, margin=0, y=A48, amax=A32, bias=A32):

@@ -82,3 +82,34 @@ def test_noalloc_native_arithmetic_matches_the_workspace_entry_point(fl):
         got = fl.scaled_gemm_noalloc(0, A, E4M3, BA, B, E4M3, BB, out, math=fl.MATH_NATIVE_FP8)
         torch.cuda.synchronize()
         assert torch.equal(got.view(torch.int32), want.view(torch.int32)), (M, N, K)
+
+
+def test_noalloc_plans_within_its_scratch(fl):
+    """A caller's workspace may be planned for two workgroups per CU; the
+    no-allocation product takes that plan only where it fits the static
+    scratch.  65 x 28672 (224 tiles of 128 x 128, contraction 8192): two
+    slices, 14.9 MB, the same plan both ways, the same bits.  192 x 10240
+    (160 tiles): three slices, 23.6 MB, past the scratch, so the
+    no-allocation product runs unsplit -- the bits of fp8_scaled_gemm; the
+    split result within the oracle's bound.  Sampled outputs (the last rows
+    and columns among them) against the oracle."""
+    rng = np.random.default_rng(11)
+    for (M, N, K), same_plan in (((65, 28672, 8192), True), ((192, 10240, 8192), False)):
+        a8, b8, shape = _operands(rng, 0, M, N, K, E4M3, E4M3)
+        A, B, BA, BB = u8_dev(a8), u8_dev(b8), i32_dev(2), i32_dev(-1)
+        nbytes = fl.gemm_workspace_bytes(0, M, N, K)
+        assert (nbytes <= fl.NOALLOC_SCRATCH_BYTES) == same_plan, nbytes
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        say("noalloc plan", M, N, K, "workspace plan bytes", nbytes)
+        split = fl.scaled_gemm(0, A, E4M3, BA, B, E4M3, BB, workspace=ws)
+        plain = fl.scaled_gemm(0, A, E4M3, BA, B, E4M3, BB)
+        out = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+        got = fl.scaled_gemm_noalloc(0, A, E4M3, BA, B, E4M3, BB, out)
+        torch.cuda.synchronize()
+        want = split if same_plan else plain
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32)), (M, N, K)
+        rows = np.concatenate([rng.integers(0, M, 300), M - 1 - np.arange(20)])
+        cols = np.concatenate([rng.integers(0, N, 300), N - 1 - np.arange(20)])
+        ref, bound = oracle.gemm_fwd_at(a8, E4M3, 2, b8, E4M3, -1, rows, cols)
+        for name, res in (("noalloc", got), ("split", split)):
+            check_gemm(res.cpu().numpy()[rows, cols], ref, bound, f"{name} {M}x{N}x{K}")
