@@ -219,9 +219,11 @@ def epilogue_accumulate(fl, w, plan, q, outs, math, op_of, reps=9):
             "gemm_then_add_pass_us": round(t_sep, 1), "saved_us": round(t_sep - t_fused, 1)}
 
 
-def small_batch_products(fl, w, plan, q, math, op_of, rows=(1, 8, 32, 64), reps=20):
+def small_batch_products(fl, w, plan, q, math, op_of, rows=(1, 8, 32, 64, 128, 256), reps=20):
     """The step's forward weights with only a few rows of activations (a
-    served model decoding a small batch): each product alone, `reps` calls
+    served model decoding a small batch; 128 and 256 rows run the tiled
+    kernels split along the contraction in the workspace the call is given):
+    each product alone, `reps` calls
     back to back between events after a spin kernel, for each row count;
     the rate at which its weight streams from HBM.  The activation rows are
     the step's own codes (its first rows)."""
