@@ -9,13 +9,14 @@
 // point", review page, "Proposed method", bullet 3 (the product of the scaled
 // FP8 operands, unscaled after the matmul) and bullet 5 (inference).
 //
-// One workgroup of eight waves per 32 output columns (32 rows of W) and all M
-// rows (RB blocks of 32).  Stage = 256 contraction bytes: a 32 x 256-byte tile
-// of W and RB of X (X's rows past M re-read row M - 1 and are zeroed in the
-// fragments), SL stages in a ring (2 or 3, chosen by launch_rows), SL - 1 in
-// flight.  Wave w multiplies bytes [32w, 32w + 32) of every stage (two
-// 32x32x16 MFMAs per row block) into its own partial sums; the eight waves'
-// partial sums meet in LDS and are added in wave order, then unscaled once.
+// One workgroup of eight waves per 32 x CN output columns (CN tiles of 32 rows
+// of W) and all M rows (RB blocks of 32).  Stage = 256 contraction bytes: CN
+// 32 x 256-byte tiles of W and RB of X (X's rows past M re-read row M - 1 and
+// are zeroed in the fragments), SL stages in a ring (2 or 3, chosen by
+// launch_rows), SL - 1 in flight.  Wave w multiplies bytes [32w, 32w + 32) of
+// every stage (two 32x32x16 MFMAs per row block and column tile) into its own
+// partial sums; the eight waves' partial sums meet in LDS and are added in
+// wave order, then unscaled once.
 //
 // Stage order: workgroup b starts at stage 5b mod (K / 256) and wraps.  Where
 // W's rows lie a power of two apart (K = 8192), workgroups that walk the
@@ -54,59 +55,78 @@ __device__ __forceinline__ void rows_dma(const uint8_t* base, int64_t ld, int r0
   dma16(base + (int64_t)gr * ld + (int64_t)s * kRowsStage + 16 * lc, tile + wave * 1024);
 }
 
-template <int FA, int FB, int MATH, bool ACC, int RB, int SL>
+template <int FA, int FB, int MATH, bool ACC, int RB, int SL, int CN>
 __global__ __launch_bounds__(kRowsWaves * 64) void gemm_rows_kernel(GemmProblem p) {
-  // ring of SL stages: slot s holds W's tile at s * (1 + RB) * 8 KB and X's RB
-  // tiles after it; at the end it holds the eight waves' partial sums
-  // (RB * 32 KB)
-  constexpr int kSlot = (1 + RB) * kRowsTile;
-  static_assert(kRowsWaves * RB * 32 * 32 * 4 <= SL * kSlot, "partial sums fit the ring");
+  // ring of SL stages: slot s holds W's CN tiles (32 rows each) at
+  // s * (CN + RB) * 8 KB and X's RB tiles after them; at the end it holds the
+  // eight waves' partial sums, kChunk row blocks (CN * 32 KB each) at a time
+  constexpr int kSlot = (CN + RB) * kRowsTile;
+  constexpr int kFit = SL * kSlot / (kRowsWaves * 32 * 32 * CN * 4);
+  constexpr int kChunk = RB <= kFit ? RB : 1;
+  static_assert(kFit >= 1, "partial sums fit the ring");
   __shared__ __attribute__((aligned(1024))) uint8_t ring[SL * kSlot];
   const int lane = (int)threadIdx.x & 63, wave = wave_id();
   const int rl = lane & 31, h = lane >> 5;
-  const int n0 = (int)blockIdx.x * 32;
+  const int n0 = (int)blockIdx.x * 32 * CN;
   const uint32_t ring0 = lds_addr(ring);
   const int nk = p.k / kRowsStage;
   const int rot = (int)((blockIdx.x * 5u) % (uint32_t)max(nk, 1));
   auto issue = [&](int s, int slot) {
     const uint32_t t = ring0 + slot * kSlot;
     const int se = s + rot < nk ? s + rot : s + rot - nk;
-    rows_dma(p.b, p.ldb, n0, p.n, se, t, wave, lane);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) rows_dma(p.a, p.lda, 32 * rb, p.m, se, t + (1 + rb) * kRowsTile, wave, lane);
+    for (int cn = 0; cn < CN; ++cn) rows_dma(p.b, p.ldb, n0 + 32 * cn, p.n, se, t + cn * kRowsTile, wave, lane);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) rows_dma(p.a, p.lda, 32 * rb, p.m, se, t + (CN + rb) * kRowsTile, wave, lane);
   };
   // this lane's fragment: logical chunk 2 wave + h of row rl
   const uint32_t frag = rl * kRowsStage + (rows_swz(rl, 2 * wave + h) << 4);
 
-  v16f acc[RB][1];
+  v16f acc[RB][CN];
   zero_acc(acc);
 #pragma unroll
   for (int s = 0; s < SL - 1; ++s)
     if (s < nk) issue(s, s);
   int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    wait_stages<1 + RB>(min(SL - 2, nk - 1 - kt));
+    wait_stages<CN + RB>(min(SL - 2, nk - 1 - kt));
     bare_barrier();
     if (kt + SL - 1 < nk) issue(kt + SL - 1, slot == 0 ? SL - 1 : slot - 1);
     typedef int v4i __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) const v4i* lds_v4i;
     const uint32_t t = ring0 + slot * kSlot + opaque(frag);
-    const v4i w = *(lds_v4i)(uintptr_t)t;
+    v4i w[CN], x[RB];
+#pragma unroll
+    for (int cn = 0; cn < CN; ++cn) w[cn] = *(lds_v4i)(uintptr_t)(t + cn * kRowsTile);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      v4i x = *(lds_v4i)(uintptr_t)(t + (1 + rb) * kRowsTile);
-      if (32 * rb + rl >= p.m) x = v4i{0, 0, 0, 0};
-      // two 32x32x16 steps over the lane's 16 bytes (8 contraction values each)
+      x[rb] = *(lds_v4i)(uintptr_t)(t + (CN + rb) * kRowsTile);
+      if (32 * rb + rl >= p.m) x[rb] = v4i{0, 0, 0, 0};
+    }
+    // two 32x32x16 steps over the lane's 16 bytes (8 contraction values each)
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        if constexpr (MATH == kMathExactBf16) {
-          const v8bf a = fp8x8_to_bf16<FA>(x[2 * q], x[2 * q + 1]);
-          const v8bf b = fp8x8_to_bf16<FB>(w[2 * q], w[2 * q + 1]);
-          acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[rb][0], 0, 0, 0);
-        } else {
-          const v8h a = fp8x8_to_f16<FA>(x[2 * q], x[2 * q + 1]);
-          const v8h b = fp8x8_to_f16<FB>(w[2 * q], w[2 * q + 1]);
-          acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[rb][0], 0, 0, 0);
+    for (int q = 0; q < 2; ++q) {
+      if constexpr (MATH == kMathExactBf16) {
+        v8bf b[CN];
+#pragma unroll
+        for (int cn = 0; cn < CN; ++cn) b[cn] = fp8x8_to_bf16<FB>(w[cn][2 * q], w[cn][2 * q + 1]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const v8bf a = fp8x8_to_bf16<FA>(x[rb][2 * q], x[rb][2 * q + 1]);
+#pragma unroll
+          for (int cn = 0; cn < CN; ++cn)
+            acc[rb][cn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[cn], acc[rb][cn], 0, 0, 0);
+        }
+      } else {
+        v8h b[CN];
+#pragma unroll
+        for (int cn = 0; cn < CN; ++cn) b[cn] = fp8x8_to_f16<FB>(w[cn][2 * q], w[cn][2 * q + 1]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const v8h a = fp8x8_to_f16<FA>(x[rb][2 * q], x[rb][2 * q + 1]);
+#pragma unroll
+          for (int cn = 0; cn < CN; ++cn)
+            acc[rb][cn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[cn], acc[rb][cn], 0, 0, 0);
         }
       }
     }
@@ -117,36 +137,41 @@ __global__ __launch_bounds__(kRowsWaves * 64) void gemm_rows_kernel(GemmProblem 
   // is in flight (the last stage was waited for): the ring takes the partial
   // sums.  32x32 accumulator layout: register r of lane l holds row
   // 8 * (r / 4) + 4 * (l / 32) + r % 4 and column l % 32.
-  __syncthreads();
-  float (*part)[RB * 32][32] = reinterpret_cast<float (*)[RB * 32][32]>(ring);
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) part[wave][32 * rb + 8 * (r >> 2) + 4 * h + (r & 3)][rl] = acc[rb][0][r];
-  __syncthreads();
-
   const int unscale = -(*p.bias_a + *p.bias_b);
   uint32_t mx = 0;
+  float (*part)[kChunk * 32][32 * CN] = reinterpret_cast<float (*)[kChunk * 32][32 * CN]>(ring);
 #pragma unroll
-  for (int o = (int)threadIdx.x; o < RB * 32 * 32; o += kRowsWaves * 64) {
-    const int row = o / 32, col = o % 32;
-    float sum = part[0][row][col];
+  for (int c0 = 0; c0 < RB; c0 += kChunk) {
+    __syncthreads();
 #pragma unroll
-    for (int w2 = 1; w2 < kRowsWaves; ++w2) sum += part[w2][row][col];
-    if (row < p.m && n0 + col < p.n) {
-      float* c = p.c + (int64_t)row * p.ldc + n0 + col;
-      float v = __builtin_ldexpf(sum, unscale);
-      if constexpr (ACC) v = *c + v;
-      *c = v;
-      mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu);
+    for (int rb = 0; rb < kChunk; ++rb)
+#pragma unroll
+      for (int cn = 0; cn < CN; ++cn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          part[wave][32 * rb + 8 * (r >> 2) + 4 * h + (r & 3)][32 * cn + rl] = acc[c0 + rb][cn][r];
+    __syncthreads();
+#pragma unroll
+    for (int o = (int)threadIdx.x; o < kChunk * 32 * 32 * CN; o += kRowsWaves * 64) {
+      const int lr = o / (32 * CN), col = o % (32 * CN), row = 32 * c0 + lr;
+      float sum = part[0][lr][col];
+#pragma unroll
+      for (int w2 = 1; w2 < kRowsWaves; ++w2) sum += part[w2][lr][col];
+      if (row < p.m && n0 + col < p.n) {
+        float* c = p.c + (int64_t)row * p.ldc + n0 + col;
+        float v = __builtin_ldexpf(sum, unscale);
+        if constexpr (ACC) v = *c + v;
+        *c = v;
+        mx = max(mx, __float_as_uint(v) & 0x7FFFFFFFu);
+      }
     }
   }
   if (p.amax) amax_fold(mx, p.amax);
 }
 
 // Whether a product takes this kernel: the forward layout (both operands
-// contraction-contiguous), exact arithmetic, 3 to 32 output rows, whole
-// 256-byte stages, 16-byte aligned rows.
+// contraction-contiguous), exact arithmetic, 1 to kRowsMax output rows, whole
+// 256-byte stages, 16-byte aligned rows, fewer than 2^28 columns.
 template <bool AK, bool BK>
 bool rows_ok(const GemmProblem& p) {
   if constexpr (!(AK && BK)) {
@@ -161,12 +186,12 @@ bool rows_ok(const GemmProblem& p) {
   }
 }
 
-template <int MATH, bool ACC, int RB, int SL>
+template <int MATH, bool ACC, int RB, int SL, int CN = 1>
 hipError_t launch_rows_acc(const GemmProblem& p, hipStream_t stream) {
-  const dim3 grid((uint32_t)((p.n + 31) / 32)), block(kRowsWaves * 64);
+  const dim3 grid((uint32_t)((p.n + 32 * CN - 1) / (32 * CN))), block(kRowsWaves * 64);
 #define FP8LIN_ROWS_CASE(FA, FB)                                                                        \
   if (p.fmt_a == FA && p.fmt_b == FB) {                                                                 \
-    hipLaunchKernelGGL((gemm_rows_kernel<FA, FB, MATH, ACC, RB, SL>), grid, block, 0, stream, p);     \
+    hipLaunchKernelGGL((gemm_rows_kernel<FA, FB, MATH, ACC, RB, SL, CN>), grid, block, 0, stream, p); \
     return hipGetLastError();                                                                           \
   }
   FP8LIN_ROWS_CASE(FP8_E4M3, FP8_E4M3)
@@ -185,16 +210,31 @@ hipError_t launch_rows_acc(const GemmProblem& p, hipStream_t stream) {
 // and the rows are few (28672 x 8192 weights at 1, 8, 16 rows: 33.0, 33.6,
 // 34.7 against 36.3, 36.0, 36.3 us; 57344 x 8192 at 24 rows 89 against 97;
 // from 28 rows mixed: 32768 x 4096 at 32 rows 21.7 against 20.8; with 256 or
-// 320 workgroups two stages lose up to 60%).  33 to 64 rows: two row blocks in
-// three stages (72 KB, two workgroups per CU; four stages, 96 KB, leave one
-// and were slower where the grid exceeds the CUs: 28672 x 8192 weights at 64
-// rows 58.0 against 47.7 us).
+// 320 workgroups two stages lose up to 60%).  From 25 rows over 768 or more
+// column tiles, two column tiles per workgroup: X's tiles, which every
+// workgroup reads, then cost half as much per weight byte (25-32 rows in
+// three stages, 72 KB: 28672 x 8192 weights 34.2-34.7 against 36.3-37.0 us,
+// 57344 x 8192 91-92 against 98-101).  33 to 64 rows: two row blocks; over
+// 768 or more column tiles two column tiles per workgroup in two stages
+// (64 KB, two workgroups per CU: 28672 x 8192 at 33 / 64 rows 37.4 / 38.5
+// against 44.8 / 48.3 us), else one in three stages (72 KB; two column tiles
+// on 256 workgroups or fewer leave CUs idle: 8192 x 28672 at 64 rows 77
+// against 49 us; four stages, 96 KB, one workgroup per CU, were slower:
+// 28672 x 8192 at 64 rows 58.0 against 47.7 us).
 template <int MATH>
 hipError_t launch_rows(const GemmProblem& p, hipStream_t stream) {
-  if (p.m <= 24 && p.n >= 768 * 32)
+  const bool wide = p.n >= 768 * 32;
+  if (p.m <= 24 && wide)
     return p.accumulate ? launch_rows_acc<MATH, true, 1, 2>(p, stream) : launch_rows_acc<MATH, false, 1, 2>(p, stream);
-  if (p.m <= 32)
+  if (p.m <= 32) {
+    if (wide)
+      return p.accumulate ? launch_rows_acc<MATH, true, 1, 3, 2>(p, stream)
+                          : launch_rows_acc<MATH, false, 1, 3, 2>(p, stream);
     return p.accumulate ? launch_rows_acc<MATH, true, 1, 3>(p, stream) : launch_rows_acc<MATH, false, 1, 3>(p, stream);
+  }
+  if (wide)
+    return p.accumulate ? launch_rows_acc<MATH, true, 2, 2, 2>(p, stream)
+                        : launch_rows_acc<MATH, false, 2, 2, 2>(p, stream);
   return p.accumulate ? launch_rows_acc<MATH, true, 2, 3>(p, stream) : launch_rows_acc<MATH, false, 2, 3>(p, stream);
 }
 

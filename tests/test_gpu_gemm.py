@@ -168,14 +168,16 @@ def test_one_and_two_row_forward_products(fl, fa, fb):
 # in the row-streaming MFMA kernel: stages of 256 contraction bytes over 32
 # weight rows through LDS DMA, each workgroup starting at its own stage and
 # wrapping, eight waves' partial sums added in a fixed order.  One row block
-# (1 to 32 rows; two-stage ring for at most 24 rows over 768 or more column
-# tiles, three stages otherwise) and two (33 to 64), ragged and small column
-# counts, one stage
+# (1 to 32 rows; over 768 or more column tiles a two-stage ring up to 24 rows
+# and two column tiles per workgroup from 25, three stages otherwise) and two
+# (33 to 64; over 768 or more column tiles two of them per workgroup in two
+# stages), ragged and small column counts, one stage
 # (K = 256), 43 stages (K = 11008) and long contractions, K = 0, a contraction
 # the kernel does not take (K % 256 != 0: the tiled kernels), 65 rows (the
 # tiled kernels).
 ROWS_SHAPES = [(1, 4103, 8192), (2, 96, 32768), (3, 1000, 256), (8, 33, 11008), (17, 4103, 2048),
                (2, 24600, 512), (8, 28672, 256), (24, 24576, 256), (25, 24600, 256),
+               (32, 24600, 512), (40, 24600, 512), (64, 24576, 256),
                (32, 96, 28672), (31, 1, 512), (33, 1000, 256), (48, 77, 11008), (64, 1000, 8192),
                (5, 40, 0), (64, 40, 0), (8, 300, 320), (65, 64, 512)]
 
